@@ -1,0 +1,235 @@
+"""Plain CPU oracle of one RTPurbo decode step (fp64 masses and attention).
+
+TEST INFRASTRUCTURE.  Only the test-suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code
+with the HIP library and never imports it; both take their inputs from the
+``workloads`` generator.
+
+The arithmetic lives in ``rtp_oracle.c`` (plain loops, single thread); this
+module converts arrays and walks the heads of a layer:
+
+* retrieval query heads: indexer score -> 256-bin histogram top-p -> exact
+  softmax attention over the selected rows (Full Attention Strikes Back,
+  xllm-io paper review, section 三 核心公式, the two adaptive-sparse-attention
+  equations; section 三 硬件感知解码内核 for the histogram);
+* local query heads: exact softmax attention over the 4 sink tokens and the
+  last 8192 positions (same page, section 五, test-configuration table;
+  gist.science summary, section 1: local heads use a sliding window with
+  attention sinks).
+
+Readings taken where the pages are silent (bin grid, threshold bin kept whole,
+p >= 1 keeps every token, window includes the current token, a ring slot
+layout for local heads) are stated next to the functions that use them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+from typing import Dict, List, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rtp_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+NBINS = 256
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (host only, no contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+                               "-shared", "-std=c99", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        L.rtpo_half_to_double.restype = ctypes.c_double
+        L.rtpo_half_to_double.argtypes = [ctypes.c_uint16]
+        L.rtpo_index_score.restype = None
+        L.rtpo_index_score.argtypes = [P, P, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                       ctypes.c_float, P]
+        L.rtpo_topp_select.restype = ctypes.c_int64
+        L.rtpo_topp_select.argtypes = [P, ctypes.c_int64, ctypes.c_double, ctypes.c_double, P, P,
+                                       P, P]
+        L.rtpo_attention.restype = None
+        L.rtpo_attention.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int64,
+                                     ctypes.c_double, P, P]
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float16:
+        return 1
+    if a.dtype == np.float32:
+        return 0
+    raise TypeError("oracle takes fp16 or fp32 arrays, got %s" % a.dtype)
+
+
+def np_of(x) -> np.ndarray:
+    """numpy view of a CPU array or torch tensor (no arithmetic)."""
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(x)
+
+
+# ----------------------------------------------------------------------------
+# single-purpose functions
+# ----------------------------------------------------------------------------
+def index_score(q_idx, k_idx, scale: float) -> np.ndarray:
+    """z[n] = fl32(scale * fp32-fma-chain(q_idx, k_idx[n])) for k_idx [L, r]."""
+    q = np.ascontiguousarray(q_idx, dtype=np.float32)
+    k = np.ascontiguousarray(k_idx)
+    L, r = k.shape
+    assert q.shape == (r,)
+    z = np.empty(L, dtype=np.float32)
+    kk = k.view(np.uint16) if k.dtype == np.float16 else k
+    lib().rtpo_index_score(_ptr(q), _ptr(kk), _dtype_code(k), L, r, ctypes.c_float(scale), _ptr(z))
+    return z
+
+
+@dataclass
+class Selection:
+    idx: np.ndarray       # ascending int32 token indices
+    hist: np.ndarray      # [256] fp64 bin masses relative to exp((A+1) w)
+    A: int                # top occupied cell
+    bstar: int            # threshold bin
+
+    @property
+    def count(self) -> int:
+        return int(self.idx.shape[0])
+
+
+def topp_select(z, p: float, bin_width: float = 0.125) -> Selection:
+    """256-bin histogram top-p over one head's logits z[0:L] (see rtp_oracle.c)."""
+    zz = np.ascontiguousarray(z, dtype=np.float32)
+    L = zz.shape[0]
+    assert L >= 1 and np.all(np.isfinite(zz)), "oracle requires L >= 1 and finite logits"
+    sel = np.empty(L, dtype=np.int32)
+    hist = np.empty(NBINS, dtype=np.float64)
+    A = ctypes.c_int64()
+    b = ctypes.c_int32()
+    n = lib().rtpo_topp_select(_ptr(zz), L, float(p), float(bin_width), _ptr(sel), _ptr(hist),
+                               ctypes.byref(A), ctypes.byref(b))
+    return Selection(sel[:n].copy(), hist, int(A.value), int(b.value))
+
+
+def cells(z, bin_width: float = 0.125) -> np.ndarray:
+    """g_n = floor(z_n / w) (exact for a power-of-two w)."""
+    return np.floor(np.asarray(z, dtype=np.float32).astype(np.float64) / bin_width).astype(np.int64)
+
+
+def select_with_bstar(z, A: int, bstar: int, bin_width: float = 0.125) -> np.ndarray:
+    """The rule's set for a given (A, b*): { n : min(A - g_n, 255) <= b* }."""
+    j = np.minimum(A - cells(z, bin_width), NBINS - 1)
+    return np.nonzero(j <= bstar)[0].astype(np.int32)
+
+
+def attention(q, K, V, rows, scale: float):
+    """fp64 softmax attention of q [d] over rows of K, V ([N, d], fp16 or fp32)."""
+    qq = np.ascontiguousarray(np.asarray(q).astype(np.float64))
+    KK = np.ascontiguousarray(K)
+    VV = np.ascontiguousarray(V)
+    assert KK.dtype == VV.dtype
+    d = KK.shape[-1]
+    rr = np.ascontiguousarray(rows, dtype=np.int64)
+    assert rr.size >= 1
+    out = np.empty(d, dtype=np.float64)
+    lse = ctypes.c_double()
+    kv = (lambda a: a.view(np.uint16)) if KK.dtype == np.float16 else (lambda a: a)
+    lib().rtpo_attention(_ptr(qq), _ptr(kv(KK)), _ptr(kv(VV)), _dtype_code(KK), d, _ptr(rr),
+                         rr.size, float(scale), _ptr(out), ctypes.byref(lse))
+    return out, float(lse.value)
+
+
+def window_positions(L: int, window: int, sinks: int) -> np.ndarray:
+    """Positions a local head attends to: the first `sinks` positions and the last
+    `window` positions (the current token included), each counted once."""
+    first = np.arange(min(sinks, L), dtype=np.int64)
+    rest = np.arange(max(sinks, L - window), L, dtype=np.int64)
+    return np.concatenate([first, rest])
+
+
+def ring_slot(pos: np.ndarray, window: int, sinks: int) -> np.ndarray:
+    """Ring layout of a local head's cache: sink position n < sinks in slot n, any later
+    position n in slot sinks + (n mod window)."""
+    pos = np.asarray(pos, dtype=np.int64)
+    return np.where(pos < sinks, pos, sinks + pos % window)
+
+
+# ----------------------------------------------------------------------------
+# one decode step over a layer
+# ----------------------------------------------------------------------------
+@dataclass
+class HeadResult:
+    out: np.ndarray
+    lse: float
+    sel: Optional[Selection] = None
+
+
+def decode_layer(layer, seq_lens, Hq: int, Hkv: int, p: float, bin_width: float,
+                 scale_idx: float, scale_attn: float, window: int, sinks: int,
+                 heads: Optional[List[int]] = None, batches: Optional[List[int]] = None
+                 ) -> Dict[tuple, HeadResult]:
+    """Oracle outputs of one layer keyed by (b, query head).  `heads` / `batches`
+    restrict the work to a sample of query heads / sequences."""
+    G = Hq // Hkv
+    mask = np.asarray(layer.kv_is_retrieval)
+    ret = [int(h) for h in np.nonzero(mask)[0]]
+    loc = [int(h) for h in np.nonzero(mask == 0)[0]]
+    q = np_of(layer.q)
+    q_idx = np_of(layer.q_idx)
+    res = {}
+    B = len(seq_lens)
+    for b in (batches if batches is not None else range(B)):
+        L = int(seq_lens[b])
+        for kh in range(Hkv):
+            for g in range(G):
+                h = kh * G + g
+                if heads is not None and h not in heads:
+                    continue
+                if mask[kh]:
+                    kr = ret.index(kh)
+                    kidx = np_of(layer.k_idx[b, kr, :L])
+                    z = index_score(q_idx[b, h], kidx, scale_idx)
+                    s = topp_select(z, p, bin_width)
+                    Kh = np_of(layer.K_ret[b, kr, :L])
+                    Vh = np_of(layer.V_ret[b, kr, :L])
+                    o, lse = attention(q[b, h], Kh, Vh, s.idx, scale_attn)
+                    res[(b, h)] = HeadResult(o, lse, s)
+                else:
+                    kl = loc.index(kh)
+                    rows = ring_slot(window_positions(L, window, sinks), window, sinks)
+                    Kh = np_of(layer.K_loc[b, kl])
+                    Vh = np_of(layer.V_loc[b, kl])
+                    o, lse = attention(q[b, h], Kh, Vh, rows, scale_attn)
+                    res[(b, h)] = HeadResult(o, lse, None)
+    return res
+
+
+def decode_step(wl, layers: Optional[List[int]] = None, heads=None, batches=None):
+    """Oracle outputs for a whole workload: list (per layer) of {(b, h): HeadResult}."""
+    out = []
+    for li, layer in enumerate(wl.layers):
+        if layers is not None and li not in layers:
+            out.append({})
+            continue
+        out.append(decode_layer(layer, wl.seq_lens, wl.Hq, wl.Hkv, wl.p, wl.bin_width,
+                                wl.scale_idx, wl.scale_attn, wl.window, wl.sinks, heads, batches))
+    return out

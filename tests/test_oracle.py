@@ -1,0 +1,368 @@
+"""Pins of the CPU oracle against what the method and the mathematics fix.
+
+None of these compares the oracle with a copy of itself: they check hand-worked
+examples (tests/golden/worked_examples.json), exact small-integer cases, error
+bounds, the exact sort-based top-p the histogram rule must contain, textbook
+dense attention (torch's scaled_dot_product_attention in fp64), and invariants
+of the rule (monotone in p, permutation equivariant, shift invariant).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+def gold():
+    with open(GOLD) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# fp16 decoding
+# ---------------------------------------------------------------------------
+def test_half_decode_matches_numpy_for_every_finite_pattern():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    f = oracle.lib().rtpo_half_to_double
+    got = np.array([f(int(b)) for b in bits])
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.all(np.isinf(got[np.isinf(ref)]))
+    assert np.all(np.isnan(got[np.isnan(ref)]))
+
+
+# ---------------------------------------------------------------------------
+# indexer score
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", [np.float16, np.float32])
+def test_index_score_exact_on_small_integers(dt):
+    # every product and partial sum is a small integer: the fma chain is exact and
+    # z must equal scale * (q . k) exactly, for every token and every dimension.
+    rng = np.random.default_rng(11)
+    L, r = 257, 16
+    q = rng.integers(-20, 21, r).astype(np.float32)
+    k = rng.integers(-30, 31, (L, r)).astype(dt)
+    z = oracle.index_score(q, k, 0.25)
+    exact = 0.25 * (k.astype(np.int64) @ q.astype(np.int64))
+    assert np.array_equal(z.astype(np.float64), exact.astype(np.float64))
+
+
+def test_index_score_each_dimension_counts():
+    # a one-hot key picks exactly one q component: catches dropped or shifted terms
+    r = 16
+    q = (np.arange(r, dtype=np.float32) + 1.0) * np.float32(1.5)
+    k = np.eye(r, dtype=np.float16)
+    z = oracle.index_score(q, k, 0.5)
+    assert np.array_equal(z, (0.5 * q).astype(np.float32))
+
+
+def test_index_score_within_fma_chain_error_bound():
+    rng = np.random.default_rng(12)
+    L, r = 4096, 16
+    q = (rng.standard_normal(r) * 4).astype(np.float32)
+    k = rng.standard_normal((L, r)).astype(np.float16)
+    z = oracle.index_score(q, k, 0.25).astype(np.float64)
+    prod = k.astype(np.float64) * q.astype(np.float64)[None, :]
+    exact = 0.25 * prod.sum(1)
+    bound = 0.25 * (r + 1) * 2.0 ** -24 * np.abs(prod).sum(1) + 2.0 ** -24 * np.abs(exact)
+    assert np.all(np.abs(z - exact) <= bound)
+    # and a transposed / wrong-head query would be far outside the bound
+    z_bad = oracle.index_score(q[::-1].copy(), k, 0.25).astype(np.float64)
+    assert np.mean(np.abs(z_bad - exact) > bound) > 0.9
+
+
+# ---------------------------------------------------------------------------
+# histogram top-p: hand-worked examples
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("ex", gold()["select"], ids=lambda e: e["name"])
+def test_worked_example_select(ex):
+    z = np.array(ex["z"], dtype=np.float32)
+    s = oracle.topp_select(z, ex["p"], ex["w"])
+    assert s.A == ex["A"]
+    assert s.bstar == ex["bstar"]
+    assert s.idx.tolist() == ex["S"]
+    assert oracle.cells(z, ex["w"]).tolist() == ex["cells"]
+    Z = s.hist.sum()
+    assert abs(Z - ex["Z"]) < 1e-6
+    for j, m in ex["masses"].items():
+        assert abs(s.hist[int(j)] - m) < 1e-6
+    nz = {int(j) for j in ex["masses"]}
+    for j in range(256):
+        if j not in nz and j != 255:
+            assert s.hist[j] == 0.0
+    assert abs(s.hist[:s.bstar + 1].sum() / Z - ex["mass_frac"]) < 1e-6
+    assert set(ex["exact_topp"]) <= set(s.idx.tolist())
+
+
+@pytest.mark.parametrize("ex", gold()["attention"], ids=lambda e: e["name"])
+def test_worked_example_attention(ex):
+    K = np.array(ex["K"], dtype=np.float32)
+    V = np.array(ex["V"], dtype=np.float32)
+    o, lse = oracle.attention(np.array(ex["q"]), K, V, ex["S"], ex["scale"])
+    assert np.allclose(o, ex["out"], atol=1e-6)
+    s = np.array([ex["scale"] * 1.0, 0.0])
+    assert abs(lse - math.log(np.exp(s).sum())) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# histogram top-p: exact top-p containment and invariants
+# ---------------------------------------------------------------------------
+def exact_topp(z, p):
+    """Exact top-p by sorting: the shortest prefix of tokens in descending logit order
+    whose softmax mass reaches p (fp64)."""
+    z64 = np.asarray(z, dtype=np.float64)
+    e = np.exp(z64 - z64.max())
+    order = np.argsort(-z64, kind="stable")
+    cum = np.cumsum(e[order])
+    k = int(np.searchsorted(cum, p * cum[-1] * (1 - 1e-12))) + 1
+    return order[:min(k, len(z64))], e
+
+
+def _logit_sets():
+    rng = np.random.default_rng(2024)
+    out = []
+    for L in [1, 2, 3, 7, 64, 255, 256, 1000, 4099]:
+        for sig in [0.05, 1.0, 3.0, 12.0]:
+            out.append(("g%d_%g" % (L, sig), (sig * rng.standard_normal(L)).astype(np.float32)))
+    # planted spikes on a flat background
+    z = rng.standard_normal(5000).astype(np.float32)
+    z[rng.choice(5000, 3, replace=False)] = 14.0
+    out.append(("spike3", z))
+    # broad: many moderately high tokens
+    z = (rng.standard_normal(8000) - 5).astype(np.float32)
+    z[rng.choice(8000, 800, replace=False)] = (2 + 0.7 * rng.standard_normal(800)).astype(np.float32)
+    out.append(("broad", z))
+    # ties and values exactly on cell edges
+    out.append(("allequal", np.full(300, 1.7, dtype=np.float32)))
+    out.append(("edges", (rng.integers(-80, 40, 2000) * 0.125).astype(np.float32)))
+    out.append(("coarse", (rng.integers(-8, 8, 500) * 0.5).astype(np.float32)))
+    # huge range: tail bin populated
+    z = (rng.standard_normal(3000) * 20).astype(np.float32)
+    out.append(("wide", z))
+    out.append(("neg", (-1000 + rng.standard_normal(700)).astype(np.float32)))
+    return out
+
+
+LOGITS = _logit_sets()
+PS = [0.1, 0.5, 0.8, 0.9, 0.95, 0.999]
+
+
+@pytest.mark.parametrize("name,z", LOGITS, ids=[n for n, _ in LOGITS])
+def test_rule_contains_exact_topp_and_reaches_p(name, z):
+    L = len(z)
+    prev = None
+    for p in PS:
+        s = oracle.topp_select(z, p)
+        idx = s.idx
+        assert 1 <= len(idx) <= L
+        assert np.all(np.diff(idx) > 0) and idx[0] >= 0 and idx[-1] < L
+        ex, e = exact_topp(z, p)
+        assert set(ex.tolist()) <= set(idx.tolist()), (name, p)
+        assert e[idx].sum() >= p * e.sum() * (1 - 1e-12)
+        # the threshold bin is the first whose cumulative mass reaches p*Z
+        C = np.cumsum(s.hist)
+        assert C[s.bstar] >= p * C[-1]
+        if s.bstar > 0:
+            assert C[s.bstar - 1] < p * C[-1]
+        # the maximum sits in bin 0, so bin 0 is never empty
+        assert s.hist[0] > 0
+        # bin totals equal the softmax normaliser relative to exp((A+1)w)
+        Zref = np.exp(z.astype(np.float64) - (s.A + 1) * 0.125).sum()
+        assert abs(C[-1] - Zref) <= 1e-12 * Zref
+        assert s.A == int(np.floor(z.astype(np.float64).max() / 0.125))
+        if prev is not None:
+            assert set(prev.tolist()) <= set(idx.tolist())   # monotone in p
+        prev = idx
+    assert oracle.topp_select(z, 1.0).count == L
+
+
+@pytest.mark.parametrize("name,z", LOGITS[::3], ids=[n for n, _ in LOGITS[::3]])
+def test_rule_permutation_equivariant(name, z):
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(len(z))
+    for p in [0.5, 0.9]:
+        s = oracle.topp_select(z, p)
+        sp = oracle.topp_select(z[perm], p)
+        back = set(perm[sp.idx].tolist())
+        assert back == set(s.idx.tolist())
+
+
+def test_rule_shift_by_whole_cells_keeps_set():
+    rng = np.random.default_rng(6)
+    z = (rng.integers(-400, 400, 3000) / 1024.0).astype(np.float32)
+    for k in [-24, -1, 1, 7, 80]:
+        for p in [0.3, 0.9]:
+            a = oracle.topp_select(z, p)
+            b = oracle.topp_select((z + np.float32(k * 0.125)).astype(np.float32), p)
+            assert np.array_equal(a.idx, b.idx)
+            assert b.A == a.A + k and b.bstar == a.bstar
+            assert np.allclose(a.hist, b.hist, rtol=1e-12, atol=0)
+
+
+def test_tail_bin_catches_far_tokens():
+    z = np.array([10.0] + [10.0 - 40.0] * 50 + [10.0 - 31.0], dtype=np.float32)
+    s = oracle.topp_select(z, 0.9)
+    assert s.idx.tolist() == [0]
+    # cells 248 below the top land in bin 248; 320 below land in the tail bin 255
+    assert s.hist[248] > 0 and s.hist[255] > 0
+    assert oracle.topp_select(z, 1.0).count == len(z)
+
+
+def test_bin_width_is_a_parameter():
+    z = np.array([0.0, 0.3, 0.55, 1.0], dtype=np.float32)
+    s = oracle.topp_select(z, 0.2, bin_width=0.5)
+    # w = 1/2: cells 0,0,1,2 -> A = 2, bins 2,2,1,0; masses e^{z-1.5}: bin 0 = 0.6065,
+    # bin 1 = 0.3867, bin 2 = 0.5243 (Z = 1.5175).  p = 0.2 stops in bin 0, p = 0.5 in bin 1.
+    assert s.A == 2
+    assert s.idx.tolist() == [3]
+    s = oracle.topp_select(z, 0.5, bin_width=0.5)
+    assert s.idx.tolist() == [2, 3]
+
+
+# ---------------------------------------------------------------------------
+# attention: textbook special cases
+# ---------------------------------------------------------------------------
+def sdpa64(q, K, V, scale, mask=None):
+    qt = torch.from_numpy(np.asarray(q, dtype=np.float64)).view(1, 1, 1, -1)
+    Kt = torch.from_numpy(np.asarray(K, dtype=np.float64)).view(1, 1, K.shape[0], -1)
+    Vt = torch.from_numpy(np.asarray(V, dtype=np.float64)).view(1, 1, V.shape[0], -1)
+    m = None if mask is None else torch.from_numpy(mask).view(1, 1, 1, -1)
+    return torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=m,
+                                                            scale=scale).view(-1).numpy()
+
+
+@pytest.mark.parametrize("dt", [np.float16, np.float32])
+def test_attention_all_rows_is_dense_softmax_attention(dt):
+    rng = np.random.default_rng(7)
+    N, d = 777, 128
+    K = rng.standard_normal((N, d)).astype(dt)
+    V = rng.standard_normal((N, d)).astype(dt)
+    q = rng.standard_normal(d).astype(dt)
+    o, lse = oracle.attention(q, K, V, np.arange(N), 1 / math.sqrt(d))
+    ref = sdpa64(q.astype(np.float64), K.astype(np.float64), V.astype(np.float64), 1 / math.sqrt(d))
+    assert np.allclose(o, ref, atol=1e-12, rtol=0)
+    from scipy.special import logsumexp
+    s = (K.astype(np.float64) @ q.astype(np.float64)) / math.sqrt(d)
+    assert abs(lse - logsumexp(s)) < 1e-12
+
+
+def test_attention_subset_is_masked_dense_attention():
+    rng = np.random.default_rng(8)
+    N, d = 500, 64
+    K = rng.standard_normal((N, d)).astype(np.float16)
+    V = rng.standard_normal((N, d)).astype(np.float16)
+    q = rng.standard_normal(d)
+    rows = np.sort(rng.choice(N, 37, replace=False))
+    o, _ = oracle.attention(q, K, V, rows, 0.2)
+    mask = np.zeros(N, dtype=bool)
+    mask[rows] = True
+    ref = sdpa64(q, K.astype(np.float64), V.astype(np.float64), 0.2, mask)
+    assert np.allclose(o, ref, atol=1e-12, rtol=0)
+    # row order does not matter
+    o2, _ = oracle.attention(q, K, V, rows[::-1].copy(), 0.2)
+    assert np.allclose(o, o2, atol=1e-13, rtol=0)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(9)
+    N, d = 64, 128
+    K = rng.standard_normal((N, d)).astype(np.float32)
+    V = rng.standard_normal((N, d)).astype(np.float32)
+    rows = np.array([3, 9, 10, 40])
+    # q = 0: uniform weights, output is the mean of the selected rows
+    o, lse = oracle.attention(np.zeros(d), K, V, rows, 0.1)
+    assert np.allclose(o, V[rows].astype(np.float64).mean(0), atol=1e-14)
+    assert abs(lse - math.log(4)) < 1e-14
+    # identical value rows: output is that row
+    Vc = np.tile(V[5:6], (N, 1))
+    o, _ = oracle.attention(rng.standard_normal(d), K, Vc, rows, 0.3)
+    assert np.allclose(o, Vc[0], atol=1e-12)
+    # a single row: output is that row, lse is its logit
+    qv = rng.standard_normal(d)
+    o, lse = oracle.attention(qv, K, V, [17], 0.3)
+    assert np.array_equal(o, V[17].astype(np.float64))
+    assert abs(lse - 0.3 * float(qv @ K[17].astype(np.float64))) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# window set and ring layout
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("window,sinks", [(8192, 4), (16, 4), (5, 2), (8, 0), (1, 4)])
+def test_window_positions_and_ring_slots(window, sinks):
+    for L in list(range(1, 40)) + [window + sinks - 1, window + sinks, window + sinks + 1,
+                                   3 * window + 7, 100000]:
+        pos = oracle.window_positions(L, window, sinks)
+        brute = [n for n in range(max(0, L - window - sinks - 1), L)
+                 if n >= L - window] + [n for n in range(min(sinks, L))]
+        assert sorted(set(brute)) == sorted(pos.tolist()) and len(set(pos.tolist())) == len(pos)
+        if L <= window + sinks:
+            assert sorted(pos.tolist()) == list(range(L))
+        slots = oracle.ring_slot(pos, window, sinks)
+        assert len(set(slots.tolist())) == len(slots)          # no two positions share a slot
+        assert slots.min() >= 0 and slots.max() < window + sinks
+
+
+# ---------------------------------------------------------------------------
+# a whole layer against dense attention
+# ---------------------------------------------------------------------------
+def _layer_dense_reference(wl, layer, b, h):
+    G = wl.G
+    kh = h // G
+    mask = layer.kv_is_retrieval
+    L = int(wl.seq_lens[b])
+    q = oracle.np_of(layer.q)[b, h].astype(np.float64)
+    if mask[kh]:
+        kr = layer.ret_heads.index(kh)
+        K = oracle.np_of(layer.K_ret[b, kr, :L]).astype(np.float64)
+        V = oracle.np_of(layer.V_ret[b, kr, :L]).astype(np.float64)
+    else:
+        kl = layer.loc_heads.index(kh)
+        Kr = oracle.np_of(layer.K_loc[b, kl]).astype(np.float64)
+        Vr = oracle.np_of(layer.V_loc[b, kl]).astype(np.float64)
+        slot = oracle.ring_slot(np.arange(L), wl.window, wl.sinks)
+        K, V = Kr[slot], Vr[slot]
+    return K, V, q
+
+
+def test_layer_with_p1_and_full_window_is_dense_attention():
+    import workloads
+    wl = workloads.make_workload("t", 2, [300, 171], 8, 4, [[1, 0, 1, 0]], seed=5, p=1.0,
+                                 window=512, sinks=4, dtype="f16")
+    res = oracle.decode_step(wl)[0]
+    layer = wl.layers[0]
+    for b in range(2):
+        for h in range(8):
+            K, V, q = _layer_dense_reference(wl, layer, b, h)
+            ref = sdpa64(q, K, V, wl.scale_attn)
+            assert np.allclose(res[(b, h)].out, ref, atol=1e-12, rtol=0), (b, h)
+            if layer.kv_is_retrieval[h // 2]:
+                assert res[(b, h)].sel.count == int(wl.seq_lens[b])
+
+
+def test_layer_local_heads_use_window_and_sinks():
+    import workloads
+    wl = workloads.make_workload("t", 1, [203], 4, 2, [[0, 1]], seed=6, p=0.9, window=32,
+                                 sinks=4, dtype="f32")
+    res = oracle.decode_step(wl)[0]
+    layer = wl.layers[0]
+    L = 203
+    for h in range(2):   # KV head 0 is local
+        K, V, q = _layer_dense_reference(wl, layer, 0, h)
+        m = np.zeros(L, dtype=bool)
+        m[:4] = True
+        m[L - 32:] = True
+        ref = sdpa64(q, K, V, wl.scale_attn, m)
+        assert np.allclose(res[(0, h)].out, ref, atol=1e-12, rtol=0)
+    for h in range(2, 4):  # KV head 1 is a retrieval head: masked attention over S
+        K, V, q = _layer_dense_reference(wl, layer, 0, h)
+        m = np.zeros(L, dtype=bool)
+        m[res[(0, h)].sel.idx] = True
+        ref = sdpa64(q, K, V, wl.scale_attn, m)
+        assert np.allclose(res[(0, h)].out, ref, atol=1e-12, rtol=0)
