@@ -1,0 +1,258 @@
+"""Benchmark: one RTPurbo decode step (all heads of a layer) on one MI355X.
+
+Default workload: 1M-token context, batch 1, 32 query / 4 KV heads, head size 128,
+fp16 K/V; KV head 0 is a retrieval head (indexer r = 16, p = 0.9; 2 needle, 4 mid and
+2 broad query heads), KV heads 1-3 are local heads (window 8192 + 4 sinks).
+
+A step is one call of rtp_decode_step: indexer score + 256-bin histogram top-p +
+sparse attention for the retrieval head, window attention for the local heads, and
+the split-K merges.  Inputs are resident in HBM; R rotated copies of every input
+defeat the 256 MB Infinity Cache between consecutive steps.
+
+value = algorithmic HBM bytes per step / time per step (GB/s), where the algorithmic
+bytes are: the indexer keys (L * 16 * 2 B per retrieval KV head), the K and V rows of
+the union of the selected sets over the KV head's query heads (512 B per token), and
+each local head's window+sink rows (512 B per row).
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def hip():
+    h = ctypes.CDLL("libamdhip64.so")
+    h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return h
+
+
+def make_events(h, n):
+    evs = []
+    for _ in range(n):
+        e = ctypes.c_void_p()
+        assert h.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e)
+    return evs
+
+
+def elapsed_ms(h, a, b):
+    ms = ctypes.c_float()
+    assert h.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+    return ms.value
+
+
+def algorithmic_bytes(rtp, wl, layer, torch):
+    """Realised bytes of one step: the union of the selected sets per retrieval KV head
+    comes from the GPU selection (the same rule the step runs)."""
+    dev = layer.q.device
+    sl = torch.as_tensor(wl.seq_lens, dtype=torch.int32, device=dev)
+    e_idx = 2 if wl.dtype == "f16" else 4
+    e_kv = e_idx
+    total = 0
+    detail = {"kidx": 0, "sparse_kv": 0, "window_kv": 0, "union_tokens": 0, "sel_tokens": []}
+    G = wl.G
+    ret = layer.ret_heads
+    if ret:
+        qi = torch.stack([layer.q_idx[:, h * G:(h + 1) * G] for h in ret], 1).reshape(
+            wl.B, len(ret) * G, wl.r).contiguous()
+        z = rtp.rtp_index_score(qi, layer.k_idx, sl, wl.scale_idx)
+        sel, cnt, _, _ = rtp.rtp_topp_select(z, sl, wl.p, wl.bin_width, want_hist=False)
+        sel, cnt = sel.cpu(), cnt.cpu()
+        for b in range(wl.B):
+            L = int(wl.seq_lens[b])
+            for k in range(len(ret)):
+                u = set()
+                for g in range(G):
+                    n = int(cnt[b, k * G + g])
+                    detail["sel_tokens"].append(n)
+                    u.update(sel[b, k * G + g, :n].tolist())
+                detail["kidx"] += L * wl.r * e_idx
+                detail["sparse_kv"] += len(u) * 2 * wl.d * e_kv
+                detail["union_tokens"] += len(u)
+    for b in range(wl.B):
+        L = int(wl.seq_lens[b])
+        detail["window_kv"] += len(layer.loc_heads) * min(L, wl.window + wl.sinks) * 2 * wl.d * e_kv
+    total = detail["kidx"] + detail["sparse_kv"] + detail["window_kv"]
+    return total, detail
+
+
+def cpu_baseline(wl, bytes_per_step, budget_s):
+    import oracle
+    cpu_wl = wl.to("cpu")
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.decode_step(cpu_wl)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / n
+    return {"value": round(bytes_per_step / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "s_per_step": round(dt, 4),
+            "sample": "%d full decode step(s) of the same workload (all 32 query heads), "
+                      "single-threaded C oracle, inputs copied to host memory" % n}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c4")
+    ap.add_argument("--p", type=float, default=None)
+    ap.add_argument("--rotations", type=int, default=0)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--phases", action="store_true", help="print a per-phase breakdown")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import head_wise_sparse_rtp_amd as rtp
+    import workloads
+
+    dev = torch.device("cuda:0")
+    kw = {} if args.p is None else {"p": args.p}
+    wl = workloads.make_config(args.workload, device=dev, **kw)
+    assert len(wl.layers) == 1, "bench.py times single-layer workloads"
+    layer = wl.layers[0]
+    bytes_step, detail = algorithmic_bytes(rtp, wl, layer, torch)
+    touched = max(bytes_step, 1)
+    R = args.rotations or max(1, math.ceil(512 * 2 ** 20 / touched))
+    sl = torch.as_tensor(wl.seq_lens, dtype=torch.int32, device=dev)
+
+    # R rotated copies of every input, one workspace and one output shared by all
+    layers = [layer]
+    for _ in range(R - 1):
+        layers.append(workloads.Layer(layer.kv_is_retrieval, layer.q.clone(), layer.q_idx.clone(),
+                                      layer.k_idx.clone(), layer.K_ret.clone(), layer.V_ret.clone(),
+                                      layer.K_loc.clone(), layer.V_loc.clone(), layer.plans))
+    steps = []
+    ws = None
+    out = None
+    for lay in layers:
+        st = rtp.DecodeStep(lay, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window, wl.sinks, wl.p,
+                            wl.bin_width, wl.scale_idx, wl.scale_attn, out=out, want_lse=False,
+                            ws=ws)
+        ws, out = st.ws, st.out
+        steps.append(st)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    h = hip()
+
+    # ---- warmup + graph capture ----
+    for i in range(args.warmup):
+        steps[i % R]()
+    torch.cuda.synchronize()
+    graphs = None
+    if not args.no_graph:
+        graphs = []
+        for i in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                steps[i]()
+            graphs.append(g)
+        for i in range(max(args.warmup, R)):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+
+    # ---- timed region: K steps ----
+    e0, e1 = make_events(h, 2)
+    torch.cuda.synchronize()
+    h.hipEventRecord(e0, ctypes.c_void_p(stream.cuda_stream))
+    for i in range(args.steps):
+        if graphs is not None:
+            graphs[i % R].replay()
+        else:
+            steps[i % R]()
+    h.hipEventRecord(e1, ctypes.c_void_p(stream.cuda_stream))
+    h.hipEventSynchronize(e1)
+    torch.cuda.synchronize()
+    ms_step = elapsed_ms(h, e0, e1) / args.steps
+
+    # ---- dominant kernel (indexer score + histogram) timed with events in the step ----
+    K = args.steps
+    evs = make_events(h, 7 * K)
+    # each step records its own 7 events: re-point them per step (eager launches)
+    torch.cuda.synchronize()
+    for i in range(K):
+        st = steps[i % R]
+        for j in range(7):
+            st.desc.prof_ev[j] = evs[i * 7 + j].value
+        st()
+    torch.cuda.synchronize()
+    for st in steps:
+        for j in range(7):
+            st.desc.prof_ev[j] = None
+    ph = {"hist": 0.0, "threshold": 0.0, "select": 0.0, "sparse+merge": 0.0, "window+merge": 0.0}
+    has_ret = bool(layer.ret_heads)
+    has_loc = bool(layer.loc_heads)
+    for i in range(K):
+        e = evs[i * 7:(i + 1) * 7]
+        if has_ret:
+            ph["hist"] += elapsed_ms(h, e[0], e[1])
+            ph["threshold"] += elapsed_ms(h, e[1], e[2])
+            ph["select"] += elapsed_ms(h, e[2], e[3])
+            ph["sparse+merge"] += elapsed_ms(h, e[3], e[4])
+        if has_loc:
+            ph["window+merge"] += elapsed_ms(h, e[5], e[6])
+    ph = {k: v / K * 1000.0 for k, v in ph.items()}  # microseconds
+    hist_us = ph["hist"]
+    hist_bytes = detail["kidx"]
+    achieved = hist_bytes / (hist_us * 1e-6) / 1e9 if hist_us > 0 else 0.0
+
+    value = bytes_step / (ms_step * 1e-3) / 1e9
+    res = {
+        "metric": "decode attention us/step and achieved HBM GB/s (% of peak) at 1M context",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1000.0, 2),
+        "pct_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 K/V, fp32 accumulation",
+        "data": "synthetic (seeded planted-logit indexer keys, counter-based N(0,1) K/V)",
+        "config": {"workload": "%s: B=%d, L=%d, Hq=%d, Hkv=%d (retrieval %s), d=%d, r=%d, "
+                               "window=%d+%d sinks, p=%g" % (
+                                   args.workload, wl.B, int(wl.seq_lens.max()), wl.Hq, wl.Hkv,
+                                   layer.ret_heads, wl.d, wl.r, wl.window, wl.sinks, wl.p),
+                   "global_batch": wl.B, "seq_len": int(wl.seq_lens.max()),
+                   "parallelism": "single GPU", "graph": graphs is not None, "rotations": R},
+        "bytes_per_step": bytes_step,
+        "bytes_detail": {k: v for k, v in detail.items() if k != "sel_tokens"},
+        "sel_tokens_per_head": detail["sel_tokens"],
+        "roofline": {"kernel": "score+histogram (k_hist)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "avg_us": round(hist_us, 3), "algorithmic_bytes_per_launch": hist_bytes},
+        "phases_us_eager": {k: round(v, 3) for k, v in ph.items()},
+    }
+    if not args.skip_cpu:
+        res["cpu_baseline"] = cpu_baseline(wl, bytes_step, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,278 @@
+"""MI355X-native RTPurbo decode attention: Python binding of librtp.so.
+
+Argument marshalling only.  Every step of the decode path runs in the HIP kernels
+of librtp.so (``csrc/``); PyTorch provides device memory and the current stream.
+The names follow the C ABI in ``include/rtp.h``:
+
+* ``rtp_index_score``   indexer logits z = q_idx . k_idx (fp32 fma chain)
+* ``rtp_topp_select``   256-bin histogram top-p over the indexer softmax
+* ``rtp_sparse_decode`` exact softmax attention over the selected tokens
+* ``rtp_window_decode`` window + sink attention of local heads
+* ``rtp_decode_step``   a whole layer: retrieval heads sparse, local heads windowed
+
+If the library is missing or fails to load, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librtp.so")
+
+RTP_OK, RTP_EINVAL, RTP_EUNSUPPORTED, RTP_EWORKSPACE, RTP_EHIP = 0, -1, -2, -3, -4
+RTP_F32, RTP_F16 = 0, 1
+NBINS = 256
+EXPORTED = [
+    "rtp_status_string", "rtp_abi_version", "rtp_index_score",
+    "rtp_topp_select_workspace_size", "rtp_topp_select",
+    "rtp_sparse_decode_workspace_size", "rtp_sparse_decode",
+    "rtp_window_decode_workspace_size", "rtp_window_decode",
+    "rtp_decode_step_workspace_size", "rtp_decode_step",
+]
+
+_lib = None
+
+P = ctypes.c_void_p
+I32 = ctypes.c_int32
+F32 = ctypes.c_float
+F64 = ctypes.c_double
+SZ = ctypes.c_size_t
+
+
+class LayerDesc(ctypes.Structure):
+    """Mirror of rtp_layer_desc."""
+    _fields_ = [
+        ("B", I32), ("Hq", I32), ("Hkv", I32), ("d", I32), ("r", I32), ("Lmax", I32),
+        ("window", I32), ("sinks", I32), ("kv_dtype", I32),
+        ("kv_is_retrieval", P), ("q", P), ("q_idx", P), ("K_ret", P), ("V_ret", P),
+        ("k_idx", P), ("K_loc", P), ("V_loc", P), ("seq_lens", P),
+        ("p", F64), ("bin_width", F32), ("scale_idx", F32), ("scale_attn", F32),
+        ("out", P), ("lse", P), ("thresh_out", P), ("count_out", P),
+        ("prof_ev", P * 8),
+    ]
+
+
+class RtpError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(lib().rtp_status_string(code).decode())
+        self.code = code
+
+
+def lib():
+    """The loaded librtp.so (raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("librtp.so not built: run `python -m head_wise_sparse_rtp_amd.build` "
+                               "(or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        L.rtp_status_string.restype = ctypes.c_char_p
+        L.rtp_status_string.argtypes = [I32]
+        L.rtp_abi_version.restype = I32
+        L.rtp_abi_version.argtypes = []
+        L.rtp_index_score.restype = I32
+        L.rtp_index_score.argtypes = [P, P, I32, P, I32, I32, I32, I32, I32, F32, P, P]
+        L.rtp_topp_select_workspace_size.restype = SZ
+        L.rtp_topp_select_workspace_size.argtypes = [I32, I32, I32]
+        L.rtp_topp_select.restype = I32
+        L.rtp_topp_select.argtypes = [P, P, I32, I32, I32, F64, F32, P, P, I32, P, P, P, SZ, P]
+        L.rtp_sparse_decode_workspace_size.restype = SZ
+        L.rtp_sparse_decode_workspace_size.argtypes = [I32, I32, I32, I32]
+        L.rtp_sparse_decode.restype = I32
+        L.rtp_sparse_decode.argtypes = [P, P, P, I32, P, P, I32, I32, I32, I32, I32, I32, F32, P,
+                                        P, P, SZ, P]
+        L.rtp_window_decode_workspace_size.restype = SZ
+        L.rtp_window_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32]
+        L.rtp_window_decode.restype = I32
+        L.rtp_window_decode.argtypes = [P, P, P, I32, P, I32, I32, I32, I32, I32, I32, F32, P, P,
+                                        P, SZ, P]
+        L.rtp_decode_step_workspace_size.restype = SZ
+        L.rtp_decode_step_workspace_size.argtypes = [ctypes.POINTER(LayerDesc)]
+        L.rtp_decode_step.restype = I32
+        L.rtp_decode_step.argtypes = [ctypes.POINTER(LayerDesc), P, SZ, P]
+        _lib = L
+    return _lib
+
+
+def _check(code: int):
+    if code != RTP_OK:
+        raise RtpError(code)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("rtp: tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("rtp: tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _kv_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return RTP_F16
+    if t.dtype == torch.float32:
+        return RTP_F32
+    raise ValueError("rtp: K/V/q/k_idx must be fp16 or fp32, got %s" % t.dtype)
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# single-purpose entry points
+# ---------------------------------------------------------------------------
+def rtp_index_score(q_idx: torch.Tensor, k_idx: torch.Tensor, seq_lens: torch.Tensor,
+                    scale_idx: float, z: Optional[torch.Tensor] = None, stream=None):
+    """z [B, Hr*G, Lmax] fp32 from q_idx [B, Hr*G, r] fp32 and k_idx [B, Hr, Lmax, r]."""
+    B, Hr, Lmax, r = k_idx.shape
+    H = q_idx.shape[1]
+    G = H // Hr
+    if q_idx.dtype != torch.float32 or seq_lens.dtype != torch.int32:
+        raise ValueError("rtp_index_score: q_idx fp32, seq_lens int32")
+    if z is None:
+        z = torch.empty((B, H, Lmax), dtype=torch.float32, device=k_idx.device)
+    _check(lib().rtp_index_score(_ptr(q_idx), _ptr(k_idx), _kv_dtype(k_idx), _ptr(seq_lens), B, Hr,
+                                 G, Lmax, r, scale_idx, _ptr(z), _stream(stream)))
+    return z
+
+
+def rtp_topp_select(z: torch.Tensor, seq_lens: torch.Tensor, p: float, bin_width: float = 0.125,
+                    cap: Optional[int] = None, want_hist: bool = True, ws=None, stream=None):
+    """Returns (sel_idx [B,H,cap] int32, sel_count [B,H] int32, hist [B,H,256] fp32 or None,
+    thresh [B,H,2] int32 = {A, b*})."""
+    B, H, Lmax = z.shape
+    cap = Lmax if cap is None else int(cap)
+    dev = z.device
+    sel_idx = torch.full((B, H, max(cap, 1)), -1, dtype=torch.int32, device=dev)
+    sel_count = torch.empty((B, H), dtype=torch.int32, device=dev)
+    hist = torch.empty((B, H, NBINS), dtype=torch.float32, device=dev) if want_hist else None
+    thresh = torch.empty((B, H, 2), dtype=torch.int32, device=dev)
+    nb = lib().rtp_topp_select_workspace_size(B, H, Lmax)
+    if ws is None:
+        ws = workspace(nb, dev)
+    _check(lib().rtp_topp_select(_ptr(z), _ptr(seq_lens), B, H, Lmax, float(p), float(bin_width),
+                                 _ptr(sel_idx), _ptr(sel_count), cap, _ptr(hist), _ptr(thresh),
+                                 _ptr(ws), ws.numel(), _stream(stream)))
+    return sel_idx, sel_count, hist, thresh
+
+
+def rtp_sparse_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, sel_idx: torch.Tensor,
+                      sel_count: torch.Tensor, scale_attn: float, want_lse: bool = True, ws=None,
+                      stream=None):
+    """out [B, Hr*G, d] fp32 (and lse [B, Hr*G]) over sel_idx [B, Hr*G, cap]."""
+    B, Hr, Lmax, d = K.shape
+    H = q.shape[1]
+    G = H // Hr
+    cap = sel_idx.shape[2]
+    dev = q.device
+    out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev) if want_lse else None
+    nb = lib().rtp_sparse_decode_workspace_size(B, Hr, G, cap)
+    if ws is None:
+        ws = workspace(nb, dev)
+    _check(lib().rtp_sparse_decode(_ptr(q), _ptr(K), _ptr(V), _kv_dtype(K), _ptr(sel_idx),
+                                   _ptr(sel_count), cap, B, Hr, G, Lmax, d, scale_attn, _ptr(out),
+                                   _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+    return out, lse
+
+
+def rtp_window_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_lens: torch.Tensor,
+                      window: int, sinks: int, scale_attn: float, want_lse: bool = True, ws=None,
+                      stream=None):
+    """out [B, Hl*G, d] fp32 over the ring K, V [B, Hl, sinks+window, d]."""
+    B, Hl, ring, d = K.shape
+    if ring != window + sinks:
+        raise ValueError("rtp_window_decode: ring size must be sinks + window")
+    H = q.shape[1]
+    G = H // Hl
+    dev = q.device
+    out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev) if want_lse else None
+    nb = lib().rtp_window_decode_workspace_size(B, Hl, G, window, sinks)
+    if ws is None:
+        ws = workspace(nb, dev)
+    _check(lib().rtp_window_decode(_ptr(q), _ptr(K), _ptr(V), _kv_dtype(K), _ptr(seq_lens), B, Hl, G,
+                                   d, window, sinks, scale_attn, _ptr(out), _ptr(lse), _ptr(ws),
+                                   ws.numel(), _stream(stream)))
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# one decode step of a layer
+# ---------------------------------------------------------------------------
+class DecodeStep:
+    """Holds the descriptor, host mask and workspace of one layer so that repeated
+    calls (a decode loop, a captured graph) only enqueue kernels."""
+
+    def __init__(self, layer, seq_lens: torch.Tensor, B: int, Hq: int, Hkv: int, Lmax: int,
+                 window: int, sinks: int, p: float, bin_width: float, scale_idx: float,
+                 scale_attn: float, out: Optional[torch.Tensor] = None, want_lse: bool = True,
+                 want_debug: bool = False, ws: Optional[torch.Tensor] = None):
+        dev = layer.q.device
+        self.keep = [layer.q, layer.q_idx, layer.K_ret, layer.V_ret, layer.k_idx, layer.K_loc,
+                     layer.V_loc, seq_lens]
+        self.mask = (ctypes.c_uint8 * Hkv)(*[int(x) for x in layer.kv_is_retrieval])
+        d = layer.q.shape[-1]
+        self.out = out if out is not None else torch.empty((B, Hq, d), dtype=torch.float32,
+                                                           device=dev)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if want_lse else None
+        self.thresh = (torch.zeros((B, Hq, 2), dtype=torch.int32, device=dev)
+                       if want_debug else None)
+        self.count = torch.zeros((B, Hq), dtype=torch.int32, device=dev) if want_debug else None
+        nret = int(sum(int(x) for x in layer.kv_is_retrieval))
+        nloc = Hkv - nret
+
+        def ptr_or_none(t, needed):
+            return _ptr(t) if needed and t is not None and t.numel() > 0 else None
+
+        self.desc = LayerDesc(
+            B, Hq, Hkv, d, layer.q_idx.shape[-1], Lmax, window, sinks, _kv_dtype(layer.q),
+            ctypes.cast(self.mask, ctypes.c_void_p), _ptr(layer.q), ptr_or_none(layer.q_idx, nret),
+            ptr_or_none(layer.K_ret, nret), ptr_or_none(layer.V_ret, nret),
+            ptr_or_none(layer.k_idx, nret), ptr_or_none(layer.K_loc, nloc),
+            ptr_or_none(layer.V_loc, nloc), _ptr(seq_lens), float(p), float(bin_width),
+            float(scale_idx), float(scale_attn), _ptr(self.out), _ptr(self.lse),
+            _ptr(self.thresh), _ptr(self.count))
+        nb = lib().rtp_decode_step_workspace_size(ctypes.byref(self.desc))
+        if nb == 0:
+            raise RtpError(RTP_EINVAL)
+        self.ws = ws if ws is not None and ws.numel() >= nb else workspace(nb, dev)
+        self.ws_bytes = nb
+
+    def __call__(self, stream=None):
+        _check(lib().rtp_decode_step(ctypes.byref(self.desc), _ptr(self.ws), self.ws.numel(),
+                                     _stream(stream)))
+        return self.out
+
+
+def rtp_decode_step(layer, seq_lens, B, Hq, Hkv, Lmax, window, sinks, p, bin_width, scale_idx,
+                    scale_attn, want_debug=False, stream=None):
+    """One layer's decode step; returns (out, lse, thresh, count)."""
+    st = DecodeStep(layer, seq_lens, B, Hq, Hkv, Lmax, window, sinks, p, bin_width, scale_idx,
+                    scale_attn, want_debug=want_debug)
+    st(stream)
+    return st.out, st.lse, st.thresh, st.count
+
+
+def decode_workload(wl, want_debug: bool = False, stream=None):
+    """Run every layer of a `workloads.Workload` already on the GPU; returns per-layer
+    (out, lse, thresh, count)."""
+    sl = torch.as_tensor(wl.seq_lens, dtype=torch.int32).to(wl.layers[0].q.device)
+    res = []
+    for layer in wl.layers:
+        res.append(rtp_decode_step(layer, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window, wl.sinks,
+                                   wl.p, wl.bin_width, wl.scale_idx, wl.scale_attn, want_debug,
+                                   stream))
+    return res

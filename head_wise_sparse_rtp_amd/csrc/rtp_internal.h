@@ -1,0 +1,126 @@
+// Internal declarations of librtp: device helpers, launch wrappers and the
+// workspace planner.  Nothing here is part of the public C ABI (include/rtp.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstddef>
+#include <cstdint>
+
+namespace rtp {
+
+constexpr int kNB = 256;        // histogram bins per head (1 KB of fp32 masses)
+constexpr int kR = 16;          // indexer size
+constexpr int kD = 128;         // head size
+constexpr int kMaxHkv = 64;     // KV heads per layer
+constexpr int kMaxG = 64;       // query heads per KV head
+constexpr int kThreads = 256;   // threads per block of the streaming kernels
+constexpr int kSplit = 64;      // selected tokens per sparse-attention work item
+constexpr int kWinSplit = 128;  // window rows per window-attention work item
+constexpr int kMerge1 = 16;     // chunk partials merged by one first-level merge block
+constexpr int kEmptyCell = INT_MIN;
+
+typedef _Float16 f16;
+
+// Row space of the retrieval kernels: row = kr * G + g for packed retrieval KV head
+// kr and query head g of that KV head.  `kv[kr]` is the KV head id in the layer, used
+// to address q / q_idx / out, whose head index is kv * G + g.
+struct HeadMap {
+  int32_t n;
+  int32_t kv[kMaxHkv];
+};
+
+// ---------------------------------------------------------------------------
+// chunk geometry of the histogram pass
+// ---------------------------------------------------------------------------
+struct ChunkGeom {
+  int tpt;     // tokens per thread (4, 8 or 16)
+  int tc;      // tokens per chunk = kThreads * tpt
+  int nchunk;  // chunks per row = ceil(Lmax / tc)
+  int nsplit;  // first-level merge blocks per row = ceil(nchunk / kMerge1)
+};
+ChunkGeom chunk_geom(int64_t rows_times_batch, int64_t Lmax);
+
+// ---------------------------------------------------------------------------
+// device buffers of the selection pipeline (all inside the caller's workspace)
+// ---------------------------------------------------------------------------
+struct SelectBufs {
+  float* part_mass;     // [BH, nchunk, 256] chunk-relative bin masses
+  int32_t* part_A;      // [BH, nchunk] chunk top cell (kEmptyCell when no token)
+  uint32_t* codes;      // [BH, nchunk, tc/4, 4 bytes] chunk-relative bin of each token
+  double* mid_mass;     // [BH, nsplit, 256] first-level merged masses
+  int32_t* mid_A;       // [BH, nsplit]
+  int32_t* thr;         // [BH, 4] = {A, b*, valid, pad}
+  int32_t* cnt;         // [BH, nchunk] selected tokens per chunk
+};
+
+struct AttnPartials {
+  float* m;    // [rows, maxs] running max of the scaled logits
+  float* l;    // [rows, maxs] sum of exp(s - m)
+  float* acc;  // [rows, maxs, d] sum of exp(s - m) * v
+};
+
+// ---------------------------------------------------------------------------
+// launch wrappers (each returns the hipError_t of its launch)
+// ---------------------------------------------------------------------------
+hipError_t launch_index_score(const float* q_idx, const void* k_idx, int k_dtype,
+                              const int32_t* seq_lens, int B, int Hr, int G, int Lmax,
+                              float scale_idx, float* z, hipStream_t st);
+
+// Histogram partials; mode 0 reads logits z [B, H, Lmax], mode 1 computes them from
+// q_idx / k_idx (rows kr*G+g; q_idx head index map.kv[kr]*G+g of a [B, Hq, r] array).
+hipError_t launch_hist_from_z(const float* z, const int32_t* seq_lens, int B, int H, int Lmax,
+                              float bin_width, const ChunkGeom& cg, const SelectBufs& sb,
+                              hipStream_t st);
+hipError_t launch_hist_from_kidx(const float* q_idx, const void* k_idx, int k_dtype,
+                                 const int32_t* seq_lens, const HeadMap& map, int B, int Hq,
+                                 int Hr, int G, int Lmax, float scale_idx, float bin_width,
+                                 const ChunkGeom& cg, const SelectBufs& sb, hipStream_t st);
+
+hipError_t launch_threshold(const int32_t* seq_lens, int B, int H, int Lmax, double p,
+                            float bin_width, const ChunkGeom& cg, const SelectBufs& sb,
+                            float* hist_out, int32_t* thresh_out, const HeadMap* out_map,
+                            int G, int Hq, hipStream_t st);
+
+hipError_t launch_select(const int32_t* seq_lens, int B, int H, int Lmax, const ChunkGeom& cg,
+                         const SelectBufs& sb, int32_t* sel_idx, int32_t* sel_count, int cap,
+                         int32_t* count_out, const HeadMap* out_map, int G, int Hq,
+                         hipStream_t st);
+
+// Sparse attention partials over sel_idx rows; rows kr*G+g, q head map.kv[kr]*G+g.
+hipError_t launch_sparse_partial(const void* q, const void* K, const void* V, int kv_dtype,
+                                 const int32_t* sel_idx, const int32_t* sel_count, int cap,
+                                 const HeadMap& map, int B, int Hq, int Hr, int G, int Lmax,
+                                 float scale_attn, const AttnPartials& pa, int maxs,
+                                 hipStream_t st);
+
+hipError_t launch_window_partial(const void* q, const void* K, const void* V, int kv_dtype,
+                                 const int32_t* seq_lens, const HeadMap& map, int B, int Hq,
+                                 int Hl, int G, int window, int sinks, float scale_attn,
+                                 const AttnPartials& pa, int maxs, hipStream_t st);
+
+// Merge split partials into out [B, Hq, d] / lse [B, Hq].  For sparse rows the number of
+// used splits comes from sel_count (ceil(min(count, cap) / kSplit)); otherwise all `maxs`.
+hipError_t launch_merge(const AttnPartials& pa, int maxs, const int32_t* sel_count, int cap,
+                        const HeadMap& map, int B, int Hq, int Hrows_kv, int G, float* out,
+                        float* lse, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// workspace planning
+// ---------------------------------------------------------------------------
+struct WsPlanner {
+  size_t off = 0;
+  template <typename T>
+  size_t take(size_t n) {
+    off = (off + 255) & ~size_t(255);
+    size_t o = off;
+    off += n * sizeof(T);
+    return o;
+  }
+};
+
+size_t plan_select(WsPlanner& wp, int B, int H, int Lmax, const ChunkGeom& cg, size_t offs[7]);
+SelectBufs bind_select(char* ws, const size_t offs[7]);
+
+}  // namespace rtp

@@ -1,0 +1,173 @@
+/*
+ * rtp.h -- C ABI of librtp.so: one RTPurbo decode step on an AMD Instinct MI355X (gfx950).
+ *
+ * The method (Full Attention Strikes Back: Transferring Full Attention into Sparse
+ * within Hundred Training Steps; xllm-io.github.io paper review, section 三 技术架构):
+ * retrieval heads score every cached token with a 16-dim pre-RoPE indexer, keep a
+ * top-p set of tokens chosen through a 256-bin histogram without sorting, and run
+ * exact softmax attention over that set; local heads attend over a sliding window
+ * plus sink tokens (section 五, test-configuration table: window 8192, 4 sinks,
+ * indexer size 16, p = 0.9, 15% retrieval heads).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer to a dense row-major array whose
+ *     shape is given next to it; all base pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls only
+ *     enqueue work: they never allocate, free or synchronise, and keep no mutable
+ *     global state.  Calls on different streams must use different workspaces.
+ *   - The caller owns every buffer.  Workspace sizes come from the matching
+ *     *_workspace_size() query; a smaller `ws_bytes` returns RTP_EWORKSPACE.
+ *   - Arguments are validated on the host before anything is enqueued; an invalid
+ *     argument returns an error and enqueues nothing.  Device-resident values
+ *     (seq_lens, sel_idx, sel_count) cannot be checked on the host: kernels clamp
+ *     sequence lengths to [0, Lmax] and skip token indices outside [0, Lmax).
+ *   - A launch failure returns RTP_EHIP.  A device fault surfaces at the caller's
+ *     next synchronisation.
+ *   - Supported shapes: r = 16 (indexer size), d = 128 (head size), 1 <= G <= 64,
+ *     1 <= Lmax <= 2^24.  Inputs must be finite.
+ *   - dtype codes: RTP_F32 (fp32) or RTP_F16 (IEEE binary16).  q, K, V and k_idx use
+ *     the given dtype; q_idx and every output are fp32; accumulation is fp32.
+ *   - A sequence with length 0 yields out = 0, lse = -inf, sel_count = 0.
+ *   - Results are deterministic: repeated calls on the same inputs are bitwise equal.
+ */
+#ifndef RTP_H_
+#define RTP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RTP_ABI_VERSION 1
+
+typedef int32_t rtp_status;
+enum {
+  RTP_OK = 0,
+  RTP_EINVAL = -1,        /* null/misaligned pointer, bad size or parameter */
+  RTP_EUNSUPPORTED = -2,  /* r != 16, d != 128, G or Lmax out of range, bad dtype */
+  RTP_EWORKSPACE = -3,    /* ws_bytes below the size query */
+  RTP_EHIP = -4           /* a HIP launch failed */
+};
+enum { RTP_F32 = 0, RTP_F16 = 1 };
+
+/* Static description of a status code. */
+const char* rtp_status_string(rtp_status s);
+/* RTP_ABI_VERSION of the loaded library. */
+int32_t rtp_abi_version(void);
+
+/*
+ * Indexer score (section 三, 核心公式, adaptive sparse attention: the first
+ * equation, s_h(m,n) = (W^Q_h q^pre)^T (W^K_h k^pre), on features projected to r
+ * dims before RoPE).  For every query head h = kr*G + g of retrieval KV head kr and
+ * every token n < L_b:
+ *     a = +0;  for i = 0..r-1:  a = fmaf(q_idx[b,h,i], k_idx[b,kr,n,i], a)
+ *     z[b,h,n] = fl32(scale_idx * a)
+ * (the fp32 fused multiply-add chain in this order; fp16 keys convert exactly).
+ *   q_idx   [B, Hr*G, r] fp32        k_idx [B, Hr, Lmax, r] (k_dtype)
+ *   seq_lens[B] int32 (device)       z     [B, Hr*G, Lmax] fp32 out; entries n >= L_b untouched
+ */
+rtp_status rtp_index_score(const float* q_idx, const void* k_idx, int32_t k_dtype,
+                           const int32_t* seq_lens, int32_t B, int32_t Hr, int32_t G,
+                           int32_t Lmax, int32_t r, float scale_idx, float* z, void* stream);
+
+/*
+ * Top-p selection without sorting through a 256-bin histogram (section 三,
+ * 硬件感知解码内核: 256 bins, 1 KB per head, independent of the sequence length;
+ * the top-p set S_h(m) = Top-P(s_h(m,.), p) of the sparse-attention equation).
+ * Per row (b, h) over n < L = L_b, with w = bin_width (a power of two):
+ *     g_n = floor(z_n / w);  A = max_n g_n;  j_n = min(A - g_n, 255)
+ *     mu_j = sum_{j_n = j} exp(z_n - (A+1) w);  Z = sum_j mu_j
+ *     b* = 255 if p >= 1, else the least j with mu_0 + ... + mu_j >= p Z
+ *     S = { n : j_n <= b* }  (ascending)
+ * S contains the exact top-p set and holds softmax mass >= p.
+ *   z        [B, H, Lmax] fp32            seq_lens [B] int32 (device)
+ *   p        in (0, 1]; values >= 1 select every token
+ *   sel_idx  [B, H, cap] int32 out: the first min(|S|, cap) indices of S, ascending
+ *   sel_count[B, H] int32 out: |S| (may exceed cap: the caller checks overflow)
+ *   hist     [B, H, 256] fp32 out or NULL: mu_j
+ *   thresh   [B, H, 2] int32 out or NULL: {A, b*}
+ * Masses are accumulated exactly per bin from fp32 exponentials and merged in fp64,
+ * so b* can differ from an fp64 evaluation only when a cumulative mass lies within
+ * about 1e-6 Z of p Z.
+ */
+size_t rtp_topp_select_workspace_size(int32_t B, int32_t H, int32_t Lmax);
+rtp_status rtp_topp_select(const float* z, const int32_t* seq_lens, int32_t B, int32_t H,
+                           int32_t Lmax, double p, float bin_width, int32_t* sel_idx,
+                           int32_t* sel_count, int32_t cap, float* hist, int32_t* thresh,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Exact softmax attention over a selected token set (section 三, 核心公式, the
+ * sparse-attention equation):
+ *     O[b,h] = sum_{n in S} exp(s_n - m) V[b,kr,n] / sum_{n in S} exp(s_n - m),
+ *     s_n = scale_attn * q[b,h] . K[b,kr,n],  m = max s_n,  lse = m + log(sum exp(s_n - m))
+ * with kr = h / G and S = sel_idx[b,h,0 : min(sel_count[b,h], cap)].
+ *   q [B, Hr*G, d] (kv_dtype)   K, V [B, Hr, Lmax, d] (kv_dtype)
+ *   out [B, Hr*G, d] fp32 out   lse [B, Hr*G] fp32 out or NULL
+ * Split-K: fixed-size slices of S give partial (max, sum, weighted V) triples that a
+ * second pass merges.
+ */
+size_t rtp_sparse_decode_workspace_size(int32_t B, int32_t Hr, int32_t G, int32_t cap);
+rtp_status rtp_sparse_decode(const void* q, const void* K, const void* V, int32_t kv_dtype,
+                             const int32_t* sel_idx, const int32_t* sel_count, int32_t cap,
+                             int32_t B, int32_t Hr, int32_t G, int32_t Lmax, int32_t d,
+                             float scale_attn, float* out, float* lse, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
+ * Local heads: exact softmax attention over the sink tokens and a sliding window
+ * (section 五, test-configuration table; gist.science summary, section 1: local heads
+ * use a sliding window with attention sinks).  The token set of a sequence of length
+ * L is { n < min(sinks, L) } united with { max(sinks, L - window) <= n < L } (the
+ * current token included).  The cache is a ring: position n < sinks lives in slot n,
+ * any later position n in slot sinks + (n mod window).
+ *   q [B, Hl*G, d] (kv_dtype)   K, V [B, Hl, sinks + window, d] (kv_dtype)
+ *   out [B, Hl*G, d] fp32       lse [B, Hl*G] fp32 or NULL
+ */
+size_t rtp_window_decode_workspace_size(int32_t B, int32_t Hl, int32_t G, int32_t window,
+                                        int32_t sinks);
+rtp_status rtp_window_decode(const void* q, const void* K, const void* V, int32_t kv_dtype,
+                             const int32_t* seq_lens, int32_t B, int32_t Hl, int32_t G,
+                             int32_t d, int32_t window, int32_t sinks, float scale_attn,
+                             float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One decode step of one attention layer: KV heads flagged in kv_is_retrieval run
+ * indexer score -> histogram top-p -> sparse attention for each of their G query
+ * heads; the other KV heads run window attention.  Retrieval heads keep the full
+ * cache and local heads a window plus sinks (section 三, solution overview and
+ * insight 1; section 五, test configuration).
+ */
+typedef struct {
+  int32_t B, Hq, Hkv, d, r, Lmax, window, sinks, kv_dtype;
+  const uint8_t* kv_is_retrieval; /* HOST [Hkv]: 1 = retrieval, 0 = local */
+  const void* q;                  /* [B, Hq, d] (kv_dtype); query head h belongs to KV head h / G */
+  const float* q_idx;             /* [B, Hq, r] fp32; rows of local heads are ignored */
+  const void* K_ret;              /* [B, Hret, Lmax, d]: retrieval KV heads in ascending order */
+  const void* V_ret;              /* [B, Hret, Lmax, d] */
+  const void* k_idx;              /* [B, Hret, Lmax, r] (kv_dtype) */
+  const void* K_loc;              /* [B, Hloc, sinks + window, d] ring (see rtp_window_decode) */
+  const void* V_loc;              /* [B, Hloc, sinks + window, d] */
+  const int32_t* seq_lens;        /* [B] device */
+  double p;                       /* top-p mass in (0, 1] */
+  float bin_width, scale_idx, scale_attn;
+  float* out;                     /* [B, Hq, d] fp32 out */
+  float* lse;                     /* [B, Hq] fp32 out or NULL */
+  int32_t* thresh_out;            /* [B, Hq, 2] {A, b*} for retrieval query heads, or NULL */
+  int32_t* count_out;             /* [B, Hq] |S| for retrieval query heads, or NULL */
+  /* Optional profiling: hipEvent_t handles (or NULL) recorded on `stream` at phase
+   * boundaries: [0] before the score/histogram kernel, [1] after it, [2] after the
+   * threshold, [3] after the selection, [4] after the sparse attention and its merge,
+   * [5] before the window attention, [6] after the window merge, [7] unused. */
+  void* prof_ev[8];
+} rtp_layer_desc;
+
+size_t rtp_decode_step_workspace_size(const rtp_layer_desc* desc);
+rtp_status rtp_decode_step(const rtp_layer_desc* desc, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RTP_H_ */

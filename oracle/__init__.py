@@ -181,6 +181,7 @@ class HeadResult:
     out: np.ndarray
     lse: float
     sel: Optional[Selection] = None
+    z: Optional[np.ndarray] = None     # indexer logits of a retrieval head
 
 
 def decode_layer(layer, seq_lens, Hq: int, Hkv: int, p: float, bin_width: float,
@@ -200,24 +201,25 @@ def decode_layer(layer, seq_lens, Hq: int, Hkv: int, p: float, bin_width: float,
     for b in (batches if batches is not None else range(B)):
         L = int(seq_lens[b])
         for kh in range(Hkv):
-            for g in range(G):
-                h = kh * G + g
-                if heads is not None and h not in heads:
-                    continue
-                if mask[kh]:
-                    kr = ret.index(kh)
-                    kidx = np_of(layer.k_idx[b, kr, :L])
+            hs = [kh * G + g for g in range(G) if heads is None or kh * G + g in heads]
+            if not hs:
+                continue
+            if mask[kh]:
+                kr = ret.index(kh)
+                kidx = np_of(layer.k_idx[b, kr, :L])
+                Kh = np_of(layer.K_ret[b, kr, :L])
+                Vh = np_of(layer.V_ret[b, kr, :L])
+                for h in hs:
                     z = index_score(q_idx[b, h], kidx, scale_idx)
                     s = topp_select(z, p, bin_width)
-                    Kh = np_of(layer.K_ret[b, kr, :L])
-                    Vh = np_of(layer.V_ret[b, kr, :L])
                     o, lse = attention(q[b, h], Kh, Vh, s.idx, scale_attn)
-                    res[(b, h)] = HeadResult(o, lse, s)
-                else:
-                    kl = loc.index(kh)
-                    rows = ring_slot(window_positions(L, window, sinks), window, sinks)
-                    Kh = np_of(layer.K_loc[b, kl])
-                    Vh = np_of(layer.V_loc[b, kl])
+                    res[(b, h)] = HeadResult(o, lse, s, z)
+            else:
+                kl = loc.index(kh)
+                rows = ring_slot(window_positions(L, window, sinks), window, sinks)
+                Kh = np_of(layer.K_loc[b, kl])
+                Vh = np_of(layer.V_loc[b, kl])
+                for h in hs:
                     o, lse = attention(q[b, h], Kh, Vh, rows, scale_attn)
                     res[(b, h)] = HeadResult(o, lse, None)
     return res

@@ -1,0 +1,134 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry point, and
+rejects invalid arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rtp.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import head_wise_sparse_rtp_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from head_wise_sparse_rtp_amd import build
+        build.build()
+    return m.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(rtp_[a-z_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    import head_wise_sparse_rtp_amd as m
+    names = declared_functions()
+    assert set(names) == set(m.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.rtp_abi_version() == 1
+    for code in [0, -1, -2, -3, -4]:
+        assert lib.rtp_status_string(code).startswith(b"RTP_")
+    assert lib.rtp_status_string(7) == b"unknown rtp_status"
+
+
+FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced on the host
+MIS = ctypes.c_void_p(0x10004)        # misaligned
+
+
+def test_index_score_validation(lib):
+    f = lib.rtp_index_score
+    ok = (FAKE, FAKE, 1, FAKE, 1, 1, 8, 1024, 16, 0.25, FAKE, None)
+    bad = [
+        ((None,) + ok[1:], -1),
+        ((MIS,) + ok[1:], -1),
+        (ok[:8] + (15,) + ok[9:], -2),          # r != 16
+        (ok[:2] + (7,) + ok[3:], -2),           # dtype
+        (ok[:6] + (0,) + ok[7:], -2),           # G = 0
+        (ok[:7] + (0,) + ok[8:], -1),           # Lmax = 0
+        (ok[:7] + ((1 << 24) + 1,) + ok[8:], -2),
+        (ok[:9] + (float("inf"),) + ok[10:], -1),
+    ]
+    for args, code in bad:
+        assert f(*args) == code, args
+
+
+def test_topp_select_validation_and_workspace(lib):
+    f = lib.rtp_topp_select
+    nb = lib.rtp_topp_select_workspace_size(2, 8, 100000)
+    assert nb > 2 * 8 * 1024  # at least the per-head histograms
+    assert lib.rtp_topp_select_workspace_size(0, 8, 10) == 0
+    ok = [FAKE, FAKE, 2, 8, 100000, 0.9, 0.125, FAKE, FAKE, 100000, None, None, FAKE, nb, None]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["z", "sl", "B", "H", "Lmax", "p", "w", "si", "sc", "cap", "hist", "thr", "ws",
+                 "wsb", "st"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(p=0.0) == -1
+    assert call(p=float("nan")) == -1
+    assert call(w=0.1) == -1            # not a power of two
+    assert call(w=2.0) == -1            # outside 2^-10 .. 1
+    assert call(ws=MIS) == -1
+    assert call(hist=MIS) == -1
+    assert call(wsb=nb - 1) == -3
+    assert call(cap=-1) == -1
+    assert call(z=None) == -1
+
+
+def test_sparse_and_window_validation(lib):
+    nb = lib.rtp_sparse_decode_workspace_size(1, 1, 8, 4096)
+    assert nb > 0
+    f = lib.rtp_sparse_decode
+    ok = [FAKE, FAKE, FAKE, 1, FAKE, FAKE, 4096, 1, 1, 8, 65536, 128, 0.088, FAKE, None, FAKE, nb,
+          None]
+    a = list(ok); a[11] = 64
+    assert f(*a) == -2                  # d != 128
+    a = list(ok); a[16] = nb - 1
+    assert f(*a) == -3
+    a = list(ok); a[3] = 2
+    assert f(*a) == -2                  # bad dtype
+    nbw = lib.rtp_window_decode_workspace_size(1, 3, 8, 8192, 4)
+    g = lib.rtp_window_decode
+    okw = [FAKE, FAKE, FAKE, 1, FAKE, 1, 3, 8, 128, 8192, 4, 0.088, FAKE, None, FAKE, nbw, None]
+    a = list(okw); a[9] = 0
+    assert g(*a) == -1                  # window = 0
+    a = list(okw); a[15] = 0
+    assert g(*a) == -3
+    a = list(okw); a[1] = MIS
+    assert g(*a) == -1
+
+
+def test_decode_step_validation(lib):
+    import head_wise_sparse_rtp_amd as m
+    mask = (ctypes.c_uint8 * 4)(1, 0, 0, 0)
+    d = m.LayerDesc(1, 32, 4, 128, 16, 65536, 8192, 4, 1, ctypes.cast(mask, ctypes.c_void_p),
+                    FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.9, 0.125, 0.25, 0.088,
+                    FAKE, None, None, None)
+    nb = lib.rtp_decode_step_workspace_size(ctypes.byref(d))
+    assert nb > 0
+    assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nb - 1, None) == -3
+    d.Hq = 30                           # not a multiple of Hkv
+    assert lib.rtp_decode_step_workspace_size(ctypes.byref(d)) == 0
+    assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nb, None) == -1
+    d.Hq = 32
+    d.r = 8
+    assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nb, None) == -2
+    d.r = 16
+    d.p = -1.0
+    assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nb, None) == -1
+    d.p = 0.9
+    d.k_idx = None
+    assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nb, None) == -1

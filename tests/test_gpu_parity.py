@@ -1,0 +1,318 @@
+"""GPU parity: every entry point of librtp.so against the CPU oracle.
+
+Small ragged cases span several chunks/tiles and ragged tails; the full-size
+configurations run in the launch configuration the benchmark times.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.parity_util import (SelCheck, compare_count, compare_sets, expected_set, max_err,
+                               out_tol)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def rtp():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import head_wise_sparse_rtp_amd as m
+    m.lib()
+    return m
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+# ---------------------------------------------------------------------------
+# rtp_index_score
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,G,lens", [("f16", 8, [5000, 1, 2049]), ("f32", 1, [4097]),
+                                          ("f16", 3, [700, 3]), ("f32", 4, [2048, 2047])])
+def test_index_score_bit_exact(rtp, dtype, G, lens):
+    say("index_score", dtype, G, lens)
+    Hkv = 2
+    wl = workloads.make_workload("t", len(lens), lens, G * Hkv, Hkv, [[1, 1]], seed=21,
+                                 dtype=dtype, device=dev(), classes=lambda b, k, r: ["gaussian"] * G)
+    lay = wl.layers[0]
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev())
+    z = torch.full((len(lens), 2 * G, wl.Lmax), 123.0, dtype=torch.float32, device=dev())
+    rtp.rtp_index_score(lay.q_idx, lay.k_idx, sl, wl.scale_idx, z)
+    zc = z.cpu().numpy()
+    qi = oracle.np_of(lay.q_idx)
+    for b, L in enumerate(lens):
+        for h in range(2 * G):
+            zo = oracle.index_score(qi[b, h], oracle.np_of(lay.k_idx[b, h // G, :L]), wl.scale_idx)
+            assert np.array_equal(zc[b, h, :L], zo), (b, h)
+            assert np.all(zc[b, h, L:] == 123.0)
+
+
+# ---------------------------------------------------------------------------
+# rtp_topp_select
+# ---------------------------------------------------------------------------
+def _logit_rows(seed, Lmax, lens):
+    rng = np.random.default_rng(seed)
+    rows = []
+    kinds = ["gauss1", "gauss4", "spike", "broad", "edges", "allequal", "wide", "flat"]
+    for i, L in enumerate(lens):
+        k = kinds[i % len(kinds)]
+        z = np.zeros(Lmax, dtype=np.float32)
+        if k == "gauss1":
+            v = rng.standard_normal(L)
+        elif k == "gauss4":
+            v = 4 * rng.standard_normal(L)
+        elif k == "spike":
+            v = rng.standard_normal(L)
+            v[rng.choice(L, min(3, L), replace=False)] = 12.0
+        elif k == "broad":
+            v = rng.standard_normal(L) - 6
+            v[rng.choice(L, max(1, L // 10), replace=False)] = 2 + 0.7 * rng.standard_normal(max(1, L // 10))
+        elif k == "edges":
+            v = rng.integers(-100, 50, L) * 0.125
+        elif k == "allequal":
+            v = np.full(L, -3.3)
+        elif k == "wide":
+            v = 25 * rng.standard_normal(L)
+        else:
+            v = 0.01 * rng.standard_normal(L)
+        z[:L] = v.astype(np.float32)
+        z[L:] = 1e6  # must never be read
+        rows.append(z)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("p", [0.5, 0.9, 0.95, 1.0])
+@pytest.mark.parametrize("lens", [[9000, 1, 2, 4097, 2048, 12345, 3, 777], [70000, 70000]])
+def test_topp_select_matches_oracle(rtp, p, lens):
+    say("topp_select", p, lens)
+    Lmax = max(lens)
+    B, H = 1, len(lens)
+    zr = _logit_rows(31 + len(lens), Lmax, lens)
+    z = torch.from_numpy(zr).view(B, H, Lmax).to(dev())
+    # each row is its own "sequence": use B = rows, H = 1 so seq_lens differ per row
+    z = z.view(H, 1, Lmax).contiguous()
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev())
+    sel_idx, cnt, hist, thr = rtp.rtp_topp_select(z, sl, p)
+    sel_idx, cnt, hist, thr = (t.cpu().numpy() for t in (sel_idx, cnt, hist, thr))
+    st = SelCheck()
+    for i, L in enumerate(lens):
+        so = oracle.topp_select(zr[i, :L], p)
+        where = "row %d L=%d p=%g" % (i, L, p)
+        ex = expected_set(zr[i, :L], so, int(thr[i, 0, 0]), int(thr[i, 0, 1]), p, 0.125, st, where)
+        n = int(cnt[i, 0])
+        compare_sets(sel_idx[i, 0, :n], ex, zr[i, :L], 0.125, st, where)
+        assert np.all(np.diff(sel_idx[i, 0, :n]) > 0)
+        Z = so.hist.sum()
+        assert np.max(np.abs(hist[i, 0] - so.hist)) <= 2e-6 * Z, where
+    say("mass ties", st.mass_ties, "edge tokens", st.edge_tokens)
+
+
+def test_topp_select_empty_and_capped(rtp):
+    say("topp_select empty/capped")
+    lens = [0, 5000]
+    zr = _logit_rows(5, 5000, [1, 5000])
+    z = torch.from_numpy(zr).view(2, 1, 5000).to(dev())
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev())
+    so = oracle.topp_select(zr[1], 1.0)
+    sel_idx, cnt, hist, thr = rtp.rtp_topp_select(z, sl, 1.0, cap=100)
+    cnt = cnt.cpu().numpy()
+    assert cnt[0, 0] == 0 and cnt[1, 0] == 5000
+    assert np.array_equal(sel_idx.cpu().numpy()[1, 0], np.arange(100))
+    assert np.all(hist.cpu().numpy()[0] == 0)
+    assert so.count == 5000
+
+
+# ---------------------------------------------------------------------------
+# rtp_sparse_decode
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_sparse_decode_matches_oracle(rtp, dtype):
+    say("sparse_decode", dtype)
+    lens = [6000, 300]
+    G, Hr = 4, 2
+    wl = workloads.make_workload("t", 2, lens, G * Hr, Hr, [[1, 1]], seed=41, dtype=dtype,
+                                 device=dev())
+    lay = wl.layers[0]
+    rng = np.random.default_rng(3)
+    cap = 6000
+    sel = np.full((2, G * Hr, cap), -1, dtype=np.int32)
+    cnt = np.zeros((2, G * Hr), dtype=np.int32)
+    sets = {}
+    sizes = [0, 1, 2, 63, 64, 65, 1000, 6000]
+    for b in range(2):
+        for h in range(G * Hr):
+            n = min(sizes[(h + b) % len(sizes)], lens[b])
+            s = np.sort(rng.choice(lens[b], n, replace=False)).astype(np.int32)
+            sel[b, h, :n] = s
+            cnt[b, h] = n
+            sets[(b, h)] = s
+    out, lse = rtp.rtp_sparse_decode(lay.q, lay.K_ret, lay.V_ret, torch.from_numpy(sel).to(dev()),
+                                     torch.from_numpy(cnt).to(dev()), wl.scale_attn)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    qn = oracle.np_of(lay.q)
+    for b in range(2):
+        for h in range(G * Hr):
+            s = sets[(b, h)]
+            if len(s) == 0:
+                assert np.all(out[b, h] == 0) and lse[b, h] == -np.inf
+                continue
+            o, l = oracle.attention(qn[b, h], oracle.np_of(lay.K_ret[b, h // G]),
+                                    oracle.np_of(lay.V_ret[b, h // G]), s, wl.scale_attn)
+            assert max_err(out[b, h], o) <= out_tol(dtype), (b, h, len(s))
+            assert abs(lse[b, h] - l) <= 1e-4 * max(1, abs(l))
+
+
+# ---------------------------------------------------------------------------
+# rtp_window_decode
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,window,sinks,lens", [
+    ("f16", 64, 4, [1, 3, 4, 5, 67, 68, 69, 500]),
+    ("f32", 64, 4, [2, 68, 1000]),
+    ("f16", 100, 0, [50, 100, 101, 333]),
+    ("f16", 8192, 4, [8196, 9000, 4000]),
+])
+def test_window_decode_matches_oracle(rtp, dtype, window, sinks, lens):
+    say("window_decode", dtype, window, sinks, lens)
+    G, Hl = 8, 2
+    wl = workloads.make_workload("t", len(lens), lens, G * Hl, Hl, [[0, 0]], seed=51, dtype=dtype,
+                                 window=window, sinks=sinks, device=dev())
+    lay = wl.layers[0]
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev())
+    out, lse = rtp.rtp_window_decode(lay.q, lay.K_loc, lay.V_loc, sl, window, sinks, wl.scale_attn)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    qn = oracle.np_of(lay.q)
+    for b, L in enumerate(lens):
+        rows = oracle.ring_slot(oracle.window_positions(L, window, sinks), window, sinks)
+        for h in range(G * Hl):
+            o, l = oracle.attention(qn[b, h], oracle.np_of(lay.K_loc[b, h // G]),
+                                    oracle.np_of(lay.V_loc[b, h // G]), rows, wl.scale_attn)
+            assert max_err(out[b, h], o) <= out_tol(dtype), (b, h, L)
+            assert abs(lse[b, h] - l) <= 1e-4 * max(1, abs(l))
+
+
+# ---------------------------------------------------------------------------
+# rtp_decode_step
+# ---------------------------------------------------------------------------
+def check_decode(rtp, wl, local_sample=None, layers=None, label=""):
+    """Run every layer on the GPU and compare with the oracle (all retrieval heads; all
+    local heads or the first `local_sample` of each layer)."""
+    res = rtp.decode_workload(wl, want_debug=True)
+    torch.cuda.synchronize()
+    st = SelCheck()
+    tol = out_tol(wl.dtype)
+    worst = 0.0
+    for li, layer in enumerate(wl.layers):
+        if layers is not None and li not in layers:
+            continue
+        if len(wl.layers) > 2:
+            say(label, "layer", li)
+        out, lse, thr, cnt = (t.cpu().numpy() for t in res[li])
+        heads = None
+        if local_sample is not None:
+            loc_q = [kh * wl.G + g for kh in layer.loc_heads for g in range(wl.G)][:local_sample]
+            ret_q = [kh * wl.G + g for kh in layer.ret_heads for g in range(wl.G)]
+            heads = ret_q + loc_q
+        orc = oracle.decode_layer(layer, wl.seq_lens, wl.Hq, wl.Hkv, wl.p, wl.bin_width,
+                                  wl.scale_idx, wl.scale_attn, wl.window, wl.sinks, heads=heads)
+        for (b, h), r in orc.items():
+            where = "%s layer %d b %d head %d" % (label, li, b, h)
+            o_ref = r.out
+            if r.sel is not None:
+                A, bs = int(thr[b, h, 0]), int(thr[b, h, 1])
+                ex = expected_set(r.z, r.sel, A, bs, wl.p, wl.bin_width, st, where)
+                compare_count(int(cnt[b, h]), ex, r.z, wl.bin_width, A, bs, st, where)
+                if ex is not r.sel.idx:
+                    kr = layer.ret_heads.index(h // wl.G)
+                    o_ref, _ = oracle.attention(oracle.np_of(layer.q)[b, h],
+                                                oracle.np_of(layer.K_ret[b, kr]),
+                                                oracle.np_of(layer.V_ret[b, kr]), ex, wl.scale_attn)
+            e = max_err(out[b, h], o_ref)
+            worst = max(worst, e)
+            assert e <= tol, "%s: max |dO| = %g > %g" % (where, e, tol)
+            assert abs(lse[b, h] - r.lse) <= 1e-3 * max(1.0, abs(r.lse)), where
+    say(label, "rows", st.rows, "mass ties", st.mass_ties, "edge tokens", st.edge_tokens,
+        "worst |dO|", worst)
+    return res
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("p", [0.5, 0.9, 1.0])
+def test_decode_step_small_ragged(rtp, dtype, p):
+    say("decode_step small", dtype, p)
+    wl = workloads.make_workload("t", 3, [3000, 1, 4099], 32, 4, [[1, 0, 1, 0]], seed=61, p=p,
+                                 dtype=dtype, window=256, sinks=4, device=dev())
+    check_decode(rtp, wl, label="small-%s-p%g" % (dtype, p))
+
+
+def test_decode_step_p1_is_dense_attention(rtp):
+    say("decode_step p=1 dense")
+    wl = workloads.make_workload("t", 2, [2500, 700], 8, 2, [[1, 0]], seed=62, p=1.0,
+                                 dtype="f16", window=4096, sinks=4, device=dev())
+    res = rtp.decode_workload(wl)[0]
+    out = res[0].cpu().numpy()
+    lay = wl.layers[0]
+    for b, L in enumerate([2500, 700]):
+        for h in range(8):
+            if h < 4:
+                K = oracle.np_of(lay.K_ret[b, 0, :L]).astype(np.float64)
+                V = oracle.np_of(lay.V_ret[b, 0, :L]).astype(np.float64)
+            else:
+                slot = oracle.ring_slot(np.arange(L), 4096, 4)
+                K = oracle.np_of(lay.K_loc[b, 0]).astype(np.float64)[slot]
+                V = oracle.np_of(lay.V_loc[b, 0]).astype(np.float64)[slot]
+            q = oracle.np_of(lay.q)[b, h].astype(np.float64)
+            s = K @ q * wl.scale_attn
+            w = np.exp(s - s.max())
+            ref = (w[:, None] * V).sum(0) / w.sum()
+            assert max_err(out[b, h], ref) <= 2e-3
+
+
+def test_decode_step_empty_sequence(rtp):
+    say("decode_step empty sequence")
+    wl = workloads.make_workload("t", 2, [0, 1500], 8, 2, [[1, 0]], seed=63, p=0.9, dtype="f16",
+                                 window=512, sinks=4, device=dev(), Lmax=1500)
+    out, lse, thr, cnt = rtp.decode_workload(wl, want_debug=True)[0]
+    out, lse, cnt = out.cpu().numpy(), lse.cpu().numpy(), cnt.cpu().numpy()
+    assert np.all(out[0] == 0) and np.all(lse[0] == -np.inf) and np.all(cnt[0] == 0)
+    assert np.all(np.isfinite(out[1]))
+
+
+def test_decode_step_deterministic(rtp):
+    say("decode_step determinism")
+    wl = workloads.make_workload("t", 2, [20000, 9000], 32, 4, [[1, 0, 0, 1]], seed=64, p=0.9,
+                                 dtype="f16", device=dev())
+    a = [t.clone() for t in rtp.decode_workload(wl, want_debug=True)[0]]
+    b = rtp.decode_workload(wl, want_debug=True)[0]
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c4"])
+def test_decode_step_config(rtp, name):
+    say("config", name)
+    wl = workloads.make_config(name, device=dev())
+    check_decode(rtp, wl, label=name)
+
+
+@pytest.mark.parametrize("p", [0.8, 0.95])
+def test_decode_step_c4_p_sweep(rtp, p):
+    say("config c4 p", p)
+    wl = workloads.make_config("c4", device=dev(), p=p)
+    check_decode(rtp, wl, label="c4-p%g" % p)
+
+
+def test_decode_step_c3_48_layers(rtp):
+    say("config c3 (48 layers; all retrieval heads, 8 local query heads per layer)")
+    wl = workloads.make_config("c3", device=dev())
+    check_decode(rtp, wl, local_sample=8, label="c3")

@@ -187,6 +187,8 @@ def _targets(rng: np.random.Generator, L: int, cls: str, k: int):
     """Target logits z[0:L] for one query head; returns (z, positions)."""
     f = PLANTED_SHARE
     odds = f / (1.0 - f)
+    if L == 0:
+        return np.zeros(0), np.zeros(0, dtype=np.int64)
     k = max(1, min(k, L))
     if cls in ("concentrated", "needle"):
         z = rng.standard_normal(L)
