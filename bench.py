@@ -187,36 +187,33 @@ def main():
     torch.cuda.synchronize()
     ms_step = elapsed_ms(h, e0, e1) / args.steps
 
-    # ---- dominant kernel (indexer score + histogram) timed with events in the step ----
+    # ---- per-kernel durations, timed live with HIP events on the launch stream ----
+    # events: [0] before stage A, [1] after stage A (score+histogram and window
+    # attention), [2] after the threshold kernel, [3] after the last kernel
     K = args.steps
-    evs = make_events(h, 7 * K)
-    # each step records its own 7 events: re-point them per step (eager launches)
+    evs = make_events(h, 4 * K)
     torch.cuda.synchronize()
     for i in range(K):
         st = steps[i % R]
-        for j in range(7):
-            st.desc.prof_ev[j] = evs[i * 7 + j].value
+        for j in range(4):
+            st.desc.prof_ev[j] = evs[i * 4 + j].value
         st()
     torch.cuda.synchronize()
     for st in steps:
-        for j in range(7):
+        for j in range(4):
             st.desc.prof_ev[j] = None
-    ph = {"hist": 0.0, "threshold": 0.0, "select": 0.0, "sparse+merge": 0.0, "window+merge": 0.0}
+    ph = {"stageA_score_hist_window": 0.0, "stageT_threshold": 0.0, "stageB_select_attend": 0.0}
     has_ret = bool(layer.ret_heads)
-    has_loc = bool(layer.loc_heads)
     for i in range(K):
-        e = evs[i * 7:(i + 1) * 7]
+        e = evs[i * 4:(i + 1) * 4]
+        ph["stageA_score_hist_window"] += elapsed_ms(h, e[0], e[1])
         if has_ret:
-            ph["hist"] += elapsed_ms(h, e[0], e[1])
-            ph["threshold"] += elapsed_ms(h, e[1], e[2])
-            ph["select"] += elapsed_ms(h, e[2], e[3])
-            ph["sparse+merge"] += elapsed_ms(h, e[3], e[4])
-        if has_loc:
-            ph["window+merge"] += elapsed_ms(h, e[5], e[6])
+            ph["stageT_threshold"] += elapsed_ms(h, e[1], e[2])
+            ph["stageB_select_attend"] += elapsed_ms(h, e[2], e[3])
     ph = {k: v / K * 1000.0 for k, v in ph.items()}  # microseconds
-    hist_us = ph["hist"]
-    hist_bytes = detail["kidx"]
-    achieved = hist_bytes / (hist_us * 1e-6) / 1e9 if hist_us > 0 else 0.0
+    a_us = ph["stageA_score_hist_window"]
+    a_bytes = detail["kidx"] + detail["window_kv"]
+    achieved = a_bytes / (a_us * 1e-6) / 1e9 if a_us > 0 else 0.0
 
     value = bytes_step / (ms_step * 1e-3) / 1e9
     res = {
@@ -243,10 +240,10 @@ def main():
         "bytes_per_step": bytes_step,
         "bytes_detail": {k: v for k, v in detail.items() if k != "sel_tokens"},
         "sel_tokens_per_head": detail["sel_tokens"],
-        "roofline": {"kernel": "score+histogram (k_hist)", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "avg_us": round(hist_us, 3), "algorithmic_bytes_per_launch": hist_bytes},
+        "roofline": {"kernel": "k_stage_a (indexer score + 256-bin histograms, window attention)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "avg_us": round(a_us, 3), "algorithmic_bytes_per_launch": a_bytes},
         "phases_us_eager": {k: round(v, 3) for k, v in ph.items()},
     }
     if not args.skip_cpu:

@@ -127,7 +127,8 @@ def _kv_dtype(t: torch.Tensor) -> int:
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    """Zero-filled workspace (the decode step keeps completion counters in it)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 # ---------------------------------------------------------------------------

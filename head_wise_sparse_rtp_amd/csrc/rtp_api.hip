@@ -84,6 +84,8 @@ int window_maxs(int window, int sinks) { return (window + sinks + kWinSplit - 1)
 // --- decode step plan -------------------------------------------------------------
 struct StepPlan {
   int Hret = 0, Hloc = 0, G = 0;
+  bool fused = false;
+  StepFusedPlan fp{};
   HeadMap ret{}, loc{};
   SelectPlan sel{};
   size_t sel_idx = 0, sel_cnt = 0;
@@ -111,6 +113,15 @@ rtp_status plan_step(const rtp_layer_desc* d, StepPlan& sp) {
   sp.Hret = sp.ret.n;
   sp.Hloc = sp.loc.n;
   if (sp.Hloc > 0 && (d->window < 1 || d->sinks < 0)) return RTP_EINVAL;
+  if (sp.Hloc > 0 && (int64_t)d->window + d->sinks > (1 << 24)) return RTP_EUNSUPPORTED;
+  if (step_fused_supported(d->kv_dtype, sp.G, sp.Hloc, d->window, d->sinks)) {
+    sp.fused = true;
+    WsPlanner wp;
+    sp.fp = plan_step_fused(wp, d->B, d->Hq, sp.G, d->Lmax, sp.Hret, sp.Hloc, d->window,
+                            d->sinks);
+    sp.bytes = sp.fp.bytes;
+    return RTP_OK;
+  }
   size_t off = 0;
   if (sp.Hret > 0) {
     const int H = sp.Hret * sp.G;
@@ -279,12 +290,42 @@ rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, v
   char* w = static_cast<char*>(ws);
   hipError_t e = hipSuccess;
   const int G = sp.G;
+  if (sp.fused) {
+    StepFusedArgs a{};
+    a.B = d->B;
+    a.Hq = d->Hq;
+    a.Lmax = d->Lmax;
+    a.window = d->window;
+    a.sinks = d->sinks;
+    a.seq_lens = d->seq_lens;
+    a.q = d->q;
+    a.q_idx = d->q_idx;
+    a.K_ret = d->K_ret;
+    a.V_ret = d->V_ret;
+    a.k_idx = d->k_idx;
+    a.K_loc = d->K_loc;
+    a.V_loc = d->V_loc;
+    a.ret = sp.ret;
+    a.loc = sp.loc;
+    a.p = d->p;
+    a.bin_width = d->bin_width;
+    a.scale_idx = d->scale_idx;
+    a.scale_attn = d->scale_attn;
+    a.out = d->out;
+    a.lse = d->lse;
+    a.hist_out = nullptr;
+    a.thresh_out = d->thresh_out;
+    a.count_out = d->count_out;
+    hipEvent_t ev[4];
+    for (int i = 0; i < 4; i++) ev[i] = (hipEvent_t)d->prof_ev[i];
+    return hip_status(launch_step_fused(sp.fp, w, a, st, ev));
+  }
   auto mark = [&](int i) {
     if (e == hipSuccess && d->prof_ev[i]) e = hipEventRecord((hipEvent_t)d->prof_ev[i], st);
   };
+  mark(0);
   if (sp.Hloc > 0) {
     const AttnPartials pa = bind_parts(w, sp.win);
-    mark(5);
     if (e == hipSuccess)
       e = launch_window_partial(d->q, d->K_loc, d->V_loc, d->kv_dtype, d->seq_lens, sp.loc, d->B,
                               d->Hq, sp.Hloc, G, d->window, d->sinks, d->scale_attn, pa, sp.wmaxs,
@@ -292,14 +333,12 @@ rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, v
     if (e == hipSuccess)
       e = launch_merge(pa, sp.wmaxs, nullptr, 0, sp.loc, d->B, d->Hq, sp.Hloc, G, d->out, d->lse,
                        st);
-    mark(6);
   }
   if (e == hipSuccess && sp.Hret > 0) {
     const int H = sp.Hret * G;
     const SelectBufs sb = bind_select(w, sp.sel.offs);
     int32_t* sel_idx = reinterpret_cast<int32_t*>(w + sp.sel_idx);
     int32_t* sel_cnt = reinterpret_cast<int32_t*>(w + sp.sel_cnt);
-    mark(0);
     if (e == hipSuccess)
       e = launch_hist_from_kidx(d->q_idx, d->k_idx, d->kv_dtype, d->seq_lens, sp.ret, d->B,
                                 d->Hq, sp.Hret, G, d->Lmax, d->scale_idx, d->bin_width, sp.sel.cg,
@@ -312,7 +351,6 @@ rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, v
     if (e == hipSuccess)
       e = launch_select(d->seq_lens, d->B, H, d->Lmax, sp.sel.cg, sb, sel_idx, sel_cnt, d->Lmax,
                         d->count_out, &sp.ret, G, d->Hq, st);
-    mark(3);
     const AttnPartials pa = bind_parts(w, sp.sparse);
     if (e == hipSuccess)
       e = launch_sparse_partial(d->q, d->K_ret, d->V_ret, d->kv_dtype, sel_idx, sel_cnt, d->Lmax,
@@ -321,8 +359,8 @@ rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, v
     if (e == hipSuccess)
       e = launch_merge(pa, sp.smaxs, sel_cnt, d->Lmax, sp.ret, d->B, d->Hq, sp.Hret, G, d->out,
                        d->lse, st);
-    mark(4);
   }
+  mark(3);
   return hip_status(e);
 }
 

@@ -120,6 +120,42 @@ struct WsPlanner {
   }
 };
 
+// ---------------------------------------------------------------------------
+// fused decode step (fp16 caches, G <= 16): stage A (window + histogram blocks),
+// stage T (threshold), stage B (selection + MFMA attention + merges)
+// ---------------------------------------------------------------------------
+struct StepFusedPlan {
+  int G, Hret, Hloc, tpt, tc, nchunk, nblk, nws, nrange;
+  size_t suf, partA, codes, bstar, Aglob, tpart;
+  size_t p1m, p1l, p1acc, p1cnt;
+  size_t wpm, wpl, wpacc;
+  size_t bytes;
+};
+
+struct StepFusedArgs {
+  int B, Hq, Lmax, window, sinks;
+  const int32_t* seq_lens;
+  const void* q;
+  const float* q_idx;
+  const void *K_ret, *V_ret, *k_idx, *K_loc, *V_loc;
+  HeadMap ret, loc;
+  double p;
+  float bin_width, scale_idx, scale_attn;
+  float* out;
+  float* lse;
+  float* hist_out;
+  int32_t* thresh_out;
+  int32_t* count_out;
+};
+
+bool step_fused_supported(int kv_dtype, int G, int Hloc, int window, int sinks);
+StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int Hret, int Hloc,
+                              int window, int sinks);
+// ev (may be null): events recorded before stage A, after stage A, after stage T and
+// after the last kernel
+hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedArgs& a,
+                             hipStream_t st, hipEvent_t* ev);
+
 size_t plan_select(WsPlanner& wp, int B, int H, int Lmax, const ChunkGeom& cg, size_t offs[7]);
 SelectBufs bind_select(char* ws, const size_t offs[7]);
 

@@ -157,13 +157,16 @@ typedef struct {
   float* lse;                     /* [B, Hq] fp32 out or NULL */
   int32_t* thresh_out;            /* [B, Hq, 2] {A, b*} for retrieval query heads, or NULL */
   int32_t* count_out;             /* [B, Hq] |S| for retrieval query heads, or NULL */
-  /* Optional profiling: hipEvent_t handles (or NULL) recorded on `stream` at phase
-   * boundaries: [0] before the score/histogram kernel, [1] after it, [2] after the
-   * threshold, [3] after the selection, [4] after the sparse attention and its merge,
-   * [5] before the window attention, [6] after the window merge, [7] unused. */
+  /* Optional profiling: hipEvent_t handles (or NULL) recorded on `stream`: [0] before
+   * the first kernel, [1] after the indexer-score/histogram kernel (which also runs the
+   * window attention of local heads), [2] after the threshold kernel, [3] after the
+   * last kernel.  [4..7] are reserved and must be NULL. */
   void* prof_ev[8];
 } rtp_layer_desc;
 
+/* fp16 caches with G <= 16 run four kernels per call (indexer score + histograms with the
+ * window attention; threshold sums with the window merge; selection + sparse attention;
+ * merge); other shapes run the single-purpose kernels in sequence. */
 size_t rtp_decode_step_workspace_size(const rtp_layer_desc* desc);
 rtp_status rtp_decode_step(const rtp_layer_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
