@@ -125,7 +125,7 @@ struct WsPlanner {
 // stage T (threshold), stage B (selection + MFMA attention + merges)
 // ---------------------------------------------------------------------------
 struct StepFusedPlan {
-  int G, Hret, Hloc, tpt, tc, nchunk, nblk, nws, nrange;
+  int G, Hret, Hloc, tpt, tc, nt, nchunk, nblk, nws, nrange;
   size_t suf, partA, codes, bstar, Aglob, tpart;
   size_t p1m, p1l, p1acc, p1cnt;
   size_t wpm, wpl, wpacc;

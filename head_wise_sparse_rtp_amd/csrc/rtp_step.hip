@@ -39,7 +39,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAttnG = 16;        // head columns of the MFMA tile
 constexpr int kStep = 32;         // cache rows per wavefront step
-constexpr int kWinRows = 256;     // window rows per block (4 waves x 2 steps)
+constexpr int kWinRows = 128;     // window rows per window block (4 waves x 1 step)
 constexpr int kBChunks = 4;       // histogram chunks per stage-B block
 constexpr int kBGroup = 16;       // stage-B blocks merged per first-level group
 
@@ -169,57 +169,72 @@ __device__ __forceinline__ void step_compute(const StepLoads& ld, const h8 (&qop
   }
 }
 
-// Combine the 4 wavefronts of a block into per-head partials in LDS:
-//   sm[16], sl[16], sacc[16][128] (unnormalised), written for heads < G.
-__device__ void block_combine(AttnState& st, int G, float* lds /* >= 4*(32+2048) floats */,
-                              float* out_m, float* out_l, float* out_acc) {
+// Combine the NWV wavefronts of a block into per-head partials (unnormalised), written
+// to out_m/out_l/out_acc for heads < G.  Waves pass through LDS four at a time;
+// lds >= 4*(32+2048) floats.
+template <int NWV>
+__device__ void block_combine(AttnState& st, int G, float* lds, float* out_m, float* out_l,
+                              float* out_acc) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int h = lane & 15;
   const int gq = lane >> 4;
-  // per-head sum over the 4 lane groups
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  float* wm = lds + wv * (32 + 2048);
-  float* wl = wm + 16;
-  float* wacc = wm + 32;
-  if (lane < 16) {
-    wm[h] = st.m;
-    wl[h] = l;
-  }
-#pragma unroll
-  for (int nb = 0; nb < 8; nb++) {
-#pragma unroll
-    for (int t = 0; t < 4; t++) wacc[(4 * gq + t) * kD + 8 * h + nb] = st.o[nb][t];
-  }
-  __syncthreads();
-  // thread -> (head, 8 dims): 16 heads x 16 dim-groups = 256 threads
+  // item of this thread (threads 0..255): head th, dims d0..d0+7
   const int th = threadIdx.x >> 4;
   const int d0 = (threadIdx.x & 15) * 8;
-  if (th < G) {
-    float M = -INFINITY;
-    for (int w = 0; w < 4; w++) M = fmaxf(M, lds[w * (32 + 2048) + th]);
-    float L = 0.0f, a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (M != -INFINITY) {
-      for (int w = 0; w < 4; w++) {
-        const float* base = lds + w * (32 + 2048);
-        const float mw = base[th];
-        if (mw == -INFINITY) continue;
-        const float f = __builtin_amdgcn_exp2f(mw - M);
-        L += base[16 + th] * f;
+  const bool item = threadIdx.x < 256 && th < G;
+  float M = -INFINITY, L = 0.0f, a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int wg = 0; wg < (NWV + 3) / 4; wg++) {
+    if (wv / 4 == wg) {
+      float* wm = lds + (wv % 4) * (32 + 2048);
+      float* wl = wm + 16;
+      float* wacc = wm + 32;
+      if (lane < 16) {
+        wm[h] = st.m;
+        wl[h] = l;
+      }
 #pragma unroll
-        for (int i = 0; i < 8; i++) a[i] += base[32 + th * kD + d0 + i] * f;
+      for (int nb = 0; nb < 8; nb++) {
+#pragma unroll
+        for (int t = 0; t < 4; t++) wacc[(4 * gq + t) * kD + 8 * h + nb] = st.o[nb][t];
       }
     }
+    __syncthreads();
+    if (item) {
+      const int nw = min(4, NWV - 4 * wg);
+      float Mn = M;
+      for (int w = 0; w < nw; w++) Mn = fmaxf(Mn, lds[w * (32 + 2048) + th]);
+      if (Mn != -INFINITY) {
+        const float fo = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+        L *= fo;
+#pragma unroll
+        for (int i = 0; i < 8; i++) a[i] *= fo;
+        for (int w = 0; w < nw; w++) {
+          const float* base = lds + w * (32 + 2048);
+          const float mw = base[th];
+          if (mw == -INFINITY) continue;
+          const float f = __builtin_amdgcn_exp2f(mw - Mn);
+          L += base[16 + th] * f;
+#pragma unroll
+          for (int i = 0; i < 8; i++) a[i] += base[32 + th * kD + d0 + i] * f;
+        }
+        M = Mn;
+      }
+    }
+    __syncthreads();
+  }
+  if (item) {
     if (d0 == 0) {
       out_m[th] = M;
       out_l[th] = L;
     }
-#pragma unroll
-    for (int i = 0; i < 8; i++) out_acc[th * kD + d0 + i] = a[i];
+    float4* dst = reinterpret_cast<float4*>(out_acc + th * kD + d0);
+    dst[0] = make_float4(a[0], a[1], a[2], a[3]);
+    dst[1] = make_float4(a[4], a[5], a[6], a[7]);
   }
-  __syncthreads();
 }
 
 // Merge the n split partials of one head g (pm/pl [n][G], pacc [n][G][128], optional
@@ -311,40 +326,43 @@ constexpr int kCopies = 2;
 constexpr int kPad = 1;
 
 struct StageAParams {
-  // common
   const int32_t* seq_lens;
   int B, Hq, G, Lmax;
-  // window
-  const f16* q;
-  const f16* K_loc;
-  const f16* V_loc;
-  HeadMap loc;
-  int Hloc, window, sinks, nws, nwin_blocks;
-  float scale2;
-  float* wpm;
-  float* wpl;
-  float* wpacc;
-  float* out;
-  float* lse;
-  // histogram
   const float* q_idx;
   const f16* k_idx;
   HeadMap ret;
-  int Hret, nchunk, ngg, nhist_blocks;
+  int Hret, nchunk, ngg;
   float yscale, c_log2;
   double w;
   float* suf;
   int32_t* partA;
   uint32_t* codes;
-  int32_t* bstar;
 };
 
-template <int GG, int TPT>
+struct WinParams {
+  const int32_t* seq_lens;
+  int Hq, G;
+  const f16* q;
+  const f16* K_loc;
+  const f16* V_loc;
+  HeadMap loc;
+  int Hloc, window, sinks, nws;
+  float scale2;
+  float* wpm;
+  float* wpl;
+  float* wpacc;
+};
+
+// Token t (0..3) of thread tid in a chunk is chunk*TC + t*NT + tid; the 4 bin codes of a
+// thread are packed into code word `tid` of the chunk (byte t).
+template <int GG, int NT>
 __device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
-  constexpr int TC = kThreads * TPT;
+  constexpr int TPT = 4;
+  constexpr int TC = NT * TPT;
+  constexpr int NWV = NT / 64;
   unsigned long long* hist = reinterpret_cast<unsigned long long*>(smem);
   float* smax = reinterpret_cast<float*>(smem + sizeof(unsigned long long) * kCopies * GG * (kNB + kPad));
-  float* sq = smax + GG * 4;  // q_idx of the GG heads, [GG][16]
+  float* sq = smax + GG * NWV;  // q_idx of the GG heads, [GG][16]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -364,12 +382,12 @@ __device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
     return;
   }
   const bool full = base + TC <= L;
-  // k_idx rows of this thread's tokens (token base + t*256 + tid), all loads in flight
+  // k_idx rows of this thread's tokens, all loads in flight
   const f16* kb = P.k_idx + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kR;
   h8 ra[TPT], rb[TPT];
 #pragma unroll
   for (int t = 0; t < TPT; t++) {
-    int n = base + t * kThreads + tid;
+    int n = base + t * NT + tid;
     n = n < L ? n : base;  // past the end: re-read a valid row, masked below
     const h8* p = reinterpret_cast<const h8*>(kb + (size_t)n * kR);
     ra[t] = p[0];
@@ -381,7 +399,7 @@ __device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
                                    (tid % kR)]
                          : 0.0f;
   }
-  for (int i = tid; i < kCopies * GG * (kNB + kPad); i += kThreads) hist[i] = 0ull;
+  for (int i = tid; i < kCopies * GG * (kNB + kPad); i += NT) hist[i] = 0ull;
   __syncthreads();
 
   // ---- pass 1: y = fl32(a * scale) / w (exact: w is a power of two) and the top cell
@@ -400,20 +418,23 @@ __device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
 #pragma unroll
       for (int i = 0; i < 8; i++) a = __builtin_fmaf(q[8 + i], (float)rb[t][i], a);
       float v = a * P.yscale;
-      if (!full && base + t * kThreads + tid >= L) v = -INFINITY;
+      if (!full && base + t * NT + tid >= L) v = -INFINITY;
       y[t][gg] = v;
       ym = fmaxf(ym, v);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) ym = fmaxf(ym, __shfl_xor(ym, o, 64));
-    if (lane == 0) smax[gg * 4 + wv] = ym;
+    if (lane == 0) smax[gg * NWV + wv] = ym;
   }
   __syncthreads();
   float Acf[GG];
 #pragma unroll
-  for (int gg = 0; gg < GG; gg++)
-    Acf[gg] = floorf(fmaxf(fmaxf(smax[gg * 4 + 0], smax[gg * 4 + 1]),
-                           fmaxf(smax[gg * 4 + 2], smax[gg * 4 + 3])));
+  for (int gg = 0; gg < GG; gg++) {
+    float m = smax[gg * NWV];
+#pragma unroll
+    for (int k = 1; k < NWV; k++) m = fmaxf(m, smax[gg * NWV + k]);
+    Acf[gg] = floorf(m);
+  }
 
   // ---- pass 2: exact per-bin sums of x * 2^24, x = exp(z - (g+1) w), and the bin codes
   const int copy = lane & (kCopies - 1);
@@ -422,13 +443,11 @@ __device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
 #pragma unroll
   for (int gg = 0; gg < GG; gg++) {
     if (gg >= nrows) break;
-    uint32_t cw[TPT / 4];
-#pragma unroll
-    for (int i = 0; i < TPT / 4; i++) cw[i] = 0u;
+    uint32_t cw = 0u;
 #pragma unroll
     for (int t = 0; t < TPT; t++) {
       const float yv = y[t][gg];
-      const bool valid = full || (base + t * kThreads + tid < L);
+      const bool valid = full || (base + t * NT + tid < L);
       const float gf = floorf(yv);
       const float diff = Acf[gg] - gf;          // exact: integral and below 2^24
       const float jf = fminf(diff, 255.0f);
@@ -438,15 +457,13 @@ __device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
       const uint32_t j = valid ? (uint32_t)jf : 255u;
       const uint32_t xi = valid ? (uint32_t)e : 0u;
       atomicAdd(&hrow[gg * (kNB + kPad) + j], (unsigned long long)xi);
-      cw[t >> 2] |= j << (8 * (t & 3));
+      cw |= j << (8 * t);
     }
-    uint32_t* cdst = P.codes + ((rowb + gg) * P.nchunk + chunk) * (size_t)(TC / 4) + tid;
-#pragma unroll
-    for (int i = 0; i < TPT / 4; i++) cdst[i * kThreads] = cw[i];
+    P.codes[((rowb + gg) * P.nchunk + chunk) * (size_t)(TC / 4) + tid] = cw;
   }
   __syncthreads();
   // suffix sums of the bin masses, one head per wavefront pass: lane k owns bins 4k..4k+3
-  for (int gg = wv; gg < nrows; gg += kThreads / 64) {
+  for (int gg = wv; gg < nrows; gg += NWV) {
     double mloc[4];
 #pragma unroll
     for (int u = 0; u < 4; u++) {
@@ -472,18 +489,17 @@ __device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
     acc += mloc[0]; outv.x = (float)acc;
     reinterpret_cast<float4*>(dst)[lane] = outv;
     if (lane == 0) {
-      const float m = fmaxf(fmaxf(smax[gg * 4 + 0], smax[gg * 4 + 1]),
-                            fmaxf(smax[gg * 4 + 2], smax[gg * 4 + 3]));
+      float m = smax[gg * NWV];
+      for (int k = 1; k < NWV; k++) m = fmaxf(m, smax[gg * NWV + k]);
       P.partA[(rowb + gg) * P.nchunk + chunk] = (int)floorf(m);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// window block (local): entries [wsplit*256, +256) of the window set -> one partial
+// window block (local): 4 wavefronts x 32 entries of the window set -> one partial
 // ---------------------------------------------------------------------------
-__device__ void window_block(const StageAParams& P, int wb, unsigned char* smem) {
-  float* lds = reinterpret_cast<float*>(smem);
+__device__ void window_block(const WinParams& P, int wb, float* lds) {
   const int wsplit = wb % P.nws;
   const int kl = (wb / P.nws) % P.Hloc;
   const int b = wb / (P.nws * P.Hloc);
@@ -501,77 +517,47 @@ __device__ void window_block(const StageAParams& P, int wb, unsigned char* smem)
   load_qop(P.q + ((size_t)b * P.Hq + (size_t)P.loc.kv[kl] * G) * kD, G, qop);
   AttnState st;
   attn_init(st);
-  const int e_wave = wsplit * kWinRows + wv * (kWinRows / 4);
+  const int e0 = wsplit * kWinRows + wv * kStep;
   const int sinks = P.sinks, window = P.window;
   auto slot_of = [&](int e) {
     e = e < nwin ? e : 0;  // rows past the end read entry 0 (masked below)
     const int pos = e < ns ? e : wstart + (e - ns);
     return pos < sinks ? pos : sinks + pos % window;
   };
-  if (nwin > 0 && e_wave < nwin) {
-    StepLoads ld[2];
-#pragma unroll
-    for (int k = 0; k < 2; k++)
-      step_load(Kb, Vb, [&](int i) { return slot_of(e_wave + k * kStep + i); }, ld[k]);
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-      const int e0 = e_wave + k * kStep;
-      step_compute(ld[k], qop, P.scale2, [&](int i, int h) { return e0 + i < nwin; }, st);
-    }
+  if (nwin > 0 && e0 < nwin) {
+    StepLoads ld;
+    step_load(Kb, Vb, [&](int i) { return slot_of(e0 + i); }, ld);
+    step_compute(ld, qop, P.scale2, [&](int i, int h) { return e0 + i < nwin; }, st);
   }
   const size_t prow = ((size_t)(b * P.Hloc + kl) * P.nws + wsplit) * G;
-  block_combine(st, G, lds, P.wpm + prow, P.wpl + prow, P.wpacc + prow * kD);
+  block_combine<kThreads / 64>(st, G, lds, P.wpm + prow, P.wpl + prow, P.wpacc + prow * kD);
 }
 
-template <int GG, int TPT>
-__global__ __launch_bounds__(kThreads, 2) void k_stage_a(StageAParams P) {
+template <int GG, int NT>
+__global__ __launch_bounds__(NT, 2) void k_stage_a(StageAParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
-  if ((int)blockIdx.x < P.nhist_blocks)
-    hist_block<GG, TPT>(P, blockIdx.x, smem);
-  else
-    window_block(P, blockIdx.x - P.nhist_blocks, smem);
+  hist_block<GG, NT>(P, blockIdx.x, smem);
 }
 
 // ---------------------------------------------------------------------------
 // stage T: threshold range sums (block (range, row), thread = global bin J):
 //   SUF_J(range) = sum_{c in range} suf_c[max(J - s_c, 0)] * exp(-s_c w),  s_c = A - A_c
-// over 32 chunks (coalesced: lanes read consecutive bins of one chunk).  Blocks past the
-// range blocks merge the window partials of one local query head each.
+// over 32 chunks (coalesced: lanes read consecutive bins of one chunk).
 // ---------------------------------------------------------------------------
 constexpr int kTRange = 32;  // chunks per stage-T block
 
 struct StageTParams {
   const float* suf;
   const int32_t* partA;
-  int nchunk, nrange, nT;
+  int nchunk, nrange;
   float c_log2;
   double* tpart;
   int32_t* Aglob;
-  // window merge
-  const float* wpm;
-  const float* wpl;
-  const float* wpacc;
-  int nws, Hloc, G, Hq;
-  HeadMap loc;
-  float* out;
-  float* lse;
 };
 
 __global__ __launch_bounds__(kThreads) void k_stage_t(StageTParams P) {
-  __shared__ float lds[1024 + kThreads + 8 * kD];
-  if ((int)blockIdx.x >= P.nT) {
-    // window merge block: (b, local KV head, query head)
-    const int wm = blockIdx.x - P.nT;
-    const int g = wm % P.G;
-    const int kl = (wm / P.G) % P.Hloc;
-    const int b = wm / (P.G * P.Hloc);
-    const size_t p0 = (size_t)(b * P.Hloc + kl) * P.nws * P.G;
-    merge_head(P.wpm + p0, P.wpl + p0, P.wpacc + p0 * kD, nullptr, P.nws, P.G, g, P.out, P.lse,
-               nullptr, (size_t)b * P.Hq + (size_t)P.loc.kv[kl] * P.G + g, lds);
-    return;
-  }
-  int* sAi = reinterpret_cast<int*>(lds);
-  int* sAc = sAi + 8;
+  __shared__ int sAi[kThreads / 64];
+  __shared__ int sAc[kTRange];
   const int row = blockIdx.x / P.nrange;
   const int rg = blockIdx.x % P.nrange;
   const int J = threadIdx.x;
@@ -629,6 +615,9 @@ struct StageBParams {
   float* p1l;
   float* p1acc;
   int32_t* p1cnt;
+  int want_count;
+  int nret_blocks;  // blocks past this index run window attention
+  WinParams win;
 };
 
 // sum over the ranges of SUF_J for head row `row` (fixed order)
@@ -647,11 +636,27 @@ __device__ __forceinline__ double suf_at(const double* __restrict__ tpart, size_
   return s;
 }
 
+// Code word w of a chunk holds the bins of tokens w + q*(TC/4), q = 0..3 (byte q).  Thread
+// tid of this kernel takes words tid + i*256, i < NW, i.e. TPT = 4*NW tokens per chunk.
+template <int TPT, int GMAX>
+__device__ void select_attend_block(const StageBParams& P, unsigned char* smem);
+
 template <int TPT, int GMAX>
 __global__ __launch_bounds__(kThreads) void k_stage_b(StageBParams P) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  if ((int)blockIdx.x < P.nret_blocks)
+    select_attend_block<TPT, GMAX>(P, smem);
+  else
+    window_block(P.win, blockIdx.x - P.nret_blocks, reinterpret_cast<float*>(smem));
+}
+
+template <int TPT, int GMAX>
+__device__ void select_attend_block(const StageBParams& P, unsigned char* smem) {
   constexpr int TC = kThreads * TPT;
   constexpr int NW = TPT / 4;  // code words per thread per chunk and head
-  extern __shared__ __align__(16) unsigned char smem[];
+  auto tok_of = [&](int chunk, int t) {  // t = 4*i + q
+    return chunk * TC + (threadIdx.x + (t >> 2) * kThreads) + (t & 3) * (TC / 4);
+  };
   __shared__ int s_tau[kBChunks][kAttnG];
   __shared__ int s_A[kAttnG], s_bs[kAttnG], s_m[kAttnG];
   __shared__ double s_suf[kAttnG][17];
@@ -771,14 +776,13 @@ __global__ __launch_bounds__(kThreads) void k_stage_b(StageBParams P) {
     }
 #pragma unroll
     for (int t = 0; t < TPT; t++) {
-      const int n = (chunk0 + c) * TC + t * kThreads + tid;
-      if (n >= L) mk[c][t] = 0u;
+      if (tok_of(chunk0 + c, t) >= L) mk[c][t] = 0u;
       mine += mk[c][t] != 0u;
     }
   }
 #pragma unroll
   for (int g = 0; g < GMAX; g++) {
-    if (g >= G) break;
+    if (g >= G || !P.want_count) break;
     int cg = 0;
 #pragma unroll
     for (int c = 0; c < kBChunks; c++)
@@ -808,7 +812,7 @@ __global__ __launch_bounds__(kThreads) void k_stage_b(StageBParams P) {
 #pragma unroll
     for (int t = 0; t < TPT; t++) {
       if (mk[c][t]) {
-        ltok[pos] = (chunk0 + c) * TC + t * kThreads + tid;
+        ltok[pos] = tok_of(chunk0 + c, t);
         lmask[pos] = (uint16_t)mk[c][t];
         pos++;
       }
@@ -839,37 +843,60 @@ __global__ __launch_bounds__(kThreads) void k_stage_b(StageBParams P) {
 
   // ---- phase 3: block partial
   const size_t s1p = ((size_t)(b * P.Hret + kr) * P.nblk + blk) * G;
-  block_combine(st, G, lds, P.p1m + s1p, P.p1l + s1p, P.p1acc + s1p * kD);
+  block_combine<kThreads / 64>(st, G, lds, P.p1m + s1p, P.p1l + s1p, P.p1acc + s1p * kD);
   if (tid < G) P.p1cnt[s1p + tid] = s_cnt[tid];
 }
 
 // ---------------------------------------------------------------------------
-// stage M: merge the slice partials of every retrieval query head
+// stage M: merge the slice partials of every retrieval query head, then (blocks past
+// them) the window partials of every local query head
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void k_stage_m(const float* __restrict__ p1m,
-                                                      const float* __restrict__ p1l,
-                                                      const float* __restrict__ p1acc,
-                                                      const int32_t* __restrict__ p1cnt,
-                                                      const int32_t* __restrict__ Aglob,
-                                                      const int32_t* __restrict__ bstar,
-                                                      int nblk, int Hret, int G, int Hq,
-                                                      HeadMap ret, float* __restrict__ out,
-                                                      float* __restrict__ lse,
-                                                      int32_t* __restrict__ count_out,
-                                                      int32_t* __restrict__ thresh_out) {
+struct StageMParams {
+  const float* p1m;
+  const float* p1l;
+  const float* p1acc;
+  const int32_t* p1cnt;
+  const int32_t* Aglob;
+  const int32_t* bstar;
+  int nblk, Hret, G, Hq, nret;
+  HeadMap ret;
+  // window
+  const float* wpm;
+  const float* wpl;
+  const float* wpacc;
+  int nws, Hloc;
+  HeadMap loc;
+  float* out;
+  float* lse;
+  int32_t* count_out;
+  int32_t* thresh_out;
+};
+
+__global__ __launch_bounds__(kThreads) void k_stage_m(StageMParams P) {
   extern __shared__ __align__(16) float mlds[];
+  const int G = P.G;
+  if ((int)blockIdx.x >= P.nret) {
+    const int wm = blockIdx.x - P.nret;
+    const int g = wm % G;
+    const int kl = (wm / G) % P.Hloc;
+    const int b = wm / (G * P.Hloc);
+    const size_t p0 = (size_t)(b * P.Hloc + kl) * P.nws * G;
+    merge_head(P.wpm + p0, P.wpl + p0, P.wpacc + p0 * kD, nullptr, P.nws, G, g, P.out, P.lse,
+               nullptr, (size_t)b * P.Hq + (size_t)P.loc.kv[kl] * G + g, mlds);
+    return;
+  }
   const int g = blockIdx.x % G;
-  const int kr = (blockIdx.x / G) % Hret;
-  const int b = blockIdx.x / (G * Hret);
-  const size_t p0 = (size_t)(b * Hret + kr) * nblk * G;
-  const size_t orow = (size_t)b * Hq + (size_t)ret.kv[kr] * G + g;
-  merge_head(p1m + p0, p1l + p0, p1acc + p0 * kD, p1cnt + p0, nblk, G, g, out, lse, count_out,
-             orow, mlds);
-  if (thresh_out && threadIdx.x == 0) {
-    const size_t row = (size_t)b * Hret * G + (size_t)kr * G + g;
-    const int A = Aglob[row];
-    thresh_out[orow * 2 + 0] = A == kEmptyCell ? 0 : A;
-    thresh_out[orow * 2 + 1] = A == kEmptyCell ? 0 : bstar[row];
+  const int kr = (blockIdx.x / G) % P.Hret;
+  const int b = blockIdx.x / (G * P.Hret);
+  const size_t p0 = (size_t)(b * P.Hret + kr) * P.nblk * G;
+  const size_t orow = (size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G + g;
+  merge_head(P.p1m + p0, P.p1l + p0, P.p1acc + p0 * kD, P.p1cnt + p0, P.nblk, G, g, P.out, P.lse,
+             P.count_out, orow, mlds);
+  if (P.thresh_out && threadIdx.x == 0) {
+    const size_t row = (size_t)b * P.Hret * G + (size_t)kr * G + g;
+    const int A = P.Aglob[row];
+    P.thresh_out[orow * 2 + 0] = A == kEmptyCell ? 0 : A;
+    P.thresh_out[orow * 2 + 1] = A == kEmptyCell ? 0 : P.bstar[row];
   }
 }
 
@@ -881,7 +908,7 @@ __global__ __launch_bounds__(kThreads) void k_stage_m(const float* __restrict__ 
 bool step_fused_supported(int kv_dtype, int G, int Hloc, int window, int sinks) {
   if (kv_dtype != 1 || G > kAttnG) return false;
   // the window merge keeps one weight per split in LDS
-  if (Hloc > 0 && (window + sinks + kWinRows - 1) / kWinRows > 1024) return false;
+  if (Hloc > 0 && (window + sinks + kWinRows - 1) / kWinRows > 8192) return false;
   return true;
 }
 
@@ -893,12 +920,15 @@ StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int
   sp.Hret = Hret;
   sp.Hloc = Hloc;
   const int H = Hret * G;
+  // 2048-token chunks (stage-A blocks of 512 threads) unless that leaves fewer than 256
+  // histogram blocks; then 1024-token chunks (256 threads)
+  {
+    const int64_t units = (int64_t)B * (Hret > 0 ? Hret : 1);
+    sp.tc = units * ((Lmax + 2047) / 2048) >= 256 ? 2048 : 1024;
+    sp.nt = sp.tc / 4;
+    sp.tpt = sp.tc / kThreads;
+  }
   if (Hret > 0) {
-    int tpt = 8;
-    const int64_t units = (int64_t)B * Hret;
-    while (tpt > 4 && units * ((Lmax + kThreads * tpt - 1) / (kThreads * tpt)) < 256) tpt >>= 1;
-    sp.tpt = tpt;
-    sp.tc = kThreads * tpt;
     sp.nchunk = (Lmax + sp.tc - 1) / sp.tc;
     sp.nblk = (sp.nchunk + kBChunks - 1) / kBChunks;
     sp.nrange = (sp.nchunk + kTRange - 1) / kTRange;
@@ -935,112 +965,74 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
                              hipStream_t st, hipEvent_t* ev) {
   const int G = sp.G;
   const int B = a.B;
+  const int H = sp.Hret * G;
   auto rec = [&](int i) {
     if (ev && ev[i]) (void)hipEventRecord(ev[i], st);
   };
+  const float scale2 = a.scale_attn * 1.4426950408889634f;
+  const float c_log2 = (float)((double)a.bin_width * 1.4426950408889634);
+  hipError_t e = hipSuccess;
+  rec(0);
+  // ---- K1: indexer score + chunk histograms
   StageAParams P{};
-  P.seq_lens = a.seq_lens;
-  P.B = B;
-  P.Hq = a.Hq;
-  P.G = G;
-  P.Lmax = a.Lmax;
-  P.q = static_cast<const f16*>(a.q);
-  P.out = a.out;
-  P.lse = a.lse;
-  P.scale2 = a.scale_attn * 1.4426950408889634f;
-  P.Hloc = sp.Hloc;
-  P.Hret = sp.Hret;
-  P.ngg = 1;
-  int nwin_blocks = 0, nhist_blocks = 0;
-  if (sp.Hloc > 0) {
-    P.K_loc = static_cast<const f16*>(a.K_loc);
-    P.V_loc = static_cast<const f16*>(a.V_loc);
-    P.loc = a.loc;
-    P.window = a.window;
-    P.sinks = a.sinks;
-    P.nws = sp.nws;
-    P.wpm = at<float>(ws, sp.wpm);
-    P.wpl = at<float>(ws, sp.wpl);
-    P.wpacc = at<float>(ws, sp.wpacc);
-    nwin_blocks = B * sp.Hloc * sp.nws;
-  }
-  const int GG = G > 4 ? 8 : (G > 2 ? 4 : (G > 1 ? 2 : 1));
   if (sp.Hret > 0) {
+    const int GG = G > 4 ? 8 : (G > 2 ? 4 : (G > 1 ? 2 : 1));
+    P.seq_lens = a.seq_lens;
+    P.B = B;
+    P.Hq = a.Hq;
+    P.G = G;
+    P.Lmax = a.Lmax;
     P.q_idx = a.q_idx;
     P.k_idx = static_cast<const f16*>(a.k_idx);
     P.ret = a.ret;
+    P.Hret = sp.Hret;
     P.nchunk = sp.nchunk;
     P.ngg = (G + GG - 1) / GG;
     P.yscale = a.scale_idx / a.bin_width;
-    P.c_log2 = (float)((double)a.bin_width * 1.4426950408889634);
+    P.c_log2 = c_log2;
     P.w = (double)a.bin_width;
     P.suf = at<float>(ws, sp.suf);
     P.partA = at<int32_t>(ws, sp.partA);
     P.codes = at<uint32_t>(ws, sp.codes);
-    P.bstar = at<int32_t>(ws, sp.bstar);
-    nhist_blocks = B * sp.Hret * P.ngg * sp.nchunk;
-  }
-  P.nwin_blocks = nwin_blocks;
-  P.nhist_blocks = nhist_blocks;
-  const int nA = nwin_blocks + nhist_blocks;
-  // LDS: window combine needs 4*(32+2048) floats; histogram 2*GG*257 u64 + extras
-  const size_t ldsA = 4 * (32 + 2048) * sizeof(float) + 1024;
-  rec(0);
-#define RTP_STAGE_A(GGV, TPTV) k_stage_a<GGV, TPTV><<<nA, kThreads, ldsA, st>>>(P)
-  if (sp.tpt == 4 || sp.Hret == 0) {
-    switch (GG) {
-      case 8: RTP_STAGE_A(8, 4); break;
-      case 4: RTP_STAGE_A(4, 4); break;
-      case 2: RTP_STAGE_A(2, 4); break;
-      default: RTP_STAGE_A(1, 4); break;
+    const int nA = B * sp.Hret * P.ngg * sp.nchunk;
+    const size_t ldsA = sizeof(unsigned long long) * kCopies * 8 * (kNB + kPad) + 1024;
+#define RTP_STAGE_A(GGV, NTV) k_stage_a<GGV, NTV><<<nA, NTV, ldsA, st>>>(P)
+    if (sp.nt == 256) {
+      switch (GG) {
+        case 8: RTP_STAGE_A(8, 256); break;
+        case 4: RTP_STAGE_A(4, 256); break;
+        case 2: RTP_STAGE_A(2, 256); break;
+        default: RTP_STAGE_A(1, 256); break;
+      }
+    } else {
+      switch (GG) {
+        case 8: RTP_STAGE_A(8, 512); break;
+        case 4: RTP_STAGE_A(4, 512); break;
+        case 2: RTP_STAGE_A(2, 512); break;
+        default: RTP_STAGE_A(1, 512); break;
+      }
     }
-  } else {
-    switch (GG) {
-      case 8: RTP_STAGE_A(8, 8); break;
-      case 4: RTP_STAGE_A(4, 8); break;
-      case 2: RTP_STAGE_A(2, 8); break;
-      default: RTP_STAGE_A(1, 8); break;
-    }
-  }
 #undef RTP_STAGE_A
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   rec(1);
-  const int H = sp.Hret * G;
+  // ---- K2: threshold range sums
   StageTParams T{};
-  T.nT = sp.Hret > 0 ? B * H * sp.nrange : 0;
-  const int nwm = sp.Hloc > 0 ? B * sp.Hloc * G : 0;
   if (sp.Hret > 0) {
     T.suf = P.suf;
     T.partA = P.partA;
     T.nchunk = sp.nchunk;
     T.nrange = sp.nrange;
-    T.c_log2 = P.c_log2;
+    T.c_log2 = c_log2;
     T.tpart = at<double>(ws, sp.tpart);
     T.Aglob = at<int32_t>(ws, sp.Aglob);
-  }
-  if (sp.Hloc > 0) {
-    T.wpm = P.wpm;
-    T.wpl = P.wpl;
-    T.wpacc = P.wpacc;
-    T.nws = sp.nws;
-    T.Hloc = sp.Hloc;
-    T.G = G;
-    T.Hq = a.Hq;
-    T.loc = a.loc;
-    T.out = a.out;
-    T.lse = a.lse;
-  }
-  if (T.nT + nwm > 0) {
-    k_stage_t<<<T.nT + nwm, kThreads, 0, st>>>(T);
+    k_stage_t<<<B * H * sp.nrange, kThreads, 0, st>>>(T);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   rec(2);
-  if (sp.Hret == 0) {
-    rec(3);
-    return hipSuccess;
-  }
+  // ---- K3: selection + sparse attention (retrieval) and window attention (local)
   StageBParams Q{};
   Q.seq_lens = a.seq_lens;
   Q.B = B;
@@ -1048,28 +1040,53 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
   Q.G = G;
   Q.Lmax = a.Lmax;
   Q.Hret = sp.Hret;
-  Q.nchunk = sp.nchunk;
-  Q.tc = sp.tc;
-  Q.nblk = sp.nblk;
-  Q.nrange = sp.nrange;
-  Q.p = a.p;
-  Q.q = static_cast<const f16*>(a.q);
-  Q.K_ret = static_cast<const f16*>(a.K_ret);
-  Q.V_ret = static_cast<const f16*>(a.V_ret);
-  Q.ret = a.ret;
-  Q.scale2 = P.scale2;
-  Q.partA = P.partA;
-  Q.codes = P.codes;
-  Q.tpart = T.tpart;
-  Q.Aglob = T.Aglob;
-  Q.bstar = P.bstar;
-  Q.p1m = at<float>(ws, sp.p1m);
-  Q.p1l = at<float>(ws, sp.p1l);
-  Q.p1acc = at<float>(ws, sp.p1acc);
-  Q.p1cnt = at<int32_t>(ws, sp.p1cnt);
+  Q.scale2 = scale2;
+  Q.nret_blocks = 0;
+  if (sp.Hret > 0) {
+    Q.nchunk = sp.nchunk;
+    Q.tc = sp.tc;
+    Q.nblk = sp.nblk;
+    Q.nrange = sp.nrange;
+    Q.p = a.p;
+    Q.q = static_cast<const f16*>(a.q);
+    Q.K_ret = static_cast<const f16*>(a.K_ret);
+    Q.V_ret = static_cast<const f16*>(a.V_ret);
+    Q.ret = a.ret;
+    Q.partA = P.partA;
+    Q.codes = P.codes;
+    Q.tpart = T.tpart;
+    Q.Aglob = T.Aglob;
+    Q.bstar = at<int32_t>(ws, sp.bstar);
+    Q.p1m = at<float>(ws, sp.p1m);
+    Q.p1l = at<float>(ws, sp.p1l);
+    Q.p1acc = at<float>(ws, sp.p1acc);
+    Q.p1cnt = at<int32_t>(ws, sp.p1cnt);
+    Q.want_count = a.count_out != nullptr;
+    Q.nret_blocks = B * sp.Hret * sp.nblk;
+  }
+  int nwin_blocks = 0;
+  if (sp.Hloc > 0) {
+    WinParams& W = Q.win;
+    W.seq_lens = a.seq_lens;
+    W.Hq = a.Hq;
+    W.G = G;
+    W.q = static_cast<const f16*>(a.q);
+    W.K_loc = static_cast<const f16*>(a.K_loc);
+    W.V_loc = static_cast<const f16*>(a.V_loc);
+    W.loc = a.loc;
+    W.Hloc = sp.Hloc;
+    W.window = a.window;
+    W.sinks = a.sinks;
+    W.nws = sp.nws;
+    W.scale2 = scale2;
+    W.wpm = at<float>(ws, sp.wpm);
+    W.wpl = at<float>(ws, sp.wpl);
+    W.wpacc = at<float>(ws, sp.wpacc);
+    nwin_blocks = B * sp.Hloc * sp.nws;
+  }
   const size_t ldsB = std::max<size_t>(4 * (32 + 2048) * sizeof(float),
                                        (sizeof(int32_t) + sizeof(uint16_t)) * kBChunks * sp.tc);
-  const int nB = B * sp.Hret * sp.nblk;
+  const int nB = Q.nret_blocks + nwin_blocks;
   if (sp.tpt == 4) {
     if (G <= 8)
       k_stage_b<4, 8><<<nB, kThreads, ldsB, st>>>(Q);
@@ -1083,10 +1100,38 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t ldsM = sizeof(float) * ((size_t)sp.nblk + kThreads + 8 * kD);
-  k_stage_m<<<B * sp.Hret * G, kThreads, ldsM, st>>>(Q.p1m, Q.p1l, Q.p1acc, Q.p1cnt, Q.Aglob,
-                                                     Q.bstar, sp.nblk, sp.Hret, G, a.Hq, a.ret,
-                                                     a.out, a.lse, a.count_out, a.thresh_out);
+  // ---- K4: merges
+  StageMParams M{};
+  M.G = G;
+  M.Hq = a.Hq;
+  M.out = a.out;
+  M.lse = a.lse;
+  M.nret = sp.Hret > 0 ? B * sp.Hret * G : 0;
+  if (sp.Hret > 0) {
+    M.p1m = Q.p1m;
+    M.p1l = Q.p1l;
+    M.p1acc = Q.p1acc;
+    M.p1cnt = Q.p1cnt;
+    M.Aglob = Q.Aglob;
+    M.bstar = Q.bstar;
+    M.nblk = sp.nblk;
+    M.Hret = sp.Hret;
+    M.ret = a.ret;
+    M.count_out = a.count_out;
+    M.thresh_out = a.thresh_out;
+  }
+  const int nwm = sp.Hloc > 0 ? B * sp.Hloc * G : 0;
+  if (sp.Hloc > 0) {
+    M.wpm = Q.win.wpm;
+    M.wpl = Q.win.wpl;
+    M.wpacc = Q.win.wpacc;
+    M.nws = sp.nws;
+    M.Hloc = sp.Hloc;
+    M.loc = a.loc;
+  }
+  const int nmax = std::max(sp.Hret > 0 ? sp.nblk : 0, sp.Hloc > 0 ? sp.nws : 0);
+  const size_t ldsM = sizeof(float) * ((size_t)nmax + kThreads + 8 * kD);
+  k_stage_m<<<M.nret + nwm, kThreads, ldsM, st>>>(M);
   e = hipGetLastError();
   rec(3);
   return e;
