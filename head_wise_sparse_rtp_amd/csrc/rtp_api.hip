@@ -114,7 +114,8 @@ rtp_status plan_step(const rtp_layer_desc* d, StepPlan& sp) {
   sp.Hloc = sp.loc.n;
   if (sp.Hloc > 0 && (d->window < 1 || d->sinks < 0)) return RTP_EINVAL;
   if (sp.Hloc > 0 && (int64_t)d->window + d->sinks > (1 << 24)) return RTP_EUNSUPPORTED;
-  if (step_fused_supported(d->kv_dtype, sp.G, sp.Hloc, d->window, d->sinks)) {
+  if (step_fused_supported(d->kv_dtype, sp.G, sp.Hloc, d->window, d->sinks, d->B, sp.Hret,
+                           d->Lmax)) {
     sp.fused = true;
     WsPlanner wp;
     sp.fp = plan_step_fused(wp, d->B, d->Hq, sp.G, d->Lmax, sp.Hret, sp.Hloc, d->window,

@@ -121,12 +121,16 @@ struct WsPlanner {
 };
 
 // ---------------------------------------------------------------------------
-// fused decode step (fp16 caches, G <= 16): stage A (window + histogram blocks),
-// stage T (threshold), stage B (selection + MFMA attention + merges)
+// fused decode step (fp16 caches, G <= 16): stage A (indexer score + chunk histograms),
+// stage T (suffix tables), stage B (selection + sparse attention, window attention),
+// stage M (merges)
 // ---------------------------------------------------------------------------
 struct StepFusedPlan {
-  int G, Hret, Hloc, tpt, tc, nt, nchunk, nblk, nws, nrange;
-  size_t suf, partA, codes, bstar, Aglob, tpart;
+  int G, Hret, Hloc;
+  int tc, nt, nchunk;  // histogram chunk tokens, stage-A threads, chunks per row
+  int nwd, tb, nblk;   // selection blocks: code words per thread, tokens, blocks per KV head
+  int wrows, nws;      // window blocks: rows per block, blocks per local KV head
+  size_t suf, partA, codes, bstar, Aglob, sufg;
   size_t p1m, p1l, p1acc, p1cnt;
   size_t wpm, wpl, wpacc;
   size_t bytes;
@@ -148,7 +152,8 @@ struct StepFusedArgs {
   int32_t* count_out;
 };
 
-bool step_fused_supported(int kv_dtype, int G, int Hloc, int window, int sinks);
+bool step_fused_supported(int kv_dtype, int G, int Hloc, int window, int sinks, int B, int Hret,
+                          int Lmax);
 StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int Hret, int Hloc,
                               int window, int sinks);
 // ev (may be null): events recorded before stage A, after stage A, after stage T and

@@ -1,15 +1,15 @@
 // Decode step for fp16 caches in four launches per layer.
 //
-//   K1 stage A  indexer-score/histogram blocks (retrieval KV heads) and window-attention
-//               blocks (local KV heads) in one grid; both write partial results.
-//   K2 stage T  threshold sums: per (head, range of 32 chunks) the suffix sums of the
-//               chunk histograms are shifted to the head's top cell and added; extra
-//               blocks merge the window partials into the local heads' outputs.
-//   K3 stage B  per (retrieval KV head, 8192-token slice): find b* from the range sums
-//               (coarse then fine search over the 256 bins), select the tokens whose bin
-//               is within the threshold, gather the K/V rows of the union over the query
-//               heads and run masked softmax attention on the matrix cores.
-//   K4 stage M  merge the slice partials of every retrieval query head.
+//   K1 stage A  indexer score and per-chunk 256-bin histograms of every retrieval query
+//               head (chunk-relative bin codes, suffix sums of the bin masses, top cell).
+//   K2 stage T  per (head, group of 16 bins): the suffix sums of all chunks, shifted to
+//               the head's top cell and added, giving the head's whole suffix table.
+//   K3 stage B  selection blocks (retrieval KV head x slice of 2048-8192 tokens): b* from
+//               the suffix table, the union over the query heads of the selected tokens
+//               of the slice, masked softmax attention on the matrix cores over the
+//               gathered K/V rows -> one partial per slice; window blocks (local KV head x
+//               run of window entries) -> one partial per run.
+//   K4 stage M  per (query head, 32 output dims): merge the partials.
 // Blocks of one launch never wait for or read each other's results: on gfx950 a
 // device-scope release fence writes back and invalidates the whole L2 of the XCD, so
 // cross-block hand-offs go through kernel boundaries instead.
@@ -37,11 +37,16 @@ namespace {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kAttnG = 16;        // head columns of the MFMA tile
-constexpr int kStep = 32;         // cache rows per wavefront step
-constexpr int kWinRows = 128;     // window rows per window block (4 waves x 1 step)
-constexpr int kBChunks = 4;       // histogram chunks per stage-B block
-constexpr int kBGroup = 16;       // stage-B blocks merged per first-level group
+constexpr int kAttnG = 16;               // head columns of the MFMA tile
+constexpr int kStep = 32;                // cache rows per wavefront step
+constexpr int kBThreads = 512;           // threads of a stage-B block
+constexpr int kBWaves = kBThreads / 64;  // wavefronts of a stage-B block
+constexpr int kMaxCPB = 8;               // histogram chunks per selection block (at most)
+constexpr int kTBins = 16;               // bins per stage-T block
+constexpr int kTBatch = 32;              // chunk loads in flight per stage-T thread
+constexpr int kMSlice = 32;              // output dims per stage-M block
+constexpr int kMSlices = kD / kMSlice;
+constexpr int kMaxParts = 4096;          // partials merged per head (stage-M LDS)
 
 __device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -237,90 +242,10 @@ __device__ void block_combine(AttnState& st, int G, float* lds, float* out_m, fl
   }
 }
 
-// Merge the n split partials of one head g (pm/pl [n][G], pacc [n][G][128], optional
-// per-split counts) into out / lse / count.  Block of 256 threads: 32 dim-groups of 4
-// x 8 split subsets; every load of a thread is issued before any is used; the sums run
-// in a fixed order, so the result is deterministic.
-__device__ void merge_head(const float* __restrict__ pm, const float* __restrict__ pl,
-                           const float* __restrict__ pacc, const int32_t* __restrict__ pcnt,
-                           int n, int G, int g, float* __restrict__ out, float* __restrict__ lse,
-                           int32_t* __restrict__ count_out, size_t orow, float* lds) {
-  float* wk = lds;                         // [n] weights 2^(m_k - M)
-  float* red = lds + n;                    // [256]
-  float* racc = red + kThreads;            // [8][128]
-  const int tid = threadIdx.x;
-  float mloc = -INFINITY;
-  for (int k = tid; k < n; k += kThreads) {
-    const float m = pm[(size_t)k * G + g];
-    wk[k] = m;
-    mloc = fmaxf(mloc, m);
-  }
-  red[tid] = mloc;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-  float lloc = 0.0f;
-  int cloc = 0;
-  for (int k = tid; k < n; k += kThreads) {
-    const float m = wk[k];
-    const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-    wk[k] = f;
-    lloc += pl[(size_t)k * G + g] * f;
-    if (pcnt) cloc += pcnt[(size_t)k * G + g];
-  }
-  red[tid] = lloc;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
-  }
-  const float Lsum = red[0];
-  __syncthreads();
-  if (count_out) {
-    int* ired = reinterpret_cast<int*>(red);
-    ired[tid] = cloc;
-    __syncthreads();
-    for (int s = kThreads / 2; s > 0; s >>= 1) {
-      if (tid < s) ired[tid] += ired[tid + s];
-      __syncthreads();
-    }
-    if (tid == 0) count_out[orow] = ired[0];
-    __syncthreads();
-  }
-  const int dg = tid & 31;
-  const int sub = tid >> 5;
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k0 = sub; k0 < n; k0 += 8 * 8) {
-    float4 x[8];
-#pragma unroll
-    for (int u = 0; u < 8; u++) {
-      const int k = min(k0 + 8 * u, n - 1);
-      x[u] = reinterpret_cast<const float4*>(pacc + ((size_t)k * G + g) * kD)[dg];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; u++) {
-      const float f = (k0 + 8 * u < n) ? wk[k0 + 8 * u] : 0.0f;
-      a.x += x[u].x * f; a.y += x[u].y * f; a.z += x[u].z * f; a.w += x[u].w * f;
-    }
-  }
-  reinterpret_cast<float4*>(racc + sub * kD)[dg] = a;
-  __syncthreads();
-  if (tid < kD) {
-    float v = 0.0f;
-#pragma unroll
-    for (int s2 = 0; s2 < 8; s2++) v += racc[s2 * kD + tid];
-    out[orow * kD + tid] = Lsum > 0.0f ? v / Lsum : 0.0f;
-  }
-  if (tid == 0 && lse) lse[orow] = Lsum > 0.0f ? (M + __log2f(Lsum)) * 0.69314718055994531f : -INFINITY;
-}
-
 // ---------------------------------------------------------------------------
-// histogram block (retrieval): same arithmetic as the chunk-histogram kernel of
-// rtp_score.hip, followed by suffix sums of the bin masses.
+// histogram block (retrieval): indexer score on the matrix cores, then the bins,
+// masses and codes of the chunk-histogram kernel of rtp_score.hip, then suffix sums
+// of the bin masses.
 // ---------------------------------------------------------------------------
 constexpr int kCopies = 2;
 constexpr int kPad = 1;
@@ -346,23 +271,32 @@ struct WinParams {
   const f16* K_loc;
   const f16* V_loc;
   HeadMap loc;
-  int Hloc, window, sinks, nws;
+  int Hloc, window, sinks, nws, wrows;
   float scale2;
   float* wpm;
   float* wpl;
   float* wpacc;
 };
 
-// Token t (0..3) of thread tid in a chunk is chunk*TC + t*NT + tid; the 4 bin codes of a
-// thread are packed into code word `tid` of the chunk (byte t).
-template <int GG, int NT>
+// Histogram block: chunk `chunk` (TC = 4*NT tokens) of up to 8 query heads g0.. of
+// retrieval KV head kr.  Wavefront wv scores tokens [256 wv, 256 wv + 256) of the chunk
+// in 8 groups of 32 on the matrix cores:
+//   A (16 x 32): row i = [k_idx(token i) | k_idx(token i + 16)]
+//   B (32 x 16): column j = head j%8 against the half j/8 (the other half zero), once
+//                with the high and once with the low fp16 part of the head's q_idx
+//   D = A.B_hi + A.B_lo: lane l holds head l%8 for the 4 consecutive tokens
+//       16*((l%16)/8) + 4*(l/16) + t of the group, t = 0..3.
+// q_idx is first scaled by a power of two so that its largest entry lies in
+// [2^13, 2^14): hi + lo then carry 22 significant bits and the products stay in fp32
+// range; the scale is undone exactly in the final multiply.  The four bin codes of a
+// lane's tokens form one code word (byte t = token 4w + t of word w).
+template <int NT>
 __device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
-  constexpr int TPT = 4;
-  constexpr int TC = NT * TPT;
+  constexpr int TC = NT * 4;
   constexpr int NWV = NT / 64;
+  constexpr int GG = 8;
   unsigned long long* hist = reinterpret_cast<unsigned long long*>(smem);
   float* smax = reinterpret_cast<float*>(smem + sizeof(unsigned long long) * kCopies * GG * (kNB + kPad));
-  float* sq = smax + GG * NWV;  // q_idx of the GG heads, [GG][16]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -382,84 +316,104 @@ __device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
     return;
   }
   const bool full = base + TC <= L;
-  // k_idx rows of this thread's tokens, all loads in flight
+  const int hh = lane & 7;         // head of this lane (B column and D column)
+  const int th = (lane >> 3) & 1;  // token half of the B column
+  const int kq = lane >> 4;        // k-group of the A / B operands
+  // ---- k_idx rows: 8 groups of 32 tokens, 16 bytes per lane and group, all in flight
   const f16* kb = P.k_idx + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kR;
-  h8 ra[TPT], rb[TPT];
+  const int wbase = base + wv * 256;
+  h8 ka[8];
 #pragma unroll
-  for (int t = 0; t < TPT; t++) {
-    int n = base + t * NT + tid;
+  for (int gi = 0; gi < 8; gi++) {
+    int n = wbase + gi * 32 + (lane & 15) + 16 * (kq >> 1);
     n = n < L ? n : base;  // past the end: re-read a valid row, masked below
-    const h8* p = reinterpret_cast<const h8*>(kb + (size_t)n * kR);
-    ra[t] = p[0];
-    rb[t] = p[1];
+    ka[gi] = *reinterpret_cast<const h8*>(kb + (size_t)n * kR + 8 * (kq & 1));
   }
-  if (tid < GG * kR) {
-    const int gg = tid / kR;
-    sq[tid] = gg < nrows ? P.q_idx[((size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G + g0 + gg) * kR +
-                                   (tid % kR)]
-                         : 0.0f;
-  }
-  for (int i = tid; i < kCopies * GG * (kNB + kPad); i += NT) hist[i] = 0ull;
-  __syncthreads();
-
-  // ---- pass 1: y = fl32(a * scale) / w (exact: w is a power of two) and the top cell
-  float y[TPT][GG];
-#pragma unroll
-  for (int gg = 0; gg < GG; gg++) {
+  // ---- q operands of head hh (zero for heads past nrows)
+  h8 qhi = h8{0, 0, 0, 0, 0, 0, 0, 0}, qlo = qhi;
+  float ysc = 0.0f;
+  if (hh < nrows) {
+    const float4* qp = reinterpret_cast<const float4*>(
+        P.q_idx + ((size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G + g0 + hh) * kR);
     float q[kR];
 #pragma unroll
-    for (int i = 0; i < kR; i++) q[i] = sq[gg * kR + i];
-    float ym = -INFINITY;
+    for (int i = 0; i < 4; i++) {
+      const float4 v = qp[i];
+      q[4 * i] = v.x;
+      q[4 * i + 1] = v.y;
+      q[4 * i + 2] = v.z;
+      q[4 * i + 3] = v.w;
+    }
+    float qm = 0.0f;
 #pragma unroll
-    for (int t = 0; t < TPT; t++) {
-      float a = 0.0f;
+    for (int i = 0; i < kR; i++) qm = fmaxf(qm, fabsf(q[i]));
+    int e = 0;
+    (void)frexpf(qm, &e);  // qm < 2^e
+    ysc = ldexpf(P.yscale, e - 14);
+    if ((kq >> 1) == th) {
 #pragma unroll
-      for (int i = 0; i < 8; i++) a = __builtin_fmaf(q[i], (float)ra[t][i], a);
+      for (int i = 0; i < 8; i++) {
+        const float v = ldexpf(q[8 * (kq & 1) + i], 14 - e);
+        const f16 hi = (f16)v;
+        qhi[i] = hi;
+        qlo[i] = (f16)(v - (float)hi);
+      }
+    }
+  }
+  for (int i = tid; i < kCopies * GG * (kNB + kPad); i += NT) hist[i] = 0ull;
+
+  // ---- pass 1: y = fl32(a * scale) / w (exact: w is a power of two) and the top cell
+  float y[8][4];
+  float ym = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 8; i++) a = __builtin_fmaf(q[8 + i], (float)rb[t][i], a);
-      float v = a * P.yscale;
-      if (!full && base + t * NT + tid >= L) v = -INFINITY;
-      y[t][gg] = v;
+  for (int gi = 0; gi < 8; gi++) {
+    f4 d = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    d = mfma32(ka[gi], qhi, d);
+    d = mfma32(ka[gi], qlo, d);
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      float v = d[t] * ysc;
+      if (!full && wbase + gi * 32 + 16 * th + 4 * kq + t >= L) v = -INFINITY;
+      y[gi][t] = v;
       ym = fmaxf(ym, v);
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) ym = fmaxf(ym, __shfl_xor(ym, o, 64));
-    if (lane == 0) smax[gg * NWV + wv] = ym;
   }
+  // lanes of one head differ in bits 3..5
+  ym = fmaxf(ym, __shfl_xor(ym, 8, 64));
+  ym = fmaxf(ym, __shfl_xor(ym, 16, 64));
+  ym = fmaxf(ym, __shfl_xor(ym, 32, 64));
+  if (lane < GG) smax[lane * NWV + wv] = ym;
   __syncthreads();
-  float Acf[GG];
+  float m = smax[hh * NWV];
 #pragma unroll
-  for (int gg = 0; gg < GG; gg++) {
-    float m = smax[gg * NWV];
-#pragma unroll
-    for (int k = 1; k < NWV; k++) m = fmaxf(m, smax[gg * NWV + k]);
-    Acf[gg] = floorf(m);
-  }
+  for (int k = 1; k < NWV; k++) m = fmaxf(m, smax[hh * NWV + k]);
+  const float Acf = floorf(m);
 
   // ---- pass 2: exact per-bin sums of x * 2^24, x = exp(z - (g+1) w), and the bin codes
-  const int copy = lane & (kCopies - 1);
   const float c = P.c_log2;
-  unsigned long long* hrow = hist + copy * GG * (kNB + kPad);
+  unsigned long long* hrow = hist + (th * GG + hh) * (kNB + kPad);
+  uint32_t* cdst = P.codes + ((rowb + hh) * P.nchunk + chunk) * (size_t)(TC / 4) + wv * 64 + 4 * th + kq;
+  if (hh < nrows) {
 #pragma unroll
-  for (int gg = 0; gg < GG; gg++) {
-    if (gg >= nrows) break;
-    uint32_t cw = 0u;
+    for (int gi = 0; gi < 8; gi++) {
+      uint32_t cw = 0u;
 #pragma unroll
-    for (int t = 0; t < TPT; t++) {
-      const float yv = y[t][gg];
-      const bool valid = full || (base + t * NT + tid < L);
-      const float gf = floorf(yv);
-      const float diff = Acf[gg] - gf;          // exact: integral and below 2^24
-      const float jf = fminf(diff, 255.0f);
-      float arg = __builtin_fmaf(__builtin_amdgcn_fractf(yv), c, -c);
-      if (diff > 255.0f) arg = __builtin_fmaf(-(diff - 255.0f), c, arg);  // deep tail
-      const float e = __builtin_amdgcn_exp2f(arg) * 16777216.0f;
-      const uint32_t j = valid ? (uint32_t)jf : 255u;
-      const uint32_t xi = valid ? (uint32_t)e : 0u;
-      atomicAdd(&hrow[gg * (kNB + kPad) + j], (unsigned long long)xi);
-      cw |= j << (8 * t);
+      for (int t = 0; t < 4; t++) {
+        const float yv = y[gi][t];
+        const bool valid = full || (wbase + gi * 32 + 16 * th + 4 * kq + t < L);
+        const float gf = floorf(yv);
+        const float diff = Acf - gf;          // exact: integral and below 2^24
+        const float jf = fminf(diff, 255.0f);
+        float arg = __builtin_fmaf(__builtin_amdgcn_fractf(yv), c, -c);
+        if (diff > 255.0f) arg = __builtin_fmaf(-(diff - 255.0f), c, arg);  // deep tail
+        const float ex = __builtin_amdgcn_exp2f(arg) * 16777216.0f;
+        const uint32_t j = valid ? (uint32_t)jf : 255u;
+        const uint32_t xi = valid ? (uint32_t)ex : 0u;
+        atomicAdd(&hrow[j], (unsigned long long)xi);
+        cw |= j << (8 * t);
+      }
+      cdst[gi * 8] = cw;
     }
-    P.codes[((rowb + gg) * P.nchunk + chunk) * (size_t)(TC / 4) + tid] = cw;
   }
   __syncthreads();
   // suffix sums of the bin masses, one head per wavefront pass: lane k owns bins 4k..4k+3
@@ -489,15 +443,47 @@ __device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
     acc += mloc[0]; outv.x = (float)acc;
     reinterpret_cast<float4*>(dst)[lane] = outv;
     if (lane == 0) {
-      float m = smax[gg * NWV];
-      for (int k = 1; k < NWV; k++) m = fmaxf(m, smax[gg * NWV + k]);
-      P.partA[(rowb + gg) * P.nchunk + chunk] = (int)floorf(m);
+      float mm = smax[gg * NWV];
+      for (int k = 1; k < NWV; k++) mm = fmaxf(mm, smax[gg * NWV + k]);
+      P.partA[(rowb + gg) * P.nchunk + chunk] = (int)floorf(mm);
     }
   }
 }
 
+template <int NT>
+__global__ __launch_bounds__(NT, 2) void k_stage_a(StageAParams P) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  hist_block<NT>(P, blockIdx.x, smem);
+}
+
+// Masked attention over the entries e = 0..n-1 of a row list: row_of(e) is the cache
+// row, mask_of(e) the heads that take part (bit h).  Wavefront wv of NWV takes steps wv,
+// wv + NWV, ...; the loads of two steps are in flight before either is used.
+template <int NWV, class RowOf, class MaskOf>
+__device__ __forceinline__ void attend_list(const f16* __restrict__ Kb, const f16* __restrict__ Vb,
+                                            int n, RowOf row_of, MaskOf mask_of,
+                                            const h8 (&qop)[4], float scale2, AttnState& st) {
+  const int wv = threadIdx.x >> 6;
+  const int nsteps = (n + kStep - 1) / kStep;
+  for (int s0 = wv; s0 < nsteps; s0 += 2 * NWV) {
+    const int s1 = s0 + NWV;
+    const int e0 = s0 * kStep, e1 = s1 * kStep;
+    StepLoads ld0, ld1;
+    step_load(Kb, Vb, [&](int i) { return row_of(e0 + i < n ? e0 + i : 0); }, ld0);
+    if (s1 < nsteps) step_load(Kb, Vb, [&](int i) { return row_of(e1 + i < n ? e1 + i : 0); }, ld1);
+    step_compute(ld0, qop, scale2,
+                 [&](int i, int h) { return e0 + i < n && ((mask_of(e0 + i < n ? e0 + i : 0) >> h) & 1u); },
+                 st);
+    if (s1 < nsteps)
+      step_compute(ld1, qop, scale2,
+                   [&](int i, int h) { return e1 + i < n && ((mask_of(e1 + i < n ? e1 + i : 0) >> h) & 1u); },
+                   st);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// window block (local): 4 wavefronts x 32 entries of the window set -> one partial
+// window block (local KV head): entries [wsplit*wrows, +wrows) of the window set of
+// sinks followed by the last `window` positions -> one partial per query head
 // ---------------------------------------------------------------------------
 __device__ void window_block(const WinParams& P, int wb, float* lds) {
   const int wsplit = wb % P.nws;
@@ -510,96 +496,111 @@ __device__ void window_block(const WinParams& P, int wb, float* lds) {
   const int ns = min(P.sinks, L);
   const int wstart = max(P.sinks, L - P.window);
   const int nwin = ns + max(0, L - wstart);
-  const int wv = threadIdx.x >> 6;
   const f16* Kb = P.K_loc + ((size_t)b * P.Hloc + kl) * (size_t)ring * kD;
   const f16* Vb = P.V_loc + ((size_t)b * P.Hloc + kl) * (size_t)ring * kD;
   h8 qop[4];
   load_qop(P.q + ((size_t)b * P.Hq + (size_t)P.loc.kv[kl] * G) * kD, G, qop);
   AttnState st;
   attn_init(st);
-  const int e0 = wsplit * kWinRows + wv * kStep;
+  const int elo = wsplit * P.wrows;
+  const int n = max(0, min(nwin - elo, P.wrows));
   const int sinks = P.sinks, window = P.window;
-  auto slot_of = [&](int e) {
-    e = e < nwin ? e : 0;  // rows past the end read entry 0 (masked below)
-    const int pos = e < ns ? e : wstart + (e - ns);
-    return pos < sinks ? pos : sinks + pos % window;
-  };
-  if (nwin > 0 && e0 < nwin) {
-    StepLoads ld;
-    step_load(Kb, Vb, [&](int i) { return slot_of(e0 + i); }, ld);
-    step_compute(ld, qop, P.scale2, [&](int i, int h) { return e0 + i < nwin; }, st);
-  }
+  attend_list<kBWaves>(
+      Kb, Vb, n,
+      [&](int e) {
+        e += elo;
+        const int pos = e < ns ? e : wstart + (e - ns);
+        return pos < sinks ? pos : sinks + pos % window;
+      },
+      [&](int) { return 0xFFFFu; }, qop, P.scale2, st);
   const size_t prow = ((size_t)(b * P.Hloc + kl) * P.nws + wsplit) * G;
-  block_combine<kThreads / 64>(st, G, lds, P.wpm + prow, P.wpl + prow, P.wpacc + prow * kD);
-}
-
-template <int GG, int NT>
-__global__ __launch_bounds__(NT, 2) void k_stage_a(StageAParams P) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  hist_block<GG, NT>(P, blockIdx.x, smem);
+  block_combine<kBWaves>(st, G, lds, P.wpm + prow, P.wpl + prow, P.wpacc + prow * kD);
 }
 
 // ---------------------------------------------------------------------------
-// stage T: threshold range sums (block (range, row), thread = global bin J):
-//   SUF_J(range) = sum_{c in range} suf_c[max(J - s_c, 0)] * exp(-s_c w),  s_c = A - A_c
-// over 32 chunks (coalesced: lanes read consecutive bins of one chunk).
+// stage T: block (head row, 16 bins J0..J0+15), thread (bin J0 + t%16, chunk group t/16):
+//   SUF_J = sum_c suf_c[max(J - s_c, 0)] * exp(-s_c w),  s_c = A - A_c,  A = max_c A_c
+// summed in a fixed order (chunks of a group in order, then the groups in order).
 // ---------------------------------------------------------------------------
-constexpr int kTRange = 32;  // chunks per stage-T block
-
 struct StageTParams {
   const float* suf;
   const int32_t* partA;
-  int nchunk, nrange;
+  int nchunk;
   float c_log2;
-  double* tpart;
+  double* sufg;
   int32_t* Aglob;
 };
 
 __global__ __launch_bounds__(kThreads) void k_stage_t(StageTParams P) {
-  __shared__ int sAi[kThreads / 64];
-  __shared__ int sAc[kTRange];
-  const int row = blockIdx.x / P.nrange;
-  const int rg = blockIdx.x % P.nrange;
-  const int J = threadIdx.x;
-  const int lane = J & 63;
-  const int wv = J >> 6;
-  const int32_t* pa = P.partA + (size_t)row * P.nchunk;
+  extern __shared__ int sA[];  // [nchunk] chunk top cells
+  __shared__ int sAw[kThreads / 64];
+  __shared__ double red[kThreads / kTBins][kTBins + 1];
+  const int row = blockIdx.x / (kNB / kTBins);
+  const int J0 = (blockIdx.x % (kNB / kTBins)) * kTBins;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int nchunk = P.nchunk;
+  const int32_t* pa = P.partA + (size_t)row * nchunk;
   int A = kEmptyCell;
-  for (int c = J; c < P.nchunk; c += kThreads) A = max(A, pa[c]);
+  for (int c = tid; c < nchunk; c += kThreads) {
+    const int a = pa[c];
+    sA[c] = a;
+    A = max(A, a);
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) A = max(A, __shfl_xor(A, o, 64));
-  if (lane == 0) sAi[wv] = A;
-  const int c0 = rg * kTRange;
-  const int nc = min(kTRange, P.nchunk - c0);
-  if (J < nc) sAc[J] = pa[c0 + J];
+  if (lane == 0) sAw[wv] = A;
   __syncthreads();
-  A = max(max(sAi[0], sAi[1]), max(sAi[2], sAi[3]));
+  A = max(max(sAw[0], sAw[1]), max(sAw[2], sAw[3]));
+  const int j = J0 + (tid % kTBins);
+  const int cg = tid / kTBins;
+  constexpr int NG = kThreads / kTBins;
   double acc = 0.0;
   if (A != kEmptyCell) {
-    float x[kTRange];
-    float f[kTRange];
+    const float* sb = P.suf + (size_t)row * nchunk * kNB;
+    for (int c0 = cg; c0 < nchunk; c0 += NG * kTBatch) {
+      // shifts first (all LDS reads in flight), then every load, then the sums
+      int sh[kTBatch];
 #pragma unroll
-    for (int i = 0; i < kTRange; i++) {
-      const int Ac = i < nc ? sAc[i] : kEmptyCell;
-      const long long s = (Ac == kEmptyCell) ? (1ll << 40) : (long long)A - (long long)Ac;
-      f[i] = s > 4096 ? 0.0f : __builtin_amdgcn_exp2f(-(float)s * P.c_log2);
-      const int jj = s > 4096 ? 0 : max(J - (int)s, 0);
-      x[i] = P.suf[((size_t)row * P.nchunk + c0 + (i < nc ? i : 0)) * kNB + jj];
+      for (int u = 0; u < kTBatch; u++) {
+        const int c = c0 + NG * u;
+        sh[u] = c < nchunk ? sA[c] : kEmptyCell;
+      }
+#pragma unroll
+      for (int u = 0; u < kTBatch; u++)  // s_c = A - A_c, or -1 for no contribution
+        sh[u] = (sh[u] != kEmptyCell && sh[u] >= A - 4096) ? A - sh[u] : -1;
+      float x[kTBatch];
+#pragma unroll
+      for (int u = 0; u < kTBatch; u++) {
+        const int c = sh[u] >= 0 ? c0 + NG * u : 0;
+        const int jj = max(j - sh[u], 0);
+        x[u] = sb[(size_t)c * kNB + (sh[u] >= 0 ? jj : 0)];
+      }
+#pragma unroll
+      for (int u = 0; u < kTBatch; u++) {
+        const float f = sh[u] >= 0 ? __builtin_amdgcn_exp2f(-(float)sh[u] * P.c_log2) : 0.0f;
+        acc += (double)x[u] * (double)f;
+      }
     }
-#pragma unroll
-    for (int i = 0; i < kTRange; i++) acc += (double)x[i] * (double)f[i];
   }
-  P.tpart[((size_t)row * P.nrange + rg) * kNB + J] = acc;
-  if (rg == 0 && J == 0) P.Aglob[row] = A;
+  red[cg][tid % kTBins] = acc;
+  __syncthreads();
+  if (tid < kTBins) {
+    double s = 0.0;
+#pragma unroll
+    for (int k = 0; k < NG; k++) s += red[k][tid];
+    P.sufg[(size_t)row * kNB + J0 + tid] = s;
+  }
+  if (J0 == 0 && tid == 0) P.Aglob[row] = A;
 }
 
 // ---------------------------------------------------------------------------
-// stage B: threshold search + selection + masked MFMA attention over the union of the
-// selected rows of a retrieval KV head within an 8192-token slice -> one partial
+// stage B
 // ---------------------------------------------------------------------------
 struct StageBParams {
   const int32_t* seq_lens;
-  int B, Hq, G, Lmax, Hret, nchunk, tc, nblk, nrange;
+  int B, Hq, G, Lmax, Hret, nchunk, tc, nblk;
   double p;
   const f16* q;
   const f16* K_ret;
@@ -608,7 +609,7 @@ struct StageBParams {
   float scale2;
   const int32_t* partA;
   const uint32_t* codes;
-  const double* tpart;
+  const double* sufg;
   const int32_t* Aglob;
   int32_t* bstar;
   float* p1m;
@@ -620,50 +621,23 @@ struct StageBParams {
   WinParams win;
 };
 
-// sum over the ranges of SUF_J for head row `row` (fixed order)
-__device__ __forceinline__ double suf_at(const double* __restrict__ tpart, size_t row, int nrange,
-                                         int J) {
-  if (J >= kNB) return 0.0;
-  double s = 0.0;
-  for (int r0 = 0; r0 < nrange; r0 += 8) {
-    double y[8];
-#pragma unroll
-    for (int u = 0; u < 8; u++)
-      y[u] = r0 + u < nrange ? tpart[(row * nrange + r0 + u) * kNB + J] : 0.0;
-#pragma unroll
-    for (int u = 0; u < 8; u++) s += y[u];
-  }
-  return s;
-}
-
-// Code word w of a chunk holds the bins of tokens w + q*(TC/4), q = 0..3 (byte q).  Thread
-// tid of this kernel takes words tid + i*256, i < NW, i.e. TPT = 4*NW tokens per chunk.
-template <int TPT, int GMAX>
-__device__ void select_attend_block(const StageBParams& P, unsigned char* smem);
-
-template <int TPT, int GMAX>
-__global__ __launch_bounds__(kThreads) void k_stage_b(StageBParams P) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  if ((int)blockIdx.x < P.nret_blocks)
-    select_attend_block<TPT, GMAX>(P, smem);
-  else
-    window_block(P.win, blockIdx.x - P.nret_blocks, reinterpret_cast<float*>(smem));
-}
-
-template <int TPT, int GMAX>
+// Selection block over the TB = 2048*NWD tokens [blk*TB, (blk+1)*TB) of retrieval KV
+// head kr.  Code word w of a chunk holds the bins of tokens 4w + q, q = 0..3 (byte q);
+// thread tid takes the block's words tid + i*512, i < NWD.
+//
+// A token is selected for head g iff its chunk-relative code j_c <= tau_g = b* - (A - A_c)
+// (all tokens when b* = 255).  Four codes are tested at once: with the bytes of a word
+// spread over two 16-bit lanes, (256 + tau) - j_c has bit 8 set iff j_c <= tau.
+template <int NWD, int GMAX>
 __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) {
-  constexpr int TC = kThreads * TPT;
-  constexpr int NW = TPT / 4;  // code words per thread per chunk and head
-  auto tok_of = [&](int chunk, int t) {  // t = 4*i + q
-    return chunk * TC + (threadIdx.x + (t >> 2) * kThreads) + (t & 3) * (TC / 4);
-  };
-  __shared__ int s_tau[kBChunks][kAttnG];
-  __shared__ int s_A[kAttnG], s_bs[kAttnG], s_m[kAttnG];
-  __shared__ double s_suf[kAttnG][17];
-  __shared__ int s_wsum[kThreads / 64];
+  constexpr int NT = kBThreads;
+  constexpr int TB = NT * 4 * NWD;
+  constexpr int HPW = (GMAX + kBWaves - 1) / kBWaves;  // heads per wavefront (b* search)
+  __shared__ int s_tau[kMaxCPB][kAttnG];
+  __shared__ int s_bs[kAttnG];
+  __shared__ int s_wsum[kBWaves];
   __shared__ int s_cnt[kAttnG];
-  int32_t* ltok = reinterpret_cast<int32_t*>(smem);
-  uint16_t* lmask = reinterpret_cast<uint16_t*>(smem + sizeof(int32_t) * kBChunks * TC);
+  uint32_t* lst = reinterpret_cast<uint32_t*>(smem);  // [TB]: in-block token | head mask << 16
   float* lds = reinterpret_cast<float*>(smem);
 
   const int tid = threadIdx.x;
@@ -673,124 +647,153 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
   const int kr = (blockIdx.x / P.nblk) % P.Hret;
   const int b = blockIdx.x / (P.nblk * P.Hret);
   const int G = P.G;
-  const int H = P.Hret * G;
-  const size_t row0 = (size_t)b * H + (size_t)kr * G;
+  const size_t row0 = (size_t)b * P.Hret * G + (size_t)kr * G;
   const int L = clamp_len(P.seq_lens, b, P.Lmax);
-  const int chunk0 = blk * kBChunks;
+  const int tc = P.tc;
+  const int WPC = tc >> 2;     // code words per chunk
+  const int cpb = TB / tc;     // chunks per block
+  const int chunk0 = blk * cpb;
+  const int tok0 = blk * TB;
   const f16* Kb = P.K_ret + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kD;
   const f16* Vb = P.V_ret + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kD;
 
-  // ---- phase 0: inputs of the selection; the code words do not depend on b*, so all of
-  // them are in flight while b* is searched
+  // ---- phase 0: every input of the selection is in flight at once
   h8 qop[4];
   load_qop(P.q + ((size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G) * kD, G, qop);
-  uint32_t cw[kBChunks][GMAX][NW];
+  // the block's chunks are consecutive, so its code words of head g are the words
+  // [chunk0*WPC, (chunk0+cpb)*WPC) of the head's row (clamped at the row's end)
+  uint32_t cw[NWD][GMAX];
+  {
+    const int rowwords = P.nchunk * WPC;
+    int off[NWD];
 #pragma unroll
-  for (int c = 0; c < kBChunks; c++) {
-    const int chunk = min(chunk0 + c, P.nchunk - 1);
+    for (int i = 0; i < NWD; i++) off[i] = min(chunk0 * WPC + tid + i * NT, rowwords - 1);
 #pragma unroll
     for (int g = 0; g < GMAX; g++) {
-      const int gg = g < G ? g : 0;
-      const uint32_t* cp = P.codes + ((row0 + gg) * P.nchunk + chunk) * (size_t)(TC / 4) + tid;
+      const uint32_t* crow = P.codes + (row0 + (g < G ? g : 0)) * (size_t)rowwords;
 #pragma unroll
-      for (int w = 0; w < NW; w++) cw[c][g][w] = cp[w * kThreads];
+      for (int i = 0; i < NWD; i++) cw[i][g] = crow[off[i]];
     }
   }
-  if (tid < kBChunks * kAttnG) {
-    const int c = tid / kAttnG, g = tid % kAttnG;
-    const int chunk = chunk0 + c;
-    s_tau[c][g] = (g < G && chunk < P.nchunk) ? P.partA[(row0 + g) * P.nchunk + chunk] : kEmptyCell;
-  }
-  if (tid < kAttnG) {
-    s_A[tid] = tid < G ? P.Aglob[row0 + tid] : kEmptyCell;
-    s_cnt[tid] = 0;
-  }
-  // coarse search: SUF at bins 16k (k = 0..15); thread (g, k)
-  const int sg = tid >> 4, sk = tid & 15;
-  if (sg < G && P.p < 1.0) s_suf[sg][sk] = suf_at(P.tpart, row0 + sg, P.nrange, 16 * sk);
-  __syncthreads();
-  if (tid < kAttnG) {
-    int m = 16;  // C_J >= pZ first happens for J in [16(m-1), 16m - 1]
-    if (tid < G && P.p < 1.0) {
-      const double Z = s_suf[tid][0];
-      for (int k = 15; k >= 1; k--)
-        if (Z - s_suf[tid][k] >= P.p * Z) m = k;
+  int Ac = kEmptyCell, Ag = kEmptyCell;
+  if (tid < cpb * kAttnG) {
+    const int cc = tid / kAttnG, g = tid % kAttnG;
+    const int chunk = chunk0 + cc;
+    if (g < G) {
+      Ag = P.Aglob[row0 + g];
+      if (chunk < P.nchunk) Ac = P.partA[(row0 + g) * P.nchunk + chunk];
     }
-    s_m[tid] = m;
   }
-  __syncthreads();
-  // fine search: SUF_{J+1} for J in [16(m-1), 16m-1]
-  if (sg < G && P.p < 1.0) {
-    const int J1 = 16 * (s_m[sg] - 1) + 1 + sk;
-    s_suf[sg][sk + 1] = suf_at(P.tpart, row0 + sg, P.nrange, J1);
-  }
-  __syncthreads();
-  if (tid < kAttnG) {
-    int bs = kNB - 1;
-    if (tid < G && P.p < 1.0) {
-      const double Z = suf_at(P.tpart, row0 + tid, P.nrange, 0);
-      const int Jlo = 16 * (s_m[tid] - 1);
-      for (int i = 15; i >= 0; i--)
-        if (Jlo + i < kNB - 1 && Z - s_suf[tid][i + 1] >= P.p * Z) bs = Jlo + i;
+  // suffix table of the wavefront's heads: lane l holds SUF at bins 4l+1 .. 4l+4
+  double sv[HPW][4], zv[HPW];
+#pragma unroll
+  for (int u = 0; u < HPW; u++) {
+    const int g = wv + u * kBWaves;
+    zv[u] = 0.0;
+#pragma unroll
+    for (int k = 0; k < 4; k++) sv[u][k] = 0.0;
+    if (g < G && P.p < 1.0) {
+      const double* sp = P.sufg + (row0 + g) * kNB;
+      zv[u] = sp[0];
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        const int J = 4 * lane + 1 + k;
+        sv[u][k] = J < kNB ? sp[J] : 0.0;
+      }
     }
-    s_bs[tid] = bs;
-    if (blk == 0 && tid < G) P.bstar[row0 + tid] = bs;
+  }
+  if (tid < kAttnG) s_cnt[tid] = 0;
+  // b*: least J < 255 with Z - SUF_{J+1} >= p Z, else 255
+#pragma unroll
+  for (int u = 0; u < HPW; u++) {
+    const int g = wv + u * kBWaves;
+    if (g < G) {
+      int J = kNB - 1;
+      if (P.p < 1.0) {
+        const double pz = P.p * zv[u];
+#pragma unroll
+        for (int k = 3; k >= 0; k--) {
+          const int Jk = 4 * lane + k;
+          if (Jk < kNB - 1 && zv[u] - sv[u][k] >= pz) J = Jk;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) J = min(J, __shfl_xor(J, o, 64));
+      }
+      if (lane == 0) {
+        s_bs[g] = J;
+        if (blk == 0) P.bstar[row0 + g] = J;
+      }
+    }
   }
   __syncthreads();
-  // chunk threshold code tau: tokens with code <= tau are selected (256: all, -1: none)
-  int tau = -1;
-  if (tid < kBChunks * kAttnG) {
-    const int c = tid / kAttnG, g = tid % kAttnG;
-    const int Ac = s_tau[c][g];
-    const int A = s_A[g];
-    const int bs = s_bs[g];
-    if (g < G && A != kEmptyCell && Ac != kEmptyCell && (chunk0 + c) * TC < L) {
+  if (tid < cpb * kAttnG) {
+    const int cc = tid / kAttnG, g = tid % kAttnG;
+    int tau = -1;
+    if (g < G && Ag != kEmptyCell && Ac != kEmptyCell && (chunk0 + cc) * tc < L) {
+      const int bs = s_bs[g];
       if (bs >= kNB - 1) {
-        tau = 256;
+        tau = kNB - 1;
       } else {
-        const long long t = (long long)bs - ((long long)A - (long long)Ac);
+        const long long t = (long long)bs - ((long long)Ag - (long long)Ac);
         tau = t < 0 ? -1 : (int)t;
       }
     }
+    s_tau[cc][g] = tau;
   }
-  __syncthreads();
-  if (tid < kBChunks * kAttnG) s_tau[tid / kAttnG][tid % kAttnG] = tau;
   __syncthreads();
 
-  // ---- phase 1: union of the selected tokens (per-token head masks), compacted in LDS
-  uint32_t mk[kBChunks][TPT];
+  // ---- phase 1: per-token head masks, union compacted into the LDS list
+  uint32_t hm[NWD][4];
   int mine = 0;
+  const bool tail = tok0 + TB > L;
 #pragma unroll
-  for (int c = 0; c < kBChunks; c++) {
-#pragma unroll
-    for (int t = 0; t < TPT; t++) mk[c][t] = 0u;
+  for (int i = 0; i < NWD; i++) {
+    const int wi = tid + i * NT;
+    const int cc = wi / WPC;  // the same for the whole wavefront
+    const int w = wi - cc * WPC;
+    uint32_t me = 0u, mo = 0u;
 #pragma unroll
     for (int g = 0; g < GMAX; g++) {
-      const int tg = s_tau[c][g];
+      // s_tau is -1 for heads past G
+      const int tg = __builtin_amdgcn_readfirstlane(s_tau[cc][g]);
       if (tg < 0) continue;
-#pragma unroll
-      for (int t = 0; t < TPT; t++) {
-        const int code = (cw[c][g][t >> 2] >> (8 * (t & 3))) & 255;
-        if (tg == 256 || code <= tg) mk[c][t] |= 1u << g;
+      const uint32_t T = 0x01000100u + (uint32_t)tg * 0x00010001u;
+      const uint32_t x = cw[i][g];
+      const uint32_t de = T - (x & 0x00FF00FFu);
+      const uint32_t dd = T - ((x >> 8) & 0x00FF00FFu);
+      const uint32_t bit = 0x00010001u << g;
+      if (g <= 8) {
+        me |= (de >> (8 - g)) & bit;
+        mo |= (dd >> (8 - g)) & bit;
+      } else {
+        me |= (de << (g - 8)) & bit;
+        mo |= (dd << (g - 8)) & bit;
       }
     }
+    hm[i][0] = me & 0xFFFFu;
+    hm[i][1] = mo & 0xFFFFu;
+    hm[i][2] = me >> 16;
+    hm[i][3] = mo >> 16;
+    if (tail) {
 #pragma unroll
-    for (int t = 0; t < TPT; t++) {
-      if (tok_of(chunk0 + c, t) >= L) mk[c][t] = 0u;
-      mine += mk[c][t] != 0u;
+      for (int q = 0; q < 4; q++)
+        if (tok0 + cc * tc + 4 * w + q >= L) hm[i][q] = 0u;
     }
+#pragma unroll
+    for (int q = 0; q < 4; q++) mine += hm[i][q] != 0u;
   }
+  if (P.want_count) {
 #pragma unroll
-  for (int g = 0; g < GMAX; g++) {
-    if (g >= G || !P.want_count) break;
-    int cg = 0;
+    for (int g = 0; g < GMAX; g++) {
+      int c = 0;
 #pragma unroll
-    for (int c = 0; c < kBChunks; c++)
+      for (int i = 0; i < NWD; i++)
 #pragma unroll
-      for (int t = 0; t < TPT; t++) cg += (mk[c][t] >> g) & 1u;
+        for (int q = 0; q < 4; q++) c += (hm[i][q] >> g) & 1u;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) cg += __shfl_xor(cg, o, 64);
-    if (lane == 0 && cg) atomicAdd(&s_cnt[g], cg);
+      for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+      if (lane == 0 && c) atomicAdd(&s_cnt[g], c);
+    }
   }
   int incl = mine;
 #pragma unroll
@@ -802,54 +805,49 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
   __syncthreads();
   int woff = 0, U = 0;
 #pragma unroll
-  for (int i = 0; i < kThreads / 64; i++) {
-    if (i < wv) woff += s_wsum[i];
-    U += s_wsum[i];
+  for (int k = 0; k < kBWaves; k++) {
+    if (k < wv) woff += s_wsum[k];
+    U += s_wsum[k];
   }
   int pos = woff + incl - mine;
 #pragma unroll
-  for (int c = 0; c < kBChunks; c++) {
+  for (int i = 0; i < NWD; i++) {
+    const int wi = tid + i * NT;
+    const int cc = wi / WPC;
+    const int w = wi - cc * WPC;
 #pragma unroll
-    for (int t = 0; t < TPT; t++) {
-      if (mk[c][t]) {
-        ltok[pos] = tok_of(chunk0 + c, t);
-        lmask[pos] = (uint16_t)mk[c][t];
-        pos++;
-      }
+    for (int q = 0; q < 4; q++) {
+      if (hm[i][q]) lst[pos++] = (uint32_t)(cc * tc + 4 * w + q) | (hm[i][q] << 16);
     }
   }
   __syncthreads();
 
-  // ---- phase 2: masked MFMA attention over the listed rows; wavefront wv takes steps
-  // wv, wv+4, ...; two steps' loads are in flight before the first is used
+  // ---- phase 2: masked MFMA attention over the listed rows
   AttnState st;
   attn_init(st);
-  const int nsteps = (U + kStep - 1) / kStep;
-  for (int s0 = wv; s0 < nsteps; s0 += 2 * (kThreads / 64)) {
-    const int s1 = s0 + kThreads / 64;
-    StepLoads ld0, ld1;
-    const int e0 = s0 * kStep, e1 = s1 * kStep;
-    step_load(Kb, Vb, [&](int i) { return ltok[e0 + i < U ? e0 + i : 0]; }, ld0);
-    if (s1 < nsteps) step_load(Kb, Vb, [&](int i) { return ltok[e1 + i < U ? e1 + i : 0]; }, ld1);
-    step_compute(ld0, qop, P.scale2,
-                 [&](int i, int h) { return e0 + i < U && ((lmask[e0 + i < U ? e0 + i : 0] >> h) & 1u); },
-                 st);
-    if (s1 < nsteps)
-      step_compute(ld1, qop, P.scale2,
-                   [&](int i, int h) { return e1 + i < U && ((lmask[e1 + i < U ? e1 + i : 0] >> h) & 1u); },
-                   st);
-  }
+  attend_list<kBWaves>(
+      Kb, Vb, U, [&](int e) { return tok0 + (int)(lst[e] & 0xFFFFu); },
+      [&](int e) { return lst[e] >> 16; }, qop, P.scale2, st);
   __syncthreads();
 
   // ---- phase 3: block partial
   const size_t s1p = ((size_t)(b * P.Hret + kr) * P.nblk + blk) * G;
-  block_combine<kThreads / 64>(st, G, lds, P.p1m + s1p, P.p1l + s1p, P.p1acc + s1p * kD);
+  block_combine<kBWaves>(st, G, lds, P.p1m + s1p, P.p1l + s1p, P.p1acc + s1p * kD);
   if (tid < G) P.p1cnt[s1p + tid] = s_cnt[tid];
 }
 
+template <int NWD, int GMAX>
+__global__ __launch_bounds__(kBThreads) void k_stage_b(StageBParams P) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  if ((int)blockIdx.x < P.nret_blocks)
+    select_attend_block<NWD, GMAX>(P, smem);
+  else
+    window_block(P.win, blockIdx.x - P.nret_blocks, reinterpret_cast<float*>(smem));
+}
+
 // ---------------------------------------------------------------------------
-// stage M: merge the slice partials of every retrieval query head, then (blocks past
-// them) the window partials of every local query head
+// stage M: block (query head, 32 output dims) merges the head's n partials
+// (m, l at [k*G + g], acc at [(k*G + g)*128 + d]) in a fixed order.
 // ---------------------------------------------------------------------------
 struct StageMParams {
   const float* p1m;
@@ -860,7 +858,6 @@ struct StageMParams {
   const int32_t* bstar;
   int nblk, Hret, G, Hq, nret;
   HeadMap ret;
-  // window
   const float* wpm;
   const float* wpl;
   const float* wpacc;
@@ -872,27 +869,116 @@ struct StageMParams {
   int32_t* thresh_out;
 };
 
+// thread (sub = t/8, dq = t%8): float4 dq of the slice for partials sub, sub+32, ...
+__device__ void merge_slice(const float* __restrict__ pm, const float* __restrict__ pl,
+                            const float* __restrict__ pacc, const int32_t* __restrict__ pcnt,
+                            int n, int G, int g, int slice, float* __restrict__ out,
+                            float* __restrict__ lse, int32_t* __restrict__ count_out, size_t orow,
+                            float* lds) {
+  constexpr int NSUB = kThreads / (kMSlice / 4);  // 32
+  float* racc = lds;                                     // [NSUB][32] (16-byte aligned)
+  float* red = racc + NSUB * kMSlice;                    // [8]
+  float* wk = red + 8;                                   // [n] m, then weights
+  float* wl = wk + n;                                    // [n] l
+  int* wc = reinterpret_cast<int*>(wl + n);              // [n] counts
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int sub = tid >> 3;
+  const int dq = tid & 7;
+  const size_t kst = (size_t)G * (kD / 4);  // float4 stride between partials
+  const float4* accb = reinterpret_cast<const float4*>(pacc + (size_t)g * kD + slice * kMSlice) + dq;
+  float4 x[8];
+#pragma unroll
+  for (int u = 0; u < 8; u++) x[u] = accb[(size_t)min(sub + NSUB * u, n - 1) * kst];
+  float mloc = -INFINITY;
+  for (int k = tid; k < n; k += kThreads) {
+    const float m = pm[(size_t)k * G + g];
+    wk[k] = m;
+    wl[k] = pl[(size_t)k * G + g];
+    if (pcnt) wc[k] = pcnt[(size_t)k * G + g];
+    mloc = fmaxf(mloc, m);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, 64));
+  if (lane == 0) red[wv] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float lloc = 0.0f;
+  int cloc = 0;
+  for (int k = tid; k < n; k += kThreads) {
+    const float m = wk[k];
+    const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+    wk[k] = f;
+    lloc += wl[k] * f;
+    if (pcnt) cloc += wc[k];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lloc += __shfl_xor(lloc, o, 64);
+    cloc += __shfl_xor(cloc, o, 64);
+  }
+  __syncthreads();
+  if (lane == 0) {
+    red[wv] = lloc;
+    reinterpret_cast<int*>(red)[4 + wv] = cloc;
+  }
+  __syncthreads();
+  const float Lsum = (red[0] + red[1]) + (red[2] + red[3]);
+  const int* ired = reinterpret_cast<const int*>(red) + 4;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < n; k0 += NSUB * 8) {
+    if (k0 > 0) {
+#pragma unroll
+      for (int u = 0; u < 8; u++) x[u] = accb[(size_t)min(k0 + sub + NSUB * u, n - 1) * kst];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const int k = k0 + sub + NSUB * u;
+      const float f = k < n ? wk[k] : 0.0f;
+      a.x += x[u].x * f;
+      a.y += x[u].y * f;
+      a.z += x[u].z * f;
+      a.w += x[u].w * f;
+    }
+  }
+  reinterpret_cast<float4*>(racc + sub * kMSlice)[dq] = a;
+  __syncthreads();
+  if (tid < kMSlice) {
+    float v = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NSUB; s++) v += racc[s * kMSlice + tid];
+    out[orow * kD + slice * kMSlice + tid] = Lsum > 0.0f ? v / Lsum : 0.0f;
+  }
+  if (slice == 0 && tid == 0) {
+    if (lse) lse[orow] = Lsum > 0.0f ? (M + __log2f(Lsum)) * 0.69314718055994531f : -INFINITY;
+    if (count_out) count_out[orow] = (ired[0] + ired[1]) + (ired[2] + ired[3]);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void k_stage_m(StageMParams P) {
   extern __shared__ __align__(16) float mlds[];
   const int G = P.G;
-  if ((int)blockIdx.x >= P.nret) {
-    const int wm = blockIdx.x - P.nret;
+  const int slice = blockIdx.x % kMSlices;
+  const int hb = blockIdx.x / kMSlices;
+  if (hb >= P.nret) {
+    const int wm = hb - P.nret;
     const int g = wm % G;
     const int kl = (wm / G) % P.Hloc;
     const int b = wm / (G * P.Hloc);
     const size_t p0 = (size_t)(b * P.Hloc + kl) * P.nws * G;
-    merge_head(P.wpm + p0, P.wpl + p0, P.wpacc + p0 * kD, nullptr, P.nws, G, g, P.out, P.lse,
-               nullptr, (size_t)b * P.Hq + (size_t)P.loc.kv[kl] * G + g, mlds);
+    merge_slice(P.wpm + p0, P.wpl + p0, P.wpacc + p0 * kD, nullptr, P.nws, G, g, slice, P.out,
+                P.lse, nullptr, (size_t)b * P.Hq + (size_t)P.loc.kv[kl] * G + g, mlds);
     return;
   }
-  const int g = blockIdx.x % G;
-  const int kr = (blockIdx.x / G) % P.Hret;
-  const int b = blockIdx.x / (G * P.Hret);
+  const int g = hb % G;
+  const int kr = (hb / G) % P.Hret;
+  const int b = hb / (G * P.Hret);
   const size_t p0 = (size_t)(b * P.Hret + kr) * P.nblk * G;
   const size_t orow = (size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G + g;
-  merge_head(P.p1m + p0, P.p1l + p0, P.p1acc + p0 * kD, P.p1cnt + p0, P.nblk, G, g, P.out, P.lse,
-             P.count_out, orow, mlds);
-  if (P.thresh_out && threadIdx.x == 0) {
+  merge_slice(P.p1m + p0, P.p1l + p0, P.p1acc + p0 * kD, P.count_out ? P.p1cnt + p0 : nullptr,
+              P.nblk, G, g, slice, P.out, P.lse, P.count_out, orow, mlds);
+  if (slice == 0 && P.thresh_out && threadIdx.x == 0) {
     const size_t row = (size_t)b * P.Hret * G + (size_t)kr * G + g;
     const int A = P.Aglob[row];
     P.thresh_out[orow * 2 + 0] = A == kEmptyCell ? 0 : A;
@@ -905,10 +991,36 @@ __global__ __launch_bounds__(kThreads) void k_stage_m(StageMParams P) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-bool step_fused_supported(int kv_dtype, int G, int Hloc, int window, int sinks) {
+namespace {
+int chunk_tokens(int B, int Hret, int Lmax) {
+  // 2048-token chunks (stage-A blocks of 512 threads) unless that leaves fewer than 256
+  // histogram blocks; then 1024-token chunks (256 threads)
+  const int64_t units = (int64_t)B * (Hret > 0 ? Hret : 1);
+  return units * ((Lmax + 2047) / 2048) >= 256 ? 2048 : 1024;
+}
+int window_rows(int B, int Hloc, int ring) {
+  // rows per window block: 256 (one step per wavefront) unless that makes more than 256
+  // window blocks; then up to 2048
+  int wr = kBWaves * kStep;
+  while (wr < 2048 && (int64_t)B * Hloc * ((ring + wr - 1) / wr) > 256) wr *= 2;
+  return wr;
+}
+}  // namespace
+
+bool step_fused_supported(int kv_dtype, int G, int Hloc, int window, int sinks, int B, int Hret,
+                          int Lmax) {
   if (kv_dtype != 1 || G > kAttnG) return false;
-  // the window merge keeps one weight per split in LDS
-  if (Hloc > 0 && (window + sinks + kWinRows - 1) / kWinRows > 8192) return false;
+  if (Hloc > 0) {
+    const int ring = window + sinks;
+    const int wr = window_rows(B, Hloc, ring);
+    if ((ring + wr - 1) / wr > kMaxParts) return false;
+  }
+  if (Hret > 0) {
+    const int tc = chunk_tokens(B, Hret, Lmax);
+    const int64_t nchunk = ((int64_t)Lmax + tc - 1) / tc;
+    if (nchunk > 16384) return false;                 // stage-T LDS
+    if ((Lmax + 8191) / 8192 > kMaxParts) return false;  // stage-M LDS
+  }
   return true;
 }
 
@@ -919,25 +1031,37 @@ StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int
   sp.G = G;
   sp.Hret = Hret;
   sp.Hloc = Hloc;
-  const int H = Hret * G;
-  // 2048-token chunks (stage-A blocks of 512 threads) unless that leaves fewer than 256
-  // histogram blocks; then 1024-token chunks (256 threads)
-  {
-    const int64_t units = (int64_t)B * (Hret > 0 ? Hret : 1);
-    sp.tc = units * ((Lmax + 2047) / 2048) >= 256 ? 2048 : 1024;
-    sp.nt = sp.tc / 4;
-    sp.tpt = sp.tc / kThreads;
+  sp.tc = chunk_tokens(B, Hret, Lmax);
+  sp.nt = sp.tc / 4;
+  int nwin_blocks = 0;
+  if (Hloc > 0) {
+    sp.wrows = window_rows(B, Hloc, window + sinks);
+    sp.nws = (window + sinks + sp.wrows - 1) / sp.wrows;
+    nwin_blocks = B * Hloc * sp.nws;
   }
   if (Hret > 0) {
     sp.nchunk = (Lmax + sp.tc - 1) / sp.tc;
-    sp.nblk = (sp.nchunk + kBChunks - 1) / kBChunks;
-    sp.nrange = (sp.nchunk + kTRange - 1) / kTRange;
+    // tokens per selection block: the smallest of 2048 / 4096 / 8192 (and at least one
+    // chunk) whose selection grid, with the window blocks, is one block per CU
+    sp.nwd = 4;
+    for (int nwd = 1; nwd <= 4; nwd *= 2) {
+      const int tb = 2048 * nwd;
+      if (tb < sp.tc) continue;
+      const int64_t nb = (int64_t)B * Hret * ((Lmax + tb - 1) / tb);
+      if (nb + nwin_blocks <= 256) {
+        sp.nwd = nwd;
+        break;
+      }
+    }
+    sp.tb = 2048 * sp.nwd;
+    sp.nblk = (Lmax + sp.tb - 1) / sp.tb;
+    const int H = Hret * G;
     sp.suf = wp.take<float>((size_t)B * H * sp.nchunk * kNB);
     sp.partA = wp.take<int32_t>((size_t)B * H * sp.nchunk);
     sp.codes = wp.take<uint32_t>((size_t)B * H * sp.nchunk * (sp.tc / 4));
     sp.bstar = wp.take<int32_t>((size_t)B * H);
     sp.Aglob = wp.take<int32_t>((size_t)B * H);
-    sp.tpart = wp.take<double>((size_t)B * H * sp.nrange * kNB);
+    sp.sufg = wp.take<double>((size_t)B * H * kNB);
     const size_t n1 = (size_t)B * Hret * sp.nblk * G;
     sp.p1m = wp.take<float>(n1);
     sp.p1l = wp.take<float>(n1);
@@ -945,7 +1069,6 @@ StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int
     sp.p1cnt = wp.take<int32_t>(n1);
   }
   if (Hloc > 0) {
-    sp.nws = (window + sinks + kWinRows - 1) / kWinRows;
     const size_t nw = (size_t)B * Hloc * sp.nws * G;
     sp.wpm = wp.take<float>(nw);
     sp.wpl = wp.take<float>(nw);
@@ -976,7 +1099,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
   // ---- K1: indexer score + chunk histograms
   StageAParams P{};
   if (sp.Hret > 0) {
-    const int GG = G > 4 ? 8 : (G > 2 ? 4 : (G > 1 ? 2 : 1));
+    constexpr int GG = 8;
     P.seq_lens = a.seq_lens;
     P.B = B;
     P.Hq = a.Hq;
@@ -995,39 +1118,27 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     P.partA = at<int32_t>(ws, sp.partA);
     P.codes = at<uint32_t>(ws, sp.codes);
     const int nA = B * sp.Hret * P.ngg * sp.nchunk;
-    const size_t ldsA = sizeof(unsigned long long) * kCopies * 8 * (kNB + kPad) + 1024;
-#define RTP_STAGE_A(GGV, NTV) k_stage_a<GGV, NTV><<<nA, NTV, ldsA, st>>>(P)
-    if (sp.nt == 256) {
-      switch (GG) {
-        case 8: RTP_STAGE_A(8, 256); break;
-        case 4: RTP_STAGE_A(4, 256); break;
-        case 2: RTP_STAGE_A(2, 256); break;
-        default: RTP_STAGE_A(1, 256); break;
-      }
-    } else {
-      switch (GG) {
-        case 8: RTP_STAGE_A(8, 512); break;
-        case 4: RTP_STAGE_A(4, 512); break;
-        case 2: RTP_STAGE_A(2, 512); break;
-        default: RTP_STAGE_A(1, 512); break;
-      }
-    }
+    const size_t ldsA = sizeof(unsigned long long) * kCopies * GG * (kNB + kPad) + 1024;
+#define RTP_STAGE_A(NTV) k_stage_a<NTV><<<nA, NTV, ldsA, st>>>(P)
+    if (sp.nt == 256)
+      RTP_STAGE_A(256);
+    else
+      RTP_STAGE_A(512);
 #undef RTP_STAGE_A
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   rec(1);
-  // ---- K2: threshold range sums
+  // ---- K2: suffix tables
   StageTParams T{};
   if (sp.Hret > 0) {
     T.suf = P.suf;
     T.partA = P.partA;
     T.nchunk = sp.nchunk;
-    T.nrange = sp.nrange;
     T.c_log2 = c_log2;
-    T.tpart = at<double>(ws, sp.tpart);
+    T.sufg = at<double>(ws, sp.sufg);
     T.Aglob = at<int32_t>(ws, sp.Aglob);
-    k_stage_t<<<B * H * sp.nrange, kThreads, 0, st>>>(T);
+    k_stage_t<<<B * H * (kNB / kTBins), kThreads, sizeof(int) * sp.nchunk, st>>>(T);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1046,7 +1157,6 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     Q.nchunk = sp.nchunk;
     Q.tc = sp.tc;
     Q.nblk = sp.nblk;
-    Q.nrange = sp.nrange;
     Q.p = a.p;
     Q.q = static_cast<const f16*>(a.q);
     Q.K_ret = static_cast<const f16*>(a.K_ret);
@@ -1054,7 +1164,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     Q.ret = a.ret;
     Q.partA = P.partA;
     Q.codes = P.codes;
-    Q.tpart = T.tpart;
+    Q.sufg = T.sufg;
     Q.Aglob = T.Aglob;
     Q.bstar = at<int32_t>(ws, sp.bstar);
     Q.p1m = at<float>(ws, sp.p1m);
@@ -1078,6 +1188,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     W.window = a.window;
     W.sinks = a.sinks;
     W.nws = sp.nws;
+    W.wrows = sp.wrows;
     W.scale2 = scale2;
     W.wpm = at<float>(ws, sp.wpm);
     W.wpl = at<float>(ws, sp.wpl);
@@ -1085,19 +1196,23 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     nwin_blocks = B * sp.Hloc * sp.nws;
   }
   const size_t ldsB = std::max<size_t>(4 * (32 + 2048) * sizeof(float),
-                                       (sizeof(int32_t) + sizeof(uint16_t)) * kBChunks * sp.tc);
+                                       sizeof(uint32_t) * (size_t)(sp.Hret > 0 ? sp.tb : 0));
   const int nB = Q.nret_blocks + nwin_blocks;
-  if (sp.tpt == 4) {
-    if (G <= 8)
-      k_stage_b<4, 8><<<nB, kThreads, ldsB, st>>>(Q);
-    else
-      k_stage_b<4, 16><<<nB, kThreads, ldsB, st>>>(Q);
+#define RTP_STAGE_B(NWDV, GMV) k_stage_b<NWDV, GMV><<<nB, kBThreads, ldsB, st>>>(Q)
+  if (G <= 8) {
+    switch (sp.nwd) {
+      case 1: RTP_STAGE_B(1, 8); break;
+      case 2: RTP_STAGE_B(2, 8); break;
+      default: RTP_STAGE_B(4, 8); break;
+    }
   } else {
-    if (G <= 8)
-      k_stage_b<8, 8><<<nB, kThreads, ldsB, st>>>(Q);
-    else
-      k_stage_b<8, 16><<<nB, kThreads, ldsB, st>>>(Q);
+    switch (sp.nwd) {
+      case 1: RTP_STAGE_B(1, 16); break;
+      case 2: RTP_STAGE_B(2, 16); break;
+      default: RTP_STAGE_B(4, 16); break;
+    }
   }
+#undef RTP_STAGE_B
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // ---- K4: merges
@@ -1130,8 +1245,8 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     M.loc = a.loc;
   }
   const int nmax = std::max(sp.Hret > 0 ? sp.nblk : 0, sp.Hloc > 0 ? sp.nws : 0);
-  const size_t ldsM = sizeof(float) * ((size_t)nmax + kThreads + 8 * kD);
-  k_stage_m<<<M.nret + nwm, kThreads, ldsM, st>>>(M);
+  const size_t ldsM = sizeof(float) * (3 * (size_t)nmax + 8 + kThreads / 8 * kMSlice);
+  k_stage_m<<<(M.nret + nwm) * kMSlices, kThreads, ldsM, st>>>(M);
   e = hipGetLastError();
   rec(3);
   return e;
