@@ -130,6 +130,7 @@ struct StepFusedPlan {
   int tc, nt, nchunk;  // histogram chunk tokens, stage-A threads, chunks per row
   int nwd, tb, nblk;   // selection blocks: code words per thread, tokens, blocks per KV head
   int wrows, nws;      // window blocks: rows per block, blocks per local KV head
+  int ncu;             // compute units of the device
   size_t suf, partA, codes, bstar, Aglob, sufg;
   size_t p1m, p1l, p1acc, p1cnt;
   size_t wpm, wpl, wpacc;

@@ -39,9 +39,9 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAttnG = 16;               // head columns of the MFMA tile
 constexpr int kStep = 32;                // cache rows per wavefront step
-constexpr int kBThreads = 512;           // threads of a stage-B block
+constexpr int kBThreads = 256;           // threads of a stage-B block (two blocks per CU)
 constexpr int kBWaves = kBThreads / 64;  // wavefronts of a stage-B block
-constexpr int kMaxCPB = 8;               // histogram chunks per selection block (at most)
+constexpr int kMaxCPB = 4;               // histogram chunks per selection block (at most)
 constexpr int kTBins = 16;               // bins per stage-T block
 constexpr int kTBatch = 32;              // chunk loads in flight per stage-T thread
 constexpr int kMSlice = 32;              // output dims per stage-M block
@@ -52,9 +52,52 @@ __device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Sequence length of batch row b through the scalar cache.  A vector load here would be
+// waited for with the in-order vector-memory counter, i.e. together with every load
+// issued before its first use; the scalar load waits only for itself (and LDS).
+__device__ __forceinline__ int seq_len(const int32_t* seq_lens, int b) {
+  const int32_t* p = seq_lens + b;
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+  return v;
+}
+
 __device__ __forceinline__ int clamp_len(const int32_t* seq_lens, int b, int Lmax) {
-  int L = seq_lens[b];
+  const int L = seq_len(seq_lens, b);
   return L < 0 ? 0 : (L > Lmax ? Lmax : L);
+}
+
+// ---------------------------------------------------------------------------
+// wavefront scans and reductions on DPP lane moves (no LDS round trip)
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float x) {
+  // lanes whose source is out of range, or whose row is masked off, read 0
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+}
+
+// minimum over the 64 lanes (every lane gets it): rotations inside the rows, then the
+// rows through lanes 15 / 31 and a final read of lane 63
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x121, 0xf, 0xf, false));  // row_ror:1
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x122, 0xf, 0xf, false));  // row_ror:2
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x124, 0xf, 0xf, false));  // row_ror:4
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x128, 0xf, 0xf, false));  // row_ror:8
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each row of 16,
+// then lane 15 of rows 0/2 into rows 1/3 and lane 31 into rows 2/3
+__device__ __forceinline__ float wave_incl_sum(float v) {
+  v += dpp_f<0x111>(v);  // row_shr:1
+  v += dpp_f<0x112>(v);  // row_shr:2
+  v += dpp_f<0x114>(v);  // row_shr:4
+  v += dpp_f<0x118>(v);  // row_shr:8
+  v += dpp_f<0x142, 0xa>(v);  // row_bcast:15
+  v += dpp_f<0x143, 0xc>(v);  // row_bcast:31
+  return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -175,11 +218,15 @@ __device__ __forceinline__ void step_compute(const StepLoads& ld, const h8 (&qop
 }
 
 // Combine the NWV wavefronts of a block into per-head partials (unnormalised), written
-// to out_m/out_l/out_acc for heads < G.  Waves pass through LDS four at a time;
-// lds >= 4*(32+2048) floats.
+// to out_m/out_l/out_acc for heads < G.  Only the first `nact` wavefronts can hold rows
+// (the others took no step); they pass through LDS in one round, then thread
+// (head, DPT dims) combines them in wavefront order.  lds >= NWV*(32+2048) floats.
 template <int NWV>
-__device__ void block_combine(AttnState& st, int G, float* lds, float* out_m, float* out_l,
-                              float* out_acc) {
+__device__ void block_combine(AttnState& st, int G, int nact, float* lds, float* out_m,
+                              float* out_l, float* out_acc) {
+  constexpr int NT = NWV * 64;
+  constexpr int DPT = 16 * kD / NT;  // dims per combining thread
+  constexpr int WS = 32 + 2048;      // LDS floats per wavefront
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int h = lane & 15;
@@ -187,58 +234,48 @@ __device__ void block_combine(AttnState& st, int G, float* lds, float* out_m, fl
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  // item of this thread (threads 0..255): head th, dims d0..d0+7
-  const int th = threadIdx.x >> 4;
-  const int d0 = (threadIdx.x & 15) * 8;
-  const bool item = threadIdx.x < 256 && th < G;
-  float M = -INFINITY, L = 0.0f, a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int wg = 0; wg < (NWV + 3) / 4; wg++) {
-    if (wv / 4 == wg) {
-      float* wm = lds + (wv % 4) * (32 + 2048);
-      float* wl = wm + 16;
-      float* wacc = wm + 32;
-      if (lane < 16) {
-        wm[h] = st.m;
-        wl[h] = l;
-      }
+  if (wv < nact) {
+    float* wm = lds + wv * WS;
+    if (lane < 16) {
+      wm[h] = st.m;
+      wm[16 + h] = l;
+    }
+    if (4 * gq < G) {
 #pragma unroll
       for (int nb = 0; nb < 8; nb++) {
 #pragma unroll
-        for (int t = 0; t < 4; t++) wacc[(4 * gq + t) * kD + 8 * h + nb] = st.o[nb][t];
+        for (int t = 0; t < 4; t++) wm[32 + (4 * gq + t) * kD + 8 * h + nb] = st.o[nb][t];
       }
     }
-    __syncthreads();
-    if (item) {
-      const int nw = min(4, NWV - 4 * wg);
-      float Mn = M;
-      for (int w = 0; w < nw; w++) Mn = fmaxf(Mn, lds[w * (32 + 2048) + th]);
-      if (Mn != -INFINITY) {
-        const float fo = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
-        L *= fo;
-#pragma unroll
-        for (int i = 0; i < 8; i++) a[i] *= fo;
-        for (int w = 0; w < nw; w++) {
-          const float* base = lds + w * (32 + 2048);
-          const float mw = base[th];
-          if (mw == -INFINITY) continue;
-          const float f = __builtin_amdgcn_exp2f(mw - Mn);
-          L += base[16 + th] * f;
-#pragma unroll
-          for (int i = 0; i < 8; i++) a[i] += base[32 + th * kD + d0 + i] * f;
-        }
-        M = Mn;
-      }
-    }
-    __syncthreads();
   }
-  if (item) {
+  __syncthreads();
+  const int th = threadIdx.x / (kD / DPT);
+  const int d0 = (threadIdx.x % (kD / DPT)) * DPT;
+  if (th < G) {
+    float M = -INFINITY;
+    for (int w = 0; w < nact; w++) M = fmaxf(M, lds[w * WS + th]);
+    float L = 0.0f, acc[DPT];
+#pragma unroll
+    for (int i = 0; i < DPT; i++) acc[i] = 0.0f;
+    if (M != -INFINITY) {
+      for (int w = 0; w < nact; w++) {
+        const float* base = lds + w * WS;
+        const float mw = base[th];
+        if (mw == -INFINITY) continue;
+        const float f = __builtin_amdgcn_exp2f(mw - M);
+        L += base[16 + th] * f;
+#pragma unroll
+        for (int i = 0; i < DPT; i++) acc[i] += base[32 + th * kD + d0 + i] * f;
+      }
+    }
     if (d0 == 0) {
       out_m[th] = M;
       out_l[th] = L;
     }
     float4* dst = reinterpret_cast<float4*>(out_acc + th * kD + d0);
-    dst[0] = make_float4(a[0], a[1], a[2], a[3]);
-    dst[1] = make_float4(a[4], a[5], a[6], a[7]);
+#pragma unroll
+    for (int i = 0; i < DPT / 4; i++)
+      dst[i] = make_float4(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
   }
 }
 
@@ -247,7 +284,7 @@ __device__ void block_combine(AttnState& st, int G, float* lds, float* out_m, fl
 // masses and codes of the chunk-histogram kernel of rtp_score.hip, then suffix sums
 // of the bin masses.
 // ---------------------------------------------------------------------------
-constexpr int kCopies = 2;
+constexpr int kCopies = 4;  // histogram copies per head (lane bits 3..4)
 constexpr int kPad = 1;
 
 struct StageAParams {
@@ -256,7 +293,7 @@ struct StageAParams {
   const float* q_idx;
   const f16* k_idx;
   HeadMap ret;
-  int Hret, nchunk, ngg;
+  int Hret, nchunk, ngg, nunits;
   float yscale, c_log2;
   double w;
   float* suf;
@@ -290,26 +327,71 @@ struct WinParams {
 // [2^13, 2^14): hi + lo then carry 22 significant bits and the products stay in fp32
 // range; the scale is undone exactly in the final multiply.  The four bin codes of a
 // lane's tokens form one code word (byte t = token 4w + t of word w).
+// Loads of one histogram unit (k_idx rows and the raw q_idx of the lane's head); they
+// are issued without waiting, so a block can prefetch its next unit.
+struct HistIn {
+  h8 ka[8];
+  float4 q[2];  // q_idx[8*(kq&1) .. +7] of the lane's head
+};
+
+struct HistUnit {
+  int chunk, grp, kr, b, nrows, L;
+  size_t rowb;
+};
+
 template <int NT>
-__device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
+__device__ __forceinline__ HistUnit hist_unit(const StageAParams& P, int hb) {
+  HistUnit u;
+  u.chunk = hb % P.nchunk;
+  u.grp = (hb / P.nchunk) % P.ngg;
+  u.kr = (hb / (P.nchunk * P.ngg)) % P.Hret;
+  u.b = hb / (P.nchunk * P.ngg * P.Hret);
+  u.nrows = min(8, P.G - u.grp * 8);
+  u.rowb = (size_t)u.b * P.Hret * P.G + (size_t)u.kr * P.G + u.grp * 8;
+  u.L = clamp_len(P.seq_lens, u.b, P.Lmax);
+  return u;
+}
+
+template <int NT>
+__device__ __forceinline__ void hist_fetch(const StageAParams& P, const HistUnit& u, HistIn& in) {
+  constexpr int TC = NT * 4;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int base = u.chunk * TC;
+  const int kq = lane >> 4;
+  const f16* kb = P.k_idx + ((size_t)u.b * P.Hret + u.kr) * (size_t)P.Lmax * kR;
+  const int wbase = base + wv * 256;
+  // the same loads on every path (the wait counts stay exact): rows past the end, also
+  // of an empty unit, re-read the last valid row (row 0 when there is none); masked later
+  const int nlast = max(u.L - 1, 0);
+#pragma unroll
+  for (int gi = 0; gi < 8; gi++) {
+    const int n = min(wbase + gi * 32 + (lane & 15) + 16 * (kq >> 1), nlast);
+    in.ka[gi] = *reinterpret_cast<const h8*>(kb + (size_t)n * kR + 8 * (kq & 1));
+  }
+  const int hh = lane & 7;
+  const float4* qp = reinterpret_cast<const float4*>(
+      P.q_idx + ((size_t)u.b * P.Hq + (size_t)P.ret.kv[u.kr] * P.G + u.grp * 8 + min(hh, u.nrows - 1)) * kR +
+      8 * (kq & 1));
+  in.q[0] = qp[0];
+  in.q[1] = qp[1];
+}
+
+template <int NT>
+__device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistIn& in,
+                           unsigned char* smem) {
   constexpr int TC = NT * 4;
   constexpr int NWV = NT / 64;
   constexpr int GG = 8;
-  unsigned long long* hist = reinterpret_cast<unsigned long long*>(smem);
-  float* smax = reinterpret_cast<float*>(smem + sizeof(unsigned long long) * kCopies * GG * (kNB + kPad));
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem);
+  float* smax = reinterpret_cast<float*>(smem + sizeof(uint32_t) * kCopies * GG * (kNB + kPad));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int chunk = hb % P.nchunk;
-  const int grp = (hb / P.nchunk) % P.ngg;
-  const int kr = (hb / (P.nchunk * P.ngg)) % P.Hret;
-  const int b = hb / (P.nchunk * P.ngg * P.Hret);
-  const int G = P.G;
-  const int g0 = grp * GG;
-  const int nrows = min(GG, G - g0);
-  const int H = P.Hret * G;
-  const size_t rowb = (size_t)b * H + (size_t)kr * G + g0;
-  const int L = clamp_len(P.seq_lens, b, P.Lmax);
+  const int chunk = U.chunk;
+  const int nrows = U.nrows;
+  const size_t rowb = U.rowb;
+  const int L = U.L;
   const int base = chunk * TC;
   if (base >= L) {
     if (tid < nrows) P.partA[(rowb + tid) * P.nchunk + chunk] = kEmptyCell;
@@ -319,48 +401,29 @@ __device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
   const int hh = lane & 7;         // head of this lane (B column and D column)
   const int th = (lane >> 3) & 1;  // token half of the B column
   const int kq = lane >> 4;        // k-group of the A / B operands
-  // ---- k_idx rows: 8 groups of 32 tokens, 16 bytes per lane and group, all in flight
-  const f16* kb = P.k_idx + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kR;
   const int wbase = base + wv * 256;
-  h8 ka[8];
-#pragma unroll
-  for (int gi = 0; gi < 8; gi++) {
-    int n = wbase + gi * 32 + (lane & 15) + 16 * (kq >> 1);
-    n = n < L ? n : base;  // past the end: re-read a valid row, masked below
-    ka[gi] = *reinterpret_cast<const h8*>(kb + (size_t)n * kR + 8 * (kq & 1));
-  }
-  // ---- q operands of head hh (zero for heads past nrows)
+  // ---- q operands of head hh (zero for heads past nrows); lanes l and l^16 hold the
+  // two halves of the head's q_idx
   h8 qhi = h8{0, 0, 0, 0, 0, 0, 0, 0}, qlo = qhi;
-  float ysc = 0.0f;
-  if (hh < nrows) {
-    const float4* qp = reinterpret_cast<const float4*>(
-        P.q_idx + ((size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G + g0 + hh) * kR);
-    float q[kR];
+  const float q[8] = {in.q[0].x, in.q[0].y, in.q[0].z, in.q[0].w,
+                      in.q[1].x, in.q[1].y, in.q[1].z, in.q[1].w};
+  float qm = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const float4 v = qp[i];
-      q[4 * i] = v.x;
-      q[4 * i + 1] = v.y;
-      q[4 * i + 2] = v.z;
-      q[4 * i + 3] = v.w;
-    }
-    float qm = 0.0f;
+  for (int i = 0; i < 8; i++) qm = fmaxf(qm, fabsf(q[i]));
+  qm = fmaxf(qm, __shfl_xor(qm, 16, 64));
+  int e = 0;
+  (void)frexpf(qm, &e);  // qm < 2^e
+  const float ysc = hh < nrows ? ldexpf(P.yscale, e - 14) : 0.0f;
+  if (hh < nrows && (kq >> 1) == th) {
 #pragma unroll
-    for (int i = 0; i < kR; i++) qm = fmaxf(qm, fabsf(q[i]));
-    int e = 0;
-    (void)frexpf(qm, &e);  // qm < 2^e
-    ysc = ldexpf(P.yscale, e - 14);
-    if ((kq >> 1) == th) {
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const float v = ldexpf(q[8 * (kq & 1) + i], 14 - e);
-        const f16 hi = (f16)v;
-        qhi[i] = hi;
-        qlo[i] = (f16)(v - (float)hi);
-      }
+    for (int i = 0; i < 8; i++) {
+      const float v = ldexpf(q[i], 14 - e);
+      const f16 hi = (f16)v;
+      qhi[i] = hi;
+      qlo[i] = (f16)(v - (float)hi);
     }
   }
-  for (int i = tid; i < kCopies * GG * (kNB + kPad); i += NT) hist[i] = 0ull;
+  for (int i = tid; i < kCopies * GG * (kNB + kPad); i += NT) hist[i] = 0u;
 
   // ---- pass 1: y = fl32(a * scale) / w (exact: w is a power of two) and the top cell
   float y[8][4];
@@ -368,8 +431,8 @@ __device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
 #pragma unroll
   for (int gi = 0; gi < 8; gi++) {
     f4 d = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    d = mfma32(ka[gi], qhi, d);
-    d = mfma32(ka[gi], qlo, d);
+    d = mfma32(in.ka[gi], qhi, d);
+    d = mfma32(in.ka[gi], qlo, d);
 #pragma unroll
     for (int t = 0; t < 4; t++) {
       float v = d[t] * ysc;
@@ -378,9 +441,10 @@ __device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
       ym = fmaxf(ym, v);
     }
   }
-  // lanes of one head differ in bits 3..5
-  ym = fmaxf(ym, __shfl_xor(ym, 8, 64));
-  ym = fmaxf(ym, __shfl_xor(ym, 16, 64));
+  // lanes of one head differ in bits 3..5: rotate by 8 inside the row, swap the rows of
+  // each half, then the halves
+  ym = fmaxf(ym, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ym), 0x128, 0xf, 0xf, false)));
+  ym = fmaxf(ym, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(ym), 0x401F)));
   ym = fmaxf(ym, __shfl_xor(ym, 32, 64));
   if (lane < GG) smax[lane * NWV + wv] = ym;
   __syncthreads();
@@ -389,9 +453,17 @@ __device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
   for (int k = 1; k < NWV; k++) m = fmaxf(m, smax[hh * NWV + k]);
   const float Acf = floorf(m);
 
-  // ---- pass 2: exact per-bin sums of x * 2^24, x = exp(z - (g+1) w), and the bin codes
+  // ---- pass 2: per-bin sums of x * 2^22 (truncated to integers: at most 2^-22 / e^-w,
+  // below 3e-7, relative to the token's mass; 512 tokens per copy cannot overflow 32
+  // bits), x = exp(z - (g+1) w), and the bin codes.
+  // With m = max(g, A_c - 255) (the cell, or the deepest bin's cell for the tail):
+  //   bin j = A_c - m,  x = 2^((y - m - 1) c),  c = w log2(e).
+  // y - m is exact (it is fract(y) unless the token is in the tail) and a token past the
+  // end (y = -inf) lands in bin 255 with zero mass.
   const float c = P.c_log2;
-  unsigned long long* hrow = hist + (th * GG + hh) * (kNB + kPad);
+  const float Kt = Acf - 255.0f;
+  const float c22 = 22.0f - c;  // x * 2^22 = 2^((y - m - 1) c + 22)
+  uint32_t* hrow = hist + (((lane >> 3) & 3) * GG + hh) * (kNB + kPad);
   uint32_t* cdst = P.codes + ((rowb + hh) * P.nchunk + chunk) * (size_t)(TC / 4) + wv * 64 + 4 * th + kq;
   if (hh < nrows) {
 #pragma unroll
@@ -400,48 +472,44 @@ __device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
 #pragma unroll
       for (int t = 0; t < 4; t++) {
         const float yv = y[gi][t];
-        const bool valid = full || (wbase + gi * 32 + 16 * th + 4 * kq + t < L);
-        const float gf = floorf(yv);
-        const float diff = Acf - gf;          // exact: integral and below 2^24
-        const float jf = fminf(diff, 255.0f);
-        float arg = __builtin_fmaf(__builtin_amdgcn_fractf(yv), c, -c);
-        if (diff > 255.0f) arg = __builtin_fmaf(-(diff - 255.0f), c, arg);  // deep tail
-        const float ex = __builtin_amdgcn_exp2f(arg) * 16777216.0f;
-        const uint32_t j = valid ? (uint32_t)jf : 255u;
-        const uint32_t xi = valid ? (uint32_t)ex : 0u;
-        atomicAdd(&hrow[j], (unsigned long long)xi);
+        const float mc = fmaxf(floorf(yv), Kt);
+        const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(yv - mc, c, c22));
+        const uint32_t j = (uint32_t)(Acf - mc);
+        atomicAdd(&hrow[j], (uint32_t)ex);
         cw |= j << (8 * t);
       }
-      cdst[gi * 8] = cw;
+      __builtin_nontemporal_store(cw, &cdst[gi * 8]);
     }
   }
   __syncthreads();
-  // suffix sums of the bin masses, one head per wavefront pass: lane k owns bins 4k..4k+3
+  // suffix sums of the bin masses, one head per wavefront pass: lane k owns bins
+  // jb..jb+3, jb = 4*(63-k), so a prefix scan over the lanes gives suffix sums (fp32:
+  // every sum is a tree of at most ten roundings)
+  const int jb = 4 * (63 - lane);
+  float fj[4];
+#pragma unroll
+  for (int u = 0; u < 4; u++) fj[u] = __builtin_amdgcn_exp2f(-(float)(jb + u) * c) * 2.384185791015625e-07f;
   for (int gg = wv; gg < nrows; gg += NWV) {
-    double mloc[4];
+    float mloc[4];
 #pragma unroll
     for (int u = 0; u < 4; u++) {
-      const int j = 4 * lane + u;
       unsigned long long sum = 0ull;
 #pragma unroll
-      for (int cp = 0; cp < kCopies; cp++) sum += hist[(cp * GG + gg) * (kNB + kPad) + j];
-      mloc[u] = (double)sum * 5.9604644775390625e-08 * exp(-(double)j * P.w);
+      for (int cp = 0; cp < kCopies; cp++) sum += hist[(cp * GG + gg) * (kNB + kPad) + jb + u];
+      const float sf = __builtin_fmaf((float)(uint32_t)(sum >> 32), 4294967296.0f, (float)(uint32_t)sum);
+      mloc[u] = sf * fj[u];
     }
-    const double part = mloc[0] + mloc[1] + mloc[2] + mloc[3];
-    double sc = part;  // inclusive suffix scan over lanes
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const double oth = __shfl_down(sc, o, 64);
-      if (lane + o < 64) sc += oth;
-    }
-    double acc = sc - part;
-    float* dst = P.suf + ((rowb + gg) * P.nchunk + chunk) * kNB;
-    float4 outv;
-    acc += mloc[3]; outv.w = (float)acc;
-    acc += mloc[2]; outv.z = (float)acc;
-    acc += mloc[1]; outv.y = (float)acc;
-    acc += mloc[0]; outv.x = (float)acc;
-    reinterpret_cast<float4*>(dst)[lane] = outv;
+    const float part = (mloc[0] + mloc[1]) + (mloc[2] + mloc[3]);
+    // exclusive scan: the inclusive one moved up by a lane
+    const float incl = wave_incl_sum(part);
+    float acc = dpp_f<0x138>(incl);  // wave_shr:1
+    f4 outv;
+    acc += mloc[3]; outv[3] = acc;
+    acc += mloc[2]; outv[2] = acc;
+    acc += mloc[1]; outv[1] = acc;
+    acc += mloc[0]; outv[0] = acc;
+    f4* dst = reinterpret_cast<f4*>(P.suf + ((rowb + gg) * P.nchunk + chunk) * kNB);
+    __builtin_nontemporal_store(outv, &dst[63 - lane]);
     if (lane == 0) {
       float mm = smax[gg * NWV];
       for (int k = 1; k < NWV; k++) mm = fmaxf(mm, smax[gg * NWV + k]);
@@ -450,10 +518,28 @@ __device__ void hist_block(const StageAParams& P, int hb, unsigned char* smem) {
   }
 }
 
-template <int NT>
-__global__ __launch_bounds__(NT, 2) void k_stage_a(StageAParams P) {
+// UPB histogram units per block; with two, the second unit's loads are in flight while
+// the first is processed.
+template <int NT, int UPB>
+__global__ __launch_bounds__(NT, 3 - UPB) void k_stage_a(StageAParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
-  hist_block<NT>(P, blockIdx.x, smem);
+  const int u0 = blockIdx.x * UPB;
+  if (UPB == 2 && u0 + 1 < P.nunits) {
+    const HistUnit U0 = hist_unit<NT>(P, u0);
+    const HistUnit U1 = hist_unit<NT>(P, u0 + 1);
+    HistIn in0, in1;
+    hist_fetch<NT>(P, U0, in0);
+    hist_fetch<NT>(P, U1, in1);
+    __builtin_amdgcn_sched_barrier(0);  // keep every load of both units ahead of the compute
+    hist_block<NT>(P, U0, in0, smem);
+    __syncthreads();
+    hist_block<NT>(P, U1, in1, smem);
+  } else {
+    const HistUnit U0 = hist_unit<NT>(P, u0);
+    HistIn in0;
+    hist_fetch<NT>(P, U0, in0);
+    hist_block<NT>(P, U0, in0, smem);
+  }
 }
 
 // Masked attention over the entries e = 0..n-1 of a row list: row_of(e) is the cache
@@ -491,7 +577,7 @@ __device__ void window_block(const WinParams& P, int wb, float* lds) {
   const int b = wb / (P.nws * P.Hloc);
   const int G = P.G;
   const int ring = P.sinks + P.window;
-  int L = P.seq_lens[b];
+  int L = seq_len(P.seq_lens, b);
   L = L < 0 ? 0 : L;
   const int ns = min(P.sinks, L);
   const int wstart = max(P.sinks, L - P.window);
@@ -514,7 +600,8 @@ __device__ void window_block(const WinParams& P, int wb, float* lds) {
       },
       [&](int) { return 0xFFFFu; }, qop, P.scale2, st);
   const size_t prow = ((size_t)(b * P.Hloc + kl) * P.nws + wsplit) * G;
-  block_combine<kBWaves>(st, G, lds, P.wpm + prow, P.wpl + prow, P.wpacc + prow * kD);
+  block_combine<kBWaves>(st, G, min(kBWaves, (n + kStep - 1) / kStep), lds, P.wpm + prow,
+                         P.wpl + prow, P.wpacc + prow * kD);
 }
 
 // ---------------------------------------------------------------------------
@@ -621,9 +708,9 @@ struct StageBParams {
   WinParams win;
 };
 
-// Selection block over the TB = 2048*NWD tokens [blk*TB, (blk+1)*TB) of retrieval KV
+// Selection block over the TB = 1024*NWD tokens [blk*TB, (blk+1)*TB) of retrieval KV
 // head kr.  Code word w of a chunk holds the bins of tokens 4w + q, q = 0..3 (byte q);
-// thread tid takes the block's words tid + i*512, i < NWD.
+// thread tid takes the block's words NWD*tid .. NWD*tid + NWD-1.
 //
 // A token is selected for head g iff its chunk-relative code j_c <= tau_g = b* - (A - A_c)
 // (all tokens when b* = 255).  Four codes are tested at once: with the bytes of a word
@@ -633,7 +720,7 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
   constexpr int NT = kBThreads;
   constexpr int TB = NT * 4 * NWD;
   constexpr int HPW = (GMAX + kBWaves - 1) / kBWaves;  // heads per wavefront (b* search)
-  __shared__ int s_tau[kMaxCPB][kAttnG];
+  __shared__ uint32_t s_T[kMaxCPB][kAttnG];  // SWAR constant of (chunk, head), 0: none
   __shared__ int s_bs[kAttnG];
   __shared__ int s_wsum[kBWaves];
   __shared__ int s_cnt[kAttnG];
@@ -660,21 +747,6 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
   // ---- phase 0: every input of the selection is in flight at once
   h8 qop[4];
   load_qop(P.q + ((size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G) * kD, G, qop);
-  // the block's chunks are consecutive, so its code words of head g are the words
-  // [chunk0*WPC, (chunk0+cpb)*WPC) of the head's row (clamped at the row's end)
-  uint32_t cw[NWD][GMAX];
-  {
-    const int rowwords = P.nchunk * WPC;
-    int off[NWD];
-#pragma unroll
-    for (int i = 0; i < NWD; i++) off[i] = min(chunk0 * WPC + tid + i * NT, rowwords - 1);
-#pragma unroll
-    for (int g = 0; g < GMAX; g++) {
-      const uint32_t* crow = P.codes + (row0 + (g < G ? g : 0)) * (size_t)rowwords;
-#pragma unroll
-      for (int i = 0; i < NWD; i++) cw[i][g] = crow[off[i]];
-    }
-  }
   int Ac = kEmptyCell, Ag = kEmptyCell;
   if (tid < cpb * kAttnG) {
     const int cc = tid / kAttnG, g = tid % kAttnG;
@@ -702,6 +774,25 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
       }
     }
   }
+  // the block's chunks are consecutive, so its code words of head g are the words
+  // [chunk0*WPC, (chunk0+cpb)*WPC) of the head's row; thread tid takes the NWD words
+  // from NWD*tid on in one load (clamped at the row's end: those tokens are masked)
+  uint32_t cw[NWD][GMAX];
+  {
+    const int rowwords = P.nchunk * WPC;
+    const int off = min(chunk0 * WPC + NWD * tid, rowwords - NWD);
+#pragma unroll
+    for (int g = 0; g < GMAX; g++) {
+      const uint32_t* crow = P.codes + (row0 + (g < G ? g : 0)) * (size_t)rowwords + off;
+      if constexpr (NWD == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(crow);
+        cw[0][g] = v.x; cw[1][g] = v.y; cw[2][g] = v.z; cw[3][g] = v.w;
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(crow);
+        cw[0][g] = v.x; cw[1][g] = v.y;
+      }
+    }
+  }
   if (tid < kAttnG) s_cnt[tid] = 0;
   // b*: least J < 255 with Z - SUF_{J+1} >= p Z, else 255
 #pragma unroll
@@ -716,8 +807,7 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
           const int Jk = 4 * lane + k;
           if (Jk < kNB - 1 && zv[u] - sv[u][k] >= pz) J = Jk;
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) J = min(J, __shfl_xor(J, o, 64));
+        J = wave_min_i(J);
       }
       if (lane == 0) {
         s_bs[g] = J;
@@ -738,26 +828,27 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
         tau = t < 0 ? -1 : (int)t;
       }
     }
-    s_tau[cc][g] = tau;
+    s_T[cc][g] = tau < 0 ? 0u : 0x01000100u + (uint32_t)tau * 0x00010001u;
   }
   __syncthreads();
 
   // ---- phase 1: per-token head masks, union compacted into the LDS list
+  // the thread's words lie in chunk cc (the same for the whole wavefront: its NWD*64
+  // words are aligned inside one chunk)
+  const int cc = (NWD * tid) / WPC;
+  uint32_t Tv[GMAX];
+#pragma unroll
+  for (int g = 0; g < GMAX; g++) Tv[g] = __builtin_amdgcn_readfirstlane(s_T[cc][g]);
   uint32_t hm[NWD][4];
-  int mine = 0;
   const bool tail = tok0 + TB > L;
 #pragma unroll
   for (int i = 0; i < NWD; i++) {
-    const int wi = tid + i * NT;
-    const int cc = wi / WPC;  // the same for the whole wavefront
-    const int w = wi - cc * WPC;
+    const int w = NWD * tid + i - cc * WPC;
     uint32_t me = 0u, mo = 0u;
 #pragma unroll
     for (int g = 0; g < GMAX; g++) {
-      // s_tau is -1 for heads past G
-      const int tg = __builtin_amdgcn_readfirstlane(s_tau[cc][g]);
-      if (tg < 0) continue;
-      const uint32_t T = 0x01000100u + (uint32_t)tg * 0x00010001u;
+      const uint32_t T = Tv[g];
+      if (T == 0u) continue;
       const uint32_t x = cw[i][g];
       const uint32_t de = T - (x & 0x00FF00FFu);
       const uint32_t dd = T - ((x >> 8) & 0x00FF00FFu);
@@ -779,8 +870,6 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
       for (int q = 0; q < 4; q++)
         if (tok0 + cc * tc + 4 * w + q >= L) hm[i][q] = 0u;
     }
-#pragma unroll
-    for (int q = 0; q < 4; q++) mine += hm[i][q] != 0u;
   }
   if (P.want_count) {
 #pragma unroll
@@ -795,29 +884,31 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
       if (lane == 0 && c) atomicAdd(&s_cnt[g], c);
     }
   }
-  int incl = mine;
+  // compaction: slot (i, q) of the wavefront's lanes goes in lane order after the
+  // earlier slots; wavefronts follow each other
+  int wtot = 0;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += v;
-  }
-  if (lane == 63) s_wsum[wv] = incl;
+  for (int i = 0; i < NWD; i++)
+#pragma unroll
+    for (int q = 0; q < 4; q++) wtot += __popcll(__ballot(hm[i][q] != 0u));
+  if (lane == 0) s_wsum[wv] = wtot;
   __syncthreads();
-  int woff = 0, U = 0;
+  int pos = 0, U = 0;
 #pragma unroll
   for (int k = 0; k < kBWaves; k++) {
-    if (k < wv) woff += s_wsum[k];
+    if (k < wv) pos += s_wsum[k];
     U += s_wsum[k];
   }
-  int pos = woff + incl - mine;
 #pragma unroll
   for (int i = 0; i < NWD; i++) {
-    const int wi = tid + i * NT;
-    const int cc = wi / WPC;
-    const int w = wi - cc * WPC;
+    const int w = NWD * tid + i - cc * WPC;
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      if (hm[i][q]) lst[pos++] = (uint32_t)(cc * tc + 4 * w + q) | (hm[i][q] << 16);
+      const unsigned long long bal = __ballot(hm[i][q] != 0u);
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      if (hm[i][q]) lst[pos + below] = (uint32_t)(cc * tc + 4 * w + q) | (hm[i][q] << 16);
+      pos += __popcll(bal);
     }
   }
   __syncthreads();
@@ -832,12 +923,13 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
 
   // ---- phase 3: block partial
   const size_t s1p = ((size_t)(b * P.Hret + kr) * P.nblk + blk) * G;
-  block_combine<kBWaves>(st, G, lds, P.p1m + s1p, P.p1l + s1p, P.p1acc + s1p * kD);
+  block_combine<kBWaves>(st, G, min(kBWaves, (U + kStep - 1) / kStep), lds, P.p1m + s1p,
+                         P.p1l + s1p, P.p1acc + s1p * kD);
   if (tid < G) P.p1cnt[s1p + tid] = s_cnt[tid];
 }
 
 template <int NWD, int GMAX>
-__global__ __launch_bounds__(kBThreads) void k_stage_b(StageBParams P) {
+__global__ __launch_bounds__(kBThreads, 2) void k_stage_b(StageBParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   if ((int)blockIdx.x < P.nret_blocks)
     select_attend_block<NWD, GMAX>(P, smem);
@@ -870,7 +962,7 @@ struct StageMParams {
 };
 
 // thread (sub = t/8, dq = t%8): float4 dq of the slice for partials sub, sub+32, ...
-__device__ void merge_slice(const float* __restrict__ pm, const float* __restrict__ pl,
+__device__ __forceinline__ void merge_slice(const float* __restrict__ pm, const float* __restrict__ pl,
                             const float* __restrict__ pacc, const int32_t* __restrict__ pcnt,
                             int n, int G, int g, int slice, float* __restrict__ out,
                             float* __restrict__ lse, int32_t* __restrict__ count_out, size_t orow,
@@ -961,29 +1053,42 @@ __global__ __launch_bounds__(kThreads) void k_stage_m(StageMParams P) {
   const int G = P.G;
   const int slice = blockIdx.x % kMSlices;
   const int hb = blockIdx.x / kMSlices;
-  if (hb >= P.nret) {
+  const bool win = hb >= P.nret;
+  const float *pm, *pl, *pacc;
+  const int32_t* pcnt = nullptr;
+  int n, g;
+  size_t orow;
+  if (win) {
     const int wm = hb - P.nret;
-    const int g = wm % G;
+    g = wm % G;
     const int kl = (wm / G) % P.Hloc;
     const int b = wm / (G * P.Hloc);
     const size_t p0 = (size_t)(b * P.Hloc + kl) * P.nws * G;
-    merge_slice(P.wpm + p0, P.wpl + p0, P.wpacc + p0 * kD, nullptr, P.nws, G, g, slice, P.out,
-                P.lse, nullptr, (size_t)b * P.Hq + (size_t)P.loc.kv[kl] * G + g, mlds);
-    return;
+    pm = P.wpm + p0;
+    pl = P.wpl + p0;
+    pacc = P.wpacc + p0 * kD;
+    n = P.nws;
+    orow = (size_t)b * P.Hq + (size_t)P.loc.kv[kl] * G + g;
+  } else {
+    g = hb % G;
+    const int kr = (hb / G) % P.Hret;
+    const int b = hb / (G * P.Hret);
+    const size_t p0 = (size_t)(b * P.Hret + kr) * P.nblk * G;
+    pm = P.p1m + p0;
+    pl = P.p1l + p0;
+    pacc = P.p1acc + p0 * kD;
+    if (P.count_out) pcnt = P.p1cnt + p0;
+    n = P.nblk;
+    orow = (size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G + g;
+    if (slice == 0 && P.thresh_out && threadIdx.x == 0) {
+      const size_t row = (size_t)b * P.Hret * G + (size_t)kr * G + g;
+      const int A = P.Aglob[row];
+      P.thresh_out[orow * 2 + 0] = A == kEmptyCell ? 0 : A;
+      P.thresh_out[orow * 2 + 1] = A == kEmptyCell ? 0 : P.bstar[row];
+    }
   }
-  const int g = hb % G;
-  const int kr = (hb / G) % P.Hret;
-  const int b = hb / (G * P.Hret);
-  const size_t p0 = (size_t)(b * P.Hret + kr) * P.nblk * G;
-  const size_t orow = (size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G + g;
-  merge_slice(P.p1m + p0, P.p1l + p0, P.p1acc + p0 * kD, P.count_out ? P.p1cnt + p0 : nullptr,
-              P.nblk, G, g, slice, P.out, P.lse, P.count_out, orow, mlds);
-  if (slice == 0 && P.thresh_out && threadIdx.x == 0) {
-    const size_t row = (size_t)b * P.Hret * G + (size_t)kr * G + g;
-    const int A = P.Aglob[row];
-    P.thresh_out[orow * 2 + 0] = A == kEmptyCell ? 0 : A;
-    P.thresh_out[orow * 2 + 1] = A == kEmptyCell ? 0 : P.bstar[row];
-  }
+  merge_slice(pm, pl, pacc, pcnt, n, G, g, slice, P.out, P.lse, win ? nullptr : P.count_out, orow,
+              mlds);
 }
 
 }  // namespace
@@ -999,10 +1104,10 @@ int chunk_tokens(int B, int Hret, int Lmax) {
   return units * ((Lmax + 2047) / 2048) >= 256 ? 2048 : 1024;
 }
 int window_rows(int B, int Hloc, int ring) {
-  // rows per window block: 256 (one step per wavefront) unless that makes more than 256
-  // window blocks; then up to 2048
+  // rows per window block: one step per wavefront unless that makes more than 256
+  // window blocks; then up to 16 steps per wavefront
   int wr = kBWaves * kStep;
-  while (wr < 2048 && (int64_t)B * Hloc * ((ring + wr - 1) / wr) > 256) wr *= 2;
+  while (wr < 16 * kBWaves * kStep && (int64_t)B * Hloc * ((ring + wr - 1) / wr) > 256) wr *= 2;
   return wr;
 }
 }  // namespace
@@ -1019,7 +1124,7 @@ bool step_fused_supported(int kv_dtype, int G, int Hloc, int window, int sinks, 
     const int tc = chunk_tokens(B, Hret, Lmax);
     const int64_t nchunk = ((int64_t)Lmax + tc - 1) / tc;
     if (nchunk > 16384) return false;                 // stage-T LDS
-    if ((Lmax + 8191) / 8192 > kMaxParts) return false;  // stage-M LDS
+    if ((Lmax + 4095) / 4096 > kMaxParts) return false;  // stage-M LDS
   }
   return true;
 }
@@ -1033,6 +1138,13 @@ StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int
   sp.Hloc = Hloc;
   sp.tc = chunk_tokens(B, Hret, Lmax);
   sp.nt = sp.tc / 4;
+  {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    sp.ncu = n;
+  }
   int nwin_blocks = 0;
   if (Hloc > 0) {
     sp.wrows = window_rows(B, Hloc, window + sinks);
@@ -1041,19 +1153,14 @@ StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int
   }
   if (Hret > 0) {
     sp.nchunk = (Lmax + sp.tc - 1) / sp.tc;
-    // tokens per selection block: the smallest of 2048 / 4096 / 8192 (and at least one
-    // chunk) whose selection grid, with the window blocks, is one block per CU
+    // tokens per selection block: 2048 if that grid, with the window blocks, fits two
+    // blocks per CU, else 4096
     sp.nwd = 4;
-    for (int nwd = 1; nwd <= 4; nwd *= 2) {
-      const int tb = 2048 * nwd;
-      if (tb < sp.tc) continue;
-      const int64_t nb = (int64_t)B * Hret * ((Lmax + tb - 1) / tb);
-      if (nb + nwin_blocks <= 256) {
-        sp.nwd = nwd;
-        break;
-      }
+    {
+      const int64_t nb = (int64_t)B * Hret * ((Lmax + 2047) / 2048);
+      if (sp.tc <= 2048 && nb + nwin_blocks <= 512) sp.nwd = 2;
     }
-    sp.tb = 2048 * sp.nwd;
+    sp.tb = 1024 * sp.nwd;
     sp.nblk = (Lmax + sp.tb - 1) / sp.tb;
     const int H = Hret * G;
     sp.suf = wp.take<float>((size_t)B * H * sp.nchunk * kNB);
@@ -1117,13 +1224,23 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     P.suf = at<float>(ws, sp.suf);
     P.partA = at<int32_t>(ws, sp.partA);
     P.codes = at<uint32_t>(ws, sp.codes);
-    const int nA = B * sp.Hret * P.ngg * sp.nchunk;
-    const size_t ldsA = sizeof(unsigned long long) * kCopies * GG * (kNB + kPad) + 1024;
-#define RTP_STAGE_A(NTV) k_stage_a<NTV><<<nA, NTV, ldsA, st>>>(P)
-    if (sp.nt == 256)
-      RTP_STAGE_A(256);
-    else
-      RTP_STAGE_A(512);
+    P.nunits = B * sp.Hret * P.ngg * sp.nchunk;
+    const size_t ldsA = sizeof(uint32_t) * kCopies * GG * (kNB + kPad) + 1024;
+    // two units per block when that still gives every CU a block
+    const bool two = P.nunits >= 2 * sp.ncu;
+    const int nA = two ? (P.nunits + 1) / 2 : P.nunits;
+#define RTP_STAGE_A(NTV, UPBV) k_stage_a<NTV, UPBV><<<nA, NTV, ldsA, st>>>(P)
+    if (sp.nt == 256) {
+      if (two)
+        RTP_STAGE_A(256, 2);
+      else
+        RTP_STAGE_A(256, 1);
+    } else {
+      if (two)
+        RTP_STAGE_A(512, 2);
+      else
+        RTP_STAGE_A(512, 1);
+    }
 #undef RTP_STAGE_A
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1195,22 +1312,20 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     W.wpacc = at<float>(ws, sp.wpacc);
     nwin_blocks = B * sp.Hloc * sp.nws;
   }
-  const size_t ldsB = std::max<size_t>(4 * (32 + 2048) * sizeof(float),
+  const size_t ldsB = std::max<size_t>(kBWaves * (32 + 2048) * sizeof(float),
                                        sizeof(uint32_t) * (size_t)(sp.Hret > 0 ? sp.tb : 0));
   const int nB = Q.nret_blocks + nwin_blocks;
 #define RTP_STAGE_B(NWDV, GMV) k_stage_b<NWDV, GMV><<<nB, kBThreads, ldsB, st>>>(Q)
   if (G <= 8) {
-    switch (sp.nwd) {
-      case 1: RTP_STAGE_B(1, 8); break;
-      case 2: RTP_STAGE_B(2, 8); break;
-      default: RTP_STAGE_B(4, 8); break;
-    }
+    if (sp.nwd == 2)
+      RTP_STAGE_B(2, 8);
+    else
+      RTP_STAGE_B(4, 8);
   } else {
-    switch (sp.nwd) {
-      case 1: RTP_STAGE_B(1, 16); break;
-      case 2: RTP_STAGE_B(2, 16); break;
-      default: RTP_STAGE_B(4, 16); break;
-    }
+    if (sp.nwd == 2)
+      RTP_STAGE_B(2, 16);
+    else
+      RTP_STAGE_B(4, 16);
   }
 #undef RTP_STAGE_B
   e = hipGetLastError();
