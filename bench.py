@@ -89,6 +89,78 @@ def algorithmic_bytes(rtp, wl, layer, torch):
     return total, detail
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_stage_a_c4.json")
+KERNEL_SOURCE = os.path.join(ROOT, "head_wise_sparse_rtp_amd", "csrc", "rtp_step.hip")
+
+
+def source_sha256() -> str:
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of k_stage_a from the committed counter summary, or None when
+    there is none for this workload or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("source_sha256") != source_sha256():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, out):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of k_stage_a and of the calibration copy
+    kernel (a unary elementwise kernel over copy_bytes bytes) from two rocprofv3 --pmc
+    runs; each counter is scaled by copy_bytes / (its reading for the copy)."""
+    import csv
+    import re
+
+    def per_kernel(path, counter):
+        agg = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                n = re.sub(r"\(.*", "", r["Kernel_Name"].replace("(anonymous namespace)::", ""))
+                agg.setdefault(n, []).append(float(r["Counter_Value"]))
+        return agg
+
+    res = {"workload": workload, "source_sha256": source_sha256(), "copy_bytes": copy_bytes}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        agg = per_kernel(path, counter)
+        stage = [v for n, vs in agg.items() if "k_stage_a" in n for v in vs]
+        copy = [v for n, vs in agg.items() if "neg_kernel" in n for v in vs]
+        if not stage or not copy:
+            raise SystemExit("no %s readings for k_stage_a or the copy kernel in %s" % (counter, path))
+        copy_kib = max(copy)  # the large calibration copies (the bench also negates tiny tensors)
+        factor = copy_bytes / (copy_kib * 1024.0)
+        kib = sum(stage) / len(stage)
+        res[counter] = {"kib_per_launch": round(kib, 1), "copy_kib": round(copy_kib, 1),
+                        "scale": round(factor, 4), "bytes_per_launch": round(kib * 1024.0 * factor)}
+    res["bytes_per_launch"] = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res))
+
+
+def calibrate_copy(mib: int, reps: int):
+    """A plain device copy of known size (negation: read N bytes, write N bytes) for
+    scaling the HBM byte counters."""
+    import torch
+    n = mib * 2 ** 20 // 4
+    src = torch.randn(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "reps": reps}), flush=True)
+
+
 def cpu_baseline(wl, bytes_per_step, budget_s):
     import oracle
     cpu_wl = wl.to("cpu")
@@ -118,7 +190,18 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--phases", action="store_true", help="print a per-phase breakdown")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the k_stage_a traffic summary from two rocprofv3 --pmc runs")
+    ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
+                      args.copy_mib * 2 ** 20, TRAFFIC_FILE)
+        return
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, 3)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr, flush=True)
@@ -250,7 +333,8 @@ def main():
         "sel_tokens_per_head": detail["sel_tokens"],
         "roofline": {"kernel": "k_stage_a (indexer score on MFMA + 256-bin chunk histograms)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(args.workload),
                      "avg_us": round(a_us, 3), "algorithmic_bytes_per_launch": a_bytes},
         "phases_us_eager": {k: round(v, 3) for k, v in ph.items()},
     }

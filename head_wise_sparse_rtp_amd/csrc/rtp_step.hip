@@ -36,6 +36,7 @@ namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAttnG = 16;               // head columns of the MFMA tile
 constexpr int kStep = 32;                // cache rows per wavefront step
@@ -327,8 +328,8 @@ struct WinParams {
 // [2^13, 2^14): hi + lo then carry 22 significant bits and the products stay in fp32
 // range; the scale is undone exactly in the final multiply.  The four bin codes of a
 // lane's tokens form one code word (byte t = token 4w + t of word w).
-// Loads of one histogram unit (k_idx rows and the raw q_idx of the lane's head); they
-// are issued without waiting, so a block can prefetch its next unit.
+// Loads of one histogram unit (k_idx rows and the raw q_idx of the lane's head), issued
+// without waiting.
 struct HistIn {
   h8 ka[8];
   float4 q[2];  // q_idx[8*(kq&1) .. +7] of the lane's head
@@ -464,7 +465,9 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
   const float Kt = Acf - 255.0f;
   const float c22 = 22.0f - c;  // x * 2^22 = 2^((y - m - 1) c + 22)
   uint32_t* hrow = hist + (((lane >> 3) & 3) * GG + hh) * (kNB + kPad);
-  uint32_t* cdst = P.codes + ((rowb + hh) * P.nchunk + chunk) * (size_t)(TC / 4) + wv * 64 + 4 * th + kq;
+  // code words pass through LDS ([wave][head][64 words]) so that the global stores
+  // cover whole 256-byte runs per head
+  uint32_t* cl = reinterpret_cast<uint32_t*>(smax + GG * NWV) + (wv * GG + hh) * 64 + 4 * th + kq;
   if (hh < nrows) {
 #pragma unroll
     for (int gi = 0; gi < 8; gi++) {
@@ -478,7 +481,19 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
         atomicAdd(&hrow[j], (uint32_t)ex);
         cw |= j << (8 * t);
       }
-      __builtin_nontemporal_store(cw, &cdst[gi * 8]);
+      cl[gi * 8] = cw;
+    }
+  }
+  {
+    // lane l: head l/8, 16-byte pieces l%8 and l%8 + 8 of the head's 256 bytes
+    const int h2 = lane >> 3;
+    if (h2 < nrows) {
+      const u4* src = reinterpret_cast<const u4*>(reinterpret_cast<uint32_t*>(smax + GG * NWV) +
+                                                  (wv * GG + h2) * 64);
+      u4* dst = reinterpret_cast<u4*>(P.codes + ((rowb + h2) * P.nchunk + chunk) * (size_t)(TC / 4) +
+                                      wv * 64);
+      __builtin_nontemporal_store(src[lane & 7], &dst[lane & 7]);
+      __builtin_nontemporal_store(src[(lane & 7) + 8], &dst[(lane & 7) + 8]);
     }
   }
   __syncthreads();
@@ -518,28 +533,15 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
   }
 }
 
-// UPB histogram units per block; with two, the second unit's loads are in flight while
-// the first is processed.
-template <int NT, int UPB>
-__global__ __launch_bounds__(NT, 3 - UPB) void k_stage_a(StageAParams P) {
+// One histogram unit per block: two blocks per CU hide the latency of the histogram
+// pass better than a block that prefetches a second unit.
+template <int NT>
+__global__ __launch_bounds__(NT, 2) void k_stage_a(StageAParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int u0 = blockIdx.x * UPB;
-  if (UPB == 2 && u0 + 1 < P.nunits) {
-    const HistUnit U0 = hist_unit<NT>(P, u0);
-    const HistUnit U1 = hist_unit<NT>(P, u0 + 1);
-    HistIn in0, in1;
-    hist_fetch<NT>(P, U0, in0);
-    hist_fetch<NT>(P, U1, in1);
-    __builtin_amdgcn_sched_barrier(0);  // keep every load of both units ahead of the compute
-    hist_block<NT>(P, U0, in0, smem);
-    __syncthreads();
-    hist_block<NT>(P, U1, in1, smem);
-  } else {
-    const HistUnit U0 = hist_unit<NT>(P, u0);
-    HistIn in0;
-    hist_fetch<NT>(P, U0, in0);
-    hist_block<NT>(P, U0, in0, smem);
-  }
+  const HistUnit U = hist_unit<NT>(P, blockIdx.x);
+  HistIn in;
+  hist_fetch<NT>(P, U, in);
+  hist_block<NT>(P, U, in, smem);
 }
 
 // Masked attention over the entries e = 0..n-1 of a row list: row_of(e) is the cache
@@ -1158,7 +1160,7 @@ StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int
     sp.nwd = 4;
     {
       const int64_t nb = (int64_t)B * Hret * ((Lmax + 2047) / 2048);
-      if (sp.tc <= 2048 && nb + nwin_blocks <= 512) sp.nwd = 2;
+      if (sp.tc <= 2048 && nb + nwin_blocks <= 2 * sp.ncu) sp.nwd = 2;
     }
     sp.tb = 1024 * sp.nwd;
     sp.nblk = (Lmax + sp.tb - 1) / sp.tb;
@@ -1225,22 +1227,15 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     P.partA = at<int32_t>(ws, sp.partA);
     P.codes = at<uint32_t>(ws, sp.codes);
     P.nunits = B * sp.Hret * P.ngg * sp.nchunk;
-    const size_t ldsA = sizeof(uint32_t) * kCopies * GG * (kNB + kPad) + 1024;
-    // two units per block when that still gives every CU a block
-    const bool two = P.nunits >= 2 * sp.ncu;
-    const int nA = two ? (P.nunits + 1) / 2 : P.nunits;
-#define RTP_STAGE_A(NTV, UPBV) k_stage_a<NTV, UPBV><<<nA, NTV, ldsA, st>>>(P)
-    if (sp.nt == 256) {
-      if (two)
-        RTP_STAGE_A(256, 2);
-      else
-        RTP_STAGE_A(256, 1);
-    } else {
-      if (two)
-        RTP_STAGE_A(512, 2);
-      else
-        RTP_STAGE_A(512, 1);
-    }
+    // histogram copies, the top cells of the wavefronts, the code words of the wavefronts
+    const size_t ldsA = sizeof(uint32_t) * kCopies * GG * (kNB + kPad) + sizeof(float) * GG * 8 +
+                        sizeof(uint32_t) * 8 * GG * 64;
+    const int nA = P.nunits;
+#define RTP_STAGE_A(NTV) k_stage_a<NTV><<<nA, NTV, ldsA, st>>>(P)
+    if (sp.nt == 256)
+      RTP_STAGE_A(256);
+    else
+      RTP_STAGE_A(512);
 #undef RTP_STAGE_A
     e = hipGetLastError();
     if (e != hipSuccess) return e;
