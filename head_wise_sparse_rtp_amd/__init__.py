@@ -127,7 +127,8 @@ def _kv_dtype(t: torch.Tensor) -> int:
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
-    """Zero-filled workspace (the decode step keeps completion counters in it)."""
+    """Workspace of `nbytes` bytes on `device` (zero-filled; the kernels need no
+    particular contents)."""
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 

@@ -668,8 +668,9 @@ __global__ __launch_bounds__(kThreads) void k_stage_t(StageTParams P) {
       }
 #pragma unroll
       for (int u = 0; u < kTBatch; u++) {
-        const float f = sh[u] >= 0 ? __builtin_amdgcn_exp2f(-(float)sh[u] * P.c_log2) : 0.0f;
-        acc += (double)x[u] * (double)f;
+        // chunks without a contribution read a placeholder that is never used
+        const double f = (double)__builtin_amdgcn_exp2f(-(float)max(sh[u], 0) * P.c_log2);
+        acc += sh[u] >= 0 ? (double)x[u] * f : 0.0;
       }
     }
   }

@@ -158,15 +158,17 @@ typedef struct {
   int32_t* thresh_out;            /* [B, Hq, 2] {A, b*} for retrieval query heads, or NULL */
   int32_t* count_out;             /* [B, Hq] |S| for retrieval query heads, or NULL */
   /* Optional profiling: hipEvent_t handles (or NULL) recorded on `stream`: [0] before
-   * the first kernel, [1] after the indexer-score/histogram kernel (which also runs the
-   * window attention of local heads), [2] after the threshold kernel, [3] after the
-   * last kernel.  [4..7] are reserved and must be NULL. */
+   * the first kernel, [1] after the indexer-score/histogram kernel, [2] after the
+   * suffix-table (threshold) kernel, [3] after the last kernel.  [4..7] are reserved
+   * and must be NULL. */
   void* prof_ev[8];
 } rtp_layer_desc;
 
-/* fp16 caches with G <= 16 run four kernels per call (indexer score + histograms with the
- * window attention; threshold sums with the window merge; selection + sparse attention;
- * merge); other shapes run the single-purpose kernels in sequence. */
+/* fp16 caches with G <= 16 run four kernels per call: indexer score + chunk histograms;
+ * per-head suffix tables of the bin masses; selection + sparse attention together with
+ * the window attention of local heads; merge of the split partials.  Other shapes run
+ * the single-purpose kernels in sequence.  The workspace needs no initialisation; calls
+ * that may overlap must not share one. */
 size_t rtp_decode_step_workspace_size(const rtp_layer_desc* desc);
 rtp_status rtp_decode_step(const rtp_layer_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
