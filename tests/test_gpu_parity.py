@@ -255,6 +255,17 @@ def test_decode_step_small_ragged(rtp, dtype, p):
     check_decode(rtp, wl, label="small-%s-p%g" % (dtype, p))
 
 
+@pytest.mark.parametrize("G", [1, 2, 3, 5, 16, 20])
+def test_decode_step_heads_per_kv(rtp, G):
+    """Query heads per KV head: the fused path takes G <= 16 (one or two 8-head groups in
+    the histogram kernel, 8- or 16-column selection tiles); G = 20 runs the single-purpose
+    kernels."""
+    say("decode_step G", G)
+    wl = workloads.make_workload("t", 3, [5000, 1, 2300], 3 * G, 3, [[1, 0, 1]], seed=70 + G,
+                                 p=0.9, dtype="f16", window=384, sinks=4, device=dev())
+    check_decode(rtp, wl, label="G%d" % G)
+
+
 def test_decode_step_p1_is_dense_attention(rtp):
     say("decode_step p=1 dense")
     wl = workloads.make_workload("t", 2, [2500, 700], 8, 2, [[1, 0]], seed=62, p=1.0,

@@ -230,24 +230,27 @@ def _build_index(rng, Ls, Lmax, G, r, classes_per_b, fixed_k, dtype_np, poison):
     """k_idx [B, Lmax, r] and q_idx [B, G, r] for one retrieval KV head."""
     B = len(Ls)
     U = _orthogonal16(rng, r)
+    # at most r heads get planted targets (one direction each); with G > r the remaining
+    # heads reuse the directions cyclically and see whatever logits those give
+    Gp = min(G, r)
     kidx = np.zeros((B, Lmax, r), dtype=dtype_np)
     qidx = np.zeros((B, G, r), dtype=np.float32)
     plans = {}
     for b in range(B):
         L = int(Ls[b])
-        Z = np.zeros((L, G))
-        for g in range(G):
+        Z = np.zeros((L, Gp))
+        for g in range(Gp):
             cls = classes_per_b[b][g]
             k = _class_k(rng, cls, L, fixed_k.get(cls) if fixed_k else None)
             z, pos = _targets(rng, L, cls, k)
             Z[:, g] = z
             plans[(b, g)] = HeadPlan(cls, len(pos), pos)
-        eps = rng.standard_normal((L, r - G))
-        kv = (Z / (INDEX_TAU * INDEX_AMPLITUDE)) @ U[:, :G].T + eps @ U[:, G:].T
+        eps = rng.standard_normal((L, r - Gp))
+        kv = (Z / (INDEX_TAU * INDEX_AMPLITUDE)) @ U[:, :Gp].T + eps @ U[:, Gp:].T
         kidx[b, :L] = kv.astype(dtype_np)
         if poison and L < Lmax:
             kidx[b, L:] = dtype_np(30000.0) if dtype_np == np.float16 else dtype_np(1e30)
-        qidx[b] = (INDEX_AMPLITUDE * U[:, :G].T).astype(np.float32)
+        qidx[b] = (INDEX_AMPLITUDE * U[:, np.arange(G) % r].T).astype(np.float32)
     return kidx, qidx, plans
 
 
