@@ -336,7 +336,7 @@ struct HistIn {
 };
 
 struct HistUnit {
-  int chunk, grp, kr, b, nrows, L;
+  int chunk, grp, kr, b, nrows;
   size_t rowb;
 };
 
@@ -349,7 +349,6 @@ __device__ __forceinline__ HistUnit hist_unit(const StageAParams& P, int hb) {
   u.b = hb / (P.nchunk * P.ngg * P.Hret);
   u.nrows = min(8, P.G - u.grp * 8);
   u.rowb = (size_t)u.b * P.Hret * P.G + (size_t)u.kr * P.G + u.grp * 8;
-  u.L = clamp_len(P.seq_lens, u.b, P.Lmax);
   return u;
 }
 
@@ -362,9 +361,9 @@ __device__ __forceinline__ void hist_fetch(const StageAParams& P, const HistUnit
   const int kq = lane >> 4;
   const f16* kb = P.k_idx + ((size_t)u.b * P.Hret + u.kr) * (size_t)P.Lmax * kR;
   const int wbase = base + wv * 256;
-  // the same loads on every path (the wait counts stay exact): rows past the end, also
-  // of an empty unit, re-read the last valid row (row 0 when there is none); masked later
-  const int nlast = max(u.L - 1, 0);
+  // issued before the sequence length is read: rows past Lmax re-read the last row, and
+  // tokens past the sequence's end are masked in hist_block
+  const int nlast = P.Lmax - 1;
 #pragma unroll
   for (int gi = 0; gi < 8; gi++) {
     const int n = min(wbase + gi * 32 + (lane & 15) + 16 * (kq >> 1), nlast);
@@ -392,10 +391,11 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
   const int chunk = U.chunk;
   const int nrows = U.nrows;
   const size_t rowb = U.rowb;
-  const int L = U.L;
+  const int L = clamp_len(P.seq_lens, U.b, P.Lmax);
   const int base = chunk * TC;
   if (base >= L) {
     if (tid < nrows) P.partA[(rowb + tid) * P.nchunk + chunk] = kEmptyCell;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the unit's loads are still in flight
     return;
   }
   const bool full = base + TC <= L;
@@ -593,12 +593,17 @@ __device__ void window_block(const WinParams& P, int wb, float* lds) {
   const int elo = wsplit * P.wrows;
   const int n = max(0, min(nwin - elo, P.wrows));
   const int sinks = P.sinks, window = P.window;
+  // entry e >= ns is position wstart + (e - ns); its slot is sinks + (pos mod window), and
+  // the positions span at most `window`, so one wrap test replaces the modulo
+  const int wbase = wstart % window;
   attend_list<kBWaves>(
       Kb, Vb, n,
       [&](int e) {
         e += elo;
-        const int pos = e < ns ? e : wstart + (e - ns);
-        return pos < sinks ? pos : sinks + pos % window;
+        if (e < ns) return e;  // sink positions 0..ns-1 sit in their own slots
+        int v = wbase + (e - ns);
+        v -= v >= window ? window : 0;
+        return sinks + v;
       },
       [&](int) { return 0xFFFFu; }, qop, P.scale2, st);
   const size_t prow = ((size_t)(b * P.Hloc + kl) * P.nws + wsplit) * G;
