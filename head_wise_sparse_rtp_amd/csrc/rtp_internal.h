@@ -128,7 +128,8 @@ struct WsPlanner {
 struct StepFusedPlan {
   int G, Hret, Hloc;
   int tc, nt, nchunk;  // histogram chunk tokens, stage-A threads, chunks per row
-  int nwd, tb, nblk;   // selection blocks: code words per thread, tokens, blocks per KV head
+  int nwd, tb, nblk;   // selection slices: code words per thread, tokens, slices per KV head
+  int nparts;          // selection blocks per slice (they share its attention steps)
   int wrows, nws;      // window blocks: rows per block, blocks per local KV head
   int ncu;             // compute units of the device
   size_t suf, partA, codes, bstar, Aglob, sufg;

@@ -117,15 +117,17 @@ __device__ __forceinline__ void attn_init(AttnState& s) {
   for (int nb = 0; nb < 8; nb++) s.o[nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
-// B operand of S^T = K . Q^T: head lane%16, dims 32*(lane/16) + 8*s + {0..7}
+// B operand of S^T = K . Q^T: head lane%16, dims 32*s + 8*(lane/16) + {0..7} in the MFMA
+// of slice s (any assignment of dims to k-slots works if K uses the same one; this one lets
+// the four lanes of a K row read 64 contiguous bytes per load)
 __device__ __forceinline__ void load_qop(const f16* __restrict__ qhead0, int G, h8 (&qop)[4]) {
   const int lane = threadIdx.x & 63;
   const int h = lane & 15;
   const int gq = lane >> 4;
   if (h < G) {
-    const h8* p = reinterpret_cast<const h8*>(qhead0 + (size_t)h * kD + 32 * gq);
+    const h8* p = reinterpret_cast<const h8*>(qhead0 + (size_t)h * kD + 8 * gq);
 #pragma unroll
-    for (int s = 0; s < 4; s++) qop[s] = p[s];
+    for (int s = 0; s < 4; s++) qop[s] = p[4 * s];
   } else {
 #pragma unroll
     for (int s = 0; s < 4; s++) qop[s] = h8{0, 0, 0, 0, 0, 0, 0, 0};
@@ -133,7 +135,7 @@ __device__ __forceinline__ void load_qop(const f16* __restrict__ qhead0, int G, 
 }
 
 struct StepLoads {
-  h8 k[2][4];  // [tile][s]: K row (tile*16 + lane%16), dims 32*gq + 8*s ..
+  h8 k[2][4];  // [tile][s]: K row (tile*16 + lane%16), dims 32*s + 8*gq ..
   h8 v[8];     // [u]: V row of k-slot u (u<4: tile0 row 4gq+u; else tile1 row 4gq+u-4)
 };
 
@@ -147,9 +149,9 @@ __device__ __forceinline__ void step_load(const f16* __restrict__ Kb, const f16*
 #pragma unroll
   for (int t = 0; t < 2; t++) {
     const int r = row_of(t * 16 + c);
-    const h8* p = reinterpret_cast<const h8*>(Kb + (size_t)r * kD + 32 * gq);
+    const h8* p = reinterpret_cast<const h8*>(Kb + (size_t)r * kD + 8 * gq);
 #pragma unroll
-    for (int s = 0; s < 4; s++) ld.k[t][s] = p[s];
+    for (int s = 0; s < 4; s++) ld.k[t][s] = p[4 * s];
   }
 #pragma unroll
   for (int u = 0; u < 8; u++) {
@@ -545,16 +547,19 @@ __global__ __launch_bounds__(NT, 2) void k_stage_a(StageAParams P) {
 }
 
 // Masked attention over the entries e = 0..n-1 of a row list: row_of(e) is the cache
-// row, mask_of(e) the heads that take part (bit h).  Wavefront wv of NWV takes steps wv,
-// wv + NWV, ...; the loads of two steps are in flight before either is used.
+// row, mask_of(e) the heads that take part (bit h).  The list is cut into 32-row steps;
+// this block takes steps part, part + nparts, ... and its wavefront wv of NWV every NWV-th
+// of those, two steps' loads in flight before either is used.
 template <int NWV, class RowOf, class MaskOf>
 __device__ __forceinline__ void attend_list(const f16* __restrict__ Kb, const f16* __restrict__ Vb,
                                             int n, RowOf row_of, MaskOf mask_of,
-                                            const h8 (&qop)[4], float scale2, AttnState& st) {
+                                            const h8 (&qop)[4], float scale2, AttnState& st,
+                                            int part = 0, int nparts = 1) {
   const int wv = threadIdx.x >> 6;
   const int nsteps = (n + kStep - 1) / kStep;
-  for (int s0 = wv; s0 < nsteps; s0 += 2 * NWV) {
-    const int s1 = s0 + NWV;
+  const int stride = nparts * NWV;
+  for (int s0 = part + nparts * wv; s0 < nsteps; s0 += 2 * stride) {
+    const int s1 = s0 + stride;
     const int e0 = s0 * kStep, e1 = s1 * kStep;
     StepLoads ld0, ld1;
     step_load(Kb, Vb, [&](int i) { return row_of(e0 + i < n ? e0 + i : 0); }, ld0);
@@ -695,7 +700,7 @@ __global__ __launch_bounds__(kThreads) void k_stage_t(StageTParams P) {
 // ---------------------------------------------------------------------------
 struct StageBParams {
   const int32_t* seq_lens;
-  int B, Hq, G, Lmax, Hret, nchunk, tc, nblk;
+  int B, Hq, G, Lmax, Hret, nchunk, tc, nblk, nparts;
   double p;
   const f16* q;
   const f16* K_ret;
@@ -738,9 +743,10 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int blk = blockIdx.x % P.nblk;
-  const int kr = (blockIdx.x / P.nblk) % P.Hret;
-  const int b = blockIdx.x / (P.nblk * P.Hret);
+  const int part = blockIdx.x % P.nparts;  // share of the attention steps of the slice
+  const int blk = (blockIdx.x / P.nparts) % P.nblk;
+  const int kr = (blockIdx.x / (P.nparts * P.nblk)) % P.Hret;
+  const int b = blockIdx.x / (P.nparts * P.nblk * P.Hret);
   const int G = P.G;
   const size_t row0 = (size_t)b * P.Hret * G + (size_t)kr * G;
   const int L = clamp_len(P.seq_lens, b, P.Lmax);
@@ -819,7 +825,7 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
       }
       if (lane == 0) {
         s_bs[g] = J;
-        if (blk == 0) P.bstar[row0 + g] = J;
+        if (blk == 0 && part == 0) P.bstar[row0 + g] = J;
       }
     }
   }
@@ -926,14 +932,16 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
   attn_init(st);
   attend_list<kBWaves>(
       Kb, Vb, U, [&](int e) { return tok0 + (int)(lst[e] & 0xFFFFu); },
-      [&](int e) { return lst[e] >> 16; }, qop, P.scale2, st);
+      [&](int e) { return lst[e] >> 16; }, qop, P.scale2, st, part, P.nparts);
   __syncthreads();
 
   // ---- phase 3: block partial
-  const size_t s1p = ((size_t)(b * P.Hret + kr) * P.nblk + blk) * G;
-  block_combine<kBWaves>(st, G, min(kBWaves, (U + kStep - 1) / kStep), lds, P.p1m + s1p,
-                         P.p1l + s1p, P.p1acc + s1p * kD);
-  if (tid < G) P.p1cnt[s1p + tid] = s_cnt[tid];
+  // partial (slice, part); the selection counts go with part 0 only
+  const int mysteps = max(0, ((U + kStep - 1) / kStep - part + P.nparts - 1) / P.nparts);
+  const size_t s1p = (((size_t)(b * P.Hret + kr) * P.nblk + blk) * P.nparts + part) * G;
+  block_combine<kBWaves>(st, G, min(kBWaves, mysteps), lds, P.p1m + s1p, P.p1l + s1p,
+                         P.p1acc + s1p * kD);
+  if (tid < G) P.p1cnt[s1p + tid] = part == 0 ? s_cnt[tid] : 0;
 }
 
 template <int NWD, int GMAX>
@@ -1170,6 +1178,14 @@ StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int
     }
     sp.tb = 1024 * sp.nwd;
     sp.nblk = (Lmax + sp.tb - 1) / sp.tb;
+    // few slices (short sequences): several blocks share a slice's attention steps, as
+    // many as still fit two blocks per CU beside the window blocks (the selected tokens per
+    // query head do not shrink with the sequence, so their attention would otherwise sit
+    // on a few CUs)
+    {
+      const int64_t nsel = (int64_t)B * Hret * sp.nblk;
+      sp.nparts = (int)std::max<int64_t>(1, std::min<int64_t>(16, (2 * (int64_t)sp.ncu - nwin_blocks) / nsel));
+    }
     const int H = Hret * G;
     sp.suf = wp.take<float>((size_t)B * H * sp.nchunk * kNB);
     sp.partA = wp.take<int32_t>((size_t)B * H * sp.nchunk);
@@ -1177,7 +1193,7 @@ StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int
     sp.bstar = wp.take<int32_t>((size_t)B * H);
     sp.Aglob = wp.take<int32_t>((size_t)B * H);
     sp.sufg = wp.take<double>((size_t)B * H * kNB);
-    const size_t n1 = (size_t)B * Hret * sp.nblk * G;
+    const size_t n1 = (size_t)B * Hret * sp.nblk * sp.nparts * G;
     sp.p1m = wp.take<float>(n1);
     sp.p1l = wp.take<float>(n1);
     sp.p1acc = wp.take<float>(n1 * kD);
@@ -1275,6 +1291,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     Q.nchunk = sp.nchunk;
     Q.tc = sp.tc;
     Q.nblk = sp.nblk;
+    Q.nparts = sp.nparts;
     Q.p = a.p;
     Q.q = static_cast<const f16*>(a.q);
     Q.K_ret = static_cast<const f16*>(a.K_ret);
@@ -1290,7 +1307,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     Q.p1acc = at<float>(ws, sp.p1acc);
     Q.p1cnt = at<int32_t>(ws, sp.p1cnt);
     Q.want_count = a.count_out != nullptr;
-    Q.nret_blocks = B * sp.Hret * sp.nblk;
+    Q.nret_blocks = B * sp.Hret * sp.nblk * sp.nparts;
   }
   int nwin_blocks = 0;
   if (sp.Hloc > 0) {
@@ -1345,7 +1362,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     M.p1cnt = Q.p1cnt;
     M.Aglob = Q.Aglob;
     M.bstar = Q.bstar;
-    M.nblk = sp.nblk;
+    M.nblk = sp.nblk * sp.nparts;
     M.Hret = sp.Hret;
     M.ret = a.ret;
     M.count_out = a.count_out;
@@ -1360,7 +1377,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     M.Hloc = sp.Hloc;
     M.loc = a.loc;
   }
-  const int nmax = std::max(sp.Hret > 0 ? sp.nblk : 0, sp.Hloc > 0 ? sp.nws : 0);
+  const int nmax = std::max(sp.Hret > 0 ? sp.nblk * sp.nparts : 0, sp.Hloc > 0 ? sp.nws : 0);
   const size_t ldsM = sizeof(float) * (3 * (size_t)nmax + 8 + kThreads / 8 * kMSlice);
   k_stage_m<<<(M.nret + nwm) * kMSlices, kThreads, ldsM, st>>>(M);
   e = hipGetLastError();
