@@ -132,7 +132,8 @@ struct StepFusedPlan {
   int nparts;          // selection blocks per slice (they share its attention steps)
   int wrows, nws;      // window blocks: rows per block, blocks per local KV head
   int ncu;             // compute units of the device
-  size_t suf, partA, codes, bstar, Aglob, sufg;
+  int tcpb, tseg;      // stage-T blocks: chunks per block, blocks per head row
+  size_t suf, partA, codes, bstar, Aglob, sufq;
   size_t p1m, p1l, p1acc, p1cnt;
   size_t wpm, wpl, wpacc;
   size_t bytes;

@@ -43,8 +43,6 @@ constexpr int kStep = 32;                // cache rows per wavefront step
 constexpr int kBThreads = 256;           // threads of a stage-B block (two blocks per CU)
 constexpr int kBWaves = kBThreads / 64;  // wavefronts of a stage-B block
 constexpr int kMaxCPB = 4;               // histogram chunks per selection block (at most)
-constexpr int kTBins = 16;               // bins per stage-T block
-constexpr int kTBatch = 32;              // chunk loads in flight per stage-T thread
 constexpr int kMSlice = 32;              // output dims per stage-M block
 constexpr int kMSlices = kD / kMSlice;
 constexpr int kMaxParts = 4096;          // partials merged per head (stage-M LDS)
@@ -302,6 +300,7 @@ struct StageAParams {
   float* suf;
   int32_t* partA;
   uint32_t* codes;
+  unsigned long long* sufq;  // zeroed here (rows of the unit, by its chunk-0 block)
 };
 
 struct WinParams {
@@ -395,6 +394,8 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
   const size_t rowb = U.rowb;
   const int L = clamp_len(P.seq_lens, U.b, P.Lmax);
   const int base = chunk * TC;
+  if (chunk == 0)
+    for (int i = tid; i < nrows * kNB; i += NT) P.sufq[rowb * kNB + i] = 0ull;
   if (base >= L) {
     if (tid < nrows) P.partA[(rowb + tid) * P.nchunk + chunk] = kEmptyCell;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the unit's loads are still in flight
@@ -617,82 +618,95 @@ __device__ void window_block(const WinParams& P, int wb, float* lds) {
 }
 
 // ---------------------------------------------------------------------------
-// stage T: block (head row, 16 bins J0..J0+15), thread (bin J0 + t%16, chunk group t/16):
-//   SUF_J = sum_c suf_c[max(J - s_c, 0)] * exp(-s_c w),  s_c = A - A_c,  A = max_c A_c
-// summed in a fixed order (chunks of a group in order, then the groups in order).
+// stage T: suffix table of every retrieval head row,
+//   SUF_J = sum_c suf_c[max(J - s_c, 0)] * exp(-s_c w),  s_c = A - A_c,  A = max_c A_c,
+// in fixed point (units of 2^-38 of the top cell's mass, unsigned 64-bit).  Block
+// (row, segment) takes the chunks [seg*cpb, seg*cpb + cpb) of the row: their 1 KB suffix
+// rows are loaded whole, together with the row's top cells, so the block waits on memory
+// once; the shift by s_c happens in LDS.  Thread J sums its bin over the block's chunks
+// in chunk order in fp64, rounds the sum down to a multiple of 2^-38 and adds it to the
+// row's table with an integer atomic: integer sums do not depend on the order of the
+// segments, so the table is the same on every run.  Per-block sums stay below 2^24
+// (one unit of mass per token at most), far inside the 2^26 the format holds.  Stage A
+// zeroes the table.
 // ---------------------------------------------------------------------------
+constexpr int kTMaxCPB = 32;                         // chunks per stage-T block (at most)
+constexpr double kSufOne = 274877906944.0;           // 2^38: fixed-point unit of the table
+
 struct StageTParams {
   const float* suf;
   const int32_t* partA;
-  int nchunk;
+  int nchunk, cpb, nseg;
   float c_log2;
-  double* sufg;
+  unsigned long long* sufq;
   int32_t* Aglob;
 };
 
+// PPT: 16-byte suffix pieces per thread (the block takes at most 4*PPT chunks).  Every
+// load is unconditional (indices clamped into the row) so that none waits on another.
+template <int PPT>
 __global__ __launch_bounds__(kThreads) void k_stage_t(StageTParams P) {
-  extern __shared__ int sA[];  // [nchunk] chunk top cells
+  __shared__ __align__(16) float sb[4 * PPT * kNB];  // the block's chunk suffix rows
+  constexpr int NCA = 4 * PPT < 8 ? 8 : 4 * PPT;
+  __shared__ __align__(16) int sAc[NCA];  // top cells of the block's chunks (kEmptyCell past nc)
   __shared__ int sAw[kThreads / 64];
-  __shared__ double red[kThreads / kTBins][kTBins + 1];
-  const int row = blockIdx.x / (kNB / kTBins);
-  const int J0 = (blockIdx.x % (kNB / kTBins)) * kTBins;
+  const int row = blockIdx.x / P.nseg;
+  const int seg = blockIdx.x % P.nseg;
+  const int nchunk = P.nchunk;
+  const int c0 = seg * P.cpb;
+  const int nc = min(P.cpb, nchunk - c0);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int nchunk = P.nchunk;
+  // ---- suffix rows (piece i = bins 4(i%64).. of chunk i/64), then the top cells
+  const f4* src = reinterpret_cast<const f4*>(P.suf + ((size_t)row * nchunk + c0) * kNB);
+  const int npiece = nc * (kNB / 4);
+  f4 v[PPT];
+#pragma unroll
+  for (int u = 0; u < PPT; u++) v[u] = src[min(tid + kThreads * u, npiece - 1)];
   const int32_t* pa = P.partA + (size_t)row * nchunk;
+  const int aown = pa[min(c0 + tid, nchunk - 1)];
   int A = kEmptyCell;
-  for (int c = tid; c < nchunk; c += kThreads) {
-    const int a = pa[c];
-    sA[c] = a;
-    A = max(A, a);
+  for (int cb = 0; cb < nchunk; cb += 8 * kThreads) {
+    int a[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) a[u] = pa[min(cb + tid + kThreads * u, nchunk - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; u++) A = max(A, a[u]);  // repeated cells leave the maximum alone
   }
+  f4* sb4 = reinterpret_cast<f4*>(sb);
+#pragma unroll
+  for (int u = 0; u < PPT; u++)
+    if (tid + kThreads * u < npiece) sb4[tid + kThreads * u] = v[u];
+  if (tid < NCA) sAc[tid] = tid < nc ? aown : kEmptyCell;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) A = max(A, __shfl_xor(A, o, 64));
   if (lane == 0) sAw[wv] = A;
   __syncthreads();
   A = max(max(sAw[0], sAw[1]), max(sAw[2], sAw[3]));
-  const int j = J0 + (tid % kTBins);
-  const int cg = tid / kTBins;
-  constexpr int NG = kThreads / kTBins;
+  if (seg == 0 && tid == 0) P.Aglob[row] = A;
+  if (A == kEmptyCell) return;
+  const int j = tid;  // bin
   double acc = 0.0;
-  if (A != kEmptyCell) {
-    const float* sb = P.suf + (size_t)row * nchunk * kNB;
-    for (int c0 = cg; c0 < nchunk; c0 += NG * kTBatch) {
-      // shifts first (all LDS reads in flight), then every load, then the sums
-      int sh[kTBatch];
+  for (int cc = 0; cc < nc; cc += 8) {
+    const int4 a0 = *reinterpret_cast<const int4*>(sAc + cc);
+    const int4 a1 = *reinterpret_cast<const int4*>(sAc + cc + 4);
+    const int ac[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    int sh[8];
 #pragma unroll
-      for (int u = 0; u < kTBatch; u++) {
-        const int c = c0 + NG * u;
-        sh[u] = c < nchunk ? sA[c] : kEmptyCell;
-      }
+    for (int u = 0; u < 8; u++)  // no token, or mass below the fp32 range: no contribution (-1)
+      sh[u] = (ac[u] != kEmptyCell && ac[u] >= A - 4096) ? A - ac[u] : -1;
+    float x[8];
 #pragma unroll
-      for (int u = 0; u < kTBatch; u++)  // s_c = A - A_c, or -1 for no contribution
-        sh[u] = (sh[u] != kEmptyCell && sh[u] >= A - 4096) ? A - sh[u] : -1;
-      float x[kTBatch];
+    for (int u = 0; u < 8; u++) x[u] = sb[min(cc + u, nc - 1) * kNB + max(j - max(sh[u], 0), 0)];
 #pragma unroll
-      for (int u = 0; u < kTBatch; u++) {
-        const int c = sh[u] >= 0 ? c0 + NG * u : 0;
-        const int jj = max(j - sh[u], 0);
-        x[u] = sb[(size_t)c * kNB + (sh[u] >= 0 ? jj : 0)];
-      }
-#pragma unroll
-      for (int u = 0; u < kTBatch; u++) {
-        // chunks without a contribution read a placeholder that is never used
-        const double f = (double)__builtin_amdgcn_exp2f(-(float)max(sh[u], 0) * P.c_log2);
-        acc += sh[u] >= 0 ? (double)x[u] * f : 0.0;
-      }
+    for (int u = 0; u < 8; u++) {
+      const double f = (double)__builtin_amdgcn_exp2f(-(float)max(sh[u], 0) * P.c_log2);
+      acc += sh[u] >= 0 ? (double)x[u] * f : 0.0;
     }
   }
-  red[cg][tid % kTBins] = acc;
-  __syncthreads();
-  if (tid < kTBins) {
-    double s = 0.0;
-#pragma unroll
-    for (int k = 0; k < NG; k++) s += red[k][tid];
-    P.sufg[(size_t)row * kNB + J0 + tid] = s;
-  }
-  if (J0 == 0 && tid == 0) P.Aglob[row] = A;
+  const unsigned long long qv = (unsigned long long)(acc * kSufOne);
+  if (qv != 0ull) atomicAdd(P.sufq + (size_t)row * kNB + j, qv);
 }
 
 // ---------------------------------------------------------------------------
@@ -709,7 +723,7 @@ struct StageBParams {
   float scale2;
   const int32_t* partA;
   const uint32_t* codes;
-  const double* sufg;
+  const unsigned long long* sufq;
   const int32_t* Aglob;
   int32_t* bstar;
   float* p1m;
@@ -770,21 +784,22 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
       if (chunk < P.nchunk) Ac = P.partA[(row0 + g) * P.nchunk + chunk];
     }
   }
-  // suffix table of the wavefront's heads: lane l holds SUF at bins 4l+1 .. 4l+4
-  double sv[HPW][4], zv[HPW];
+  // suffix table of the wavefront's heads (fixed point): lane l holds SUF at bins
+  // 4l+1 .. 4l+4
+  unsigned long long sv[HPW][4], zv[HPW];
 #pragma unroll
   for (int u = 0; u < HPW; u++) {
     const int g = wv + u * kBWaves;
-    zv[u] = 0.0;
+    zv[u] = 0ull;
 #pragma unroll
-    for (int k = 0; k < 4; k++) sv[u][k] = 0.0;
+    for (int k = 0; k < 4; k++) sv[u][k] = 0ull;
     if (g < G && P.p < 1.0) {
-      const double* sp = P.sufg + (row0 + g) * kNB;
+      const unsigned long long* sp = P.sufq + (row0 + g) * kNB;
       zv[u] = sp[0];
 #pragma unroll
       for (int k = 0; k < 4; k++) {
         const int J = 4 * lane + 1 + k;
-        sv[u][k] = J < kNB ? sp[J] : 0.0;
+        sv[u][k] = J < kNB ? sp[J] : 0ull;
       }
     }
   }
@@ -815,11 +830,11 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
     if (g < G) {
       int J = kNB - 1;
       if (P.p < 1.0) {
-        const double pz = P.p * zv[u];
+        const double pz = P.p * (double)zv[u];
 #pragma unroll
         for (int k = 3; k >= 0; k--) {
           const int Jk = 4 * lane + k;
-          if (Jk < kNB - 1 && zv[u] - sv[u][k] >= pz) J = Jk;
+          if (Jk < kNB - 1 && (double)(zv[u] - sv[u][k]) >= pz) J = Jk;
         }
         J = wave_min_i(J);
       }
@@ -1136,12 +1151,7 @@ bool step_fused_supported(int kv_dtype, int G, int Hloc, int window, int sinks, 
     const int wr = window_rows(B, Hloc, ring);
     if ((ring + wr - 1) / wr > kMaxParts) return false;
   }
-  if (Hret > 0) {
-    const int tc = chunk_tokens(B, Hret, Lmax);
-    const int64_t nchunk = ((int64_t)Lmax + tc - 1) / tc;
-    if (nchunk > 16384) return false;                 // stage-T LDS
-    if ((Lmax + 4095) / 4096 > kMaxParts) return false;  // stage-M LDS
-  }
+  if (Hret > 0 && (Lmax + 4095) / 4096 > kMaxParts) return false;  // stage-M LDS
   return true;
 }
 
@@ -1192,7 +1202,13 @@ StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int
     sp.codes = wp.take<uint32_t>((size_t)B * H * sp.nchunk * (sp.tc / 4));
     sp.bstar = wp.take<int32_t>((size_t)B * H);
     sp.Aglob = wp.take<int32_t>((size_t)B * H);
-    sp.sufg = wp.take<double>((size_t)B * H * kNB);
+    sp.sufq = wp.take<unsigned long long>((size_t)B * H * kNB);
+    // stage-T blocks: chunks per block so that the grid is about one block per CU
+    {
+      const int64_t rc = (int64_t)B * H * sp.nchunk;
+      sp.tcpb = (int)std::min<int64_t>(kTMaxCPB, std::max<int64_t>(1, (rc + sp.ncu - 1) / sp.ncu));
+      sp.tseg = (sp.nchunk + sp.tcpb - 1) / sp.tcpb;
+    }
     const size_t n1 = (size_t)B * Hret * sp.nblk * sp.nparts * G;
     sp.p1m = wp.take<float>(n1);
     sp.p1l = wp.take<float>(n1);
@@ -1248,6 +1264,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     P.suf = at<float>(ws, sp.suf);
     P.partA = at<int32_t>(ws, sp.partA);
     P.codes = at<uint32_t>(ws, sp.codes);
+    P.sufq = at<unsigned long long>(ws, sp.sufq);
     P.nunits = B * sp.Hret * P.ngg * sp.nchunk;
     // histogram copies, the top cells of the wavefronts, the code words of the wavefronts
     const size_t ldsA = sizeof(uint32_t) * kCopies * GG * (kNB + kPad) + sizeof(float) * GG * 8 +
@@ -1269,10 +1286,20 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     T.suf = P.suf;
     T.partA = P.partA;
     T.nchunk = sp.nchunk;
+    T.cpb = sp.tcpb;
+    T.nseg = sp.tseg;
     T.c_log2 = c_log2;
-    T.sufg = at<double>(ws, sp.sufg);
+    T.sufq = P.sufq;
     T.Aglob = at<int32_t>(ws, sp.Aglob);
-    k_stage_t<<<B * H * (kNB / kTBins), kThreads, sizeof(int) * sp.nchunk, st>>>(T);
+    const dim3 gT(B * H * sp.tseg);
+    if (sp.tcpb <= 4)
+      k_stage_t<1><<<gT, kThreads, 0, st>>>(T);
+    else if (sp.tcpb <= 8)
+      k_stage_t<2><<<gT, kThreads, 0, st>>>(T);
+    else if (sp.tcpb <= 16)
+      k_stage_t<4><<<gT, kThreads, 0, st>>>(T);
+    else
+      k_stage_t<8><<<gT, kThreads, 0, st>>>(T);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1299,7 +1326,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     Q.ret = a.ret;
     Q.partA = P.partA;
     Q.codes = P.codes;
-    Q.sufg = T.sufg;
+    Q.sufq = T.sufq;
     Q.Aglob = T.Aglob;
     Q.bstar = at<int32_t>(ws, sp.bstar);
     Q.p1m = at<float>(ws, sp.p1m);
