@@ -63,6 +63,9 @@ def lib():
         L.rtpo_topp_select.restype = ctypes.c_int64
         L.rtpo_topp_select.argtypes = [P, ctypes.c_int64, ctypes.c_double, ctypes.c_double, P, P,
                                        P, P]
+        L.rtpo_topk_select.restype = ctypes.c_int64
+        L.rtpo_topk_select.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_double, P, P,
+                                       P, P]
         L.rtpo_attention.restype = None
         L.rtpo_attention.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int64,
                                      ctypes.c_double, P, P]
@@ -130,6 +133,23 @@ def topp_select(z, p: float, bin_width: float = 0.125) -> Selection:
     return Selection(sel[:n].copy(), hist, int(A.value), int(b.value))
 
 
+def topk_select(z, k: int, bin_width: float = 0.125) -> Selection:
+    """Fixed top-k through the same 256-bin histogram: every token weighs one, b* is
+    the least bin whose cumulative count reaches k (see rtp_oracle.c).  `hist` holds
+    the counts."""
+    zz = np.ascontiguousarray(z, dtype=np.float32)
+    L = zz.shape[0]
+    assert L >= 1 and np.all(np.isfinite(zz)), "oracle requires L >= 1 and finite logits"
+    assert int(k) >= 1, "top-k needs k >= 1"
+    sel = np.empty(L, dtype=np.int32)
+    hist = np.empty(NBINS, dtype=np.float64)
+    A = ctypes.c_int64()
+    b = ctypes.c_int32()
+    n = lib().rtpo_topk_select(_ptr(zz), L, int(k), float(bin_width), _ptr(sel), _ptr(hist),
+                               ctypes.byref(A), ctypes.byref(b))
+    return Selection(sel[:n].copy(), hist, int(A.value), int(b.value))
+
+
 def cells(z, bin_width: float = 0.125) -> np.ndarray:
     """g_n = floor(z_n / w) (exact for a power-of-two w)."""
     return np.floor(np.asarray(z, dtype=np.float32).astype(np.float64) / bin_width).astype(np.int64)
@@ -186,10 +206,11 @@ class HeadResult:
 
 def decode_layer(layer, seq_lens, Hq: int, Hkv: int, p: float, bin_width: float,
                  scale_idx: float, scale_attn: float, window: int, sinks: int,
-                 heads: Optional[List[int]] = None, batches: Optional[List[int]] = None
-                 ) -> Dict[tuple, HeadResult]:
+                 heads: Optional[List[int]] = None, batches: Optional[List[int]] = None,
+                 topk: int = 0) -> Dict[tuple, HeadResult]:
     """Oracle outputs of one layer keyed by (b, query head).  `heads` / `batches`
-    restrict the work to a sample of query heads / sequences."""
+    restrict the work to a sample of query heads / sequences.  topk > 0 selects with
+    the fixed top-k rule instead of top-p."""
     G = Hq // Hkv
     mask = np.asarray(layer.kv_is_retrieval)
     ret = [int(h) for h in np.nonzero(mask)[0]]
@@ -211,7 +232,7 @@ def decode_layer(layer, seq_lens, Hq: int, Hkv: int, p: float, bin_width: float,
                 Vh = np_of(layer.V_ret[b, kr, :L])
                 for h in hs:
                     z = index_score(q_idx[b, h], kidx, scale_idx)
-                    s = topp_select(z, p, bin_width)
+                    s = topk_select(z, topk, bin_width) if topk > 0 else topp_select(z, p, bin_width)
                     o, lse = attention(q[b, h], Kh, Vh, s.idx, scale_attn)
                     res[(b, h)] = HeadResult(o, lse, s, z)
             else:
@@ -233,5 +254,6 @@ def decode_step(wl, layers: Optional[List[int]] = None, heads=None, batches=None
             out.append({})
             continue
         out.append(decode_layer(layer, wl.seq_lens, wl.Hq, wl.Hkv, wl.p, wl.bin_width,
-                                wl.scale_idx, wl.scale_attn, wl.window, wl.sinks, heads, batches))
+                                wl.scale_idx, wl.scale_attn, wl.window, wl.sinks, heads, batches,
+                                getattr(wl, "topk", 0)))
     return out

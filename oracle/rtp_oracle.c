@@ -119,6 +119,44 @@ int64_t rtpo_topp_select(const float* z, int64_t L, double p, double w, int32_t*
   return cnt;
 }
 
+/* Fixed top-k through the same histogram (the pages' comparison of fixed budgets with
+ * top-p: section 三, insight 3 and its top-k vs top-p table).  The bins are those of
+ * rtpo_topp_select; each token weighs one instead of its softmax mass:
+ *   c_j = #{ n : j_n = j };  b* = the least j with c_0 + .. + c_j >= k, or 255 when the
+ *   whole sequence holds fewer than k tokens;  S = { n : j_n <= b* }, ascending.
+ * S holds at least min(k, L) tokens and contains the k highest logits (ties at the k-th
+ * value included), because the bins are whole cells in logit order.
+ * Writes hist[256] (the counts), *A_out, *bstar_out and sel; returns |S|. */
+int64_t rtpo_topk_select(const float* z, int64_t L, int64_t k, double w, int32_t* sel,
+                         double* hist, int64_t* A_out, int32_t* bstar_out) {
+  int64_t A = INT64_MIN;
+  for (int64_t n = 0; n < L; n++) {
+    int64_t g = cell_of(z[n], w);
+    if (g > A) A = g;
+  }
+  for (int j = 0; j < ORACLE_NBINS; j++) hist[j] = 0.0;
+  for (int64_t n = 0; n < L; n++) {
+    int64_t j = A - cell_of(z[n], w);
+    if (j > ORACLE_NBINS - 1) j = ORACLE_NBINS - 1;
+    hist[j] += 1.0;
+  }
+  int32_t b = ORACLE_NBINS - 1;
+  double c = 0.0;
+  for (int j = 0; j < ORACLE_NBINS; j++) {
+    c += hist[j];
+    if (c >= (double)k) { b = j; break; }
+  }
+  int64_t cnt = 0;
+  for (int64_t n = 0; n < L; n++) {
+    int64_t j = A - cell_of(z[n], w);
+    if (j > ORACLE_NBINS - 1) j = ORACLE_NBINS - 1;
+    if (j <= b) sel[cnt++] = (int32_t)n;
+  }
+  *A_out = A;
+  *bstar_out = b;
+  return cnt;
+}
+
 /* Exact softmax attention over a list of rows, in fp64.
  *   s_i = scale * sum_c q[c] K[row_i][c];  m = max_i s_i
  *   out[c] = sum_i e^{s_i - m} V[row_i][c] / sum_i e^{s_i - m};  lse = m + log(sum_i e^{s_i - m})

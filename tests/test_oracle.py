@@ -366,3 +366,91 @@ def test_layer_local_heads_use_window_and_sinks():
         m[res[(0, h)].sel.idx] = True
         ref = sdpa64(q, K, V, wl.scale_attn, m)
         assert np.allclose(res[(0, h)].out, ref, atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# fixed top-k through the same histogram
+# ---------------------------------------------------------------------------
+GOLD_TOPK = os.path.join(os.path.dirname(__file__), "golden", "topk_examples.json")
+
+
+def _topk_gold():
+    with open(GOLD_TOPK) as f:
+        return json.load(f)["select"]
+
+
+@pytest.mark.parametrize("ex", _topk_gold(), ids=lambda e: e["name"])
+def test_topk_worked_example(ex):
+    z = np.asarray(ex["z"], dtype=np.float32)
+    s = oracle.topk_select(z, ex["k"], ex["w"])
+    assert s.A == ex["A"]
+    assert s.bstar == ex["bstar"]
+    assert s.idx.tolist() == ex["S"]
+    want = np.zeros(256)
+    for j, c in ex["counts"].items():
+        want[int(j)] = c
+    assert np.array_equal(s.hist, want)
+
+
+def _topk_by_sorting_cells(z, k, w=0.125):
+    """Brute force from another angle: visit the occupied cells from the top down (every
+    cell 255 or more below the top counts as one tail cell) and keep whole cells until
+    at least k tokens are kept."""
+    g = np.floor(np.asarray(z, dtype=np.float32).astype(np.float64) / w).astype(np.int64)
+    A = g.max()
+    key = np.maximum(g, A - 255)
+    kept = np.zeros(len(z), dtype=bool)
+    for c in sorted(set(key.tolist()), reverse=True):
+        kept |= key == c
+        if kept.sum() >= k:
+            break
+    return np.nonzero(kept)[0]
+
+
+KS = [1, 2, 3, 10, 100, 2048, 4096, 10 ** 6]
+
+
+@pytest.mark.parametrize("name,z", LOGITS, ids=[n for n, _ in LOGITS])
+def test_topk_rule_contains_top_k_and_is_minimal(name, z):
+    L = len(z)
+    zs = np.sort(z.astype(np.float64))[::-1]
+    prev = None
+    for k in KS:
+        s = oracle.topk_select(z, k)
+        idx = s.idx
+        assert np.all(np.diff(idx) > 0)
+        assert len(idx) >= min(k, L)
+        # every token at or above the k-th largest logit is kept (ties included) ...
+        kth = zs[min(k, L) - 1]
+        assert set(np.nonzero(z.astype(np.float64) >= kth)[0].tolist()) <= set(idx.tolist())
+        # ... the kept set is an upper set in z ...
+        out = np.setdiff1d(np.arange(L), idx)
+        if len(out):
+            assert z[out].max() < z[idx].min()
+        # ... counts are exact and the threshold bin is the first to reach k
+        assert s.hist.sum() == L and np.all(s.hist == np.round(s.hist))
+        C = np.cumsum(s.hist)
+        if k <= L:
+            assert C[s.bstar] >= k
+        else:
+            assert s.bstar == 255 and len(idx) == L
+        if s.bstar > 0 and k <= L:
+            assert C[s.bstar - 1] < k
+        assert np.array_equal(idx, _topk_by_sorting_cells(z, k))
+        if prev is not None:
+            assert set(prev.tolist()) <= set(idx.tolist())   # monotone in k
+        prev = idx
+
+
+@pytest.mark.parametrize("name,z", LOGITS[::3], ids=[n for n, _ in LOGITS[::3]])
+def test_topk_permutation_and_cell_shift(name, z):
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(len(z))
+    for k in [1, 5, 300]:
+        s = oracle.topk_select(z, k)
+        sp = oracle.topk_select(z[perm], k)
+        assert set(perm[sp.idx].tolist()) == set(s.idx.tolist())
+        sh = oracle.topk_select((z.astype(np.float64) + 3 * 0.125).astype(np.float32), k)
+        if np.array_equal(np.floor(z.astype(np.float64) / 0.125) + 3,
+                          np.floor((z.astype(np.float64) + 0.375).astype(np.float32) / 0.125)):
+            assert np.array_equal(sh.idx, s.idx) and sh.A == s.A + 3

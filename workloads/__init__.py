@@ -158,6 +158,7 @@ class Workload:
     scale_attn: float
     layers: List[Layer]
     seed: int = 0
+    topk: int = 0                          # > 0: fixed top-k selection instead of top-p
 
     @property
     def G(self) -> int:
