@@ -6,6 +6,7 @@ The names follow the C ABI in ``include/rtp.h``:
 
 * ``rtp_index_score``   indexer logits z = q_idx . k_idx (fp32 fma chain)
 * ``rtp_topp_select``   256-bin histogram top-p over the indexer softmax
+* ``rtp_topk_select``   fixed top-k through the same histogram (token counts per bin)
 * ``rtp_sparse_decode`` exact softmax attention over the selected tokens
 * ``rtp_window_decode`` window + sink attention of local heads
 * ``rtp_decode_step``   a whole layer: retrieval heads sparse, local heads windowed
@@ -29,6 +30,7 @@ NBINS = 256
 EXPORTED = [
     "rtp_status_string", "rtp_abi_version", "rtp_index_score",
     "rtp_topp_select_workspace_size", "rtp_topp_select",
+    "rtp_topk_select_workspace_size", "rtp_topk_select",
     "rtp_sparse_decode_workspace_size", "rtp_sparse_decode",
     "rtp_window_decode_workspace_size", "rtp_window_decode",
     "rtp_decode_step_workspace_size", "rtp_decode_step",
@@ -53,6 +55,7 @@ class LayerDesc(ctypes.Structure):
         ("p", F64), ("bin_width", F32), ("scale_idx", F32), ("scale_attn", F32),
         ("out", P), ("lse", P), ("thresh_out", P), ("count_out", P),
         ("prof_ev", P * 8),
+        ("topk", I32),
     ]
 
 
@@ -80,6 +83,10 @@ def lib():
         L.rtp_topp_select_workspace_size.argtypes = [I32, I32, I32]
         L.rtp_topp_select.restype = I32
         L.rtp_topp_select.argtypes = [P, P, I32, I32, I32, F64, F32, P, P, I32, P, P, P, SZ, P]
+        L.rtp_topk_select_workspace_size.restype = SZ
+        L.rtp_topk_select_workspace_size.argtypes = [I32, I32, I32]
+        L.rtp_topk_select.restype = I32
+        L.rtp_topk_select.argtypes = [P, P, I32, I32, I32, I32, F32, P, P, I32, P, P, P, SZ, P]
         L.rtp_sparse_decode_workspace_size.restype = SZ
         L.rtp_sparse_decode_workspace_size.argtypes = [I32, I32, I32, I32]
         L.rtp_sparse_decode.restype = I32
@@ -170,6 +177,26 @@ def rtp_topp_select(z: torch.Tensor, seq_lens: torch.Tensor, p: float, bin_width
     return sel_idx, sel_count, hist, thresh
 
 
+def rtp_topk_select(z: torch.Tensor, seq_lens: torch.Tensor, k: int, bin_width: float = 0.125,
+                    cap: Optional[int] = None, want_hist: bool = True, ws=None, stream=None):
+    """Fixed top-k through the 256-bin histogram.  Returns (sel_idx [B,H,cap] int32,
+    sel_count [B,H] int32, hist [B,H,256] fp32 token counts or None, thresh [B,H,2])."""
+    B, H, Lmax = z.shape
+    cap = Lmax if cap is None else int(cap)
+    dev = z.device
+    sel_idx = torch.full((B, H, max(cap, 1)), -1, dtype=torch.int32, device=dev)
+    sel_count = torch.empty((B, H), dtype=torch.int32, device=dev)
+    hist = torch.empty((B, H, NBINS), dtype=torch.float32, device=dev) if want_hist else None
+    thresh = torch.empty((B, H, 2), dtype=torch.int32, device=dev)
+    nb = lib().rtp_topk_select_workspace_size(B, H, Lmax)
+    if ws is None:
+        ws = workspace(nb, dev)
+    _check(lib().rtp_topk_select(_ptr(z), _ptr(seq_lens), B, H, Lmax, int(k), float(bin_width),
+                                 _ptr(sel_idx), _ptr(sel_count), cap, _ptr(hist), _ptr(thresh),
+                                 _ptr(ws), ws.numel(), _stream(stream)))
+    return sel_idx, sel_count, hist, thresh
+
+
 def rtp_sparse_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, sel_idx: torch.Tensor,
                       sel_count: torch.Tensor, scale_attn: float, want_lse: bool = True, ws=None,
                       stream=None):
@@ -221,7 +248,7 @@ class DecodeStep:
     def __init__(self, layer, seq_lens: torch.Tensor, B: int, Hq: int, Hkv: int, Lmax: int,
                  window: int, sinks: int, p: float, bin_width: float, scale_idx: float,
                  scale_attn: float, out: Optional[torch.Tensor] = None, want_lse: bool = True,
-                 want_debug: bool = False, ws: Optional[torch.Tensor] = None):
+                 want_debug: bool = False, ws: Optional[torch.Tensor] = None, topk: int = 0):
         dev = layer.q.device
         self.keep = [layer.q, layer.q_idx, layer.K_ret, layer.V_ret, layer.k_idx, layer.K_loc,
                      layer.V_loc, seq_lens]
@@ -247,6 +274,7 @@ class DecodeStep:
             ptr_or_none(layer.V_loc, nloc), _ptr(seq_lens), float(p), float(bin_width),
             float(scale_idx), float(scale_attn), _ptr(self.out), _ptr(self.lse),
             _ptr(self.thresh), _ptr(self.count))
+        self.desc.topk = int(topk)
         nb = lib().rtp_decode_step_workspace_size(ctypes.byref(self.desc))
         if nb == 0:
             raise RtpError(RTP_EINVAL)
@@ -260,10 +288,11 @@ class DecodeStep:
 
 
 def rtp_decode_step(layer, seq_lens, B, Hq, Hkv, Lmax, window, sinks, p, bin_width, scale_idx,
-                    scale_attn, want_debug=False, stream=None):
-    """One layer's decode step; returns (out, lse, thresh, count)."""
+                    scale_attn, want_debug=False, stream=None, topk=0):
+    """One layer's decode step; returns (out, lse, thresh, count).  topk > 0 selects the
+    retrieval heads' tokens with the fixed top-k rule instead of top-p."""
     st = DecodeStep(layer, seq_lens, B, Hq, Hkv, Lmax, window, sinks, p, bin_width, scale_idx,
-                    scale_attn, want_debug=want_debug)
+                    scale_attn, want_debug=want_debug, topk=topk)
     st(stream)
     return st.out, st.lse, st.thresh, st.count
 
@@ -276,5 +305,5 @@ def decode_workload(wl, want_debug: bool = False, stream=None):
     for layer in wl.layers:
         res.append(rtp_decode_step(layer, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window, wl.sinks,
                                    wl.p, wl.bin_width, wl.scale_idx, wl.scale_attn, want_debug,
-                                   stream))
+                                   stream, getattr(wl, "topk", 0)))
     return res

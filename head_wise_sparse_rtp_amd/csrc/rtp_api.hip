@@ -194,10 +194,38 @@ rtp_status rtp_topp_select(const float* z, const int32_t* seq_lens, int32_t B, i
   if (ws_bytes < sp.bytes) return RTP_EWORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   const SelectBufs sb = bind_select(static_cast<char*>(ws), sp.offs);
-  hipError_t e = launch_hist_from_z(z, seq_lens, B, H, Lmax, bin_width, sp.cg, sb, st);
+  hipError_t e = launch_hist_from_z(z, seq_lens, B, H, Lmax, bin_width, false, sp.cg, sb, st);
   if (e == hipSuccess)
-    e = launch_threshold(seq_lens, B, H, Lmax, p, bin_width, sp.cg, sb, hist, thresh, nullptr, 1,
-                         H, st);
+    e = launch_threshold(seq_lens, B, H, Lmax, p, 0, bin_width, sp.cg, sb, hist, thresh, nullptr,
+                         1, H, st);
+  if (e == hipSuccess)
+    e = launch_select(seq_lens, B, H, Lmax, sp.cg, sb, sel_idx, sel_count, cap, nullptr, nullptr,
+                      1, H, st);
+  return hip_status(e);
+}
+
+size_t rtp_topk_select_workspace_size(int32_t B, int32_t H, int32_t Lmax) {
+  return rtp_topp_select_workspace_size(B, H, Lmax);
+}
+
+rtp_status rtp_topk_select(const float* z, const int32_t* seq_lens, int32_t B, int32_t H,
+                           int32_t Lmax, int32_t k, float bin_width, int32_t* sel_idx,
+                           int32_t* sel_count, int32_t cap, float* hist, int32_t* thresh,
+                           void* ws, size_t ws_bytes, void* stream) {
+  if (B < 1 || H < 1 || Lmax < 1 || cap < 0 || k < 1) return RTP_EINVAL;
+  if (Lmax > (1 << 24)) return RTP_EUNSUPPORTED;
+  if (!pow2_width(bin_width)) return RTP_EINVAL;
+  if (!ptr_ok(z) || !ptr_ok(seq_lens) || !ptr_ok(sel_count) || !ptr_ok(ws)) return RTP_EINVAL;
+  if (cap > 0 && !ptr_ok(sel_idx)) return RTP_EINVAL;
+  if (!opt_ptr_ok(hist) || !opt_ptr_ok(thresh)) return RTP_EINVAL;
+  const SelectPlan sp = plan_topp(B, H, Lmax, (int64_t)B * H);
+  if (ws_bytes < sp.bytes) return RTP_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const SelectBufs sb = bind_select(static_cast<char*>(ws), sp.offs);
+  hipError_t e = launch_hist_from_z(z, seq_lens, B, H, Lmax, bin_width, true, sp.cg, sb, st);
+  if (e == hipSuccess)
+    e = launch_threshold(seq_lens, B, H, Lmax, 1.0, k, bin_width, sp.cg, sb, hist, thresh,
+                         nullptr, 1, H, st);
   if (e == hipSuccess)
     e = launch_select(seq_lens, B, H, Lmax, sp.cg, sb, sel_idx, sel_count, cap, nullptr, nullptr,
                       1, H, st);
@@ -282,7 +310,8 @@ rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, v
   if (sp.Hret > 0) {
     if (!ptr_ok(d->q_idx) || !ptr_ok(d->K_ret) || !ptr_ok(d->V_ret) || !ptr_ok(d->k_idx))
       return RTP_EINVAL;
-    if (!(d->p > 0.0) || std::isnan(d->p) || !pow2_width(d->bin_width)) return RTP_EINVAL;
+    if (d->topk < 0 || !pow2_width(d->bin_width)) return RTP_EINVAL;
+    if (d->topk == 0 && (!(d->p > 0.0) || std::isnan(d->p))) return RTP_EINVAL;
   }
   if (sp.Hloc > 0 && (!ptr_ok(d->K_loc) || !ptr_ok(d->V_loc))) return RTP_EINVAL;
   if (ws_bytes < sp.bytes) return RTP_EWORKSPACE;
@@ -309,6 +338,7 @@ rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, v
     a.ret = sp.ret;
     a.loc = sp.loc;
     a.p = d->p;
+    a.topk = d->topk;
     a.bin_width = d->bin_width;
     a.scale_idx = d->scale_idx;
     a.scale_attn = d->scale_attn;
@@ -342,12 +372,12 @@ rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, v
     int32_t* sel_cnt = reinterpret_cast<int32_t*>(w + sp.sel_cnt);
     if (e == hipSuccess)
       e = launch_hist_from_kidx(d->q_idx, d->k_idx, d->kv_dtype, d->seq_lens, sp.ret, d->B,
-                                d->Hq, sp.Hret, G, d->Lmax, d->scale_idx, d->bin_width, sp.sel.cg,
-                                sb, st);
+                                d->Hq, sp.Hret, G, d->Lmax, d->scale_idx, d->bin_width,
+                                d->topk > 0, sp.sel.cg, sb, st);
     mark(1);
     if (e == hipSuccess)
-      e = launch_threshold(d->seq_lens, d->B, H, d->Lmax, d->p, d->bin_width, sp.sel.cg, sb,
-                           nullptr, d->thresh_out, &sp.ret, G, d->Hq, st);
+      e = launch_threshold(d->seq_lens, d->B, H, d->Lmax, d->p, d->topk, d->bin_width, sp.sel.cg,
+                           sb, nullptr, d->thresh_out, &sp.ret, G, d->Hq, st);
     mark(2);
     if (e == hipSuccess)
       e = launch_select(d->seq_lens, d->B, H, d->Lmax, sp.sel.cg, sb, sel_idx, sel_cnt, d->Lmax,

@@ -70,15 +70,19 @@ hipError_t launch_index_score(const float* q_idx, const void* k_idx, int k_dtype
 
 // Histogram partials; mode 0 reads logits z [B, H, Lmax], mode 1 computes them from
 // q_idx / k_idx (rows kr*G+g; q_idx head index map.kv[kr]*G+g of a [B, Hq, r] array).
+// counts: every token weighs one (fixed top-k) instead of its softmax mass.
 hipError_t launch_hist_from_z(const float* z, const int32_t* seq_lens, int B, int H, int Lmax,
-                              float bin_width, const ChunkGeom& cg, const SelectBufs& sb,
-                              hipStream_t st);
+                              float bin_width, bool counts, const ChunkGeom& cg,
+                              const SelectBufs& sb, hipStream_t st);
 hipError_t launch_hist_from_kidx(const float* q_idx, const void* k_idx, int k_dtype,
                                  const int32_t* seq_lens, const HeadMap& map, int B, int Hq,
                                  int Hr, int G, int Lmax, float scale_idx, float bin_width,
-                                 const ChunkGeom& cg, const SelectBufs& sb, hipStream_t st);
+                                 bool counts, const ChunkGeom& cg, const SelectBufs& sb,
+                                 hipStream_t st);
 
-hipError_t launch_threshold(const int32_t* seq_lens, int B, int H, int Lmax, double p,
+// b* per row: the least bin whose cumulative mass reaches p Z (topk == 0), or whose
+// cumulative count reaches topk (topk > 0, histograms built with counts = true).
+hipError_t launch_threshold(const int32_t* seq_lens, int B, int H, int Lmax, double p, int topk,
                             float bin_width, const ChunkGeom& cg, const SelectBufs& sb,
                             float* hist_out, int32_t* thresh_out, const HeadMap* out_map,
                             int G, int Hq, hipStream_t st);
@@ -147,6 +151,7 @@ struct StepFusedArgs {
   const void *K_ret, *V_ret, *k_idx, *K_loc, *V_loc;
   HeadMap ret, loc;
   double p;
+  int topk;  // > 0: fixed top-k (count bins) instead of top-p
   float bin_width, scale_idx, scale_attn;
   float* out;
   float* lse;

@@ -346,31 +346,36 @@ hipError_t launch_index_score(const float* q_idx, const void* k_idx, int k_dtype
 
 static constexpr double kLog2e = 1.4426950408889634;
 
+// With counts, the mass exponent is zero: every token adds exactly 2^24 to its bin and
+// the partial holds exact token counts (bins still come from the cells of width w).
 hipError_t launch_hist_from_z(const float* z, const int32_t* seq_lens, int B, int H, int Lmax,
-                              float bin_width, const ChunkGeom& cg, const SelectBufs& sb,
-                              hipStream_t st) {
+                              float bin_width, bool counts, const ChunkGeom& cg,
+                              const SelectBufs& sb, hipStream_t st) {
   HeadMap map{};
   dim3 grid(cg.nchunk, H, B);
   const float inv_w = 1.0f / bin_width;
-  const float c = (float)(bin_width * kLog2e);
+  const float c = counts ? 0.0f : (float)(bin_width * kLog2e);
+  const double wm = counts ? 0.0 : (double)bin_width;
   return hist_dispatch_tpt<0, float, 1>(grid, cg, st, z, nullptr, nullptr, seq_lens, map, H, H,
-                                        0, 1, Lmax, 1, 0.0f, inv_w, c, (double)bin_width, sb);
+                                        0, 1, Lmax, 1, 0.0f, inv_w, c, wm, sb);
 }
 
 hipError_t launch_hist_from_kidx(const float* q_idx, const void* k_idx, int k_dtype,
                                  const int32_t* seq_lens, const HeadMap& map, int B, int Hq,
                                  int Hr, int G, int Lmax, float scale_idx, float bin_width,
-                                 const ChunkGeom& cg, const SelectBufs& sb, hipStream_t st) {
+                                 bool counts, const ChunkGeom& cg, const SelectBufs& sb,
+                                 hipStream_t st) {
   const int GG = pick_gg(G);
   const int ngrp = (G + GG - 1) / GG;
   dim3 grid(cg.nchunk, Hr * ngrp, B);
   const float inv_w = 1.0f / bin_width;
   const float yscale = scale_idx * inv_w;
-  const float c = (float)(bin_width * kLog2e);
+  const float c = counts ? 0.0f : (float)(bin_width * kLog2e);
+  const double wm = counts ? 0.0 : (double)bin_width;
   const int H = Hr * G;
 #define RTP_HK(KT, GGV)                                                                        \
   hist_dispatch_tpt<1, KT, GGV>(grid, cg, st, nullptr, q_idx, k_idx, seq_lens, map, H, Hq, Hr, \
-                                G, Lmax, ngrp, yscale, inv_w, c, (double)bin_width, sb)
+                                G, Lmax, ngrp, yscale, inv_w, c, wm, sb)
   if (k_dtype == 1) {
     switch (GG) {
       case 8: return RTP_HK(f16, 8);

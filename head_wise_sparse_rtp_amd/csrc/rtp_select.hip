@@ -36,6 +36,7 @@ __device__ double block_sum(double v, double* red) {
 
 // Shift-merge `n` partials (anchor cells A[i], masses m[i*256 + j], either precision)
 // into the global anchor Ag.  Thread j returns global bin j (bin 255: the tail total).
+// w = 0 merges token counts: no decay with the shift, and no partial is too far down.
 template <typename MT>
 __device__ double shift_merge(const int32_t* sA, const MT* __restrict__ m, int n, int Ag,
                               double w, double* red) {
@@ -45,7 +46,7 @@ __device__ double shift_merge(const int32_t* sA, const MT* __restrict__ m, int n
     const int Ai = sA[i];
     if (Ai == kEmptyCell) continue;
     const long long s = (long long)Ag - (long long)Ai;
-    if (s > 4096) continue;  // exp(-s w) underflows for every supported w
+    if (w > 0.0 && s > 4096) continue;  // exp(-s w) underflows for every supported w
     const double f = exp(-(double)s * w);
     const MT* mi = m + (size_t)i * kNB;
     if (j < kNB - 1 && j - s >= 0) acc += (double)mi[j - s] * f;
@@ -80,10 +81,12 @@ __global__ __launch_bounds__(kThreads) void k_merge1(const float* __restrict__ p
   if (threadIdx.x == 0) mid_A[row * nsplit + split] = Ag;
 }
 
-// Second level: merge the first-level partials of one row, scan, find b*.
+// Second level: merge the first-level partials of one row, scan, find b*: the least
+// bin whose cumulative mass reaches p Z, or (topk > 0, count histograms) whose cumulative
+// count reaches topk; 255 when none does.
 __global__ __launch_bounds__(kThreads) void k_threshold(
     const double* __restrict__ mid_mass, const int32_t* __restrict__ mid_A, int nsplit,
-    double w, double p, int32_t* __restrict__ thr, float* __restrict__ hist_out,
+    double w, double p, int topk, int32_t* __restrict__ thr, float* __restrict__ hist_out,
     int32_t* __restrict__ thresh_out, HeadMap omap, int H, int G, int Hq, int use_map) {
   extern __shared__ int32_t sA[];  // nsplit entries
   __shared__ double red[kThreads];
@@ -127,10 +130,11 @@ __global__ __launch_bounds__(kThreads) void k_threshold(
   if (j == 0) bstar_s = kNB - 1;
   __syncthreads();
   const double Z = scan[kNB - 1];
-  if (p < 1.0) {
-    const bool reach = scan[j] >= p * Z;
-    const bool prev = j > 0 ? scan[j - 1] >= p * Z : false;
-    if (reach && !prev) bstar_s = j;  // cumulative mass is monotone: exactly one thread
+  if (topk > 0 || p < 1.0) {
+    const double target = topk > 0 ? (double)topk : p * Z;
+    const bool reach = scan[j] >= target;
+    const bool prev = j > 0 ? scan[j - 1] >= target : false;
+    if (reach && !prev) bstar_s = j;  // the cumulative sum is monotone: one thread at most
   }
   __syncthreads();
   if (hist_out) hist_out[orow * kNB + j] = (float)mu;
@@ -262,13 +266,13 @@ __global__ __launch_bounds__(kThreads) void k_select_write(
 
 }  // namespace
 
-hipError_t launch_threshold(const int32_t* seq_lens, int B, int H, int Lmax, double p,
+hipError_t launch_threshold(const int32_t* seq_lens, int B, int H, int Lmax, double p, int topk,
                             float bin_width, const ChunkGeom& cg, const SelectBufs& sb,
                             float* hist_out, int32_t* thresh_out, const HeadMap* out_map,
                             int G, int Hq, hipStream_t st) {
   (void)seq_lens;
   (void)Lmax;
-  const double w = (double)bin_width;
+  const double w = topk > 0 ? 0.0 : (double)bin_width;
   dim3 g1(cg.nsplit, B * H);
   k_merge1<<<g1, kThreads, 0, st>>>(sb.part_mass, sb.part_A, cg.nchunk, cg.nsplit, w,
                                     sb.mid_mass, sb.mid_A);
@@ -277,7 +281,7 @@ hipError_t launch_threshold(const int32_t* seq_lens, int B, int H, int Lmax, dou
   HeadMap m{};
   if (out_map) m = *out_map;
   k_threshold<<<B * H, kThreads, sizeof(int32_t) * cg.nsplit, st>>>(
-      sb.mid_mass, sb.mid_A, cg.nsplit, w, p, sb.thr, hist_out, thresh_out, m, H, G, Hq,
+      sb.mid_mass, sb.mid_A, cg.nsplit, w, p, topk, sb.thr, hist_out, thresh_out, m, H, G, Hq,
       out_map ? 1 : 0);
   return hipGetLastError();
 }

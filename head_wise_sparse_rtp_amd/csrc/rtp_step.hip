@@ -287,6 +287,10 @@ __device__ void block_combine(AttnState& st, int G, int nact, float* lds, float*
 // ---------------------------------------------------------------------------
 constexpr int kCopies = 4;  // histogram copies per head (lane bits 3..4)
 constexpr int kPad = 1;
+// y of a token past the sequence's end: finite and far below every cell, so that its
+// mass is exactly zero and it lands in the tail bin (with unit weights it is taken back
+// out of that bin after the pass)
+constexpr float kMaskY = -3.0e38f;
 
 struct StageAParams {
   const int32_t* seq_lens;
@@ -295,6 +299,7 @@ struct StageAParams {
   const f16* k_idx;
   HeadMap ret;
   int Hret, nchunk, ngg, nunits;
+  int counts;  // unit weight per token (fixed top-k); c_log2 is then 0
   float yscale, c_log2;
   double w;
   float* suf;
@@ -440,7 +445,7 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
 #pragma unroll
     for (int t = 0; t < 4; t++) {
       float v = d[t] * ysc;
-      if (!full && wbase + gi * 32 + 16 * th + 4 * kq + t >= L) v = -INFINITY;
+      if (!full && wbase + gi * 32 + 16 * th + 4 * kq + t >= L) v = kMaskY;
       y[gi][t] = v;
       ym = fmaxf(ym, v);
     }
@@ -463,7 +468,7 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
   // With m = max(g, A_c - 255) (the cell, or the deepest bin's cell for the tail):
   //   bin j = A_c - m,  x = 2^((y - m - 1) c),  c = w log2(e).
   // y - m is exact (it is fract(y) unless the token is in the tail) and a token past the
-  // end (y = -inf) lands in bin 255 with zero mass.
+  // end (y = kMaskY) lands in bin 255 with zero mass.  With c = 0 every token adds 2^22.
   const float c = P.c_log2;
   const float Kt = Acf - 255.0f;
   const float c22 = 22.0f - c;  // x * 2^22 = 2^((y - m - 1) c + 22)
@@ -504,6 +509,7 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
   // jb..jb+3, jb = 4*(63-k), so a prefix scan over the lanes gives suffix sums (fp32:
   // every sum is a tree of at most ten roundings)
   const int jb = 4 * (63 - lane);
+  const int ninv = full ? 0 : base + TC - L;  // tokens past the end, all in bin 255
   float fj[4];
 #pragma unroll
   for (int u = 0; u < 4; u++) fj[u] = __builtin_amdgcn_exp2f(-(float)(jb + u) * c) * 2.384185791015625e-07f;
@@ -514,6 +520,7 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
       unsigned long long sum = 0ull;
 #pragma unroll
       for (int cp = 0; cp < kCopies; cp++) sum += hist[(cp * GG + gg) * (kNB + kPad) + jb + u];
+      if (P.counts && jb + u == kNB - 1) sum -= (unsigned long long)ninv << 22;
       const float sf = __builtin_fmaf((float)(uint32_t)(sum >> 32), 4294967296.0f, (float)(uint32_t)sum);
       mloc[u] = sf * fj[u];
     }
@@ -637,6 +644,7 @@ struct StageTParams {
   const float* suf;
   const int32_t* partA;
   int nchunk, cpb, nseg;
+  int maxshift;  // chunks more than this many cells below the top add nothing (masses)
   float c_log2;
   unsigned long long* sufq;
   int32_t* Aglob;
@@ -695,7 +703,7 @@ __global__ __launch_bounds__(kThreads) void k_stage_t(StageTParams P) {
     int sh[8];
 #pragma unroll
     for (int u = 0; u < 8; u++)  // no token, or mass below the fp32 range: no contribution (-1)
-      sh[u] = (ac[u] != kEmptyCell && ac[u] >= A - 4096) ? A - ac[u] : -1;
+      sh[u] = (ac[u] != kEmptyCell && A - ac[u] <= P.maxshift) ? A - ac[u] : -1;
     float x[8];
 #pragma unroll
     for (int u = 0; u < 8; u++) x[u] = sb[min(cc + u, nc - 1) * kNB + max(j - max(sh[u], 0), 0)];
@@ -716,6 +724,7 @@ struct StageBParams {
   const int32_t* seq_lens;
   int B, Hq, G, Lmax, Hret, nchunk, tc, nblk, nparts;
   double p;
+  int topk;  // > 0: b* from token counts (fixed top-k) instead of masses
   const f16* q;
   const f16* K_ret;
   const f16* V_ret;
@@ -793,7 +802,7 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
     zv[u] = 0ull;
 #pragma unroll
     for (int k = 0; k < 4; k++) sv[u][k] = 0ull;
-    if (g < G && P.p < 1.0) {
+    if (g < G && (P.topk > 0 || P.p < 1.0)) {
       const unsigned long long* sp = P.sufq + (row0 + g) * kNB;
       zv[u] = sp[0];
 #pragma unroll
@@ -823,14 +832,15 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
     }
   }
   if (tid < kAttnG) s_cnt[tid] = 0;
-  // b*: least J < 255 with Z - SUF_{J+1} >= p Z, else 255
+  // b*: least J < 255 with Z - SUF_{J+1} >= p Z (top-k: >= k tokens), else 255
 #pragma unroll
   for (int u = 0; u < HPW; u++) {
     const int g = wv + u * kBWaves;
     if (g < G) {
       int J = kNB - 1;
-      if (P.p < 1.0) {
-        const double pz = P.p * (double)zv[u];
+      if (P.topk > 0 || P.p < 1.0) {
+        // the table counts in units of 2^-38 of a token (exact for every count)
+        const double pz = P.topk > 0 ? (double)P.topk * kSufOne : P.p * (double)zv[u];
 #pragma unroll
         for (int k = 3; k >= 0; k--) {
           const int Jk = 4 * lane + k;
@@ -1240,7 +1250,8 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     if (ev && ev[i]) (void)hipEventRecord(ev[i], st);
   };
   const float scale2 = a.scale_attn * 1.4426950408889634f;
-  const float c_log2 = (float)((double)a.bin_width * 1.4426950408889634);
+  // top-k weighs every token one: a zero exponent turns the bin masses into counts
+  const float c_log2 = a.topk > 0 ? 0.0f : (float)((double)a.bin_width * 1.4426950408889634);
   hipError_t e = hipSuccess;
   rec(0);
   // ---- K1: indexer score + chunk histograms
@@ -1260,6 +1271,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     P.ngg = (G + GG - 1) / GG;
     P.yscale = a.scale_idx / a.bin_width;
     P.c_log2 = c_log2;
+    P.counts = a.topk > 0 ? 1 : 0;
     P.w = (double)a.bin_width;
     P.suf = at<float>(ws, sp.suf);
     P.partA = at<int32_t>(ws, sp.partA);
@@ -1287,6 +1299,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     T.partA = P.partA;
     T.nchunk = sp.nchunk;
     T.cpb = sp.tcpb;
+    T.maxshift = a.topk > 0 ? INT_MAX : 4096;
     T.nseg = sp.tseg;
     T.c_log2 = c_log2;
     T.sufq = P.sufq;
@@ -1320,6 +1333,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     Q.nblk = sp.nblk;
     Q.nparts = sp.nparts;
     Q.p = a.p;
+    Q.topk = a.topk;
     Q.q = static_cast<const f16*>(a.q);
     Q.K_ret = static_cast<const f16*>(a.K_ret);
     Q.V_ret = static_cast<const f16*>(a.V_ret);

@@ -7,7 +7,8 @@
  * top-p set of tokens chosen through a 256-bin histogram without sorting, and run
  * exact softmax attention over that set; local heads attend over a sliding window
  * plus sink tokens (section 五, test-configuration table: window 8192, 4 sinks,
- * indexer size 16, p = 0.9, 15% retrieval heads).
+ * indexer size 16, p = 0.9, 15% retrieval heads).  A fixed top-k budget through the
+ * same histogram (section 三, insight 3) is offered beside top-p.
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer to a dense row-major array whose
@@ -40,7 +41,7 @@
 extern "C" {
 #endif
 
-#define RTP_ABI_VERSION 1
+#define RTP_ABI_VERSION 2
 
 typedef int32_t rtp_status;
 enum {
@@ -99,6 +100,25 @@ rtp_status rtp_topp_select(const float* z, const int32_t* seq_lens, int32_t B, i
                            void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Fixed top-k through the same histogram (section 三, insight 3 and its top-k vs top-p
+ * table: fixed token budgets set against top-p).  The bins are those of rtp_topp_select;
+ * every token weighs one instead of its softmax mass:
+ *     c_j = #{ n < L : j_n = j }
+ *     b* = the least j with c_0 + ... + c_j >= k, or 255 when L < k
+ *     S = { n : j_n <= b* }  (ascending)
+ * S holds at least min(k, L) tokens, including every token whose logit is at least the
+ * k-th largest.  Counts are exact, so the result depends on z only through the cells.
+ *   k        >= 1 (RTP_EINVAL otherwise)
+ *   hist     [B, H, 256] fp32 out or NULL: c_j
+ * Every other argument, the workspace size and the outputs are those of rtp_topp_select.
+ */
+size_t rtp_topk_select_workspace_size(int32_t B, int32_t H, int32_t Lmax);
+rtp_status rtp_topk_select(const float* z, const int32_t* seq_lens, int32_t B, int32_t H,
+                           int32_t Lmax, int32_t k, float bin_width, int32_t* sel_idx,
+                           int32_t* sel_count, int32_t cap, float* hist, int32_t* thresh,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Exact softmax attention over a selected token set (section 三, 核心公式, the
  * sparse-attention equation):
  *     O[b,h] = sum_{n in S} exp(s_n - m) V[b,kr,n] / sum_{n in S} exp(s_n - m),
@@ -151,7 +171,7 @@ typedef struct {
   const void* K_loc;              /* [B, Hloc, sinks + window, d] ring (see rtp_window_decode) */
   const void* V_loc;              /* [B, Hloc, sinks + window, d] */
   const int32_t* seq_lens;        /* [B] device */
-  double p;                       /* top-p mass in (0, 1] */
+  double p;                       /* top-p mass in (0, 1]; ignored when topk > 0 */
   float bin_width, scale_idx, scale_attn;
   float* out;                     /* [B, Hq, d] fp32 out */
   float* lse;                     /* [B, Hq] fp32 out or NULL */
@@ -162,13 +182,15 @@ typedef struct {
    * suffix-table (threshold) kernel, [3] after the last kernel.  [4..7] are reserved
    * and must be NULL. */
   void* prof_ev[8];
+  int32_t topk;                   /* 0: top-p with p; > 0: fixed top-k (rtp_topk_select's rule)
+                                   * for every retrieval query head; < 0: RTP_EINVAL */
 } rtp_layer_desc;
 
 /* fp16 caches with G <= 16 run four kernels per call: indexer score + chunk histograms;
- * per-head suffix tables of the bin masses; selection + sparse attention together with
- * the window attention of local heads; merge of the split partials.  Other shapes run
- * the single-purpose kernels in sequence.  The workspace needs no initialisation; calls
- * that may overlap must not share one. */
+ * per-head suffix tables of the bin masses (token counts under top-k); selection +
+ * sparse attention together with the window attention of local heads; merge of the
+ * split partials.  Other shapes run the single-purpose kernels in sequence.  The
+ * workspace needs no initialisation; calls that may overlap must not share one. */
 size_t rtp_decode_step_workspace_size(const rtp_layer_desc* desc);
 rtp_status rtp_decode_step(const rtp_layer_desc* desc, void* ws, size_t ws_bytes, void* stream);
 

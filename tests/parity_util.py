@@ -7,6 +7,8 @@ Selection (256-bin histogram top-p):
     cumulative mass at the disputed bin lies within 1e-5 Z of p Z;
   * the selected set must equal the oracle rule's set under the GPU's (A, b*), except
     for tokens whose logit lies within 1e-5 relative of a bin edge.
+Selection (fixed top-k through the same histogram): counts are exact, so b* must match
+unless tokens in the edge band could move the cumulative count across k ("count tie").
 Outputs: max |O_gpu - O_oracle| <= 2e-3 (fp16 K/V) or 1e-5 (fp32 K/V).
 """
 from __future__ import annotations
@@ -40,6 +42,17 @@ def mass_tie(sel: oracle.Selection, b_gpu: int, p: float) -> bool:
     return False
 
 
+def count_tie(z, sel: oracle.Selection, b_gpu: int, k: int, w: float) -> bool:
+    """A different b* under top-k is explained only by edge-band tokens: the oracle's
+    cumulative count at the lower of the two bins lies within that many tokens of k."""
+    n_amb = int(edge_ambiguous(z, w).sum())
+    if n_amb == 0:
+        return False
+    C = np.cumsum(sel.hist)
+    lo = min(b_gpu, sel.bstar)
+    return abs(C[lo] - k) <= n_amb
+
+
 class SelCheck:
     def __init__(self):
         self.mass_ties = 0
@@ -48,16 +61,18 @@ class SelCheck:
 
 
 def expected_set(z, sel: oracle.Selection, A_gpu: int, b_gpu: int, p: float, w: float,
-                 stats: SelCheck, where: str) -> np.ndarray:
-    """Validate (A, b*) from the GPU and return the oracle rule's set under them."""
+                 stats: SelCheck, where: str, topk: int = 0) -> np.ndarray:
+    """Validate (A, b*) from the GPU and return the oracle rule's set under them
+    (top-p with p, or the fixed top-k rule when topk > 0)."""
     stats.rows += 1
     if A_gpu != sel.A:
         zmax_edge = edge_ambiguous(np.array([np.max(z)]), w)[0]
         assert abs(A_gpu - sel.A) == 1 and zmax_edge, \
             "%s: top cell %d != oracle %d" % (where, A_gpu, sel.A)
     if b_gpu != sel.bstar:
-        assert mass_tie(sel, b_gpu, p), "%s: b* %d != oracle %d (no mass tie)" % (
-            where, b_gpu, sel.bstar)
+        ok = count_tie(z, sel, b_gpu, topk, w) if topk > 0 else mass_tie(sel, b_gpu, p)
+        assert ok, "%s: b* %d != oracle %d (no %s tie)" % (where, b_gpu, sel.bstar,
+                                                          "count" if topk > 0 else "mass")
         stats.mass_ties += 1
     if A_gpu == sel.A and b_gpu == sel.bstar:
         return sel.idx

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.rtp_abi_version() == 1
+    assert lib.rtp_abi_version() == 2
     for code in [0, -1, -2, -3, -4]:
         assert lib.rtp_status_string(code).startswith(b"RTP_")
     assert lib.rtp_status_string(7) == b"unknown rtp_status"
@@ -88,6 +88,44 @@ def test_topp_select_validation_and_workspace(lib):
     assert call(z=None) == -1
 
 
+def test_topk_select_validation_and_workspace(lib):
+    f = lib.rtp_topk_select
+    nb = lib.rtp_topk_select_workspace_size(2, 8, 100000)
+    assert nb == lib.rtp_topp_select_workspace_size(2, 8, 100000)
+    ok = [FAKE, FAKE, 2, 8, 100000, 2048, 0.125, FAKE, FAKE, 100000, None, None, FAKE, nb, None]
+    names = ["z", "sl", "B", "H", "Lmax", "k", "w", "si", "sc", "cap", "hist", "thr", "ws", "wsb",
+             "st"]
+
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(k=0) == -1
+    assert call(k=-5) == -1
+    assert call(w=0.3) == -1
+    assert call(wsb=nb - 1) == -3
+    assert call(thr=MIS) == -1
+    assert call(sc=None) == -1
+    assert call(Lmax=(1 << 24) + 1) == -2
+
+
+def test_layer_desc_matches_the_header():
+    import head_wise_sparse_rtp_amd as m
+    # the ctypes mirror lists the header's fields in the header's order
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{(.*?)\} rtp_layer_desc;", src, re.S).group(1)
+    names = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        for part in decl.split(","):
+            names.append(re.findall(r"(\w+)\s*(?:\[\d+\])?\s*$", part.strip())[0])
+    assert names == [f[0] for f in m.LayerDesc._fields_]
+
+
 def test_sparse_and_window_validation(lib):
     nb = lib.rtp_sparse_decode_workspace_size(1, 1, 8, 4096)
     assert nb > 0
@@ -129,6 +167,11 @@ def test_decode_step_validation(lib):
     d.r = 16
     d.p = -1.0
     assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nb, None) == -1
+    d.topk = 64                         # top-k: same workspace, p not consulted
+    assert lib.rtp_decode_step_workspace_size(ctypes.byref(d)) == nb
+    d.topk = -1
+    assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nb, None) == -1
+    d.topk = 0
     d.p = 0.9
     d.k_idx = None
     assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nb, None) == -1

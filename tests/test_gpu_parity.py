@@ -118,6 +118,41 @@ def test_topp_select_matches_oracle(rtp, p, lens):
     say("mass ties", st.mass_ties, "edge tokens", st.edge_tokens)
 
 
+@pytest.mark.parametrize("k", [1, 3, 100, 4096, 100000])
+@pytest.mark.parametrize("lens", [[9000, 1, 2, 4097, 2048, 12345, 3, 777], [70000, 70000]])
+def test_topk_select_bit_exact(rtp, k, lens):
+    """Fixed top-k through the histogram: cells come from the same z on both sides and
+    the counts are exact, so A, b*, the counts and the set must match exactly."""
+    say("topk_select", k, lens)
+    Lmax = max(lens)
+    H = len(lens)
+    zr = _logit_rows(71 + len(lens), Lmax, lens)
+    z = torch.from_numpy(zr).view(H, 1, Lmax).to(dev())
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev())
+    sel_idx, cnt, hist, thr = rtp.rtp_topk_select(z, sl, k)
+    sel_idx, cnt, hist, thr = (t.cpu().numpy() for t in (sel_idx, cnt, hist, thr))
+    for i, L in enumerate(lens):
+        so = oracle.topk_select(zr[i, :L], k)
+        where = "row %d L=%d k=%d" % (i, L, k)
+        assert int(thr[i, 0, 0]) == so.A and int(thr[i, 0, 1]) == so.bstar, where
+        assert np.array_equal(hist[i, 0].astype(np.float64), so.hist), where
+        n = int(cnt[i, 0])
+        assert np.array_equal(sel_idx[i, 0, :n], so.idx), where
+
+
+def test_topk_select_empty_and_capped(rtp):
+    say("topk_select empty/capped")
+    zr = _logit_rows(6, 5000, [1, 5000])
+    z = torch.from_numpy(zr).view(2, 1, 5000).to(dev())
+    sl = torch.tensor([0, 5000], dtype=torch.int32, device=dev())
+    so = oracle.topk_select(zr[1], 1000)
+    sel_idx, cnt, hist, thr = rtp.rtp_topk_select(z, sl, 1000, cap=100)
+    cnt = cnt.cpu().numpy()
+    assert cnt[0, 0] == 0 and cnt[1, 0] == so.count
+    assert np.array_equal(sel_idx.cpu().numpy()[1, 0], so.idx[:100])
+    assert np.all(hist.cpu().numpy()[0] == 0)
+
+
 def test_topp_select_empty_and_capped(rtp):
     say("topp_select empty/capped")
     lens = [0, 5000]
@@ -224,13 +259,14 @@ def check_decode(rtp, wl, local_sample=None, layers=None, label=""):
             ret_q = [kh * wl.G + g for kh in layer.ret_heads for g in range(wl.G)]
             heads = ret_q + loc_q
         orc = oracle.decode_layer(layer, wl.seq_lens, wl.Hq, wl.Hkv, wl.p, wl.bin_width,
-                                  wl.scale_idx, wl.scale_attn, wl.window, wl.sinks, heads=heads)
+                                  wl.scale_idx, wl.scale_attn, wl.window, wl.sinks, heads=heads,
+                                  topk=wl.topk)
         for (b, h), r in orc.items():
             where = "%s layer %d b %d head %d" % (label, li, b, h)
             o_ref = r.out
             if r.sel is not None:
                 A, bs = int(thr[b, h, 0]), int(thr[b, h, 1])
-                ex = expected_set(r.z, r.sel, A, bs, wl.p, wl.bin_width, st, where)
+                ex = expected_set(r.z, r.sel, A, bs, wl.p, wl.bin_width, st, where, wl.topk)
                 compare_count(int(cnt[b, h]), ex, r.z, wl.bin_width, A, bs, st, where)
                 if ex is not r.sel.idx:
                     kr = layer.ret_heads.index(h // wl.G)
@@ -264,6 +300,32 @@ def test_decode_step_heads_per_kv(rtp, G):
     wl = workloads.make_workload("t", 3, [5000, 1, 2300], 3 * G, 3, [[1, 0, 1]], seed=70 + G,
                                  p=0.9, dtype="f16", window=384, sinks=4, device=dev())
     check_decode(rtp, wl, label="G%d" % G)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("k", [1, 64, 3000, 5000])
+def test_decode_step_topk_small_ragged(rtp, dtype, k):
+    """Fixed top-k on the fused path (f16) and on the single-purpose kernels (f32); k =
+    5000 exceeds every sequence, so every token is kept."""
+    say("decode_step topk small", dtype, k)
+    wl = workloads.make_workload("t", 3, [3000, 1, 4099], 32, 4, [[1, 0, 1, 0]], seed=65,
+                                 dtype=dtype, window=256, sinks=4, device=dev())
+    wl.topk = k
+    res = check_decode(rtp, wl, label="topk-%s-k%d" % (dtype, k))
+    cnt = res[0][3].cpu().numpy()
+    for b, L in enumerate([3000, 1, 4099]):
+        for h in list(range(8)) + list(range(16, 24)):
+            assert cnt[b, h] >= min(k, L)
+            if k >= L:
+                assert cnt[b, h] == L
+
+
+@pytest.mark.parametrize("name,k", [("c1", 2048), ("c4", 2048), ("c4", 16384)])
+def test_decode_step_topk_config(rtp, name, k):
+    say("config", name, "topk", k)
+    wl = workloads.make_config(name, device=dev())
+    wl.topk = k
+    check_decode(rtp, wl, label="%s-topk%d" % (name, k))
 
 
 def test_decode_step_p1_is_dense_attention(rtp):
