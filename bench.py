@@ -58,23 +58,29 @@ def elapsed_ms(h, a, b):
     return ms.value
 
 
-def algorithmic_bytes(rtp, wl, layer, torch):
+def algorithmic_bytes(rtp, wl, layer, torch, topk=0):
     """Realised bytes of one step: the union of the selected sets per retrieval KV head
-    comes from the GPU selection (the same rule the step runs)."""
+    comes from the GPU selection (the same rule the step runs: top-p, or the fixed top-k
+    when topk > 0).  Also returns, per retrieval query head, the share of the indexer
+    softmax mass that its selected set holds (outside any timed region)."""
     dev = layer.q.device
     sl = torch.as_tensor(wl.seq_lens, dtype=torch.int32, device=dev)
     e_idx = 2 if wl.dtype == "f16" else 4
     e_kv = e_idx
     total = 0
-    detail = {"kidx": 0, "sparse_kv": 0, "window_kv": 0, "union_tokens": 0, "sel_tokens": []}
+    detail = {"kidx": 0, "sparse_kv": 0, "window_kv": 0, "union_tokens": 0, "sel_tokens": [],
+              "sel_mass": []}
     G = wl.G
     ret = layer.ret_heads
     if ret:
         qi = torch.stack([layer.q_idx[:, h * G:(h + 1) * G] for h in ret], 1).reshape(
             wl.B, len(ret) * G, wl.r).contiguous()
         z = rtp.rtp_index_score(qi, layer.k_idx, sl, wl.scale_idx)
-        sel, cnt, _, _ = rtp.rtp_topp_select(z, sl, wl.p, wl.bin_width, want_hist=False)
-        sel, cnt = sel.cpu(), cnt.cpu()
+        if topk > 0:
+            sel, cnt, _, _ = rtp.rtp_topk_select(z, sl, topk, wl.bin_width, want_hist=False)
+        else:
+            sel, cnt, _, _ = rtp.rtp_topp_select(z, sl, wl.p, wl.bin_width, want_hist=False)
+        zc, sel, cnt = z.double().cpu(), sel.cpu(), cnt.cpu()
         for b in range(wl.B):
             L = int(wl.seq_lens[b])
             for k in range(len(ret)):
@@ -82,7 +88,11 @@ def algorithmic_bytes(rtp, wl, layer, torch):
                 for g in range(G):
                     n = int(cnt[b, k * G + g])
                     detail["sel_tokens"].append(n)
-                    u.update(sel[b, k * G + g, :n].tolist())
+                    idx = sel[b, k * G + g, :n].long()
+                    zz = zc[b, k * G + g, :L]
+                    e = torch.exp(zz - zz.max())
+                    detail["sel_mass"].append(round(float(e[idx].sum() / e.sum()), 4))
+                    u.update(idx.tolist())
                 detail["kidx"] += L * wl.r * e_idx
                 detail["sparse_kv"] += len(u) * 2 * wl.d * e_kv
                 detail["union_tokens"] += len(u)
@@ -189,6 +199,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4")
     ap.add_argument("--p", type=float, default=None)
+    ap.add_argument("--topk", type=int, default=0,
+                    help="fixed top-k through the histogram instead of top-p")
     ap.add_argument("--rotations", type=int, default=0)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -220,7 +232,7 @@ def main():
     wl = workloads.make_config(args.workload, device=dev, **kw)
     assert len(wl.layers) == 1, "bench.py times single-layer workloads"
     layer = wl.layers[0]
-    bytes_step, detail = algorithmic_bytes(rtp, wl, layer, torch)
+    bytes_step, detail = algorithmic_bytes(rtp, wl, layer, torch, args.topk)
     touched = max(bytes_step, 1)
     R = args.rotations or max(1, math.ceil(512 * 2 ** 20 / touched))
     sl = torch.as_tensor(wl.seq_lens, dtype=torch.int32, device=dev)
@@ -237,7 +249,7 @@ def main():
     for lay in layers:
         st = rtp.DecodeStep(lay, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window, wl.sinks, wl.p,
                             wl.bin_width, wl.scale_idx, wl.scale_attn, out=out, want_lse=False,
-                            ws=ws)
+                            ws=ws, topk=args.topk)
         ws, out = st.ws, st.out
         steps.append(st)
     torch.cuda.synchronize()
@@ -328,18 +340,20 @@ def main():
         "dtype": "f16 K/V, fp32 accumulation",
         "data": "synthetic (seeded planted-logit indexer keys, counter-based N(0,1) K/V)",
         "config": {"workload": "%s: B=%d, L=%d, Hq=%d, Hkv=%d (retrieval %s), d=%d, r=%d, "
-                               "window=%d+%d sinks, p=%g" % (
+                               "window=%d+%d sinks, %s" % (
                                    args.workload, wl.B, int(wl.seq_lens.max()), wl.Hq, wl.Hkv,
-                                   layer.ret_heads, wl.d, wl.r, wl.window, wl.sinks, wl.p),
+                                   layer.ret_heads, wl.d, wl.r, wl.window, wl.sinks,
+                                   "top-k k=%d" % args.topk if args.topk else "p=%g" % wl.p),
                    "global_batch": wl.B, "seq_len": int(wl.seq_lens.max()),
                    "parallelism": "single GPU", "graph": g_full is not None, "rotations": R},
         "bytes_per_step": bytes_step,
-        "bytes_detail": {k: v for k, v in detail.items() if k != "sel_tokens"},
+        "bytes_detail": {k: v for k, v in detail.items() if k not in ("sel_tokens", "sel_mass")},
         "sel_tokens_per_head": detail["sel_tokens"],
+        "sel_mass_per_head": detail["sel_mass"],
         "roofline": {"kernel": "k_stage_a (indexer score on MFMA + 256-bin chunk histograms)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(args.workload),
+                     "traffic": None if args.topk else measured_traffic(args.workload),
                      "avg_us": round(a_us, 3), "algorithmic_bytes_per_launch": a_bytes},
         "phases_us": {k: round(v, 3) for k, v in ph.items()},
     }
