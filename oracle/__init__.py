@@ -66,6 +66,8 @@ def lib():
         L.rtpo_topk_select.restype = ctypes.c_int64
         L.rtpo_topk_select.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_double, P, P,
                                        P, P]
+        L.rtpo_project.restype = None
+        L.rtpo_project.argtypes = [P, P, ctypes.c_int, ctypes.c_int, P]
         L.rtpo_attention.restype = None
         L.rtpo_attention.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int64,
                                      ctypes.c_double, P, P]
@@ -148,6 +150,59 @@ def topk_select(z, k: int, bin_width: float = 0.125) -> Selection:
     n = lib().rtpo_topk_select(_ptr(zz), L, int(k), float(bin_width), _ptr(sel), _ptr(hist),
                                ctypes.byref(A), ctypes.byref(b))
     return Selection(sel[:n].copy(), hist, int(A.value), int(b.value))
+
+
+def project(x, W) -> np.ndarray:
+    """Indexer projection of one pre-RoPE vector x [d] by W [d, r]: an fp32 fma chain
+    over the d inputs in order, per output feature (see rtp_oracle.c)."""
+    xx = np.ascontiguousarray(x, dtype=np.float32)
+    WW = np.ascontiguousarray(W, dtype=np.float32)
+    d, r = WW.shape
+    assert xx.shape == (d,)
+    out = np.empty(r, dtype=np.float32)
+    lib().rtpo_project(_ptr(xx), _ptr(WW), d, r, _ptr(out))
+    return out
+
+
+def append_project(layer, new_lens, q_pre, k_pre, k_new, v_new, Wq, Wk, window: int,
+                   sinks: int):
+    """One decode step's cache update, on numpy copies of a layer's arrays.
+
+    Per sequence b whose length after the step is L = new_lens[b] >= 1 (the new token
+    sits at position n = L - 1):
+      * q_idx[b, h] = project(q_pre[b, h], Wq[h]) for every query head of a retrieval KV
+        head (other rows keep their values);
+      * retrieval KV head kr: k_idx[b, kr, n] = fl16(project(k_pre[b, kv], Wk[kr])) in
+        the cache's dtype, K_ret/V_ret[b, kr, n] = k_new/v_new[b, kv];
+      * local KV head: K_loc/V_loc[b, kl, ring_slot(n)] = k_new/v_new[b, kv].
+    Returns the updated (q_idx, k_idx, K_ret, V_ret, K_loc, V_loc)."""
+    mask = np.asarray(layer.kv_is_retrieval)
+    ret = [int(h) for h in np.nonzero(mask)[0]]
+    loc = [int(h) for h in np.nonzero(mask == 0)[0]]
+    q_idx, k_idx = np_of(layer.q_idx).copy(), np_of(layer.k_idx).copy()
+    K_ret, V_ret = np_of(layer.K_ret).copy(), np_of(layer.V_ret).copy()
+    K_loc, V_loc = np_of(layer.K_loc).copy(), np_of(layer.V_loc).copy()
+    q_pre, k_pre = np_of(q_pre), np_of(k_pre)
+    k_new, v_new = np_of(k_new), np_of(v_new)
+    Wq, Wk = np_of(Wq), np_of(Wk)
+    Hkv = mask.shape[0]
+    G = q_idx.shape[1] // Hkv
+    for b, L in enumerate(np.asarray(new_lens).tolist()):
+        if L < 1:
+            continue
+        n = L - 1
+        for kr, kv in enumerate(ret):
+            for g in range(G):
+                h = kv * G + g
+                q_idx[b, h] = project(q_pre[b, h], Wq[h])
+            k_idx[b, kr, n] = project(k_pre[b, kv], Wk[kr]).astype(k_idx.dtype)
+            K_ret[b, kr, n] = k_new[b, kv]
+            V_ret[b, kr, n] = v_new[b, kv]
+        for kl, kv in enumerate(loc):
+            slot = int(ring_slot(np.array([n]), window, sinks)[0])
+            K_loc[b, kl, slot] = k_new[b, kv]
+            V_loc[b, kl, slot] = v_new[b, kv]
+    return q_idx, k_idx, K_ret, V_ret, K_loc, V_loc
 
 
 def cells(z, bin_width: float = 0.125) -> np.ndarray:

@@ -75,6 +75,19 @@ void rtpo_index_score(const float* q_idx, const void* k_idx, int k_dtype, int64_
   }
 }
 
+/* Indexer projection of one head's pre-RoPE feature vector (section 三, 核心公式: the
+ * indexer compares W^Q_h q^pre with W^K_h k^pre, projected to r dims before RoPE).
+ * W is stored [d][r] (column i maps x to feature i):
+ *   out[i] = fp32 fused-multiply-add chain over c = 0..d-1, starting from +0:
+ *            a <- fmaf(x[c], W[c][i], a)                                          */
+void rtpo_project(const float* x, const float* W, int d, int r, float* out) {
+  for (int i = 0; i < r; i++) {
+    float a = 0.0f;
+    for (int c = 0; c < d; c++) a = fmaf(x[c], W[c * r + i], a);
+    out[i] = a;
+  }
+}
+
 /* Cell of a logit on the global grid of width w (w a power of two). */
 static int64_t cell_of(float z, double w) { return (int64_t)floor((double)z / w); }
 

@@ -454,3 +454,101 @@ def test_topk_permutation_and_cell_shift(name, z):
         if np.array_equal(np.floor(z.astype(np.float64) / 0.125) + 3,
                           np.floor((z.astype(np.float64) + 0.375).astype(np.float32) / 0.125)):
             assert np.array_equal(sh.idx, s.idx) and sh.A == s.A + 3
+
+
+# ---------------------------------------------------------------------------
+# indexer projection and the cache append of a decode step
+# ---------------------------------------------------------------------------
+def test_project_exact_on_small_integers():
+    rng = np.random.default_rng(11)
+    x = rng.integers(-8, 8, 128).astype(np.float32)
+    W = rng.integers(-8, 8, (128, 16)).astype(np.float32)
+    want = x.astype(np.int64) @ W.astype(np.int64)
+    assert np.array_equal(oracle.project(x, W), want.astype(np.float32))
+
+
+def test_project_each_input_counts_once():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal(128).astype(np.float32)
+    W = rng.standard_normal((128, 16)).astype(np.float32)
+    for c in [0, 1, 63, 127]:
+        e = np.zeros(128, dtype=np.float32)
+        e[c] = 1.0
+        assert np.array_equal(oracle.project(e, W), W[c])
+        U = np.zeros((128, 16), dtype=np.float32)
+        U[c, 5] = 1.0
+        out = oracle.project(x, U)
+        assert out[5] == x[c] and np.all(np.delete(out, 5) == 0)
+
+
+def test_project_follows_the_left_to_right_chain():
+    # in the prescribed order 1e8 + 1 rounds back to 1e8 before -1e8 cancels it: 0; any
+    # order that cancels the large terms first would give 1
+    x = np.array([1e8, 1.0, -1e8], dtype=np.float32)
+    W = np.ones((3, 1), dtype=np.float32)
+    assert oracle.project(x, W)[0] == 0.0
+    assert oracle.project(x[[0, 2, 1]], W)[0] == 1.0
+
+
+def test_project_within_fma_chain_error_bound():
+    rng = np.random.default_rng(13)
+    u = 2.0 ** -24
+    for _ in range(20):
+        x = rng.standard_normal(128).astype(np.float32)
+        W = (rng.standard_normal((128, 16)) / math.sqrt(128)).astype(np.float32)
+        exact = x.astype(np.float64) @ W.astype(np.float64)
+        bound = 128 * u / (1 - 128 * u) * (np.abs(x).astype(np.float64) @ np.abs(W).astype(np.float64))
+        assert np.all(np.abs(oracle.project(x, W) - exact) <= bound)
+
+
+class _Lay:
+    def __init__(self, mask, q_idx, k_idx, K_ret, V_ret, K_loc, V_loc):
+        self.kv_is_retrieval = np.asarray(mask, dtype=np.uint8)
+        self.q_idx, self.k_idx, self.K_ret, self.V_ret = q_idx, k_idx, K_ret, V_ret
+        self.K_loc, self.V_loc = K_loc, V_loc
+
+
+def test_append_places_rows_and_rounds_to_half():
+    B, Hkv, G, d, r, Lmax, window, sinks = 2, 2, 2, 1, 1, 12, 6, 2
+    lay = _Lay([1, 0], np.full((B, Hkv * G, r), 7.0, np.float32),
+               np.zeros((B, 1, Lmax, r), np.float16), np.zeros((B, 1, Lmax, d), np.float16),
+               np.zeros((B, 1, Lmax, d), np.float16), np.zeros((B, 1, window + sinks, d), np.float16),
+               np.zeros((B, 1, window + sinks, d), np.float16))
+    q_pre = np.ones((B, Hkv * G, d), np.float32)
+    k_pre = np.ones((B, Hkv, d), np.float32)
+    k_new = np.array([[[1.5], [2.5]], [[3.5], [4.5]]], np.float16)
+    v_new = -k_new
+    # 1 + 2^-11 lies halfway between fp16 1 and 1 + 2^-10: ties to even give 1;
+    # 1 + 3 * 2^-11 lies halfway between 1 + 2^-10 and 1 + 2^-9: ties to even give 1 + 2^-9
+    Wq = np.array([[[0.5]], [[0.25]], [[9.0]], [[9.0]]], np.float32)
+    for wk, want in [(1 + 2 ** -11, 1.0), (1 + 3 * 2 ** -11, 1 + 2 ** -9)]:
+        Wk = np.array([[[wk]]], np.float32)
+        q_idx, k_idx, K_ret, V_ret, K_loc, V_loc = oracle.append_project(
+            lay, [10, 0], q_pre, k_pre, k_new, v_new, Wq, Wk, window, sinks)
+        assert float(k_idx[0, 0, 9, 0]) == want
+        assert np.count_nonzero(k_idx) == 1          # only row 9 of sequence 0
+        assert K_ret[0, 0, 9, 0] == 1.5 and V_ret[0, 0, 9, 0] == -1.5
+        assert np.count_nonzero(K_ret) == 1
+        # position 9 of a local head: slot 2 + 9 % 6 = 5
+        assert K_loc[0, 0, 5, 0] == 2.5 and V_loc[0, 0, 5, 0] == -2.5
+        assert np.count_nonzero(K_loc) == 1
+        # query heads 0, 1 (retrieval KV head 0) are projected, the local heads' keep theirs
+        assert q_idx[0, 0, 0] == 0.5 and q_idx[0, 1, 0] == 0.25
+        assert np.all(q_idx[0, 2:] == 7.0) and np.all(q_idx[1] == 7.0)
+
+
+def test_append_sink_position_and_empty_sequence():
+    B, Hkv, G, d, r, Lmax, window, sinks = 2, 2, 1, 1, 1, 12, 6, 2
+    z16 = lambda *s: np.zeros(s, np.float16)
+    lay = _Lay([0, 1], np.zeros((B, 2, r), np.float32), z16(B, 1, Lmax, r), z16(B, 1, Lmax, d),
+               z16(B, 1, Lmax, d), z16(B, 1, window + sinks, d), z16(B, 1, window + sinks, d))
+    k_new = np.full((B, Hkv, d), 2.0, np.float16)
+    out = oracle.append_project(lay, [0, 2], np.ones((B, 2, d), np.float32),
+                                np.ones((B, Hkv, d), np.float32), k_new, k_new,
+                                np.ones((2, d, r), np.float32), np.full((1, d, r), 3.0, np.float32),
+                                window, sinks)
+    q_idx, k_idx, K_ret, V_ret, K_loc, V_loc = out
+    assert np.count_nonzero(K_loc[0]) == 0 and np.count_nonzero(K_ret[0]) == 0   # L = 0
+    assert K_loc[1, 0, 1, 0] == 2.0 and np.count_nonzero(K_loc) == 1             # sink slot 1
+    assert K_ret[1, 0, 1, 0] == 2.0 and k_idx[1, 0, 1, 0] == 3.0
+    assert q_idx[1, 1, 0] == 1.0 and q_idx[1, 0, 0] == 0.0   # only the retrieval head's query
