@@ -10,6 +10,8 @@ The names follow the C ABI in ``include/rtp.h``:
 * ``rtp_sparse_decode`` exact softmax attention over the selected tokens
 * ``rtp_window_decode`` window + sink attention of local heads
 * ``rtp_decode_step``   a whole layer: retrieval heads sparse, local heads windowed
+* ``rtp_append_project`` the step's cache update: indexer projections of the new token
+  and the append of its K/V rows
 
 If the library is missing or fails to load, every call raises: there is no fallback.
 """
@@ -33,7 +35,7 @@ EXPORTED = [
     "rtp_topk_select_workspace_size", "rtp_topk_select",
     "rtp_sparse_decode_workspace_size", "rtp_sparse_decode",
     "rtp_window_decode_workspace_size", "rtp_window_decode",
-    "rtp_decode_step_workspace_size", "rtp_decode_step",
+    "rtp_decode_step_workspace_size", "rtp_decode_step", "rtp_append_project",
 ]
 
 _lib = None
@@ -56,6 +58,17 @@ class LayerDesc(ctypes.Structure):
         ("out", P), ("lse", P), ("thresh_out", P), ("count_out", P),
         ("prof_ev", P * 8),
         ("topk", I32),
+    ]
+
+
+class AppendDesc(ctypes.Structure):
+    """Mirror of rtp_append_desc."""
+    _fields_ = [
+        ("B", I32), ("Hq", I32), ("Hkv", I32), ("d", I32), ("r", I32), ("Lmax", I32),
+        ("window", I32), ("sinks", I32), ("kv_dtype", I32),
+        ("kv_is_retrieval", P), ("q_pre", P), ("k_pre", P), ("Wq_idx", P), ("Wk_idx", P),
+        ("k_new", P), ("v_new", P), ("seq_lens", P), ("q_idx", P), ("k_idx", P),
+        ("K_ret", P), ("V_ret", P), ("K_loc", P), ("V_loc", P),
     ]
 
 
@@ -101,6 +114,8 @@ def lib():
         L.rtp_decode_step_workspace_size.argtypes = [ctypes.POINTER(LayerDesc)]
         L.rtp_decode_step.restype = I32
         L.rtp_decode_step.argtypes = [ctypes.POINTER(LayerDesc), P, SZ, P]
+        L.rtp_append_project.restype = I32
+        L.rtp_append_project.argtypes = [ctypes.POINTER(AppendDesc), P]
         _lib = L
     return _lib
 
@@ -295,6 +310,42 @@ def rtp_decode_step(layer, seq_lens, B, Hq, Hkv, Lmax, window, sinks, p, bin_wid
                     scale_attn, want_debug=want_debug, topk=topk)
     st(stream)
     return st.out, st.lse, st.thresh, st.count
+
+
+class AppendProject:
+    """Holds the descriptor of one layer's cache update so that repeated calls (a decode
+    loop, a captured graph) only enqueue the kernel.  The caches of `layer` are updated in
+    place; seq_lens holds the lengths after the append."""
+
+    def __init__(self, layer, seq_lens: torch.Tensor, B: int, Hq: int, Hkv: int, Lmax: int,
+                 window: int, sinks: int, q_pre: torch.Tensor, k_pre: torch.Tensor,
+                 Wq: torch.Tensor, Wk: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor):
+        self.keep = [layer.q_idx, layer.k_idx, layer.K_ret, layer.V_ret, layer.K_loc, layer.V_loc,
+                     seq_lens, q_pre, k_pre, Wq, Wk, k_new, v_new]
+        self.mask = (ctypes.c_uint8 * Hkv)(*[int(x) for x in layer.kv_is_retrieval])
+        nret = int(sum(int(x) for x in layer.kv_is_retrieval))
+        nloc = Hkv - nret
+
+        def opt(t, needed):
+            return _ptr(t) if needed and t is not None and t.numel() > 0 else None
+
+        self.desc = AppendDesc(
+            B, Hq, Hkv, k_new.shape[-1], layer.q_idx.shape[-1], Lmax, window, sinks,
+            _kv_dtype(k_new), ctypes.cast(self.mask, ctypes.c_void_p), opt(q_pre, nret),
+            opt(k_pre, nret), opt(Wq, nret), opt(Wk, nret), _ptr(k_new), _ptr(v_new),
+            _ptr(seq_lens), opt(layer.q_idx, nret), opt(layer.k_idx, nret),
+            opt(layer.K_ret, nret), opt(layer.V_ret, nret), opt(layer.K_loc, nloc),
+            opt(layer.V_loc, nloc))
+
+    def __call__(self, stream=None):
+        _check(lib().rtp_append_project(ctypes.byref(self.desc), _stream(stream)))
+
+
+def rtp_append_project(layer, seq_lens, B, Hq, Hkv, Lmax, window, sinks, q_pre, k_pre, Wq, Wk,
+                       k_new, v_new, stream=None):
+    """One layer's cache update in place (see AppendProject)."""
+    AppendProject(layer, seq_lens, B, Hq, Hkv, Lmax, window, sinks, q_pre, k_pre, Wq, Wk,
+                  k_new, v_new)(stream)
 
 
 def decode_workload(wl, want_debug: bool = False, stream=None):

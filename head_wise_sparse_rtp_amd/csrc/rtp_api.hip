@@ -293,6 +293,52 @@ rtp_status rtp_window_decode(const void* q, const void* K, const void* V, int32_
   return hip_status(e);
 }
 
+rtp_status rtp_append_project(const rtp_append_desc* d, void* stream) {
+  if (!d) return RTP_EINVAL;
+  if (d->B < 1 || d->Lmax < 1 || d->Hkv < 1 || d->Hq < 1 || d->Hq % d->Hkv != 0)
+    return RTP_EINVAL;
+  const int G = d->Hq / d->Hkv;
+  if (G > kMaxG || d->Hkv > kMaxHkv || d->Lmax > (1 << 24)) return RTP_EUNSUPPORTED;
+  if (d->r != kR || d->d != kD || !dtype_ok(d->kv_dtype)) return RTP_EUNSUPPORTED;
+  if (!d->kv_is_retrieval) return RTP_EINVAL;
+  AppendArgs a{};
+  a.B = d->B;
+  a.Hq = d->Hq;
+  a.Hkv = d->Hkv;
+  a.G = G;
+  a.Lmax = d->Lmax;
+  a.window = d->window;
+  a.sinks = d->sinks;
+  for (int h = 0; h < d->Hkv; h++) {
+    a.is_ret[h] = d->kv_is_retrieval[h] ? 1 : 0;
+    a.rank[h] = a.is_ret[h] ? a.Hret++ : a.Hloc++;
+  }
+  if (!ptr_ok(d->k_new) || !ptr_ok(d->v_new) || !ptr_ok(d->seq_lens)) return RTP_EINVAL;
+  if (a.Hret > 0 && (!ptr_ok(d->q_pre) || !ptr_ok(d->k_pre) || !ptr_ok(d->Wq_idx) ||
+                     !ptr_ok(d->Wk_idx) || !ptr_ok(d->q_idx) || !ptr_ok(d->k_idx) ||
+                     !ptr_ok(d->K_ret) || !ptr_ok(d->V_ret)))
+    return RTP_EINVAL;
+  if (a.Hloc > 0) {
+    if (d->window < 1 || d->sinks < 0) return RTP_EINVAL;
+    if ((int64_t)d->window + d->sinks > (1 << 24)) return RTP_EUNSUPPORTED;
+    if (!ptr_ok(d->K_loc) || !ptr_ok(d->V_loc)) return RTP_EINVAL;
+  }
+  a.seq_lens = d->seq_lens;
+  a.q_pre = d->q_pre;
+  a.k_pre = d->k_pre;
+  a.Wq = d->Wq_idx;
+  a.Wk = d->Wk_idx;
+  a.k_new = d->k_new;
+  a.v_new = d->v_new;
+  a.q_idx = d->q_idx;
+  a.k_idx = d->k_idx;
+  a.K_ret = d->K_ret;
+  a.V_ret = d->V_ret;
+  a.K_loc = d->K_loc;
+  a.V_loc = d->V_loc;
+  return hip_status(launch_append_project(a, d->kv_dtype, (hipStream_t)stream));
+}
+
 size_t rtp_decode_step_workspace_size(const rtp_layer_desc* desc) {
   StepPlan sp;
   if (plan_step(desc, sp) != RTP_OK) return 0;

@@ -110,6 +110,27 @@ hipError_t launch_merge(const AttnPartials& pa, int maxs, const int32_t* sel_cou
                         const HeadMap& map, int B, int Hq, int Hrows_kv, int G, float* out,
                         float* lse, hipStream_t st);
 
+// Cache update of a decode step (projections of the new token and its K/V rows).
+struct AppendArgs {
+  int B, Hq, Hkv, G, Hret, Hloc, Lmax, window, sinks;
+  const int32_t* seq_lens;  // lengths after the append
+  const float* q_pre;       // [B, Hq, 128]
+  const float* k_pre;       // [B, Hkv, 128]
+  const float* Wq;          // [Hq, 128, 16]
+  const float* Wk;          // [Hret, 128, 16]
+  const void* k_new;        // [B, Hkv, 128] cache dtype
+  const void* v_new;
+  float* q_idx;             // [B, Hq, 16]
+  void* k_idx;              // [B, Hret, Lmax, 16]
+  void* K_ret;
+  void* V_ret;              // [B, Hret, Lmax, 128]
+  void* K_loc;
+  void* V_loc;              // [B, Hloc, sinks + window, 128]
+  int32_t is_ret[kMaxHkv];  // per KV head: 1 = retrieval
+  int32_t rank[kMaxHkv];    // per KV head: index among the retrieval (or local) heads
+};
+hipError_t launch_append_project(const AppendArgs& a, int kv_dtype, hipStream_t st);
+
 // ---------------------------------------------------------------------------
 // workspace planning
 // ---------------------------------------------------------------------------

@@ -194,6 +194,43 @@ typedef struct {
 size_t rtp_decode_step_workspace_size(const rtp_layer_desc* desc);
 rtp_status rtp_decode_step(const rtp_layer_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Cache update of one decode step, before rtp_decode_step (section 三, 核心公式: the
+ * indexer compares W^Q_h q^pre with W^K_h k^pre, both projected to r dims before RoPE;
+ * section 五, test configuration: retrieval heads keep the whole cache, local heads a
+ * window plus sinks).  For every sequence b with L = seq_lens[b] >= 1 the new token sits
+ * at position n = L - 1 (seq_lens holds the lengths after the append, the same array the
+ * following rtp_decode_step takes):
+ *   retrieval KV head kv (the kr-th flagged head), every query head h = kv*G + g:
+ *     q_idx[b,h,i] = a_i,  a <- +0;  for c = 0..d-1: a <- fmaf(q_pre[b,h,c], Wq_idx[h,c,i], a)
+ *     k_idx[b,kr,n,i] = the same chain over k_pre[b,kv] and Wk_idx[kr], rounded to the
+ *                       cache dtype (round to nearest even)
+ *     K_ret[b,kr,n] = k_new[b,kv];  V_ret[b,kr,n] = v_new[b,kv]
+ *   local KV head kv (the kl-th unflagged head):
+ *     K_loc[b,kl,slot] = k_new[b,kv];  V_loc[b,kl,slot] = v_new[b,kv],  slot = n if n < sinks,
+ *     else sinks + (n mod window)  (the ring of rtp_window_decode)
+ * Rows of q_idx that belong to local heads, and every other cache row, are left as they
+ * are; sequences with L = 0 are left alone.  No workspace; the call never allocates.
+ */
+typedef struct {
+  int32_t B, Hq, Hkv, d, r, Lmax, window, sinks, kv_dtype;
+  const uint8_t* kv_is_retrieval; /* HOST [Hkv]: 1 = retrieval, 0 = local */
+  const float* q_pre;             /* [B, Hq, d] fp32 pre-RoPE queries (retrieval rows read) */
+  const float* k_pre;             /* [B, Hkv, d] fp32 pre-RoPE keys of the new token */
+  const float* Wq_idx;            /* [Hq, d, r] fp32 (rows of local heads' queries unread) */
+  const float* Wk_idx;            /* [Hret, d, r] fp32, retrieval KV heads in ascending order */
+  const void* k_new;              /* [B, Hkv, d] (kv_dtype) key of the new token (post-RoPE) */
+  const void* v_new;              /* [B, Hkv, d] (kv_dtype) */
+  const int32_t* seq_lens;        /* [B] device: lengths after the append */
+  float* q_idx;                   /* [B, Hq, r] fp32 out */
+  void* k_idx;                    /* [B, Hret, Lmax, r] (kv_dtype) in/out */
+  void* K_ret;                    /* [B, Hret, Lmax, d] in/out */
+  void* V_ret;
+  void* K_loc;                    /* [B, Hloc, sinks + window, d] in/out */
+  void* V_loc;
+} rtp_append_desc;
+rtp_status rtp_append_project(const rtp_append_desc* desc, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -126,6 +126,44 @@ def test_layer_desc_matches_the_header():
     assert names == [f[0] for f in m.LayerDesc._fields_]
 
 
+def test_append_desc_matches_the_header():
+    import head_wise_sparse_rtp_amd as m
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{([^{}]*)\} rtp_append_desc;", src).group(1)
+    names = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if decl:
+            names += [re.findall(r"(\w+)\s*$", part.strip())[0] for part in decl.split(",")]
+    assert names == [f[0] for f in m.AppendDesc._fields_]
+
+
+def test_append_project_validation(lib):
+    import head_wise_sparse_rtp_amd as m
+    mask = (ctypes.c_uint8 * 4)(1, 0, 0, 0)
+    d = m.AppendDesc(1, 32, 4, 128, 16, 65536, 8192, 4, 1, ctypes.cast(mask, ctypes.c_void_p),
+                     *([FAKE] * 13))
+    f = lambda: lib.rtp_append_project(ctypes.byref(d), None)
+    d.r = 8
+    assert f() == -2
+    d.r = 16
+    d.Hq = 30
+    assert f() == -1
+    d.Hq = 32
+    d.Wk_idx = None                      # needed: KV head 0 is a retrieval head
+    assert f() == -1
+    d.Wk_idx = FAKE
+    d.K_loc = MIS
+    assert f() == -1
+    d.K_loc = FAKE
+    d.window = 0
+    assert f() == -1
+    d.window = 8192
+    d.kv_dtype = 5
+    assert f() == -2
+    assert lib.rtp_append_project(None, None) == -1
+
+
 def test_sparse_and_window_validation(lib):
     nb = lib.rtp_sparse_decode_workspace_size(1, 1, 8, 4096)
     assert nb > 0

@@ -239,9 +239,10 @@ def test_window_decode_matches_oracle(rtp, dtype, window, sinks, lens):
 # ---------------------------------------------------------------------------
 # rtp_decode_step
 # ---------------------------------------------------------------------------
-def check_decode(rtp, wl, local_sample=None, layers=None, label=""):
+def check_decode(rtp, wl, local_sample=None, layers=None, label="", oracle_layers=None):
     """Run every layer on the GPU and compare with the oracle (all retrieval heads; all
-    local heads or the first `local_sample` of each layer)."""
+    local heads or the first `local_sample` of each layer).  `oracle_layers`, when given,
+    are the oracle's own copies of the layers (after its own cache update)."""
     res = rtp.decode_workload(wl, want_debug=True)
     torch.cuda.synchronize()
     st = SelCheck()
@@ -252,6 +253,8 @@ def check_decode(rtp, wl, local_sample=None, layers=None, label=""):
             continue
         if len(wl.layers) > 2:
             say(label, "layer", li)
+        if oracle_layers is not None:
+            layer = oracle_layers[li]
         out, lse, thr, cnt = (t.cpu().numpy() for t in res[li])
         heads = None
         if local_sample is not None:
@@ -326,6 +329,59 @@ def test_decode_step_topk_config(rtp, name, k):
     wl = workloads.make_config(name, device=dev())
     wl.topk = k
     check_decode(rtp, wl, label="%s-topk%d" % (name, k))
+
+
+# ---------------------------------------------------------------------------
+# rtp_append_project: the step's cache update
+# ---------------------------------------------------------------------------
+def _bits(a):
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint16) if a.dtype == np.float16 else a.view(np.uint32)
+
+
+def _oracle_layer(lay, arrays):
+    q_idx, k_idx, K_ret, V_ret, K_loc, V_loc = (torch.from_numpy(a) for a in arrays)
+    return workloads.Layer(lay.kv_is_retrieval, lay.q.cpu(), q_idx, k_idx, K_ret, V_ret, K_loc,
+                           V_loc)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_append_project_bit_exact(rtp, dtype):
+    """Projections are fp32 fma chains in input order on both sides and the rows are
+    copies: every cache array must match bit for bit (ring wrap, a sink position, an
+    empty sequence, L = 1)."""
+    lens = [1, 5000, 0, 70, 3]
+    say("append_project", dtype, lens)
+    wl = workloads.make_workload("t", len(lens), lens, 32, 4, [[1, 0, 1, 0]], seed=81,
+                                 dtype=dtype, window=64, sinks=4, device=dev(), Lmax=5000)
+    lay = wl.layers[0]
+    si = workloads.make_step_inputs(wl, seed=1, device=dev())
+    want = oracle.append_project(lay, lens, si.q_pre, si.k_pre, si.k_new, si.v_new, si.Wq, si.Wk,
+                                 wl.window, wl.sinks)
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev())
+    rtp.rtp_append_project(lay, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window, wl.sinks, si.q_pre,
+                           si.k_pre, si.Wq, si.Wk, si.k_new, si.v_new)
+    got = [oracle.np_of(t) for t in (lay.q_idx, lay.k_idx, lay.K_ret, lay.V_ret, lay.K_loc,
+                                     lay.V_loc)]
+    for name, g, w in zip(["q_idx", "k_idx", "K_ret", "V_ret", "K_loc", "V_loc"], got, want):
+        assert np.array_equal(_bits(g), _bits(w)), name
+
+
+def test_append_then_decode_c1(rtp):
+    """A whole step at 64K context: the new token's cache update, then the layer step that
+    attends over it; the oracle runs its own update and its own decode."""
+    say("append + decode c1")
+    wl = workloads.make_config("c1", device=dev())
+    lay = wl.layers[0]
+    si = workloads.make_step_inputs(wl, seed=2, device=dev())
+    want = oracle.append_project(lay, wl.seq_lens, si.q_pre, si.k_pre, si.k_new, si.v_new, si.Wq,
+                                 si.Wk, wl.window, wl.sinks)
+    olay = _oracle_layer(lay, want)
+    sl = torch.tensor(wl.seq_lens, dtype=torch.int32, device=dev())
+    rtp.rtp_append_project(lay, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window, wl.sinks, si.q_pre,
+                           si.k_pre, si.Wq, si.Wk, si.k_new, si.v_new)
+    assert np.array_equal(_bits(oracle.np_of(lay.k_idx)), _bits(want[1]))
+    check_decode(rtp, wl, label="append-c1", oracle_layers=[olay])
 
 
 def test_decode_step_p1_is_dense_attention(rtp):

@@ -399,6 +399,36 @@ def make_c4(device="cpu", p: float = 0.9, L: int = 1048576) -> Workload:
                          classes=classes, fixed_k={"needle": 2, "mid": 500, "broad": 8500})
 
 
+@dataclass
+class StepInputs:
+    """The new token of one decode step: pre-RoPE vectors for the indexer projections,
+    the projection weights and the new K/V rows."""
+    q_pre: torch.Tensor   # [B, Hq, d] fp32
+    k_pre: torch.Tensor   # [B, Hkv, d] fp32
+    Wq: torch.Tensor      # [Hq, d, r] fp32, N(0, 1/d)
+    Wk: torch.Tensor      # [Hret, d, r] fp32, N(0, 1/d)
+    k_new: torch.Tensor   # [B, Hkv, d] cache dtype
+    v_new: torch.Tensor
+
+
+def make_step_inputs(wl: Workload, layer_id: int = 0, seed: int = 0, device="cpu") -> StepInputs:
+    """Seeded N(0, 1) pre-RoPE vectors and new K/V rows; projection weights N(0, 1/d) as in
+    the single-head config's W^Q_idx / W^K_idx.  Draw order: q_pre, k_pre, Wq, Wk, k_new,
+    v_new."""
+    rng = np.random.default_rng(10_000 + 97 * seed + layer_id)
+    nret = int(np.asarray(wl.layers[layer_id].kv_is_retrieval).sum())
+    B, Hq, Hkv, d, r = wl.B, wl.Hq, wl.Hkv, wl.d, wl.r
+    kv = np.float16 if wl.dtype == "f16" else np.float32
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    q_pre = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    k_pre = rng.standard_normal((B, Hkv, d)).astype(np.float32)
+    Wq = (rng.standard_normal((Hq, d, r)) * math.sqrt(1.0 / d)).astype(np.float32)
+    Wk = (rng.standard_normal((max(nret, 1), d, r)) * math.sqrt(1.0 / d)).astype(np.float32)
+    k_new = rng.standard_normal((B, Hkv, d)).astype(kv)
+    v_new = rng.standard_normal((B, Hkv, d)).astype(kv)
+    return StepInputs(t(q_pre), t(k_pre), t(Wq), t(Wk), t(k_new), t(v_new))
+
+
 CONFIGS = {"c0": make_c0, "c1": make_c1, "c2": make_c2, "c3": make_c3, "c4": make_c4}
 
 
