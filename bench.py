@@ -201,6 +201,9 @@ def main():
     ap.add_argument("--p", type=float, default=None)
     ap.add_argument("--topk", type=int, default=0,
                     help="fixed top-k through the histogram instead of top-p")
+    ap.add_argument("--with-append", action="store_true",
+                    help="each step also runs the cache update of the new token "
+                         "(indexer projections + K/V append) before the attention")
     ap.add_argument("--rotations", type=int, default=0)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -232,10 +235,18 @@ def main():
     wl = workloads.make_config(args.workload, device=dev, **kw)
     assert len(wl.layers) == 1, "bench.py times single-layer workloads"
     layer = wl.layers[0]
+    sl = torch.as_tensor(wl.seq_lens, dtype=torch.int32, device=dev)
+    # the cache update's inputs reproduce the workload's own last row and q_idx, so the
+    # timed step keeps the planted selection (the update's work does not depend on values)
+    si = workloads.make_embedding_step_inputs(wl, device=dev) if args.with_append else None
+    if si is not None:
+        # the update is idempotent: apply it once, so that the byte count and every
+        # rotated copy see the appended caches and the projected q_idx
+        rtp.rtp_append_project(layer, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window, wl.sinks,
+                               si.q_pre, si.k_pre, si.Wq, si.Wk, si.k_new, si.v_new)
     bytes_step, detail = algorithmic_bytes(rtp, wl, layer, torch, args.topk)
     touched = max(bytes_step, 1)
     R = args.rotations or max(1, math.ceil(512 * 2 ** 20 / touched))
-    sl = torch.as_tensor(wl.seq_lens, dtype=torch.int32, device=dev)
 
     # R rotated copies of every input, one workspace and one output shared by all
     layers = [layer]
@@ -244,6 +255,7 @@ def main():
                                       layer.k_idx.clone(), layer.K_ret.clone(), layer.V_ret.clone(),
                                       layer.K_loc.clone(), layer.V_loc.clone(), layer.plans))
     steps = []
+    apps = []
     ws = None
     out = None
     for lay in layers:
@@ -252,6 +264,15 @@ def main():
                             ws=ws, topk=args.topk)
         ws, out = st.ws, st.out
         steps.append(st)
+        if si is not None:
+            apps.append(rtp.AppendProject(lay, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window,
+                                          wl.sinks, si.q_pre, si.k_pre, si.Wq, si.Wk, si.k_new,
+                                          si.v_new))
+
+    def step(i):
+        if apps:
+            apps[i]()
+        steps[i]()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     h = hip()
@@ -259,7 +280,7 @@ def main():
     # ---- warmup + graph capture: one graph runs the R rotations in order (a decode loop
     # captures its layers the same way); a second graph holds the K % R remaining steps
     for i in range(args.warmup):
-        steps[i % R]()
+        step(i % R)
     torch.cuda.synchronize()
     K = args.steps
     g_full = g_rest = None
@@ -267,12 +288,12 @@ def main():
         g_full = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_full):
             for i in range(R):
-                steps[i]()
+                step(i)
         if K % R:
             g_rest = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g_rest):
                 for i in range(K % R):
-                    steps[i]()
+                    step(i)
         for _ in range(max(1, args.warmup // R)):
             g_full.replay()
         torch.cuda.synchronize()
@@ -288,7 +309,7 @@ def main():
             g_rest.replay()
     else:
         for i in range(K):
-            steps[i % R]()
+            step(i % R)
     h.hipEventRecord(e1, ctypes.c_void_p(stream.cuda_stream))
     h.hipEventSynchronize(e1)
     torch.cuda.synchronize()
@@ -319,6 +340,17 @@ def main():
         for j in range(4):
             st.desc.prof_ev[j] = None
     ph = {k: v / K * 1000.0 for k, v in ph.items()}  # microseconds
+    if apps:
+        # the cache update alone, timed the same way
+        tot = 0.0
+        for k in range(K):
+            torch.cuda._sleep(200000)
+            h.hipEventRecord(evs[0], ctypes.c_void_p(stream.cuda_stream))
+            apps[k % R]()
+            h.hipEventRecord(evs[1], ctypes.c_void_p(stream.cuda_stream))
+            torch.cuda.synchronize()
+            tot += elapsed_ms(h, evs[0], evs[1])
+        ph["append_project"] = tot / K * 1000.0
     a_us = ph["stageA_score_hist"]
     a_bytes = detail["kidx"]
     achieved = a_bytes / (a_us * 1e-6) / 1e9 if a_us > 0 else 0.0
@@ -345,7 +377,8 @@ def main():
                                    layer.ret_heads, wl.d, wl.r, wl.window, wl.sinks,
                                    "top-k k=%d" % args.topk if args.topk else "p=%g" % wl.p),
                    "global_batch": wl.B, "seq_len": int(wl.seq_lens.max()),
-                   "parallelism": "single GPU", "graph": g_full is not None, "rotations": R},
+                   "parallelism": "single GPU", "graph": g_full is not None, "rotations": R,
+                   "with_append": bool(apps)},
         "bytes_per_step": bytes_step,
         "bytes_detail": {k: v for k, v in detail.items() if k not in ("sel_tokens", "sel_mass")},
         "sel_tokens_per_head": detail["sel_tokens"],

@@ -6,12 +6,13 @@
 // dims before RoPE; retrieval heads keep the whole cache and local heads a window plus
 // sinks (section 五, test configuration).
 //
-// Block (sequence b, KV head kv), 128 threads.  For a retrieval head the block computes
-// the G query projections and the key projection as fp32 fused-multiply-add chains over
-// the 128 inputs in order (one chain per thread and output feature; the inputs are
-// staged in LDS, the weights are read 16 contiguous floats per input row), stores the
-// key row in the cache's dtype (round to nearest even), and copies the new K/V rows to
-// position L - 1.  A local head's block copies the rows to the position's ring slot.
+// Block (sequence b, KV head kv, output group u), one wavefront.  For a retrieval head,
+// group u < G projects query head kv*G + u and group u = G the key; each block stages its
+// 128 x 16 weight matrix and its input row in LDS with every load in flight, then lanes
+// 0..15 each run one fp32 fused-multiply-add chain over the 128 inputs in order.  The key
+// row is stored in the cache's dtype (round to nearest even).  Group G also copies the new
+// K/V rows: to position L - 1 of a retrieval head, or to the position's ring slot of a
+// local head (whose other groups have nothing to do).
 #include "rtp_internal.h"
 
 namespace rtp {
@@ -35,55 +36,72 @@ __device__ __forceinline__ float to_cache<float>(float x) {
 }
 
 template <typename KT>
-__global__ __launch_bounds__(kD) void k_append_project(AppendArgs A) {
-  extern __shared__ float xs[];  // [G + 1][128]: q_pre rows of the KV head's query heads, k_pre
-  const int kv = blockIdx.x % A.Hkv;
-  const int b = blockIdx.x / A.Hkv;
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(64) void k_append_project(AppendArgs A) {
+  __shared__ __align__(16) float ws[kD * kR];  // W[c][i]
+  __shared__ __align__(16) float xs[kD];       // the input row
+  const int G = A.G;
+  const int u = blockIdx.x % (G + 1);
+  const int kv = (blockIdx.x / (G + 1)) % A.Hkv;
+  const int b = blockIdx.x / ((G + 1) * A.Hkv);
+  const int lane = threadIdx.x;
   const int L = clamp_len(A.seq_lens, b, A.Lmax);
   if (L < 1) return;
   const int n = L - 1;
-  const int G = A.G;
-  const KT* knew = static_cast<const KT*>(A.k_new) + ((size_t)b * A.Hkv + kv) * kD;
-  const KT* vnew = static_cast<const KT*>(A.v_new) + ((size_t)b * A.Hkv + kv) * kD;
   const int kr = A.rank[kv];
-  if (!A.is_ret[kv]) {
-    const int slot = n < A.sinks ? n : A.sinks + n % A.window;
-    const size_t row = ((size_t)b * A.Hloc + kr) * (size_t)(A.sinks + A.window) + slot;
-    static_cast<KT*>(A.K_loc)[row * kD + tid] = knew[tid];
-    static_cast<KT*>(A.V_loc)[row * kD + tid] = vnew[tid];
-    return;
+  const bool ret = A.is_ret[kv] != 0;
+  if (!ret && u < G) return;
+  if (u == G) {
+    const KT* knew = static_cast<const KT*>(A.k_new) + ((size_t)b * A.Hkv + kv) * kD;
+    const KT* vnew = static_cast<const KT*>(A.v_new) + ((size_t)b * A.Hkv + kv) * kD;
+    size_t row;
+    KT *Kc, *Vc;
+    if (ret) {
+      row = ((size_t)b * A.Hret + kr) * (size_t)A.Lmax + n;
+      Kc = static_cast<KT*>(A.K_ret);
+      Vc = static_cast<KT*>(A.V_ret);
+    } else {
+      const int slot = n < A.sinks ? n : A.sinks + n % A.window;
+      row = ((size_t)b * A.Hloc + kr) * (size_t)(A.sinks + A.window) + slot;
+      Kc = static_cast<KT*>(A.K_loc);
+      Vc = static_cast<KT*>(A.V_loc);
+    }
+    for (int c = lane; c < kD; c += 64) {
+      Kc[row * kD + c] = knew[c];
+      Vc[row * kD + c] = vnew[c];
+    }
+    if (!ret) return;
   }
-  const size_t row = ((size_t)b * A.Hret + kr) * (size_t)A.Lmax + n;
-  static_cast<KT*>(A.K_ret)[row * kD + tid] = knew[tid];
-  static_cast<KT*>(A.V_ret)[row * kD + tid] = vnew[tid];
-  const float* qp = A.q_pre + ((size_t)b * A.Hq + (size_t)kv * G) * kD;
-  for (int i = tid; i < G * kD; i += kD) xs[i] = qp[i];
-  xs[G * kD + tid] = A.k_pre[((size_t)b * A.Hkv + kv) * kD + tid];
+  const float* W = u < G ? A.Wq + ((size_t)kv * G + u) * kD * kR : A.Wk + (size_t)kr * kD * kR;
+  const float* x = u < G ? A.q_pre + ((size_t)b * A.Hq + (size_t)kv * G + u) * kD
+                         : A.k_pre + ((size_t)b * A.Hkv + kv) * kD;
+  float4 wv[kD * kR / 4 / 64];
+#pragma unroll
+  for (int j = 0; j < kD * kR / 4 / 64; j++) wv[j] = reinterpret_cast<const float4*>(W)[lane + 64 * j];
+  const float2 xv = reinterpret_cast<const float2*>(x)[lane];
+#pragma unroll
+  for (int j = 0; j < kD * kR / 4 / 64; j++) reinterpret_cast<float4*>(ws)[lane + 64 * j] = wv[j];
+  reinterpret_cast<float2*>(xs)[lane] = xv;
   __syncthreads();
-  // output (u, i): u < G is query head kv*G + u, u = G the key; i the feature
-  for (int o = tid; o < (G + 1) * kR; o += kD) {
-    const int u = o / kR, i = o % kR;
-    const float* W = u < G ? A.Wq + ((size_t)kv * G + u) * kD * kR : A.Wk + (size_t)kr * kD * kR;
-    const float* x = xs + u * kD;
-    float a = 0.0f;
-    for (int c = 0; c < kD; c++) a = __builtin_fmaf(x[c], W[c * kR + i], a);
-    if (u < G)
-      A.q_idx[((size_t)b * A.Hq + (size_t)kv * G + u) * kR + i] = a;
-    else
-      static_cast<KT*>(A.k_idx)[row * kR + i] = to_cache<KT>(a);
-  }
+  if (lane >= kR) return;
+  const int i = lane;
+  float a = 0.0f;
+#pragma unroll 16
+  for (int c = 0; c < kD; c++) a = __builtin_fmaf(xs[c], ws[c * kR + i], a);
+  if (u < G)
+    A.q_idx[((size_t)b * A.Hq + (size_t)kv * G + u) * kR + i] = a;
+  else
+    static_cast<KT*>(A.k_idx)[(((size_t)b * A.Hret + kr) * (size_t)A.Lmax + n) * kR + i] =
+        to_cache<KT>(a);
 }
 
 }  // namespace
 
 hipError_t launch_append_project(const AppendArgs& a, int kv_dtype, hipStream_t st) {
-  const size_t lds = sizeof(float) * (size_t)(a.G + 1) * kD;
-  const dim3 grid(a.B * a.Hkv);
+  const dim3 grid(a.B * a.Hkv * (a.G + 1));
   if (kv_dtype == 1)
-    k_append_project<f16><<<grid, kD, lds, st>>>(a);
+    k_append_project<f16><<<grid, 64, 0, st>>>(a);
   else
-    k_append_project<float><<<grid, kD, lds, st>>>(a);
+    k_append_project<float><<<grid, 64, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -552,3 +552,18 @@ def test_append_sink_position_and_empty_sequence():
     assert K_loc[1, 0, 1, 0] == 2.0 and np.count_nonzero(K_loc) == 1             # sink slot 1
     assert K_ret[1, 0, 1, 0] == 2.0 and k_idx[1, 0, 1, 0] == 3.0
     assert q_idx[1, 1, 0] == 1.0 and q_idx[1, 0, 0] == 0.0   # only the retrieval head's query
+
+
+def test_embedding_step_inputs_leave_the_layer_unchanged():
+    import workloads
+    wl = workloads.make_workload("t", 2, [300, 9], 8, 2, [[1, 0]], seed=3, window=16, sinks=4)
+    lay = wl.layers[0]
+    si = workloads.make_embedding_step_inputs(wl)
+    out = oracle.append_project(lay, wl.seq_lens, si.q_pre, si.k_pre, si.k_new, si.v_new, si.Wq,
+                                si.Wk, wl.window, wl.sinks)
+    before = [oracle.np_of(t) for t in (lay.q_idx, lay.k_idx, lay.K_ret, lay.V_ret, lay.K_loc,
+                                        lay.V_loc)]
+    for name, a, b in zip(["q_idx", "k_idx", "K_ret", "V_ret", "K_loc", "V_loc"], out, before):
+        a16 = a.view(np.uint16) if a.dtype == np.float16 else a.view(np.uint32)
+        b16 = b.view(np.uint16) if b.dtype == np.float16 else b.view(np.uint32)
+        assert np.array_equal(a16, b16), name

@@ -429,6 +429,45 @@ def make_step_inputs(wl: Workload, layer_id: int = 0, seed: int = 0, device="cpu
     return StepInputs(t(q_pre), t(k_pre), t(Wq), t(Wk), t(k_new), t(v_new))
 
 
+def make_embedding_step_inputs(wl: Workload, layer_id: int = 0, device="cpu") -> StepInputs:
+    """Step inputs that reproduce the workload's own state: q_pre and k_pre carry the
+    existing q_idx and the k_idx row at position L-1 in their first r entries (zeros
+    after), the weights embed those entries by the identity, and k_new / v_new are the
+    K/V rows already at position L-1.  A cache update with these inputs rewrites the
+    values the caches already hold, so a timed step sees the planted selection."""
+    lay = wl.layers[layer_id]
+    mask = np.asarray(lay.kv_is_retrieval)
+    ret = [int(h) for h in np.nonzero(mask)[0]]
+    loc = [int(h) for h in np.nonzero(mask == 0)[0]]
+    B, Hq, Hkv, d, r, G = wl.B, wl.Hq, wl.Hkv, wl.d, wl.r, wl.G
+    q_idx = lay.q_idx.detach().cpu().numpy()
+    q_pre = np.zeros((B, Hq, d), np.float32)
+    q_pre[:, :, :r] = q_idx
+    k_pre = np.zeros((B, Hkv, d), np.float32)
+    kv_np = lay.K_ret.detach().cpu().numpy() if ret else lay.K_loc.detach().cpu().numpy()
+    k_new = np.zeros((B, Hkv, d), kv_np.dtype)
+    v_new = np.zeros((B, Hkv, d), kv_np.dtype)
+    eye = np.zeros((d, r), np.float32)
+    eye[np.arange(r), np.arange(r)] = 1.0
+    Wq = np.broadcast_to(eye, (Hq, d, r)).copy()
+    Wk = np.broadcast_to(eye, (max(len(ret), 1), d, r)).copy()
+    for b in range(B):
+        L = int(wl.seq_lens[b])
+        if L < 1:
+            continue
+        n = L - 1
+        for kr, kv in enumerate(ret):
+            k_pre[b, kv, :r] = lay.k_idx[b, kr, n].detach().cpu().numpy().astype(np.float32)
+            k_new[b, kv] = lay.K_ret[b, kr, n].detach().cpu().numpy()
+            v_new[b, kv] = lay.V_ret[b, kr, n].detach().cpu().numpy()
+        for kl, kv in enumerate(loc):
+            slot = n if n < wl.sinks else wl.sinks + n % wl.window
+            k_new[b, kv] = lay.K_loc[b, kl, slot].detach().cpu().numpy()
+            v_new[b, kv] = lay.V_loc[b, kl, slot].detach().cpu().numpy()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return StepInputs(t(q_pre), t(k_pre), t(Wq), t(Wk), t(k_new), t(v_new))
+
+
 CONFIGS = {"c0": make_c0, "c1": make_c1, "c2": make_c2, "c3": make_c3, "c4": make_c4}
 
 
