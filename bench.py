@@ -58,7 +58,7 @@ def elapsed_ms(h, a, b):
     return ms.value
 
 
-def algorithmic_bytes(rtp, wl, layer, torch, topk=0):
+def algorithmic_bytes(rtp, wl, layer, torch, topk=0, ret_window=False):
     """Realised bytes of one step: the union of the selected sets per retrieval KV head
     comes from the GPU selection (the same rule the step runs: top-p, or the fixed top-k
     when topk > 0).  Also returns, per retrieval query head, the share of the indexer
@@ -93,6 +93,9 @@ def algorithmic_bytes(rtp, wl, layer, torch, topk=0):
                     e = torch.exp(zz - zz.max())
                     detail["sel_mass"].append(round(float(e[idx].sum() / e.sum()), 4))
                     u.update(idx.tolist())
+                if ret_window:  # the retrieval head also reads its sinks and window rows
+                    u.update(range(min(wl.sinks, L)))
+                    u.update(range(max(wl.sinks, L - wl.window), L))
                 detail["kidx"] += L * wl.r * e_idx
                 detail["sparse_kv"] += len(u) * 2 * wl.d * e_kv
                 detail["union_tokens"] += len(u)
@@ -201,6 +204,8 @@ def main():
     ap.add_argument("--p", type=float, default=None)
     ap.add_argument("--topk", type=int, default=0,
                     help="fixed top-k through the histogram instead of top-p")
+    ap.add_argument("--ret-window", action="store_true",
+                    help="retrieval heads also attend to the sinks and the window")
     ap.add_argument("--with-append", action="store_true",
                     help="each step also runs the cache update of the new token "
                          "(indexer projections + K/V append) before the attention")
@@ -244,7 +249,7 @@ def main():
         # rotated copy see the appended caches and the projected q_idx
         rtp.rtp_append_project(layer, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window, wl.sinks,
                                si.q_pre, si.k_pre, si.Wq, si.Wk, si.k_new, si.v_new)
-    bytes_step, detail = algorithmic_bytes(rtp, wl, layer, torch, args.topk)
+    bytes_step, detail = algorithmic_bytes(rtp, wl, layer, torch, args.topk, args.ret_window)
     touched = max(bytes_step, 1)
     R = args.rotations or max(1, math.ceil(512 * 2 ** 20 / touched))
 
@@ -261,7 +266,7 @@ def main():
     for lay in layers:
         st = rtp.DecodeStep(lay, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window, wl.sinks, wl.p,
                             wl.bin_width, wl.scale_idx, wl.scale_attn, out=out, want_lse=False,
-                            ws=ws, topk=args.topk)
+                            ws=ws, topk=args.topk, ret_window=args.ret_window)
         ws, out = st.ws, st.out
         steps.append(st)
         if si is not None:
@@ -378,7 +383,7 @@ def main():
                                    "top-k k=%d" % args.topk if args.topk else "p=%g" % wl.p),
                    "global_batch": wl.B, "seq_len": int(wl.seq_lens.max()),
                    "parallelism": "single GPU", "graph": g_full is not None, "rotations": R,
-                   "with_append": bool(apps)},
+                   "with_append": bool(apps), "retrieval_window": bool(args.ret_window)},
         "bytes_per_step": bytes_step,
         "bytes_detail": {k: v for k, v in detail.items() if k not in ("sel_tokens", "sel_mass")},
         "sel_tokens_per_head": detail["sel_tokens"],

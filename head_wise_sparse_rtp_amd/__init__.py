@@ -57,7 +57,7 @@ class LayerDesc(ctypes.Structure):
         ("p", F64), ("bin_width", F32), ("scale_idx", F32), ("scale_attn", F32),
         ("out", P), ("lse", P), ("thresh_out", P), ("count_out", P),
         ("prof_ev", P * 8),
-        ("topk", I32),
+        ("topk", I32), ("ret_window", I32),
     ]
 
 
@@ -263,7 +263,8 @@ class DecodeStep:
     def __init__(self, layer, seq_lens: torch.Tensor, B: int, Hq: int, Hkv: int, Lmax: int,
                  window: int, sinks: int, p: float, bin_width: float, scale_idx: float,
                  scale_attn: float, out: Optional[torch.Tensor] = None, want_lse: bool = True,
-                 want_debug: bool = False, ws: Optional[torch.Tensor] = None, topk: int = 0):
+                 want_debug: bool = False, ws: Optional[torch.Tensor] = None, topk: int = 0,
+                 ret_window: bool = False):
         dev = layer.q.device
         self.keep = [layer.q, layer.q_idx, layer.K_ret, layer.V_ret, layer.k_idx, layer.K_loc,
                      layer.V_loc, seq_lens]
@@ -290,6 +291,7 @@ class DecodeStep:
             float(scale_idx), float(scale_attn), _ptr(self.out), _ptr(self.lse),
             _ptr(self.thresh), _ptr(self.count))
         self.desc.topk = int(topk)
+        self.desc.ret_window = 1 if ret_window else 0
         nb = lib().rtp_decode_step_workspace_size(ctypes.byref(self.desc))
         if nb == 0:
             raise RtpError(RTP_EINVAL)
@@ -303,11 +305,11 @@ class DecodeStep:
 
 
 def rtp_decode_step(layer, seq_lens, B, Hq, Hkv, Lmax, window, sinks, p, bin_width, scale_idx,
-                    scale_attn, want_debug=False, stream=None, topk=0):
+                    scale_attn, want_debug=False, stream=None, topk=0, ret_window=False):
     """One layer's decode step; returns (out, lse, thresh, count).  topk > 0 selects the
     retrieval heads' tokens with the fixed top-k rule instead of top-p."""
     st = DecodeStep(layer, seq_lens, B, Hq, Hkv, Lmax, window, sinks, p, bin_width, scale_idx,
-                    scale_attn, want_debug=want_debug, topk=topk)
+                    scale_attn, want_debug=want_debug, topk=topk, ret_window=ret_window)
     st(stream)
     return st.out, st.lse, st.thresh, st.count
 
@@ -356,5 +358,5 @@ def decode_workload(wl, want_debug: bool = False, stream=None):
     for layer in wl.layers:
         res.append(rtp_decode_step(layer, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window, wl.sinks,
                                    wl.p, wl.bin_width, wl.scale_idx, wl.scale_attn, want_debug,
-                                   stream, getattr(wl, "topk", 0)))
+                                   stream, getattr(wl, "topk", 0), getattr(wl, "ret_window", False)))
     return res

@@ -114,12 +114,13 @@ rtp_status plan_step(const rtp_layer_desc* d, StepPlan& sp) {
   sp.Hloc = sp.loc.n;
   if (sp.Hloc > 0 && (d->window < 1 || d->sinks < 0)) return RTP_EINVAL;
   if (sp.Hloc > 0 && (int64_t)d->window + d->sinks > (1 << 24)) return RTP_EUNSUPPORTED;
+  if (sp.Hret > 0 && d->ret_window && (d->window < 1 || d->sinks < 0)) return RTP_EINVAL;
   if (step_fused_supported(d->kv_dtype, sp.G, sp.Hloc, d->window, d->sinks, d->B, sp.Hret,
-                           d->Lmax)) {
+                           d->Lmax, d->ret_window != 0)) {
     sp.fused = true;
     WsPlanner wp;
     sp.fp = plan_step_fused(wp, d->B, d->Hq, sp.G, d->Lmax, sp.Hret, sp.Hloc, d->window,
-                            d->sinks);
+                            d->sinks, d->ret_window != 0);
     sp.bytes = sp.fp.bytes;
     return RTP_OK;
   }
@@ -357,6 +358,8 @@ rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, v
     if (!ptr_ok(d->q_idx) || !ptr_ok(d->K_ret) || !ptr_ok(d->V_ret) || !ptr_ok(d->k_idx))
       return RTP_EINVAL;
     if (d->topk < 0 || !pow2_width(d->bin_width)) return RTP_EINVAL;
+    if (d->ret_window != 0 && d->ret_window != 1) return RTP_EINVAL;
+    if (d->ret_window && (d->window < 1 || d->sinks < 0)) return RTP_EINVAL;
     if (d->topk == 0 && (!(d->p > 0.0) || std::isnan(d->p))) return RTP_EINVAL;
   }
   if (sp.Hloc > 0 && (!ptr_ok(d->K_loc) || !ptr_ok(d->V_loc))) return RTP_EINVAL;
@@ -385,6 +388,7 @@ rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, v
     a.loc = sp.loc;
     a.p = d->p;
     a.topk = d->topk;
+    a.ret_window = d->ret_window;
     a.bin_width = d->bin_width;
     a.scale_idx = d->scale_idx;
     a.scale_attn = d->scale_attn;
@@ -427,7 +431,8 @@ rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, v
     mark(2);
     if (e == hipSuccess)
       e = launch_select(d->seq_lens, d->B, H, d->Lmax, sp.sel.cg, sb, sel_idx, sel_cnt, d->Lmax,
-                        d->count_out, &sp.ret, G, d->Hq, st);
+                        d->count_out, &sp.ret, G, d->Hq, st, d->ret_window ? d->sinks : 0,
+                        d->ret_window ? d->window : 0);
     const AttnPartials pa = bind_parts(w, sp.sparse);
     if (e == hipSuccess)
       e = launch_sparse_partial(d->q, d->K_ret, d->V_ret, d->kv_dtype, sel_idx, sel_cnt, d->Lmax,

@@ -87,10 +87,12 @@ hipError_t launch_threshold(const int32_t* seq_lens, int B, int H, int Lmax, dou
                             float* hist_out, int32_t* thresh_out, const HeadMap* out_map,
                             int G, int Hq, hipStream_t st);
 
+// force_window > 0 also keeps every token n < force_sinks or n >= L - force_window
+// (retrieval heads that attend to the sinks and the window besides their selected set).
 hipError_t launch_select(const int32_t* seq_lens, int B, int H, int Lmax, const ChunkGeom& cg,
                          const SelectBufs& sb, int32_t* sel_idx, int32_t* sel_count, int cap,
                          int32_t* count_out, const HeadMap* out_map, int G, int Hq,
-                         hipStream_t st);
+                         hipStream_t st, int force_sinks = 0, int force_window = 0);
 
 // Sparse attention partials over sel_idx rows; rows kr*G+g, q head map.kv[kr]*G+g.
 hipError_t launch_sparse_partial(const void* q, const void* K, const void* V, int kv_dtype,
@@ -157,6 +159,7 @@ struct StepFusedPlan {
   int nparts;          // selection blocks per slice (they share its attention steps)
   int wrows, nws;      // window blocks: rows per block, blocks per local KV head
   int ncu;             // compute units of the device
+  int rwnws, rwrows;   // retrieval window blocks per KV head and their rows (0: none)
   int tcpb, tseg;      // stage-T blocks: chunks per block, blocks per head row
   size_t suf, partA, codes, bstar, Aglob, sufq;
   size_t p1m, p1l, p1acc, p1cnt;
@@ -172,7 +175,8 @@ struct StepFusedArgs {
   const void *K_ret, *V_ret, *k_idx, *K_loc, *V_loc;
   HeadMap ret, loc;
   double p;
-  int topk;  // > 0: fixed top-k (count bins) instead of top-p
+  int topk;        // > 0: fixed top-k (count bins) instead of top-p
+  int ret_window;  // retrieval heads also attend to the sinks and the window
   float bin_width, scale_idx, scale_attn;
   float* out;
   float* lse;
@@ -182,9 +186,9 @@ struct StepFusedArgs {
 };
 
 bool step_fused_supported(int kv_dtype, int G, int Hloc, int window, int sinks, int B, int Hret,
-                          int Lmax);
+                          int Lmax, bool ret_window);
 StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int Hret, int Hloc,
-                              int window, int sinks);
+                              int window, int sinks, bool ret_window);
 // ev (may be null): events recorded before stage A, after stage A, after stage T and
 // after the last kernel
 hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedArgs& a,

@@ -150,6 +150,11 @@ __global__ __launch_bounds__(kThreads) void k_threshold(
   }
 }
 
+// Tokens kept whatever their bin: the first fs positions and the last fw (fw > 0 only).
+__device__ __forceinline__ bool forced(int n, int L, int fs, int fw) {
+  return fw > 0 && (n < fs || n >= L - fw);
+}
+
 // Per-chunk selection test.  Returns the chunk threshold code: tokens with code <= tau
 // are selected; tau = 256 selects every valid token; tau < 0 selects none.
 __device__ __forceinline__ int chunk_tau(const int32_t* thr, const int32_t* part_A, size_t row,
@@ -168,7 +173,7 @@ template <int TPT>
 __global__ __launch_bounds__(kThreads) void k_select_count(
     const int32_t* __restrict__ seq_lens, int H, int Lmax, int nchunk,
     const int32_t* __restrict__ thr, const int32_t* __restrict__ part_A,
-    const uint32_t* __restrict__ codes, int32_t* __restrict__ cnt) {
+    const uint32_t* __restrict__ codes, int32_t* __restrict__ cnt, int fs, int fw) {
   __shared__ int red[kThreads / 64];
   constexpr int TC = kThreads * TPT;
   const size_t row = blockIdx.y;
@@ -178,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void k_select_count(
   const int tau = chunk_tau(thr, part_A, row, nchunk, chunk);
   const int tid = threadIdx.x;
   int c = 0;
-  if (tau >= 0) {
+  if (tau >= 0 || fw > 0) {
     const uint32_t* cp = codes + (row * nchunk + chunk) * (size_t)(TC / 4);
 #pragma unroll
     for (int qd = 0; qd < TPT / 4; qd++) {
@@ -187,7 +192,8 @@ __global__ __launch_bounds__(kThreads) void k_select_count(
       for (int i = 0; i < 4; i++) {
         const int n = chunk * TC + (4 * qd + i) * kThreads + tid;
         const int code = (wd >> (8 * i)) & 255;
-        c += (n < L && (tau == 256 || code <= tau)) ? 1 : 0;
+        const bool s = (tau >= 0 && (tau == 256 || code <= tau)) || forced(n, L, fs, fw);
+        c += (n < L && s) ? 1 : 0;
       }
     }
   }
@@ -207,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void k_select_write(
     const int32_t* __restrict__ thr, const int32_t* __restrict__ part_A,
     const uint32_t* __restrict__ codes, const int32_t* __restrict__ cnt,
     int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count, int cap,
-    int32_t* __restrict__ count_out, HeadMap omap, int G, int Hq, int use_map) {
+    int32_t* __restrict__ count_out, HeadMap omap, int G, int Hq, int use_map, int fs, int fw) {
   __shared__ int wsum[kThreads / 64];
   __shared__ int red[kThreads / 64];
   constexpr int TC = kThreads * TPT;
@@ -246,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void k_select_write(
     const int n = chunk * TC + t * kThreads + tid;
     const uint32_t wd = cp[(t >> 2) * kThreads + tid];
     const int code = (wd >> (8 * (t & 3))) & 255;
-    const bool sel = n < L && tau >= 0 && (tau == 256 || code <= tau);
+    const bool sel = n < L && ((tau >= 0 && (tau == 256 || code <= tau)) || forced(n, L, fs, fw));
     const unsigned long long bal = __ballot(sel);
     const int before = __popcll(bal & ((1ull << lane) - 1ull));
     if (lane == 0) wsum[wv] = __popcll(bal);
@@ -289,16 +295,17 @@ hipError_t launch_threshold(const int32_t* seq_lens, int B, int H, int Lmax, dou
 hipError_t launch_select(const int32_t* seq_lens, int B, int H, int Lmax, const ChunkGeom& cg,
                          const SelectBufs& sb, int32_t* sel_idx, int32_t* sel_count, int cap,
                          int32_t* count_out, const HeadMap* out_map, int G, int Hq,
-                         hipStream_t st) {
+                         hipStream_t st, int force_sinks, int force_window) {
+  const int fs = force_sinks, fw = force_window;
   dim3 grid(cg.nchunk, B * H);
   HeadMap m{};
   if (out_map) m = *out_map;
   if (cg.tpt == 4) {
     k_select_count<4><<<grid, kThreads, 0, st>>>(seq_lens, H, Lmax, cg.nchunk, sb.thr,
-                                                 sb.part_A, sb.codes, sb.cnt);
+                                                 sb.part_A, sb.codes, sb.cnt, fs, fw);
   } else {
     k_select_count<8><<<grid, kThreads, 0, st>>>(seq_lens, H, Lmax, cg.nchunk, sb.thr,
-                                                 sb.part_A, sb.codes, sb.cnt);
+                                                 sb.part_A, sb.codes, sb.cnt, fs, fw);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -306,12 +313,12 @@ hipError_t launch_select(const int32_t* seq_lens, int B, int H, int Lmax, const 
     k_select_write<4><<<grid, kThreads, 0, st>>>(seq_lens, H, Lmax, cg.nchunk, sb.thr,
                                                  sb.part_A, sb.codes, sb.cnt, sel_idx,
                                                  sel_count, cap, count_out, m, G, Hq,
-                                                 out_map ? 1 : 0);
+                                                 out_map ? 1 : 0, fs, fw);
   } else {
     k_select_write<8><<<grid, kThreads, 0, st>>>(seq_lens, H, Lmax, cg.nchunk, sb.thr,
                                                  sb.part_A, sb.codes, sb.cnt, sel_idx,
                                                  sel_count, cap, count_out, m, G, Hq,
-                                                 out_map ? 1 : 0);
+                                                 out_map ? 1 : 0, fs, fw);
   }
   return hipGetLastError();
 }

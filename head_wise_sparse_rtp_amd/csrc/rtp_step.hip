@@ -725,6 +725,11 @@ struct StageBParams {
   int B, Hq, G, Lmax, Hret, nchunk, tc, nblk, nparts;
   double p;
   int topk;  // > 0: b* from token counts (fixed top-k) instead of masses
+  // rw_window > 0: every head also attends to n < rw_sinks and n >= L - rw_window; those
+  // rows are left out of the selection lists and taken by the retrieval window blocks
+  // (rw_nws per KV head, rw_rows rows each), whose partials follow the selection partials
+  int rw_sinks, rw_window, rw_nws, rw_rows;
+  int np_row;  // partials per retrieval KV head: nblk * nparts + rw_nws
   const f16* q;
   const f16* K_ret;
   const f16* V_ret;
@@ -909,6 +914,13 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
       for (int q = 0; q < 4; q++)
         if (tok0 + cc * tc + 4 * w + q >= L) hm[i][q] = 0u;
     }
+    if (P.rw_window > 0) {  // the sinks and the window belong to the window blocks
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int n = tok0 + cc * tc + 4 * w + q;
+        if (n < P.rw_sinks || n >= L - P.rw_window) hm[i][q] = 0u;
+      }
+    }
   }
   if (P.want_count) {
 #pragma unroll
@@ -963,19 +975,56 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
   // ---- phase 3: block partial
   // partial (slice, part); the selection counts go with part 0 only
   const int mysteps = max(0, ((U + kStep - 1) / kStep - part + P.nparts - 1) / P.nparts);
-  const size_t s1p = (((size_t)(b * P.Hret + kr) * P.nblk + blk) * P.nparts + part) * G;
+  const size_t s1p = ((size_t)(b * P.Hret + kr) * P.np_row + (size_t)blk * P.nparts + part) * G;
   block_combine<kBWaves>(st, G, min(kBWaves, mysteps), lds, P.p1m + s1p, P.p1l + s1p,
                          P.p1acc + s1p * kD);
   if (tid < G) P.p1cnt[s1p + tid] = part == 0 ? s_cnt[tid] : 0;
 }
 
+// Retrieval window block: the sink and window rows of a retrieval KV head (positions of
+// the full cache, no ring), attended by all G query heads; its partial follows the
+// head's selection partials, with the row count as its count.
+__device__ void ret_window_block(const StageBParams& P, int wb, float* lds) {
+  const int wsplit = wb % P.rw_nws;
+  const int kr = (wb / P.rw_nws) % P.Hret;
+  const int b = wb / (P.rw_nws * P.Hret);
+  const int G = P.G;
+  const int L = clamp_len(P.seq_lens, b, P.Lmax);
+  const int ns = min(P.rw_sinks, L);
+  const int wstart = max(P.rw_sinks, L - P.rw_window);
+  const int nwin = ns + max(0, L - wstart);
+  const f16* Kb = P.K_ret + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kD;
+  const f16* Vb = P.V_ret + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kD;
+  h8 qop[4];
+  load_qop(P.q + ((size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G) * kD, G, qop);
+  AttnState st;
+  attn_init(st);
+  const int elo = wsplit * P.rw_rows;
+  const int n = max(0, min(nwin - elo, P.rw_rows));
+  attend_list<kBWaves>(
+      Kb, Vb, n,
+      [&](int e) {
+        e += elo;
+        return e < ns ? e : wstart + (e - ns);
+      },
+      [&](int) { return 0xFFFFu; }, qop, P.scale2, st);
+  const size_t prow =
+      ((size_t)(b * P.Hret + kr) * P.np_row + (size_t)P.nblk * P.nparts + wsplit) * G;
+  block_combine<kBWaves>(st, G, min(kBWaves, (n + kStep - 1) / kStep), lds, P.p1m + prow,
+                         P.p1l + prow, P.p1acc + prow * kD);
+  if ((int)threadIdx.x < G) P.p1cnt[prow + threadIdx.x] = n;
+}
+
 template <int NWD, int GMAX>
 __global__ __launch_bounds__(kBThreads, 2) void k_stage_b(StageBParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
+  const int nrw = P.rw_window > 0 ? P.B * P.Hret * P.rw_nws : 0;
   if ((int)blockIdx.x < P.nret_blocks)
     select_attend_block<NWD, GMAX>(P, smem);
+  else if ((int)blockIdx.x < P.nret_blocks + nrw)
+    ret_window_block(P, blockIdx.x - P.nret_blocks, reinterpret_cast<float*>(smem));
   else
-    window_block(P.win, blockIdx.x - P.nret_blocks, reinterpret_cast<float*>(smem));
+    window_block(P.win, blockIdx.x - P.nret_blocks - nrw, reinterpret_cast<float*>(smem));
 }
 
 // ---------------------------------------------------------------------------
@@ -1154,19 +1203,24 @@ int window_rows(int B, int Hloc, int ring) {
 }  // namespace
 
 bool step_fused_supported(int kv_dtype, int G, int Hloc, int window, int sinks, int B, int Hret,
-                          int Lmax) {
+                          int Lmax, bool ret_window) {
   if (kv_dtype != 1 || G > kAttnG) return false;
   if (Hloc > 0) {
     const int ring = window + sinks;
     const int wr = window_rows(B, Hloc, ring);
     if ((ring + wr - 1) / wr > kMaxParts) return false;
   }
+  if (Hret > 0 && ret_window) {
+    const int ring = window + sinks;
+    const int wr = window_rows(B, Hret, ring);
+    if ((ring + wr - 1) / wr + (Lmax + 2047) / 2048 > kMaxParts) return false;
+  }
   if (Hret > 0 && (Lmax + 4095) / 4096 > kMaxParts) return false;  // stage-M LDS
   return true;
 }
 
 StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int Hret, int Hloc,
-                              int window, int sinks) {
+                              int window, int sinks, bool ret_window) {
   (void)Hq;
   StepFusedPlan sp{};
   sp.G = G;
@@ -1186,6 +1240,11 @@ StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int
     sp.wrows = window_rows(B, Hloc, window + sinks);
     sp.nws = (window + sinks + sp.wrows - 1) / sp.wrows;
     nwin_blocks = B * Hloc * sp.nws;
+  }
+  if (Hret > 0 && ret_window) {  // window blocks of the retrieval heads, sized the same way
+    sp.rwrows = window_rows(B, Hret, window + sinks);
+    sp.rwnws = (window + sinks + sp.rwrows - 1) / sp.rwrows;
+    nwin_blocks += B * Hret * sp.rwnws;
   }
   if (Hret > 0) {
     sp.nchunk = (Lmax + sp.tc - 1) / sp.tc;
@@ -1219,7 +1278,7 @@ StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int
       sp.tcpb = (int)std::min<int64_t>(kTMaxCPB, std::max<int64_t>(1, (rc + sp.ncu - 1) / sp.ncu));
       sp.tseg = (sp.nchunk + sp.tcpb - 1) / sp.tcpb;
     }
-    const size_t n1 = (size_t)B * Hret * sp.nblk * sp.nparts * G;
+    const size_t n1 = (size_t)B * Hret * ((size_t)sp.nblk * sp.nparts + sp.rwnws) * G;
     sp.p1m = wp.take<float>(n1);
     sp.p1l = wp.take<float>(n1);
     sp.p1acc = wp.take<float>(n1 * kD);
@@ -1334,6 +1393,8 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     Q.nparts = sp.nparts;
     Q.p = a.p;
     Q.topk = a.topk;
+    Q.rw_sinks = a.ret_window ? a.sinks : 0;
+    Q.rw_window = a.ret_window ? a.window : 0;  // the plan holds rwnws > 0 blocks then
     Q.q = static_cast<const f16*>(a.q);
     Q.K_ret = static_cast<const f16*>(a.K_ret);
     Q.V_ret = static_cast<const f16*>(a.V_ret);
@@ -1349,7 +1410,11 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     Q.p1cnt = at<int32_t>(ws, sp.p1cnt);
     Q.want_count = a.count_out != nullptr;
     Q.nret_blocks = B * sp.Hret * sp.nblk * sp.nparts;
+    Q.rw_nws = sp.rwnws;
+    Q.rw_rows = sp.rwrows;
+    Q.np_row = sp.nblk * sp.nparts + sp.rwnws;
   }
+  const int nrw_blocks = Q.rw_window > 0 ? B * sp.Hret * sp.rwnws : 0;
   int nwin_blocks = 0;
   if (sp.Hloc > 0) {
     WinParams& W = Q.win;
@@ -1373,7 +1438,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
   }
   const size_t ldsB = std::max<size_t>(kBWaves * (32 + 2048) * sizeof(float),
                                        sizeof(uint32_t) * (size_t)(sp.Hret > 0 ? sp.tb : 0));
-  const int nB = Q.nret_blocks + nwin_blocks;
+  const int nB = Q.nret_blocks + nrw_blocks + nwin_blocks;
 #define RTP_STAGE_B(NWDV, GMV) k_stage_b<NWDV, GMV><<<nB, kBThreads, ldsB, st>>>(Q)
   if (G <= 8) {
     if (sp.nwd == 2)
@@ -1403,7 +1468,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     M.p1cnt = Q.p1cnt;
     M.Aglob = Q.Aglob;
     M.bstar = Q.bstar;
-    M.nblk = sp.nblk * sp.nparts;
+    M.nblk = sp.nblk * sp.nparts + sp.rwnws;
     M.Hret = sp.Hret;
     M.ret = a.ret;
     M.count_out = a.count_out;
@@ -1418,7 +1483,8 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     M.Hloc = sp.Hloc;
     M.loc = a.loc;
   }
-  const int nmax = std::max(sp.Hret > 0 ? sp.nblk * sp.nparts : 0, sp.Hloc > 0 ? sp.nws : 0);
+  const int nmax =
+      std::max(sp.Hret > 0 ? sp.nblk * sp.nparts + sp.rwnws : 0, sp.Hloc > 0 ? sp.nws : 0);
   const size_t ldsM = sizeof(float) * (3 * (size_t)nmax + 8 + kThreads / 8 * kMSlice);
   k_stage_m<<<(M.nret + nwm) * kMSlices, kThreads, ldsM, st>>>(M);
   e = hipGetLastError();

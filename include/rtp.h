@@ -184,6 +184,10 @@ typedef struct {
   void* prof_ev[8];
   int32_t topk;                   /* 0: top-p with p; > 0: fixed top-k (rtp_topk_select's rule)
                                    * for every retrieval query head; < 0: RTP_EINVAL */
+  int32_t ret_window;             /* 0: retrieval heads attend to their selected set only;
+                                   * 1: to that set united with { n < sinks } and
+                                   * { n >= L - window } (the local heads' window, in the
+                                   * full cache); count_out then counts the union */
 } rtp_layer_desc;
 
 /* fp16 caches with G <= 16 run four kernels per call: indexer score + chunk histograms;

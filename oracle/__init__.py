@@ -257,15 +257,17 @@ class HeadResult:
     lse: float
     sel: Optional[Selection] = None
     z: Optional[np.ndarray] = None     # indexer logits of a retrieval head
+    rows: Optional[np.ndarray] = None  # the rows attended to (retrieval heads)
 
 
 def decode_layer(layer, seq_lens, Hq: int, Hkv: int, p: float, bin_width: float,
                  scale_idx: float, scale_attn: float, window: int, sinks: int,
                  heads: Optional[List[int]] = None, batches: Optional[List[int]] = None,
-                 topk: int = 0) -> Dict[tuple, HeadResult]:
+                 topk: int = 0, ret_window: bool = False) -> Dict[tuple, HeadResult]:
     """Oracle outputs of one layer keyed by (b, query head).  `heads` / `batches`
     restrict the work to a sample of query heads / sequences.  topk > 0 selects with
-    the fixed top-k rule instead of top-p."""
+    the fixed top-k rule instead of top-p.  ret_window: retrieval heads attend to their
+    selected set united with the sink and window positions (rows of the full cache)."""
     G = Hq // Hkv
     mask = np.asarray(layer.kv_is_retrieval)
     ret = [int(h) for h in np.nonzero(mask)[0]]
@@ -288,8 +290,11 @@ def decode_layer(layer, seq_lens, Hq: int, Hkv: int, p: float, bin_width: float,
                 for h in hs:
                     z = index_score(q_idx[b, h], kidx, scale_idx)
                     s = topk_select(z, topk, bin_width) if topk > 0 else topp_select(z, p, bin_width)
-                    o, lse = attention(q[b, h], Kh, Vh, s.idx, scale_attn)
-                    res[(b, h)] = HeadResult(o, lse, s, z)
+                    rows = s.idx
+                    if ret_window:
+                        rows = np.union1d(rows, window_positions(L, window, sinks))
+                    o, lse = attention(q[b, h], Kh, Vh, rows, scale_attn)
+                    res[(b, h)] = HeadResult(o, lse, s, z, np.asarray(rows, dtype=np.int64))
             else:
                 kl = loc.index(kh)
                 rows = ring_slot(window_positions(L, window, sinks), window, sinks)
@@ -310,5 +315,5 @@ def decode_step(wl, layers: Optional[List[int]] = None, heads=None, batches=None
             continue
         out.append(decode_layer(layer, wl.seq_lens, wl.Hq, wl.Hkv, wl.p, wl.bin_width,
                                 wl.scale_idx, wl.scale_attn, wl.window, wl.sinks, heads, batches,
-                                getattr(wl, "topk", 0)))
+                                getattr(wl, "topk", 0), getattr(wl, "ret_window", False)))
     return out

@@ -210,6 +210,9 @@ def test_decode_step_validation(lib):
     d.topk = -1
     assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nb, None) == -1
     d.topk = 0
+    d.ret_window = 2
+    assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nb, None) == -1
+    d.ret_window = 0
     d.p = 0.9
     d.k_idx = None
     assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nb, None) == -1

@@ -263,15 +263,19 @@ def check_decode(rtp, wl, local_sample=None, layers=None, label="", oracle_layer
             heads = ret_q + loc_q
         orc = oracle.decode_layer(layer, wl.seq_lens, wl.Hq, wl.Hkv, wl.p, wl.bin_width,
                                   wl.scale_idx, wl.scale_attn, wl.window, wl.sinks, heads=heads,
-                                  topk=wl.topk)
+                                  topk=wl.topk, ret_window=wl.ret_window)
         for (b, h), r in orc.items():
             where = "%s layer %d b %d head %d" % (label, li, b, h)
             o_ref = r.out
             if r.sel is not None:
                 A, bs = int(thr[b, h, 0]), int(thr[b, h, 1])
                 ex = expected_set(r.z, r.sel, A, bs, wl.p, wl.bin_width, st, where, wl.topk)
+                same = ex is r.sel.idx
+                if wl.ret_window:
+                    win = oracle.window_positions(int(wl.seq_lens[b]), wl.window, wl.sinks)
+                    ex = np.union1d(ex, win).astype(np.int64)
                 compare_count(int(cnt[b, h]), ex, r.z, wl.bin_width, A, bs, st, where)
-                if ex is not r.sel.idx:
+                if not same:
                     kr = layer.ret_heads.index(h // wl.G)
                     o_ref, _ = oracle.attention(oracle.np_of(layer.q)[b, h],
                                                 oracle.np_of(layer.K_ret[b, kr]),
@@ -382,6 +386,26 @@ def test_append_then_decode_c1(rtp):
                            si.k_pre, si.Wq, si.Wk, si.k_new, si.v_new)
     assert np.array_equal(_bits(oracle.np_of(lay.k_idx)), _bits(want[1]))
     check_decode(rtp, wl, label="append-c1", oracle_layers=[olay])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("p", [0.5, 0.9])
+def test_decode_step_retrieval_window_small_ragged(rtp, dtype, p):
+    """Retrieval heads that also attend to the sinks and the window (fused path f16,
+    single-purpose kernels f32); lengths below, at and above window + sinks."""
+    say("decode_step retrieval+window", dtype, p)
+    wl = workloads.make_workload("t", 4, [3000, 1, 4099, 200], 32, 4, [[1, 0, 1, 0]], seed=66,
+                                 p=p, dtype=dtype, window=256, sinks=4, device=dev())
+    wl.ret_window = True
+    check_decode(rtp, wl, label="retwin-%s-p%g" % (dtype, p))
+
+
+@pytest.mark.parametrize("name", ["c1", "c4"])
+def test_decode_step_retrieval_window_config(rtp, name):
+    say("config", name, "retrieval + window")
+    wl = workloads.make_config(name, device=dev())
+    wl.ret_window = True
+    check_decode(rtp, wl, label="%s-retwin" % name)
 
 
 def test_decode_step_p1_is_dense_attention(rtp):

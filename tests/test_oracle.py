@@ -567,3 +567,26 @@ def test_embedding_step_inputs_leave_the_layer_unchanged():
         a16 = a.view(np.uint16) if a.dtype == np.float16 else a.view(np.uint32)
         b16 = b.view(np.uint16) if b.dtype == np.float16 else b.view(np.uint32)
         assert np.array_equal(a16, b16), name
+
+
+def test_layer_retrieval_heads_with_the_window_attend_to_the_union():
+    """With the window variant a retrieval head attends to S united with the sinks and the
+    last `window` positions; with p chosen so that S is the single top token, that is
+    the window set plus that token, checked against dense attention on those rows."""
+    import workloads
+    wl = workloads.make_workload("t", 1, [600], 4, 1, [[1]], seed=9, dtype="f32", window=64,
+                                 sinks=4, p=1e-6, classes=lambda b, k, r: ["concentrated"] * 4,
+                                 fixed_k={"concentrated": 2})
+    wl.ret_window = True
+    res = oracle.decode_step(wl)[0]
+    lay = wl.layers[0]
+    for h in range(4):
+        r = res[(0, h)]
+        win = oracle.window_positions(600, 64, 4)
+        assert np.array_equal(r.rows, np.union1d(r.sel.idx, win))
+        assert len(r.rows) >= 68
+        K = oracle.np_of(lay.K_ret[0, 0]).astype(np.float64)[r.rows]
+        V = oracle.np_of(lay.V_ret[0, 0]).astype(np.float64)[r.rows]
+        s = K @ oracle.np_of(lay.q)[0, h].astype(np.float64) * wl.scale_attn
+        e = np.exp(s - s.max())
+        assert np.allclose(r.out, (e[:, None] * V).sum(0) / e.sum(), rtol=0, atol=1e-12)

@@ -159,6 +159,7 @@ class Workload:
     layers: List[Layer]
     seed: int = 0
     topk: int = 0                          # > 0: fixed top-k selection instead of top-p
+    ret_window: bool = False               # retrieval heads also attend to sinks + window
 
     @property
     def G(self) -> int:
