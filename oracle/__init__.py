@@ -306,6 +306,75 @@ def decode_layer(layer, seq_lens, Hq: int, Hkv: int, p: float, bin_width: float,
     return res
 
 
+# ----------------------------------------------------------------------------
+# prefill of a prompt (dense causal attention for retrieval heads, causal window +
+# sinks for local heads) and the decode state it leaves
+# ----------------------------------------------------------------------------
+def prefill_rows(t: int, retrieval: bool, window: int, sinks: int) -> np.ndarray:
+    """Keys query position t attends to: every n <= t (retrieval heads), or the first
+    `sinks` positions and the last `window` positions up to t (local heads: the decode
+    window of a sequence of length t + 1)."""
+    if retrieval:
+        return np.arange(t + 1, dtype=np.int64)
+    return window_positions(t + 1, window, sinks)
+
+
+def prefill_layer(q, K, V, kv_is_retrieval, seq_lens, scale: float, window: int, sinks: int,
+                  heads: Optional[List[int]] = None, positions: Optional[List[int]] = None):
+    """Prefill attention outputs {(b, h, t): out [d] fp64} for q [B, Hq, Lmax, d] and
+    K, V [B, Hkv, Lmax, d] (fp16 or fp32), query head h on KV head h // G.  `heads` /
+    `positions` restrict the work to a sample."""
+    qn, Kn, Vn = np_of(q), np_of(K), np_of(V)
+    B, Hq = qn.shape[0], qn.shape[1]
+    Hkv = Kn.shape[1]
+    G = Hq // Hkv
+    mask = np.asarray(kv_is_retrieval)
+    res = {}
+    for b in range(B):
+        L = int(seq_lens[b])
+        for h in (heads if heads is not None else range(Hq)):
+            kv = h // G
+            for t in (positions if positions is not None else range(L)):
+                if t >= L:
+                    continue
+                rows = prefill_rows(t, bool(mask[kv]), window, sinks)
+                o, _ = attention(qn[b, h, t], Kn[b, kv], Vn[b, kv], rows, scale)
+                res[(b, h, t)] = o
+    return res
+
+
+def prefill_state(K, V, k_pre, Wk, kv_is_retrieval, seq_lens, window: int, sinks: int,
+                  Lmax: int):
+    """The decode state a prompt leaves: for retrieval KV head kv (the kr-th flagged),
+    k_idx[b, kr, n] = fl(project(k_pre[b, kv, n], Wk[kr])) in K's dtype and the K/V rows
+    copied for every n < L; for local KV heads the ring [sinks + window] holding the
+    positions of window_positions(L) at their ring slots (other slots zero)."""
+    Kn, Vn, kp, W = np_of(K), np_of(V), np_of(k_pre), np_of(Wk)
+    mask = np.asarray(kv_is_retrieval)
+    ret = [int(h) for h in np.nonzero(mask)[0]]
+    loc = [int(h) for h in np.nonzero(mask == 0)[0]]
+    B, d = Kn.shape[0], Kn.shape[-1]
+    r = W.shape[-1]
+    k_idx = np.zeros((B, len(ret), Lmax, r), Kn.dtype)
+    K_ret = np.zeros((B, len(ret), Lmax, d), Kn.dtype)
+    V_ret = np.zeros((B, len(ret), Lmax, d), Kn.dtype)
+    K_loc = np.zeros((B, len(loc), sinks + window, d), Kn.dtype)
+    V_loc = np.zeros((B, len(loc), sinks + window, d), Kn.dtype)
+    for b in range(B):
+        L = int(seq_lens[b])
+        for kr, kv in enumerate(ret):
+            for n in range(L):
+                k_idx[b, kr, n] = project(kp[b, kv, n], W[kr]).astype(Kn.dtype)
+            K_ret[b, kr, :L] = Kn[b, kv, :L]
+            V_ret[b, kr, :L] = Vn[b, kv, :L]
+        pos = window_positions(L, window, sinks)
+        slots = ring_slot(pos, window, sinks)
+        for kl, kv in enumerate(loc):
+            K_loc[b, kl, slots] = Kn[b, kv, pos]
+            V_loc[b, kl, slots] = Vn[b, kv, pos]
+    return k_idx, K_ret, V_ret, K_loc, V_loc
+
+
 def decode_step(wl, layers: Optional[List[int]] = None, heads=None, batches=None):
     """Oracle outputs for a whole workload: list (per layer) of {(b, h): HeadResult}."""
     out = []

@@ -590,3 +590,79 @@ def test_layer_retrieval_heads_with_the_window_attend_to_the_union():
         s = K @ oracle.np_of(lay.q)[0, h].astype(np.float64) * wl.scale_attn
         e = np.exp(s - s.max())
         assert np.allclose(r.out, (e[:, None] * V).sum(0) / e.sum(), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# prefill: causal attention of a prompt and the decode state it leaves
+# ---------------------------------------------------------------------------
+def _masked_attention_matrix(q, K, V, scale, allowed):
+    """Textbook masked attention in fp64: scores q K^T * scale, -inf where not allowed,
+    row softmax, times V (numpy matrix form, one call for every query)."""
+    S = q.astype(np.float64) @ K.astype(np.float64).T * scale
+    S = np.where(allowed, S, -np.inf)
+    P = np.exp(S - S.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    return P @ V.astype(np.float64)
+
+
+@pytest.mark.parametrize("dt", [np.float16, np.float32])
+def test_prefill_is_masked_dense_attention(dt):
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, L, d, window, sinks = 1, 4, 2, 150, 32, 40, 3
+    q = rng.standard_normal((B, Hq, L, d)).astype(dt)
+    K = rng.standard_normal((B, Hkv, L, d)).astype(dt)
+    V = rng.standard_normal((B, Hkv, L, d)).astype(dt)
+    res = oracle.prefill_layer(q, K, V, [1, 0], [L], 0.2, window, sinks)
+    t = np.arange(L)[:, None]
+    n = np.arange(L)[None, :]
+    causal = n <= t
+    local = causal & ((n < sinks) | (n > t - window))
+    for h in range(Hq):
+        allowed = causal if h // 2 == 0 else local
+        ref = _masked_attention_matrix(q[0, h], K[0, h // 2], V[0, h // 2], 0.2, allowed)
+        got = np.stack([res[(0, h, tt)] for tt in range(L)])
+        assert np.max(np.abs(got - ref)) <= 1e-12, h
+
+
+def test_prefill_last_row_is_the_decode_step():
+    """Query position L-1 of a prompt attends exactly like a decode step at length L:
+    p = 1 for a retrieval head (every token), the sink + window set for a local head."""
+    import workloads
+    wl = workloads.make_workload("t", 1, [300], 4, 2, [[1, 0]], seed=5, dtype="f32", p=1.0,
+                                 window=64, sinks=4)
+    lay = wl.layers[0]
+    dec = oracle.decode_step(wl)[0]
+    q = np.zeros((1, 4, 300, wl.d), np.float32)
+    q[0, :, 299] = oracle.np_of(lay.q)[0]
+    Kp = np.zeros((1, 2, 300, wl.d), np.float32)
+    Vp = np.zeros((1, 2, 300, wl.d), np.float32)
+    Kp[0, 0], Vp[0, 0] = oracle.np_of(lay.K_ret)[0, 0], oracle.np_of(lay.V_ret)[0, 0]
+    pos = oracle.window_positions(300, 64, 4)
+    slots = oracle.ring_slot(pos, 64, 4)
+    Kp[0, 1, pos] = oracle.np_of(lay.K_loc)[0, 0, slots]
+    Vp[0, 1, pos] = oracle.np_of(lay.V_loc)[0, 0, slots]
+    pre = oracle.prefill_layer(q, Kp, Vp, [1, 0], [300], wl.scale_attn, 64, 4, positions=[299])
+    for h in range(4):
+        assert np.max(np.abs(pre[(0, h, 299)] - dec[(0, h)].out)) <= 1e-12, h
+
+
+def test_prefill_state_places_the_prompt():
+    rng = np.random.default_rng(22)
+    B, Hkv, Lmax, d, r, window, sinks = 2, 2, 20, 4, 2, 6, 2
+    K = rng.standard_normal((B, Hkv, Lmax, d)).astype(np.float16)
+    V = rng.standard_normal((B, Hkv, Lmax, d)).astype(np.float16)
+    k_pre = rng.standard_normal((B, Hkv, Lmax, d)).astype(np.float32)
+    Wk = rng.standard_normal((1, d, r)).astype(np.float32)
+    k_idx, K_ret, V_ret, K_loc, V_loc = oracle.prefill_state(K, V, k_pre, Wk, [0, 1], [17, 3],
+                                                             window, sinks, Lmax)
+    # retrieval KV head 1: rows < L copied, k_idx projected; nothing past L
+    assert np.array_equal(K_ret[0, 0, :17], K[0, 1, :17]) and not K_ret[0, 0, 17:].any()
+    assert np.array_equal(k_idx[1, 0, 2], oracle.project(k_pre[1, 1, 2], Wk[0]).astype(np.float16))
+    assert not k_idx[1, 0, 3:].any()
+    # local KV head 0 at L = 17: sinks 0, 1 in slots 0, 1; positions 11..16 in 2 + n % 6
+    for n in [0, 1]:
+        assert np.array_equal(K_loc[0, 0, n], K[0, 0, n])
+    for n in range(11, 17):
+        assert np.array_equal(V_loc[0, 0, 2 + n % 6], V[0, 0, n])
+    # L = 3: only slots 0, 1 (sinks) and 2 + 2 % 6 = 4 are written
+    assert [s for s in range(8) if K_loc[1, 0, s].any()] == [0, 1, 4]
