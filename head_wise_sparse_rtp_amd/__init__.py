@@ -12,6 +12,8 @@ The names follow the C ABI in ``include/rtp.h``:
 * ``rtp_decode_step``   a whole layer: retrieval heads sparse, local heads windowed
 * ``rtp_append_project`` the step's cache update: indexer projections of the new token
   and the append of its K/V rows
+* ``rtp_prefill``       causal attention of a prompt (retrieval heads dense, local heads
+  windowed) and the decode state it leaves
 
 If the library is missing or fails to load, every call raises: there is no fallback.
 """
@@ -35,7 +37,7 @@ EXPORTED = [
     "rtp_topk_select_workspace_size", "rtp_topk_select",
     "rtp_sparse_decode_workspace_size", "rtp_sparse_decode",
     "rtp_window_decode_workspace_size", "rtp_window_decode",
-    "rtp_decode_step_workspace_size", "rtp_decode_step", "rtp_append_project",
+    "rtp_decode_step_workspace_size", "rtp_decode_step", "rtp_append_project", "rtp_prefill",
 ]
 
 _lib = None
@@ -68,6 +70,17 @@ class AppendDesc(ctypes.Structure):
         ("window", I32), ("sinks", I32), ("kv_dtype", I32),
         ("kv_is_retrieval", P), ("q_pre", P), ("k_pre", P), ("Wq_idx", P), ("Wk_idx", P),
         ("k_new", P), ("v_new", P), ("seq_lens", P), ("q_idx", P), ("k_idx", P),
+        ("K_ret", P), ("V_ret", P), ("K_loc", P), ("V_loc", P),
+    ]
+
+
+class PrefillDesc(ctypes.Structure):
+    """Mirror of rtp_prefill_desc."""
+    _fields_ = [
+        ("B", I32), ("Hq", I32), ("Hkv", I32), ("d", I32), ("r", I32), ("Lmax", I32),
+        ("window", I32), ("sinks", I32), ("kv_dtype", I32),
+        ("kv_is_retrieval", P), ("q", P), ("K", P), ("V", P), ("seq_lens", P),
+        ("scale_attn", F32), ("out", P), ("k_pre", P), ("Wk_idx", P), ("k_idx", P),
         ("K_ret", P), ("V_ret", P), ("K_loc", P), ("V_loc", P),
     ]
 
@@ -116,6 +129,8 @@ def lib():
         L.rtp_decode_step.argtypes = [ctypes.POINTER(LayerDesc), P, SZ, P]
         L.rtp_append_project.restype = I32
         L.rtp_append_project.argtypes = [ctypes.POINTER(AppendDesc), P]
+        L.rtp_prefill.restype = I32
+        L.rtp_prefill.argtypes = [ctypes.POINTER(PrefillDesc), P]
         _lib = L
     return _lib
 
@@ -348,6 +363,55 @@ def rtp_append_project(layer, seq_lens, B, Hq, Hkv, Lmax, window, sinks, q_pre, 
     """One layer's cache update in place (see AppendProject)."""
     AppendProject(layer, seq_lens, B, Hq, Hkv, Lmax, window, sinks, q_pre, k_pre, Wq, Wk,
                   k_new, v_new)(stream)
+
+
+class Prefill:
+    """Holds the descriptor of one prompt's prefill (so that repeated calls only enqueue
+    the kernels).  out [B, Hq, Lmax, d] fp32; with_state also allocates the decode state
+    (k_idx, K_ret, V_ret of the retrieval heads, the local heads' rings)."""
+
+    def __init__(self, seq_lens: torch.Tensor, mask, q: torch.Tensor, K: torch.Tensor,
+                 V: torch.Tensor, window: int, sinks: int, scale_attn: float,
+                 k_pre: Optional[torch.Tensor] = None, Wk: Optional[torch.Tensor] = None,
+                 with_state: bool = False, out: Optional[torch.Tensor] = None):
+        B, Hq, Lmax, d = q.shape
+        Hkv = K.shape[1]
+        dev = q.device
+        self.mask = (ctypes.c_uint8 * Hkv)(*[int(x) for x in mask])
+        nret = int(sum(int(x) for x in mask))
+        nloc = Hkv - nret
+        self.out = out if out is not None else torch.empty((B, Hq, Lmax, d), dtype=torch.float32,
+                                                           device=dev)
+        self.k_idx = self.K_ret = self.V_ret = self.K_loc = self.V_loc = None
+        if with_state:
+            r = Wk.shape[-1]
+            if nret:
+                self.k_idx = torch.zeros((B, nret, Lmax, r), dtype=K.dtype, device=dev)
+                self.K_ret = torch.zeros((B, nret, Lmax, d), dtype=K.dtype, device=dev)
+                self.V_ret = torch.zeros_like(self.K_ret)
+            if nloc:
+                self.K_loc = torch.zeros((B, nloc, sinks + window, d), dtype=K.dtype, device=dev)
+                self.V_loc = torch.zeros_like(self.K_loc)
+        self.keep = [seq_lens, q, K, V, k_pre, Wk]
+        self.desc = PrefillDesc(
+            B, Hq, Hkv, d, Wk.shape[-1] if Wk is not None else 16, Lmax, window, sinks,
+            _kv_dtype(q), ctypes.cast(self.mask, ctypes.c_void_p), _ptr(q), _ptr(K), _ptr(V),
+            _ptr(seq_lens), float(scale_attn), _ptr(self.out),
+            _ptr(k_pre) if self.k_idx is not None else None,
+            _ptr(Wk) if self.k_idx is not None else None, _ptr(self.k_idx), _ptr(self.K_ret),
+            _ptr(self.V_ret), _ptr(self.K_loc), _ptr(self.V_loc))
+
+    def __call__(self, stream=None):
+        _check(lib().rtp_prefill(ctypes.byref(self.desc), _stream(stream)))
+        return self.out
+
+
+def rtp_prefill(seq_lens, mask, q, K, V, window, sinks, scale_attn, k_pre=None, Wk=None,
+                with_state=False, stream=None):
+    """One prompt's prefill; returns the Prefill object (out and, with_state, the state)."""
+    pf = Prefill(seq_lens, mask, q, K, V, window, sinks, scale_attn, k_pre, Wk, with_state)
+    pf(stream)
+    return pf
 
 
 def decode_workload(wl, want_debug: bool = False, stream=None):

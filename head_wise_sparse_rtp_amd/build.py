@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librtp.so")
 SOURCES = ["rtp_api.hip", "rtp_score.hip", "rtp_select.hip", "rtp_attn.hip", "rtp_step.hip",
-           "rtp_append.hip"]
+           "rtp_append.hip", "rtp_prefill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -340,6 +340,56 @@ rtp_status rtp_append_project(const rtp_append_desc* d, void* stream) {
   return hip_status(launch_append_project(a, d->kv_dtype, (hipStream_t)stream));
 }
 
+rtp_status rtp_prefill(const rtp_prefill_desc* d, void* stream) {
+  if (!d) return RTP_EINVAL;
+  if (d->B < 1 || d->Lmax < 1 || d->Hkv < 1 || d->Hq < 1 || d->Hq % d->Hkv != 0)
+    return RTP_EINVAL;
+  const int G = d->Hq / d->Hkv;
+  if (G > kMaxG || d->Hkv > kMaxHkv || d->Lmax > (1 << 24)) return RTP_EUNSUPPORTED;
+  if (d->r != kR || d->d != kD || d->kv_dtype != RTP_F16) return RTP_EUNSUPPORTED;
+  if (!d->kv_is_retrieval || !std::isfinite(d->scale_attn)) return RTP_EINVAL;
+  PrefillArgs a{};
+  a.B = d->B;
+  a.Hq = d->Hq;
+  a.Hkv = d->Hkv;
+  a.G = G;
+  a.Lmax = d->Lmax;
+  a.window = d->window;
+  a.sinks = d->sinks;
+  a.ntile = (d->Lmax + 15) / 16;
+  for (int h = 0; h < d->Hkv; h++) {
+    a.is_ret[h] = d->kv_is_retrieval[h] ? 1 : 0;
+    a.rank[h] = a.is_ret[h] ? a.Hret++ : a.Hloc++;
+  }
+  if (!ptr_ok(d->q) || !ptr_ok(d->K) || !ptr_ok(d->V) || !ptr_ok(d->seq_lens) || !ptr_ok(d->out))
+    return RTP_EINVAL;
+  if (a.Hloc > 0) {
+    if (d->window < 1 || d->sinks < 0) return RTP_EINVAL;
+    if ((int64_t)d->window + d->sinks > (1 << 24)) return RTP_EUNSUPPORTED;
+  }
+  // optional decode state: each group all present or all absent
+  if (!opt_ptr_ok(d->k_idx) || !opt_ptr_ok(d->K_ret) || !opt_ptr_ok(d->V_ret) ||
+      !opt_ptr_ok(d->K_loc) || !opt_ptr_ok(d->V_loc))
+    return RTP_EINVAL;
+  if ((d->K_ret == nullptr) != (d->V_ret == nullptr) || (d->K_loc == nullptr) != (d->V_loc == nullptr))
+    return RTP_EINVAL;
+  if (d->k_idx && (!ptr_ok(d->k_pre) || !ptr_ok(d->Wk_idx))) return RTP_EINVAL;
+  a.seq_lens = d->seq_lens;
+  a.q = static_cast<const f16*>(d->q);
+  a.K = static_cast<const f16*>(d->K);
+  a.V = static_cast<const f16*>(d->V);
+  a.scale2 = d->scale_attn * 1.4426950408889634f;
+  a.out = d->out;
+  a.k_pre = d->k_pre;
+  a.Wk = d->Wk_idx;
+  a.k_idx = a.Hret > 0 ? static_cast<f16*>(d->k_idx) : nullptr;
+  a.K_ret = a.Hret > 0 ? static_cast<f16*>(d->K_ret) : nullptr;
+  a.V_ret = a.Hret > 0 ? static_cast<f16*>(d->V_ret) : nullptr;
+  a.K_loc = a.Hloc > 0 ? static_cast<f16*>(d->K_loc) : nullptr;
+  a.V_loc = a.Hloc > 0 ? static_cast<f16*>(d->V_loc) : nullptr;
+  return hip_status(launch_prefill(a, (hipStream_t)stream));
+}
+
 size_t rtp_decode_step_workspace_size(const rtp_layer_desc* desc) {
   StepPlan sp;
   if (plan_step(desc, sp) != RTP_OK) return 0;

@@ -1,0 +1,147 @@
+// MFMA attention tile shared by the decode step and the prefill: one wavefront scores 32
+// cache rows against 16 query columns (query heads in decode, query positions in prefill)
+// with S^T = K . Q^T on 16x16x32 fp16 MFMAs, keeps an online softmax per column, and
+// accumulates O += P . V on the same instruction.
+//
+// Method: Full Attention Strikes Back (xllm-io.github.io paper review), section 三,
+// 核心公式: softmax attention over a set of cached rows.  The accumulator layout of S^T
+// gives lane l the logits of column l%16 for rows 4*(l/16)+t, which is exactly the
+// A-operand layout of P for O += P . V (8 MFMAs, one per 16 output columns).  Output
+// column c of MFMA nb holds head-dim 8*c + nb, so each lane loads 16 contiguous bytes of
+// each V row it needs.
+#pragma once
+
+#include "rtp_internal.h"
+
+namespace rtp {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+constexpr int kAttnG = 16;               // head columns of the MFMA tile
+constexpr int kStep = 32;                // cache rows per wavefront step
+__device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA attention engine
+// ---------------------------------------------------------------------------
+struct AttnState {
+  float m;     // running max (base-2 logits) of head lane%16
+  float l;     // this lane's share of sum 2^(s - m) for head lane%16
+  f4 o[8];     // o[nb][t]: head 4*(lane/16)+t, dim 8*(lane%16)+nb
+};
+
+__device__ __forceinline__ void attn_init(AttnState& s) {
+  s.m = -INFINITY;
+  s.l = 0.0f;
+#pragma unroll
+  for (int nb = 0; nb < 8; nb++) s.o[nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// B operand of S^T = K . Q^T: head lane%16, dims 32*s + 8*(lane/16) + {0..7} in the MFMA
+// of slice s (any assignment of dims to k-slots works if K uses the same one; this one lets
+// the four lanes of a K row read 64 contiguous bytes per load)
+__device__ __forceinline__ void load_qop(const f16* __restrict__ qhead0, int G, h8 (&qop)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane & 15;
+  const int gq = lane >> 4;
+  if (h < G) {
+    const h8* p = reinterpret_cast<const h8*>(qhead0 + (size_t)h * kD + 8 * gq);
+#pragma unroll
+    for (int s = 0; s < 4; s++) qop[s] = p[4 * s];
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; s++) qop[s] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+}
+
+struct StepLoads {
+  h8 k[2][4];  // [tile][s]: K row (tile*16 + lane%16), dims 32*s + 8*gq ..
+  h8 v[8];     // [u]: V row of k-slot u (u<4: tile0 row 4gq+u; else tile1 row 4gq+u-4)
+};
+
+// rows[i] for i in 0..31 supplied through `row_of(i)` (already clamped to a valid row)
+template <class RowOf>
+__device__ __forceinline__ void step_load(const f16* __restrict__ Kb, const f16* __restrict__ Vb,
+                                          RowOf row_of, StepLoads& ld) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int gq = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    const int r = row_of(t * 16 + c);
+    const h8* p = reinterpret_cast<const h8*>(Kb + (size_t)r * kD + 8 * gq);
+#pragma unroll
+    for (int s = 0; s < 4; s++) ld.k[t][s] = p[4 * s];
+  }
+#pragma unroll
+  for (int u = 0; u < 8; u++) {
+    const int i = (u < 4) ? (4 * gq + u) : (16 + 4 * gq + (u - 4));
+    const int r = row_of(i);
+    ld.v[u] = *reinterpret_cast<const h8*>(Vb + (size_t)r * kD + 8 * c);
+  }
+}
+
+// One step over 32 rows.  active(i, h) says whether row i takes part for head h
+// (rows past the end and unselected rows are masked to -inf).
+template <class Active>
+__device__ __forceinline__ void step_compute(const StepLoads& ld, const h8 (&qop)[4], float scale2,
+                                             Active active, AttnState& st) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane & 15;
+  const int gq = lane >> 4;
+  f4 s0 = f4{0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    s0 = mfma32(ld.k[0][s], qop[s], s0);
+    s1 = mfma32(ld.k[1][s], qop[s], s1);
+  }
+  float sc[8];
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    sc[t] = active(4 * gq + t, h) ? s0[t] * scale2 : -INFINITY;
+    sc[4 + t] = active(16 + 4 * gq + t, h) ? s1[t] * scale2 : -INFINITY;
+  }
+  float mx = sc[0];
+#pragma unroll
+  for (int i = 1; i < 8; i++) mx = fmaxf(mx, sc[i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float mn = fmaxf(st.m, mx);
+  const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st.m - mn);
+  // P = hi + lo in fp16 keeps the weights at about fp32 accuracy through the fp16 MFMA
+  h8 pa, pb;
+  float psum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float pv = (sc[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[i] - mn);
+    psum += pv;
+    const f16 hi = (f16)pv;
+    pa[i] = hi;
+    pb[i] = (f16)(pv - (float)hi);
+  }
+  st.l = st.l * alpha + psum;
+  st.m = mn;
+  // rescale the output rows (heads 4gq+t) by their heads' alpha
+  float at[4];
+#pragma unroll
+  for (int t = 0; t < 4; t++) at[t] = __shfl(alpha, 4 * gq + t, 64);
+#pragma unroll
+  for (int nb = 0; nb < 8; nb++) {
+#pragma unroll
+    for (int t = 0; t < 4; t++) st.o[nb][t] *= at[t];
+  }
+#pragma unroll
+  for (int nb = 0; nb < 8; nb++) {
+    h8 vb;
+#pragma unroll
+    for (int u = 0; u < 8; u++) vb[u] = ld.v[u][nb];
+    st.o[nb] = mfma32(pa, vb, st.o[nb]);
+    st.o[nb] = mfma32(pb, vb, st.o[nb]);
+  }
+}
+
+}  // namespace rtp

@@ -235,6 +235,45 @@ typedef struct {
 } rtp_append_desc;
 rtp_status rtp_append_project(const rtp_append_desc* desc, void* stream);
 
+/*
+ * Prefill of a prompt (section 五, efficiency evaluation: local heads windowed and
+ * retrieval heads dense during prefill; section 五, test configuration: window 8192,
+ * 4 sinks).  For every sequence b, prompt position t < L = seq_lens[b] and query head
+ * h = kv*G + g:
+ *     out[b,h,t] = sum_{n in R} e^{s_n - m} V[b,kv,n] / sum_{n in R} e^{s_n - m},
+ *     s_n = scale_attn * q[b,h,t] . K[b,kv,n],  m = max s_n,
+ *     R = { n <= t } (retrieval KV head) or { n < min(sinks, t+1) } united with
+ *         { max(sinks, t+1-window) <= n <= t } (local KV head: the decode window of a
+ *         sequence of length t + 1).
+ * fp16 inputs, fp32 accumulation; rows t >= L of out are left as they are.
+ * It also writes the decode state the prompt leaves, for each group whose pointers are
+ * given (NULL skips the group):
+ *   - k_idx[b,kr,n] = the fp32 fma chain of rtp_append_project over k_pre[b,kv,n] and
+ *     Wk_idx[kr], rounded to fp16, for n < L (retrieval KV head kv, the kr-th flagged);
+ *   - K_ret/V_ret[b,kr,n] = K/V[b,kv,n] for n < L;
+ *   - K_loc/V_loc[b,kl,slot(n)] = K/V[b,kv,n] for the positions n of the final window set
+ *     (rtp_window_decode's ring; other slots are left as they are).
+ * Only fp16 (RTP_F16) is supported.  No workspace; the call never allocates.
+ */
+typedef struct {
+  int32_t B, Hq, Hkv, d, r, Lmax, window, sinks, kv_dtype;
+  const uint8_t* kv_is_retrieval; /* HOST [Hkv]: 1 = retrieval, 0 = local */
+  const void* q;                  /* [B, Hq, Lmax, d] post-RoPE queries of the prompt */
+  const void* K;                  /* [B, Hkv, Lmax, d] post-RoPE keys of the prompt */
+  const void* V;                  /* [B, Hkv, Lmax, d] */
+  const int32_t* seq_lens;        /* [B] device prompt lengths */
+  float scale_attn;
+  float* out;                     /* [B, Hq, Lmax, d] fp32 out */
+  const float* k_pre;             /* [B, Hkv, Lmax, d] fp32 pre-RoPE keys (with k_idx) */
+  const float* Wk_idx;            /* [Hret, d, r] fp32 (with k_idx) */
+  void* k_idx;                    /* [B, Hret, Lmax, r] out, or NULL */
+  void* K_ret;                    /* [B, Hret, Lmax, d] out, or NULL (together with V_ret) */
+  void* V_ret;
+  void* K_loc;                    /* [B, Hloc, sinks + window, d] out, or NULL (with V_loc) */
+  void* V_loc;
+} rtp_prefill_desc;
+rtp_status rtp_prefill(const rtp_prefill_desc* desc, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -138,6 +138,42 @@ def test_append_desc_matches_the_header():
     assert names == [f[0] for f in m.AppendDesc._fields_]
 
 
+def test_prefill_desc_matches_the_header():
+    import head_wise_sparse_rtp_amd as m
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{([^{}]*)\} rtp_prefill_desc;", src).group(1)
+    names = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if decl:
+            names += [re.findall(r"(\w+)\s*$", part.strip())[0] for part in decl.split(",")]
+    assert names == [f[0] for f in m.PrefillDesc._fields_]
+
+
+def test_prefill_validation(lib):
+    import head_wise_sparse_rtp_amd as m
+    mask = (ctypes.c_uint8 * 4)(1, 0, 0, 0)
+    d = m.PrefillDesc(1, 32, 4, 128, 16, 4096, 8192, 4, 1, ctypes.cast(mask, ctypes.c_void_p),
+                      FAKE, FAKE, FAKE, FAKE, 0.088, FAKE, None, None, None, None, None, None,
+                      None)
+    f = lambda: lib.rtp_prefill(ctypes.byref(d), None)
+    d.kv_dtype = 0
+    assert f() == -2                     # fp16 only
+    d.kv_dtype = 1
+    d.K_ret = FAKE                       # K_ret without V_ret
+    assert f() == -1
+    d.K_ret = None
+    d.k_idx = FAKE                       # k_idx without k_pre / Wk_idx
+    assert f() == -1
+    d.k_idx = None
+    d.window = 0
+    assert f() == -1
+    d.window = 8192
+    d.out = MIS
+    assert f() == -1
+    assert lib.rtp_prefill(None, None) == -1
+
+
 def test_append_project_validation(lib):
     import head_wise_sparse_rtp_amd as m
     mask = (ctypes.c_uint8 * 4)(1, 0, 0, 0)

@@ -469,3 +469,48 @@ def test_decode_step_c3_48_layers(rtp):
     say("config c3 (48 layers; all retrieval heads, 8 local query heads per layer)")
     wl = workloads.make_config("c3", device=dev())
     check_decode(rtp, wl, local_sample=8, label="c3")
+
+
+# ---------------------------------------------------------------------------
+# rtp_prefill: causal attention of a prompt and the decode state it leaves
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("lens,window,sinks", [([300, 37, 1], 64, 4), ([17], 8, 0),
+                                               ([200], 4096, 4)])
+def test_prefill_matches_oracle(rtp, lens, window, sinks):
+    say("prefill", lens, window, sinks)
+    pr = workloads.make_prompt(lens, 8, 2, [1, 0], seed=91, device=dev())
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev())
+    scale = 1.0 / math.sqrt(128)
+    pf = rtp.rtp_prefill(sl, pr.kv_is_retrieval, pr.q, pr.K, pr.V, window, sinks, scale,
+                         pr.k_pre, pr.Wk, with_state=True)
+    out = pf.out.cpu().numpy()
+    ref = oracle.prefill_layer(pr.q, pr.K, pr.V, pr.kv_is_retrieval, lens, scale, window, sinks)
+    worst = 0.0
+    for (b, h, t), o in ref.items():
+        e = max_err(out[b, h, t], o)
+        worst = max(worst, e)
+        assert e <= 2e-3, (b, h, t, e)
+    say("worst |dO|", worst)
+    want = oracle.prefill_state(pr.K, pr.V, pr.k_pre, pr.Wk, pr.kv_is_retrieval, lens, window,
+                                sinks, max(lens))
+    got = [pf.k_idx, pf.K_ret, pf.V_ret, pf.K_loc, pf.V_loc]
+    for name, g, w in zip(["k_idx", "K_ret", "V_ret", "K_loc", "V_loc"], got, want):
+        assert np.array_equal(_bits(oracle.np_of(g)), _bits(w)), name
+
+
+def test_prefill_long_prompt_sampled(rtp):
+    """A 9000-token prompt with the pages' window (8192 + 4 sinks): positions around the
+    tile edges and the window's edges, every head, against the oracle."""
+    say("prefill 9000 sampled")
+    L = 9000
+    pr = workloads.make_prompt([L], 8, 2, [1, 0], seed=92, device=dev(), with_kpre=False)
+    sl = torch.tensor([L], dtype=torch.int32, device=dev())
+    scale = 1.0 / math.sqrt(128)
+    out = rtp.rtp_prefill(sl, pr.kv_is_retrieval, pr.q, pr.K, pr.V, 8192, 4, scale).out
+    out = out.cpu().numpy()
+    pos = [0, 1, 3, 4, 15, 16, 17, 31, 32, 4099, 8191, 8192, 8195, 8196, 8197, 8211, 8212,
+           8999]
+    ref = oracle.prefill_layer(pr.q, pr.K, pr.V, pr.kv_is_retrieval, [L], scale, 8192, 4,
+                               positions=pos)
+    for (b, h, t), o in ref.items():
+        assert max_err(out[b, h, t], o) <= 2e-3, (h, t)

@@ -469,6 +469,38 @@ def make_embedding_step_inputs(wl: Workload, layer_id: int = 0, device="cpu") ->
     return StepInputs(t(q_pre), t(k_pre), t(Wq), t(Wk), t(k_new), t(v_new))
 
 
+@dataclass
+class Prompt:
+    """A prompt for prefill: post-RoPE q/K/V (fp16, counter-based N(0, 1)), pre-RoPE keys
+    for the indexer projection (fp32 N(0, 1)) and the projection weights N(0, 1/d)."""
+    kv_is_retrieval: np.ndarray   # [Hkv] uint8
+    seq_lens: np.ndarray          # [B] int32
+    q: torch.Tensor               # [B, Hq, Lmax, d] fp16
+    K: torch.Tensor               # [B, Hkv, Lmax, d] fp16
+    V: torch.Tensor
+    k_pre: torch.Tensor           # [B, Hkv, Lmax, d] fp32
+    Wk: torch.Tensor              # [Hret, d, r] fp32
+
+
+def make_prompt(seq_lens, Hq: int, Hkv: int, mask, seed: int = 0, d: int = 128, r: int = 16,
+                device="cpu", Lmax: Optional[int] = None, with_kpre: bool = True) -> Prompt:
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    B = len(seq_lens)
+    Lmax = int(Lmax if Lmax is not None else seq_lens.max())
+    q = counter_normal_f16((B, Hq, Lmax, d), seed, 11, device)
+    K = counter_normal_f16((B, Hkv, Lmax, d), seed, 12, device)
+    V = counter_normal_f16((B, Hkv, Lmax, d), seed, 13, device)
+    nret = int(np.asarray(mask).sum())
+    rng = np.random.default_rng(20_000 + seed)
+    if with_kpre:
+        k_pre = counter_normal_f16((B, Hkv, Lmax, d), seed, 14, device).float()
+    else:
+        k_pre = torch.zeros((0,), dtype=torch.float32, device=device)
+    Wk = torch.from_numpy((rng.standard_normal((max(nret, 1), d, r)) *
+                           math.sqrt(1.0 / d)).astype(np.float32)).to(device)
+    return Prompt(np.asarray(mask, dtype=np.uint8), seq_lens, q, K, V, k_pre, Wk)
+
+
 CONFIGS = {"c0": make_c0, "c1": make_c1, "c2": make_c2, "c3": make_c3, "c4": make_c4}
 
 
