@@ -195,6 +195,69 @@ def cpu_baseline(wl, bytes_per_step, budget_s):
                       "single-threaded C oracle, inputs copied to host memory" % n}
 
 
+PEAK_MFMA_F16_TFLOPS = 2500.0
+
+
+def prefill_pairs(L: int, retrieval: bool, window: int, sinks: int) -> int:
+    """Query-key pairs a prompt of length L attends: every n <= t for a retrieval head, the
+    sinks plus the last `window` positions up to t for a local head."""
+    if retrieval:
+        return L * (L + 1) // 2
+    tot = 0
+    W = window + sinks
+    full = min(L, W)
+    tot += full * (full + 1) // 2          # t + 1 <= window + sinks: every n <= t
+    tot += max(0, L - W) * W               # later: the sinks and the last `window`
+    return tot
+
+
+def bench_prefill(args):
+    """Prefill of one prompt at the decode configurations' head layout: 32 query heads on
+    4 KV heads, KV head 0 dense (retrieval), the others windowed (8192 + 4 sinks)."""
+    import torch
+    import head_wise_sparse_rtp_amd as rtp
+    import workloads
+    dev = torch.device("cuda:0")
+    L, Hq, Hkv, d, window, sinks = args.prefill, 32, 4, 128, 8192, 4
+    mask = [1, 0, 0, 0]
+    pr = workloads.make_prompt([L], Hq, Hkv, mask, seed=7, device=dev)
+    sl = torch.tensor([L], dtype=torch.int32, device=dev)
+    pf = rtp.Prefill(sl, mask, pr.q, pr.K, pr.V, window, sinks, 1.0 / math.sqrt(d), pr.k_pre,
+                     pr.Wk, with_state=True)
+    for _ in range(args.warmup):
+        pf()
+    torch.cuda.synchronize()
+    h = hip()
+    stream = torch.cuda.current_stream()
+    e0, e1 = make_events(h, 2)
+    h.hipEventRecord(e0, ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(args.steps):
+        pf()
+    h.hipEventRecord(e1, ctypes.c_void_p(stream.cuda_stream))
+    h.hipEventSynchronize(e1)
+    ms = elapsed_ms(h, e0, e1) / args.steps
+    G = Hq // Hkv
+    pairs = sum(G * prefill_pairs(L, bool(m), window, sinks) for m in mask)
+    dense = Hq * prefill_pairs(L, True, window, sinks)
+    flops = 4 * d * pairs
+    tfs = flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "prefill attention TFLOP/s (algorithmic: 4*d flops per attended query-key pair)",
+        "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_prefill": round(ms, 4), "higher_is_better": True,
+        "dtype": "f16 q/K/V, fp32 accumulation", "data": "synthetic (counter-based N(0,1))",
+        "config": {"workload": "prefill: B=1, L=%d, Hq=%d, Hkv=%d (retrieval [0]), d=%d, "
+                               "window=%d+%d sinks; with the decode state (k_idx, caches, rings)"
+                               % (L, Hq, Hkv, d, window, sinks)},
+        "attended_pairs": pairs, "dense_causal_pairs": dense,
+        "dense_over_sparse_work": round(dense / pairs, 3),
+        "roofline": {"kernel": "k_prefill_attn (MFMA 16x16x32 f16)", "bound": "mfma",
+                     "achieved": round(tfs, 2), "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tfs / PEAK_MFMA_F16_TFLOPS, 4), "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,7 +282,15 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the k_stage_a traffic summary from two rocprofv3 --pmc runs")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--prefill", type=int, default=0, metavar="L",
+                    help="time the prefill of an L-token prompt instead of the decode step")
     args = ap.parse_args()
+    if args.prefill:
+        if args.gpus != 1:
+            print("bench.py measures one GPU", file=sys.stderr, flush=True)
+            sys.exit(2)
+        bench_prefill(args)
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
                       args.copy_mib * 2 ** 20, TRAFFIC_FILE)

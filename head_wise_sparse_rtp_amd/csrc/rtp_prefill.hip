@@ -7,12 +7,16 @@
 // test configuration: window 8192, 4 sinks) and section 三, 核心公式 (the indexer
 // projection to r = 16 dims before RoPE).
 //
-// Attention: block (sequence, KV head, tile of 16 query positions), four wavefronts; each
-// wavefront takes query heads kv*G + w, w + 4, ... and runs the decode step's MFMA tile
-// with the tile's 16 positions as its columns: S^T = K . Q^T over 32 keys per step, an
-// online softmax per position, O += P . V, and a per-(key, position) mask for causality
-// and the window.  The tile's keys are its sinks followed by one contiguous run ending at
-// its last position.  Longer tiles (later positions) are launched first.
+// Attention: block (sequence, KV head, tile of 16 query positions), eight wavefronts;
+// wavefront w takes query head kv*G + w (then w + 8, ... in further passes) and runs the
+// decode step's MFMA tile with the tile's 16 positions as its columns: S^T = K . Q^T over
+// 32 keys per step, an online softmax per position, O += P . V (P as one fp16 operand),
+// and a per-(key, position)
+// mask for causality and the window.  The block stages each step's 32 K and V rows in LDS
+// once for all its wavefronts (two buffers, rows padded to 272 bytes; the next step's
+// global loads are in flight during this step's MFMAs).  The tile's keys are its sinks
+// followed by one contiguous run ending at its last position.  Longer tiles (later
+// positions) are launched first.
 #include "rtp_attn_tile.h"
 
 namespace rtp {
@@ -20,7 +24,7 @@ namespace rtp {
 namespace {
 
 constexpr int kPQ = 16;  // query positions per tile (the MFMA tile's columns)
-constexpr int kPW = 4;   // wavefronts per attention block
+constexpr int kPW = 8;   // wavefronts per attention block (query heads of one KV head)
 constexpr int kPR = 64;  // prompt rows per cache block
 
 __device__ __forceinline__ int clamp_len_p(const int32_t* seq_lens, int b, int Lmax) {
@@ -28,7 +32,72 @@ __device__ __forceinline__ int clamp_len_p(const int32_t* seq_lens, int b, int L
   return L < 0 ? 0 : (L > Lmax ? Lmax : L);
 }
 
-__global__ __launch_bounds__(kPW * 64, 2) void k_prefill_attn(PrefillArgs A) {
+constexpr int kKS = kD + 8;  // LDS row stride of a staged K/V tile (halfs): 272 bytes
+
+// One 32-row step from the staged tile, in the layout of the decode step's tile: the K
+// operands first (S^T = K . Q^T), the V operands only after the S MFMAs, so that the two
+// are never live together; P enters O += P . V as one fp16 operand (relative error 2^-11
+// per weight, against the decode step's hi + lo pair).
+template <class Active>
+__device__ __forceinline__ void step_lds(const f16* Kl, const f16* Vl, const h8 (&qop)[4],
+                                         float scale2, Active active, AttnState& st) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int gq = lane >> 4;
+  f4 s0 = f4{0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    const h8 k0 = *reinterpret_cast<const h8*>(Kl + c * kKS + 8 * gq + 32 * s);
+    const h8 k1 = *reinterpret_cast<const h8*>(Kl + (16 + c) * kKS + 8 * gq + 32 * s);
+    s0 = mfma32(k0, qop[s], s0);
+    s1 = mfma32(k1, qop[s], s1);
+  }
+  h8 vv[8];
+#pragma unroll
+  for (int u = 0; u < 8; u++) {
+    const int i = (u < 4) ? (4 * gq + u) : (16 + 4 * gq + (u - 4));
+    vv[u] = *reinterpret_cast<const h8*>(Vl + i * kKS + 8 * c);
+  }
+  float sc[8];
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    sc[t] = active(4 * gq + t, c) ? s0[t] * scale2 : -INFINITY;
+    sc[4 + t] = active(16 + 4 * gq + t, c) ? s1[t] * scale2 : -INFINITY;
+  }
+  float mx = sc[0];
+#pragma unroll
+  for (int i = 1; i < 8; i++) mx = fmaxf(mx, sc[i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float mn = fmaxf(st.m, mx);
+  const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st.m - mn);
+  h8 pa;
+  float psum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float pv = (sc[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[i] - mn);
+    psum += pv;
+    pa[i] = (f16)pv;
+  }
+  st.l = st.l * alpha + psum;
+  st.m = mn;
+  float at[4];
+#pragma unroll
+  for (int t = 0; t < 4; t++) at[t] = __shfl(alpha, 4 * gq + t, 64);
+#pragma unroll
+  for (int nb = 0; nb < 8; nb++) {
+#pragma unroll
+    for (int t = 0; t < 4; t++) st.o[nb][t] *= at[t];
+    h8 vb;
+#pragma unroll
+    for (int u = 0; u < 8; u++) vb[u] = vv[u][nb];
+    st.o[nb] = mfma32(pa, vb, st.o[nb]);
+  }
+}
+
+__global__ __launch_bounds__(kPW * 64, 4) void k_prefill_attn(PrefillArgs A) {
+  // two buffers of a 32-row K tile and V tile
+  __shared__ __align__(16) f16 kvs[2][2][kStep * kKS];
   const int qt = A.ntile - 1 - (int)(blockIdx.x % A.ntile);
   const int kv = (blockIdx.x / A.ntile) % A.Hkv;
   const int b = blockIdx.x / (A.ntile * A.Hkv);
@@ -46,47 +115,71 @@ __global__ __launch_bounds__(kPW * 64, 2) void k_prefill_attn(PrefillArgs A) {
   const int nsteps = (nent + kStep - 1) / kStep;
   const f16* Kb = A.K + ((size_t)b * A.Hkv + kv) * (size_t)A.Lmax * kD;
   const f16* Vb = A.V + ((size_t)b * A.Hkv + kv) * (size_t)A.Lmax * kD;
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
   const int c = lane & 15;
   const int gq = lane >> 4;
   auto key_of = [&](int e) { return e < ns ? e : kstart + (e - ns); };
-  for (int g = wv; g < A.G; g += kPW) {
-    const int h = kv * A.G + g;
+  // staging: thread tid moves 16 bytes of K and of V: row tid/16, piece tid%16
+  const int srow = tid >> 4, spiece = tid & 15;
+  auto fetch = [&](int step, u4& kx, u4& vx) {
+    const int e = step * kStep + srow;
+    const size_t r = (size_t)key_of(e < nent ? e : 0);
+    kx = reinterpret_cast<const u4*>(Kb + r * kD)[spiece];
+    vx = reinterpret_cast<const u4*>(Vb + r * kD)[spiece];
+  };
+  auto store = [&](int buf, const u4& kx, const u4& vx) {
+    reinterpret_cast<u4*>(&kvs[buf][0][srow * kKS])[spiece] = kx;
+    reinterpret_cast<u4*>(&kvs[buf][1][srow * kKS])[spiece] = vx;
+  };
+  // every wavefront takes one query head per pass; all take part in the staging
+  for (int g0 = 0; g0 < A.G; g0 += kPW) {
+    const int g = g0 + wv;
+    const bool has = g < A.G;
+    const int h = kv * A.G + (has ? g : 0);
     h8 qop[4];
-    load_qop(A.q + ((size_t)(b * A.Hq + h) * A.Lmax + t0) * kD, ncol, qop);
+    load_qop(A.q + ((size_t)(b * A.Hq + h) * A.Lmax + t0) * kD, has ? ncol : 0, qop);
     AttnState st;
     attn_init(st);
-    for (int s0 = 0; s0 < nsteps; s0 += 2) {
-      const int s1 = s0 + 1;
-      const int e0 = s0 * kStep, e1 = s1 * kStep;
-      StepLoads ld0, ld1;
-      step_load(Kb, Vb, [&](int i) { return key_of(e0 + i < nent ? e0 + i : 0); }, ld0);
-      if (s1 < nsteps) step_load(Kb, Vb, [&](int i) { return key_of(e1 + i < nent ? e1 + i : 0); }, ld1);
-      auto active = [&](int e, int col) {
-        if (e >= nent || col >= ncol) return false;
-        const int n = key_of(e), t = t0 + col;
-        return n <= t && (ret || n < sinks || n > t - window);
-      };
-      step_compute(ld0, qop, A.scale2, [&](int i, int col) { return active(e0 + i, col); }, st);
-      if (s1 < nsteps)
-        step_compute(ld1, qop, A.scale2, [&](int i, int col) { return active(e1 + i, col); }, st);
+    u4 kx, vx;
+    fetch(0, kx, vx);
+    store(0, kx, vx);
+    __syncthreads();
+    for (int s = 0; s < nsteps; s++) {
+      const int buf = s & 1;
+      if (s + 1 < nsteps) fetch(s + 1, kx, vx);  // in flight during this step's MFMAs
+      if (has) {
+        const int e0 = s * kStep;
+        step_lds(kvs[buf][0], kvs[buf][1], qop, A.scale2,
+                     [&](int i, int col) {
+                       const int e = e0 + i;
+                       if (e >= nent || col >= ncol) return false;
+                       const int n = key_of(e), t = t0 + col;
+                       return n <= t && (ret || n < sinks || n > t - window);
+                     },
+                     st);
+      }
+      if (s + 1 < nsteps) store(buf ^ 1, kx, vx);
+      __syncthreads();
     }
-    // lane (gq, c) holds positions 4gq+t, dims 8c + nb; every position attends to itself,
-    // so its sum is positive
-    float l = st.l;
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    if (has) {
+      // lane (gq, c) holds positions 4gq+t, dims 8c + nb; every position attends to
+      // itself, so its sum is positive
+      float l = st.l;
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
 #pragma unroll
-    for (int t = 0; t < 4; t++) {
-      const int col = 4 * gq + t;
-      const float lc = __shfl(l, col, 64);
-      if (col < ncol) {
-        const float r = 1.0f / lc;
-        float4* dst = reinterpret_cast<float4*>(
-            A.out + ((size_t)(b * A.Hq + h) * A.Lmax + t0 + col) * kD + 8 * c);
-        dst[0] = make_float4(st.o[0][t] * r, st.o[1][t] * r, st.o[2][t] * r, st.o[3][t] * r);
-        dst[1] = make_float4(st.o[4][t] * r, st.o[5][t] * r, st.o[6][t] * r, st.o[7][t] * r);
+      for (int t = 0; t < 4; t++) {
+        const int col = 4 * gq + t;
+        const float lc = __shfl(l, col, 64);
+        if (col < ncol) {
+          const float r = 1.0f / lc;
+          float4* dst = reinterpret_cast<float4*>(
+              A.out + ((size_t)(b * A.Hq + h) * A.Lmax + t0 + col) * kD + 8 * c);
+          dst[0] = make_float4(st.o[0][t] * r, st.o[1][t] * r, st.o[2][t] * r, st.o[3][t] * r);
+          dst[1] = make_float4(st.o[4][t] * r, st.o[5][t] * r, st.o[6][t] * r, st.o[7][t] * r);
+        }
       }
     }
   }
