@@ -81,13 +81,18 @@ __device__ __forceinline__ void step_lds(const f16* Kl, const f16* Vl, const h8 
   }
   st.l = st.l * alpha + psum;
   st.m = mn;
-  float at[4];
+  // the output rows need rescaling only when some column's maximum moved
+  if (__ballot(alpha != 1.0f) != 0ull) {
+    float at[4];
 #pragma unroll
-  for (int t = 0; t < 4; t++) at[t] = __shfl(alpha, 4 * gq + t, 64);
+    for (int t = 0; t < 4; t++) at[t] = __shfl(alpha, 4 * gq + t, 64);
+#pragma unroll
+    for (int nb = 0; nb < 8; nb++)
+#pragma unroll
+      for (int t = 0; t < 4; t++) st.o[nb][t] *= at[t];
+  }
 #pragma unroll
   for (int nb = 0; nb < 8; nb++) {
-#pragma unroll
-    for (int t = 0; t < 4; t++) st.o[nb][t] *= at[t];
     h8 vb;
 #pragma unroll
     for (int u = 0; u < 8; u++) vb[u] = vv[u][nb];
@@ -151,14 +156,20 @@ __global__ __launch_bounds__(kPW * 64, 4) void k_prefill_attn(PrefillArgs A) {
       if (s + 1 < nsteps) fetch(s + 1, kx, vx);  // in flight during this step's MFMAs
       if (has) {
         const int e0 = s * kStep;
+        // a full step: every key exists, lies at or before the tile's first position and
+        // (local heads) is a sink or inside every column's window; keys grow with e
+        const int ehi = e0 + kStep - 1;
+        bool full = ehi < nent && ncol == kPQ && key_of(ehi) <= t0;
+        if (!ret && ehi >= ns) full = full && key_of(max(e0, ns)) >= tend - window;
         step_lds(kvs[buf][0], kvs[buf][1], qop, A.scale2,
-                     [&](int i, int col) {
-                       const int e = e0 + i;
-                       if (e >= nent || col >= ncol) return false;
-                       const int n = key_of(e), t = t0 + col;
-                       return n <= t && (ret || n < sinks || n > t - window);
-                     },
-                     st);
+                 [&](int i, int col) {
+                   if (full) return true;
+                   const int e = e0 + i;
+                   if (e >= nent || col >= ncol) return false;
+                   const int n = key_of(e), t = t0 + col;
+                   return n <= t && (ret || n < sinks || n > t - window);
+                 },
+                 st);
       }
       if (s + 1 < nsteps) store(buf ^ 1, kx, vx);
       __syncthreads();
