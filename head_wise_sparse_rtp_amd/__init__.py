@@ -29,7 +29,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librtp.so")
 
 RTP_OK, RTP_EINVAL, RTP_EUNSUPPORTED, RTP_EWORKSPACE, RTP_EHIP = 0, -1, -2, -3, -4
-RTP_F32, RTP_F16 = 0, 1
+RTP_F32, RTP_F16, RTP_BF16 = 0, 1, 2
 NBINS = 256
 EXPORTED = [
     "rtp_status_string", "rtp_abi_version", "rtp_index_score",
@@ -160,7 +160,9 @@ def _kv_dtype(t: torch.Tensor) -> int:
         return RTP_F16
     if t.dtype == torch.float32:
         return RTP_F32
-    raise ValueError("rtp: K/V/q/k_idx must be fp16 or fp32, got %s" % t.dtype)
+    if t.dtype == torch.bfloat16:
+        return RTP_BF16
+    raise ValueError("rtp: K/V/q/k_idx must be fp16, bf16 or fp32, got %s" % t.dtype)
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:

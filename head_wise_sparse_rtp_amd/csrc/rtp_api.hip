@@ -13,7 +13,7 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
 bool opt_ptr_ok(const void* p) { return p == nullptr || aligned16(p); }
-bool dtype_ok(int32_t t) { return t == RTP_F32 || t == RTP_F16; }
+bool dtype_ok(int32_t t) { return t == RTP_F32 || t == RTP_F16 || t == RTP_BF16; }
 
 bool pow2_width(float w) {
   if (!(w > 0.0f) || !std::isfinite(w)) return false;

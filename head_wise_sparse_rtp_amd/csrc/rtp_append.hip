@@ -34,6 +34,10 @@ template <>
 __device__ __forceinline__ float to_cache<float>(float x) {
   return x;
 }
+template <>
+__device__ __forceinline__ bf16s to_cache<bf16s>(float x) {
+  return f_to_bf16(x);
+}
 
 template <typename KT>
 __global__ __launch_bounds__(64) void k_append_project(AppendArgs A) {
@@ -100,6 +104,8 @@ hipError_t launch_append_project(const AppendArgs& a, int kv_dtype, hipStream_t 
   const dim3 grid(a.B * a.Hkv * (a.G + 1));
   if (kv_dtype == 1)
     k_append_project<f16><<<grid, 64, 0, st>>>(a);
+  else if (kv_dtype == 2)
+    k_append_project<bf16s><<<grid, 64, 0, st>>>(a);
   else
     k_append_project<float><<<grid, 64, 0, st>>>(a);
   return hipGetLastError();

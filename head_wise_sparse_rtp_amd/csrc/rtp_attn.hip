@@ -47,6 +47,19 @@ struct Vec8<float> {
   }
 };
 
+template <>
+struct Vec8<bf16s> {
+  uint4 v;  // 8 bfloat16 values, two per word
+  __device__ __forceinline__ void load(const bf16s* __restrict__ p) {
+    v = *reinterpret_cast<const uint4*>(p);
+  }
+  __device__ __forceinline__ float at(int i) const {
+    const int j = i >> 1;
+    const uint32_t w = j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
+    return bf16_to_f((i & 1) ? (w >> 16) : (w & 0xFFFFu));
+  }
+};
+
 __device__ __forceinline__ int clamp_len(const int32_t* seq_lens, int b, int Lmax) {
   int L = seq_lens[b];
   return L < 0 ? 0 : (L > Lmax ? Lmax : L);
@@ -355,6 +368,10 @@ hipError_t launch_sparse_partial(const void* q, const void* K, const void* V, in
     k_sparse_partial<f16><<<(int)blocks, kThreads, 0, st>>>(
         (const f16*)q, (const f16*)K, (const f16*)V, sel_idx, sel_count, cap, map, Hq, Hr, G,
         Lmax, scale2, BH, maxs, pa.m, pa.l, pa.acc);
+  } else if (kv_dtype == 2) {
+    k_sparse_partial<bf16s><<<(int)blocks, kThreads, 0, st>>>(
+        (const bf16s*)q, (const bf16s*)K, (const bf16s*)V, sel_idx, sel_count, cap, map, Hq, Hr,
+        G, Lmax, scale2, BH, maxs, pa.m, pa.l, pa.acc);
   } else {
     k_sparse_partial<float><<<(int)blocks, kThreads, 0, st>>>(
         (const float*)q, (const float*)K, (const float*)V, sel_idx, sel_count, cap, map, Hq, Hr,
@@ -381,6 +398,13 @@ hipError_t launch_window_partial(const void* q, const void* K, const void* V, in
       case 4: RTP_WIN(f16, 4); break;
       case 2: RTP_WIN(f16, 2); break;
       default: RTP_WIN(f16, 1); break;
+    }
+  } else if (kv_dtype == 2) {
+    switch (GG) {
+      case 8: RTP_WIN(bf16s, 8); break;
+      case 4: RTP_WIN(bf16s, 4); break;
+      case 2: RTP_WIN(bf16s, 2); break;
+      default: RTP_WIN(bf16s, 1); break;
     }
   } else {
     switch (GG) {

@@ -22,6 +22,14 @@ constexpr int kMerge1 = 16;     // chunk partials merged by one first-level merg
 constexpr int kEmptyCell = INT_MIN;
 
 typedef _Float16 f16;
+typedef uint16_t bf16s;  // bfloat16 storage: the upper 16 bits of an fp32
+
+__device__ __forceinline__ float bf16_to_f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+// round to nearest, ties to even (finite inputs)
+__device__ __forceinline__ bf16s f_to_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (bf16s)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
 
 // Row space of the retrieval kernels: row = kr * G + g for packed retrieval KV head
 // kr and query head g of that KV head.  `kv[kr]` is the KV head id in the layer, used

@@ -58,6 +58,22 @@ struct Row16<float> {
   }
 };
 
+template <>
+struct Row16<bf16s> {
+  uint4 a, b;  // 16 bfloat16 values, two per word
+  __device__ __forceinline__ void load(const bf16s* __restrict__ p) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    a = q[0];
+    b = q[1];
+  }
+  __device__ __forceinline__ float at(int i) const {
+    const uint4& x = i < 8 ? a : b;
+    const int j = (i & 7) >> 1;
+    const uint32_t w = j == 0 ? x.x : (j == 1 ? x.y : (j == 2 ? x.z : x.w));
+    return bf16_to_f((i & 1) ? (w >> 16) : (w & 0xFFFFu));
+  }
+};
+
 // fp32 fused multiply-add chain over the 16 features, in index order.
 template <typename KT>
 __device__ __forceinline__ float fma_chain(const float* q, const Row16<KT>& k) {
@@ -332,6 +348,13 @@ hipError_t launch_index_score(const float* q_idx, const void* k_idx, int k_dtype
       case 2: RTP_SCORE_LAUNCH(f16, 2); break;
       default: RTP_SCORE_LAUNCH(f16, 1); break;
     }
+  } else if (k_dtype == 2) {
+    switch (GG) {
+      case 8: RTP_SCORE_LAUNCH(bf16s, 8); break;
+      case 4: RTP_SCORE_LAUNCH(bf16s, 4); break;
+      case 2: RTP_SCORE_LAUNCH(bf16s, 2); break;
+      default: RTP_SCORE_LAUNCH(bf16s, 1); break;
+    }
   } else {
     switch (GG) {
       case 8: RTP_SCORE_LAUNCH(float, 8); break;
@@ -382,6 +405,14 @@ hipError_t launch_hist_from_kidx(const float* q_idx, const void* k_idx, int k_dt
       case 4: return RTP_HK(f16, 4);
       case 2: return RTP_HK(f16, 2);
       default: return RTP_HK(f16, 1);
+    }
+  }
+  if (k_dtype == 2) {
+    switch (GG) {
+      case 8: return RTP_HK(bf16s, 8);
+      case 4: return RTP_HK(bf16s, 4);
+      case 2: return RTP_HK(bf16s, 2);
+      default: return RTP_HK(bf16s, 1);
     }
   }
   switch (GG) {

@@ -26,8 +26,11 @@
  *     next synchronisation.
  *   - Supported shapes: r = 16 (indexer size), d = 128 (head size), 1 <= G <= 64,
  *     1 <= Lmax <= 2^24.  Inputs must be finite.
- *   - dtype codes: RTP_F32 (fp32) or RTP_F16 (IEEE binary16).  q, K, V and k_idx use
- *     the given dtype; q_idx and every output are fp32; accumulation is fp32.
+ *   - dtype codes: RTP_F32 (fp32), RTP_F16 (IEEE binary16) or RTP_BF16 (bfloat16: the
+ *     upper half of an fp32).  q, K, V and k_idx use the given dtype; q_idx and every
+ *     output are fp32; accumulation is fp32.  Every stored value converts to fp32
+ *     exactly; values written in a cache dtype (rtp_append_project, rtp_prefill) are
+ *     rounded to nearest, ties to even.
  *   - A sequence with length 0 yields out = 0, lse = -inf, sel_count = 0.
  *   - Results are deterministic: repeated calls on the same inputs are bitwise equal.
  */
@@ -51,7 +54,7 @@ enum {
   RTP_EWORKSPACE = -3,    /* ws_bytes below the size query */
   RTP_EHIP = -4           /* a HIP launch failed */
 };
-enum { RTP_F32 = 0, RTP_F16 = 1 };
+enum { RTP_F32 = 0, RTP_F16 = 1, RTP_BF16 = 2 };
 
 /* Static description of a status code. */
 const char* rtp_status_string(rtp_status s);
@@ -193,8 +196,9 @@ typedef struct {
 /* fp16 caches with G <= 16 run four kernels per call: indexer score + chunk histograms;
  * per-head suffix tables of the bin masses (token counts under top-k); selection +
  * sparse attention together with the window attention of local heads; merge of the
- * split partials.  Other shapes run the single-purpose kernels in sequence.  The
- * workspace needs no initialisation; calls that may overlap must not share one. */
+ * split partials.  Other shapes (bf16 or fp32 caches, G > 16) run the single-purpose
+ * kernels in sequence.  The workspace needs no initialisation; calls that may overlap
+ * must not share one. */
 size_t rtp_decode_step_workspace_size(const rtp_layer_desc* desc);
 rtp_status rtp_decode_step(const rtp_layer_desc* desc, void* ws, size_t ws_bytes, void* stream);
 

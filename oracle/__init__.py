@@ -68,6 +68,8 @@ def lib():
                                        P, P]
         L.rtpo_project.restype = None
         L.rtpo_project.argtypes = [P, P, ctypes.c_int, ctypes.c_int, P]
+        L.rtpo_round_bf16.restype = ctypes.c_double
+        L.rtpo_round_bf16.argtypes = [ctypes.c_double]
         L.rtpo_attention.restype = None
         L.rtpo_attention.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int64,
                                      ctypes.c_double, P, P]
@@ -88,10 +90,28 @@ def _dtype_code(a: np.ndarray) -> int:
 
 
 def np_of(x) -> np.ndarray:
-    """numpy view of a CPU array or torch tensor (no arithmetic)."""
+    """numpy view of a CPU array or torch tensor (no arithmetic; bfloat16 tensors become
+    fp32 arrays, which hold every bfloat16 value exactly)."""
     if hasattr(x, "detach"):
-        x = x.detach().cpu().numpy()
+        x = x.detach()
+        if str(x.dtype) == "torch.bfloat16":
+            x = x.float()
+        x = x.cpu().numpy()
     return np.ascontiguousarray(x)
+
+
+def round_bf16(x) -> np.ndarray:
+    """Each value rounded to bfloat16 (see rtp_oracle.c), as fp32."""
+    a = np.asarray(x, dtype=np.float64)
+    f = lib().rtpo_round_bf16
+    return np.array([f(float(v)) for v in a.ravel()], dtype=np.float32).reshape(a.shape)
+
+
+def _to_cache(values, like) -> np.ndarray:
+    """Values stored into a cache of `like`'s dtype (round to nearest even)."""
+    if hasattr(like, "dtype") and str(like.dtype) == "torch.bfloat16":
+        return round_bf16(values)
+    return np.asarray(values).astype(np_of(like[:0]).dtype if hasattr(like, "detach") else like.dtype)
 
 
 # ----------------------------------------------------------------------------
@@ -195,7 +215,7 @@ def append_project(layer, new_lens, q_pre, k_pre, k_new, v_new, Wq, Wk, window: 
             for g in range(G):
                 h = kv * G + g
                 q_idx[b, h] = project(q_pre[b, h], Wq[h])
-            k_idx[b, kr, n] = project(k_pre[b, kv], Wk[kr]).astype(k_idx.dtype)
+            k_idx[b, kr, n] = _to_cache(project(k_pre[b, kv], Wk[kr]), layer.k_idx)
             K_ret[b, kr, n] = k_new[b, kv]
             V_ret[b, kr, n] = v_new[b, kv]
         for kl, kv in enumerate(loc):

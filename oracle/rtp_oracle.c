@@ -88,6 +88,23 @@ void rtpo_project(const float* x, const float* W, int d, int r, float* out) {
   }
 }
 
+/* bfloat16 rounding, from the format: 8 significant bits (7 stored) with fp32's exponent
+ * range, round to nearest with ties to even; below 2^-126 the spacing is fixed at 2^-133
+ * (subnormals).  Returns the rounded value. */
+double rtpo_round_bf16(double x) {
+  if (x == 0.0 || !isfinite(x)) return x;
+  const double ax = fabs(x);
+  double r;
+  if (ax < ldexp(1.0, -126)) {
+    r = nearbyint(ax * ldexp(1.0, 133)) * ldexp(1.0, -133);
+  } else {
+    int e;
+    const double m = frexp(ax, &e);          /* ax = m 2^e, m in [0.5, 1) */
+    r = ldexp(nearbyint(ldexp(m, 8)), e - 8); /* 8 significant bits, ties to even */
+  }
+  return x < 0 ? -r : r;
+}
+
 /* Cell of a logit on the global grid of width w (w a power of two). */
 static int64_t cell_of(float z, double w) { return (int64_t)floor((double)z / w); }
 

@@ -210,7 +210,7 @@ def test_sparse_and_window_validation(lib):
     assert f(*a) == -2                  # d != 128
     a = list(ok); a[16] = nb - 1
     assert f(*a) == -3
-    a = list(ok); a[3] = 2
+    a = list(ok); a[3] = 5
     assert f(*a) == -2                  # bad dtype
     nbw = lib.rtp_window_decode_workspace_size(1, 3, 8, 8192, 4)
     g = lib.rtp_window_decode

@@ -39,7 +39,8 @@ def dev():
 # rtp_index_score
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype,G,lens", [("f16", 8, [5000, 1, 2049]), ("f32", 1, [4097]),
-                                          ("f16", 3, [700, 3]), ("f32", 4, [2048, 2047])])
+                                          ("f16", 3, [700, 3]), ("f32", 4, [2048, 2047]),
+                                          ("bf16", 8, [5000, 1, 2049])])
 def test_index_score_bit_exact(rtp, dtype, G, lens):
     say("index_score", dtype, G, lens)
     Hkv = 2
@@ -171,7 +172,7 @@ def test_topp_select_empty_and_capped(rtp):
 # ---------------------------------------------------------------------------
 # rtp_sparse_decode
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("dtype", ["f16", "f32", "bf16"])
 def test_sparse_decode_matches_oracle(rtp, dtype):
     say("sparse_decode", dtype)
     lens = [6000, 300]
@@ -216,6 +217,7 @@ def test_sparse_decode_matches_oracle(rtp, dtype):
     ("f32", 64, 4, [2, 68, 1000]),
     ("f16", 100, 0, [50, 100, 101, 333]),
     ("f16", 8192, 4, [8196, 9000, 4000]),
+    ("bf16", 64, 4, [1, 3, 4, 5, 67, 68, 69, 500]),
 ])
 def test_window_decode_matches_oracle(rtp, dtype, window, sinks, lens):
     say("window_decode", dtype, window, sinks, lens)
@@ -289,7 +291,7 @@ def check_decode(rtp, wl, local_sample=None, layers=None, label="", oracle_layer
     return res
 
 
-@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("dtype", ["f16", "f32", "bf16"])
 @pytest.mark.parametrize("p", [0.5, 0.9, 1.0])
 def test_decode_step_small_ragged(rtp, dtype, p):
     say("decode_step small", dtype, p)
@@ -349,7 +351,7 @@ def _oracle_layer(lay, arrays):
                            V_loc)
 
 
-@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("dtype", ["f16", "f32", "bf16"])
 def test_append_project_bit_exact(rtp, dtype):
     """Projections are fp32 fma chains in input order on both sides and the rows are
     copies: every cache array must match bit for bit (ring wrap, a sink position, an
@@ -449,6 +451,14 @@ def test_decode_step_deterministic(rtp):
     b = rtp.decode_workload(wl, want_debug=True)[0]
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_decode_step_bf16_64k(rtp):
+    """bfloat16 caches at the 64K layout (single-purpose kernels)."""
+    say("bf16 64K")
+    wl = workloads.make_workload("c1-bf16", 1, [65536], 32, 4, [[1, 0, 0, 0]], seed=1,
+                                 dtype="bf16", device=dev())
+    check_decode(rtp, wl, label="c1-bf16")
 
 
 @pytest.mark.parametrize("name", ["c0", "c1", "c2", "c4"])

@@ -666,3 +666,16 @@ def test_prefill_state_places_the_prompt():
         assert np.array_equal(V_loc[0, 0, 2 + n % 6], V[0, 0, n])
     # L = 3: only slots 0, 1 (sinks) and 2 + 2 % 6 = 4 are written
     assert [s for s in range(8) if K_loc[1, 0, s].any()] == [0, 1, 4]
+
+
+def test_round_bf16_ties_and_library_conversion():
+    # 1 + 2^-8 lies halfway between bf16 1 and 1 + 2^-7: ties to even give 1; 1 + 3 * 2^-8
+    # lies halfway between 1 + 2^-7 and 1 + 2^-6: ties to even give 1 + 2^-6
+    assert oracle.round_bf16([1 + 2 ** -8])[0] == 1.0
+    assert oracle.round_bf16([1 + 3 * 2 ** -8])[0] == 1 + 2 ** -6
+    assert oracle.round_bf16([-(1 + 3 * 2 ** -8)])[0] == -(1 + 2 ** -6)
+    rng = np.random.default_rng(31)
+    x = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-30, 30, 4000),
+                        np.array([0.0, 3e-39, -1e-40, 2.0 ** -126, 1e38])]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(oracle.round_bf16(x), want)

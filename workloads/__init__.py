@@ -151,7 +151,7 @@ class Workload:
     seq_lens: np.ndarray                   # [B] int32
     window: int
     sinks: int
-    dtype: str                             # "f16" | "f32"  (K, V, q, k_idx)
+    dtype: str                             # "f16" | "bf16" | "f32"  (K, V, q, k_idx)
     p: float
     bin_width: float
     scale_idx: float
@@ -273,14 +273,14 @@ def make_layer(seed: int, layer_id: int, B: int, seq_lens, Lmax: int, Hq: int, H
     ret = [int(h) for h in np.nonzero(mask)[0]]
     loc = [int(h) for h in np.nonzero(mask == 0)[0]]
     rng = rng if rng is not None else np.random.default_rng(seed * 7919 + layer_id)
-    tdt = torch.float16 if dtype == "f16" else torch.float32
-    ndt = np.float16 if dtype == "f16" else np.float32
+    tdt = {"f16": torch.float16, "f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    ndt = np.float16 if dtype == "f16" else np.float32   # bf16 keys are rounded on assignment
     base = 1000 * layer_id
 
-    # attention tensors from the counter-based generator
+    # attention tensors from the counter-based generator (bf16: its fp16 values rounded)
     def cn(shape, stream):
         t = counter_normal_f16(shape, seed, base + stream, device)
-        return t if tdt == torch.float16 else t.float()
+        return t if tdt == torch.float16 else t.to(tdt)
 
     q = cn((B, Hq, d), 1)
     K_ret = cn((B, len(ret), Lmax, d), 2)
@@ -421,13 +421,14 @@ def make_step_inputs(wl: Workload, layer_id: int = 0, seed: int = 0, device="cpu
     B, Hq, Hkv, d, r = wl.B, wl.Hq, wl.Hkv, wl.d, wl.r
     kv = np.float16 if wl.dtype == "f16" else np.float32
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    tkv = (lambda a: t(a).to(torch.bfloat16)) if wl.dtype == "bf16" else t
     q_pre = rng.standard_normal((B, Hq, d)).astype(np.float32)
     k_pre = rng.standard_normal((B, Hkv, d)).astype(np.float32)
     Wq = (rng.standard_normal((Hq, d, r)) * math.sqrt(1.0 / d)).astype(np.float32)
     Wk = (rng.standard_normal((max(nret, 1), d, r)) * math.sqrt(1.0 / d)).astype(np.float32)
     k_new = rng.standard_normal((B, Hkv, d)).astype(kv)
     v_new = rng.standard_normal((B, Hkv, d)).astype(kv)
-    return StepInputs(t(q_pre), t(k_pre), t(Wq), t(Wk), t(k_new), t(v_new))
+    return StepInputs(t(q_pre), t(k_pre), t(Wq), t(Wk), tkv(k_new), tkv(v_new))
 
 
 def make_embedding_step_inputs(wl: Workload, layer_id: int = 0, device="cpu") -> StepInputs:
@@ -445,9 +446,9 @@ def make_embedding_step_inputs(wl: Workload, layer_id: int = 0, device="cpu") ->
     q_pre = np.zeros((B, Hq, d), np.float32)
     q_pre[:, :, :r] = q_idx
     k_pre = np.zeros((B, Hkv, d), np.float32)
-    kv_np = lay.K_ret.detach().cpu().numpy() if ret else lay.K_loc.detach().cpu().numpy()
-    k_new = np.zeros((B, Hkv, d), kv_np.dtype)
-    v_new = np.zeros((B, Hkv, d), kv_np.dtype)
+    kdt = lay.K_ret.dtype if ret else lay.K_loc.dtype
+    k_new = torch.zeros((B, Hkv, d), dtype=kdt)
+    v_new = torch.zeros((B, Hkv, d), dtype=kdt)
     eye = np.zeros((d, r), np.float32)
     eye[np.arange(r), np.arange(r)] = 1.0
     Wq = np.broadcast_to(eye, (Hq, d, r)).copy()
@@ -458,15 +459,15 @@ def make_embedding_step_inputs(wl: Workload, layer_id: int = 0, device="cpu") ->
             continue
         n = L - 1
         for kr, kv in enumerate(ret):
-            k_pre[b, kv, :r] = lay.k_idx[b, kr, n].detach().cpu().numpy().astype(np.float32)
-            k_new[b, kv] = lay.K_ret[b, kr, n].detach().cpu().numpy()
-            v_new[b, kv] = lay.V_ret[b, kr, n].detach().cpu().numpy()
+            k_pre[b, kv, :r] = lay.k_idx[b, kr, n].detach().float().cpu().numpy()
+            k_new[b, kv] = lay.K_ret[b, kr, n].detach().cpu()
+            v_new[b, kv] = lay.V_ret[b, kr, n].detach().cpu()
         for kl, kv in enumerate(loc):
             slot = n if n < wl.sinks else wl.sinks + n % wl.window
-            k_new[b, kv] = lay.K_loc[b, kl, slot].detach().cpu().numpy()
-            v_new[b, kv] = lay.V_loc[b, kl, slot].detach().cpu().numpy()
+            k_new[b, kv] = lay.K_loc[b, kl, slot].detach().cpu()
+            v_new[b, kv] = lay.V_loc[b, kl, slot].detach().cpu()
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
-    return StepInputs(t(q_pre), t(k_pre), t(Wq), t(Wk), t(k_new), t(v_new))
+    return StepInputs(t(q_pre), t(k_pre), t(Wq), t(Wk), k_new.to(device), v_new.to(device))
 
 
 @dataclass
