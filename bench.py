@@ -65,7 +65,7 @@ def algorithmic_bytes(rtp, wl, layer, torch, topk=0, ret_window=False):
     softmax mass that its selected set holds (outside any timed region)."""
     dev = layer.q.device
     sl = torch.as_tensor(wl.seq_lens, dtype=torch.int32, device=dev)
-    e_idx = 2 if wl.dtype == "f16" else 4
+    e_idx = 4 if wl.dtype == "f32" else 2
     e_kv = e_idx
     total = 0
     detail = {"kidx": 0, "sparse_kv": 0, "window_kv": 0, "union_tokens": 0, "sel_tokens": [],
@@ -267,6 +267,8 @@ def main():
     ap.add_argument("--p", type=float, default=None)
     ap.add_argument("--topk", type=int, default=0,
                     help="fixed top-k through the histogram instead of top-p")
+    ap.add_argument("--dtype", default="f16", choices=["f16", "bf16"],
+                    help="cache dtype of the single-layer configs (bf16: single-purpose kernels)")
     ap.add_argument("--ret-window", action="store_true",
                     help="retrieval heads also attend to the sinks and the window")
     ap.add_argument("--with-append", action="store_true",
@@ -308,6 +310,8 @@ def main():
 
     dev = torch.device("cuda:0")
     kw = {} if args.p is None else {"p": args.p}
+    if args.dtype != "f16":
+        kw["dtype"] = args.dtype
     wl = workloads.make_config(args.workload, device=dev, **kw)
     assert len(wl.layers) == 1, "bench.py times single-layer workloads"
     layer = wl.layers[0]
@@ -445,7 +449,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 K/V, fp32 accumulation",
+        "dtype": "%s K/V, fp32 accumulation" % args.dtype,
         "data": "synthetic (seeded planted-logit indexer keys, counter-based N(0,1) K/V)",
         "config": {"workload": "%s: B=%d, L=%d, Hq=%d, Hkv=%d (retrieval %s), d=%d, r=%d, "
                                "window=%d+%d sinks, %s" % (

@@ -362,13 +362,15 @@ def make_c0(device="cpu", p: float = 0.9) -> Workload:
                     p, 0.125, 0.25, 1.0 / math.sqrt(d), [lay], 0)
 
 
-def make_c1(device="cpu", p: float = 0.9, L: int = 65536) -> Workload:
+def make_c1(device="cpu", p: float = 0.9, L: int = 65536, dtype: str = "f16") -> Workload:
     """One layer, B=1, L=64K, 32 q heads / 4 KV heads; KV head 0 retrieval (q heads 0-3
     concentrated, 4-7 broad), KV heads 1-3 local.  Seed 1."""
-    return make_workload("c1", 1, [L], 32, 4, [[1, 0, 0, 0]], seed=1, p=p, device=device)
+    return make_workload("c1", 1, [L], 32, 4, [[1, 0, 0, 0]], seed=1, p=p, device=device,
+                         dtype=dtype)
 
 
-def make_c2(device="cpu", p: float = 0.9, L: int = 131072, B: int = 8) -> Workload:
+def make_c2(device="cpu", p: float = 0.9, L: int = 131072, B: int = 8,
+            dtype: str = "f16") -> Workload:
     """One layer, B=8, L=128K each, KV head 0 retrieval; per sequence b a generator seeded
     2000+b picks which 4 of the 8 query heads are concentrated (the rest broad)."""
     def classes(b, ki, _rng):
@@ -376,7 +378,7 @@ def make_c2(device="cpu", p: float = 0.9, L: int = 131072, B: int = 8) -> Worklo
         conc = set(rb.permutation(8)[:4].tolist())
         return ["concentrated" if g in conc else "broad" for g in range(8)]
     return make_workload("c2", B, [L] * B, 32, 4, [[1, 0, 0, 0]], seed=2, p=p, device=device,
-                         classes=classes)
+                         classes=classes, dtype=dtype)
 
 
 def c3_masks(layers: int = 48, hkv: int = 4, n_ret: int = 29, seed: int = 3):
@@ -391,13 +393,14 @@ def make_c3(device="cpu", p: float = 0.9, L: int = 524288, layers: int = 48) -> 
     return make_workload("c3", 1, [L], 32, 4, c3_masks(layers), seed=3, p=p, device=device)
 
 
-def make_c4(device="cpu", p: float = 0.9, L: int = 1048576) -> Workload:
+def make_c4(device="cpu", p: float = 0.9, L: int = 1048576, dtype: str = "f16") -> Workload:
     """One layer, B=1, L=1M, KV head 0 retrieval: q heads 0-1 needle (2 tokens), 2-5 mid
     (~500 tokens), 6-7 broad (~8.5k tokens, logits N(2, 0.5)).  Seed 4."""
     def classes(b, ki, _rng):
         return ["needle"] * 2 + ["mid"] * 4 + ["broad"] * 2
     return make_workload("c4", 1, [L], 32, 4, [[1, 0, 0, 0]], seed=4, p=p, device=device,
-                         classes=classes, fixed_k={"needle": 2, "mid": 500, "broad": 8500})
+                         classes=classes, fixed_k={"needle": 2, "mid": 500, "broad": 8500},
+                         dtype=dtype)
 
 
 @dataclass
