@@ -156,7 +156,12 @@ __device__ void block_combine(AttnState& st, int G, int nact, float* lds, float*
 // masses and codes of the chunk-histogram kernel of rtp_score.hip, then suffix sums
 // of the bin masses.
 // ---------------------------------------------------------------------------
-constexpr int kCopies = 4;  // histogram copies per head (lane bits 3..4)
+// histogram copies per head: lane bits 3..4 (512-thread blocks) or bit 3 (256-thread
+// blocks); either way a copy takes at most 512 tokens of a head, so no counter overflows
+template <int NT>
+constexpr int copies_of() {
+  return NT >= 512 ? 4 : 2;
+}
 constexpr int kPad = 1;
 // y of a token past the sequence's end: finite and far below every cell, so that its
 // mass is exactly zero and it lands in the tail bin (with unit weights it is taken back
@@ -261,7 +266,8 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
   constexpr int NWV = NT / 64;
   constexpr int GG = 8;
   uint32_t* hist = reinterpret_cast<uint32_t*>(smem);
-  float* smax = reinterpret_cast<float*>(smem + sizeof(uint32_t) * kCopies * GG * (kNB + kPad));
+  constexpr int CP = copies_of<NT>();
+  float* smax = reinterpret_cast<float*>(smem + sizeof(uint32_t) * CP * GG * (kNB + kPad));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -303,7 +309,7 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
       qlo[i] = (f16)(v - (float)hi);
     }
   }
-  for (int i = tid; i < kCopies * GG * (kNB + kPad); i += NT) hist[i] = 0u;
+  for (int i = tid; i < CP * GG * (kNB + kPad); i += NT) hist[i] = 0u;
 
   // ---- pass 1: y = fl32(a * scale) / w (exact: w is a power of two) and the top cell
   float y[8][4];
@@ -343,7 +349,7 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
   const float c = P.c_log2;
   const float Kt = Acf - 255.0f;
   const float c22 = 22.0f - c;  // x * 2^22 = 2^((y - m - 1) c + 22)
-  uint32_t* hrow = hist + (((lane >> 3) & 3) * GG + hh) * (kNB + kPad);
+  uint32_t* hrow = hist + (((lane >> 3) & (CP - 1)) * GG + hh) * (kNB + kPad);
   // code words pass through LDS ([wave][head][64 words]) so that the global stores
   // cover whole 256-byte runs per head
   uint32_t* cl = reinterpret_cast<uint32_t*>(smax + GG * NWV) + (wv * GG + hh) * 64 + 4 * th + kq;
@@ -390,7 +396,7 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
     for (int u = 0; u < 4; u++) {
       unsigned long long sum = 0ull;
 #pragma unroll
-      for (int cp = 0; cp < kCopies; cp++) sum += hist[(cp * GG + gg) * (kNB + kPad) + jb + u];
+      for (int cp = 0; cp < CP; cp++) sum += hist[(cp * GG + gg) * (kNB + kPad) + jb + u];
       if (P.counts && jb + u == kNB - 1) sum -= (unsigned long long)ninv << 22;
       const float sf = __builtin_fmaf((float)(uint32_t)(sum >> 32), 4294967296.0f, (float)(uint32_t)sum);
       mloc[u] = sf * fj[u];
@@ -417,7 +423,7 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
 // One histogram unit per block: two blocks per CU hide the latency of the histogram
 // pass better than a block that prefetches a second unit.
 template <int NT>
-__global__ __launch_bounds__(NT, 2) void k_stage_a(StageAParams P) {
+__global__ __launch_bounds__(NT, NT >= 512 ? 2 : 4) void k_stage_a(StageAParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   const HistUnit U = hist_unit<NT>(P, blockIdx.x);
   HistIn in;
@@ -1209,8 +1215,9 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     P.sufq = at<unsigned long long>(ws, sp.sufq);
     P.nunits = B * sp.Hret * P.ngg * sp.nchunk;
     // histogram copies, the top cells of the wavefronts, the code words of the wavefronts
-    const size_t ldsA = sizeof(uint32_t) * kCopies * GG * (kNB + kPad) + sizeof(float) * GG * 8 +
-                        sizeof(uint32_t) * 8 * GG * 64;
+    const int cpA = sp.nt >= 512 ? copies_of<512>() : copies_of<256>();
+    const size_t ldsA = sizeof(uint32_t) * cpA * GG * (kNB + kPad) + sizeof(float) * GG * 8 +
+                        sizeof(uint32_t) * (sp.nt / 64) * GG * 64;
     const int nA = P.nunits;
 #define RTP_STAGE_A(NTV) k_stage_a<NTV><<<nA, NTV, ldsA, st>>>(P)
     if (sp.nt == 256)
