@@ -383,7 +383,7 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, 3)
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr, flush=True)
         sys.exit(2)
 
