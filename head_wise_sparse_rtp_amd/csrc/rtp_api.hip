@@ -426,6 +426,7 @@ rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, v
     a.Lmax = d->Lmax;
     a.window = d->window;
     a.sinks = d->sinks;
+    a.kv_dtype = d->kv_dtype;
     a.seq_lens = d->seq_lens;
     a.q = d->q;
     a.q_idx = d->q_idx;

@@ -16,6 +16,15 @@
 namespace rtp {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+// operand vectors of the MFMA tile for an element type: _Float16 (fp16 caches) or
+// __bf16 (bfloat16 caches); h8 is v8<f16>
+typedef __bf16 bf16e;
+template <typename T>
+struct V8T {
+  typedef T type __attribute__((ext_vector_type(8)));
+};
+template <typename T>
+using v8 = typename V8T<T>::type;
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
@@ -23,6 +32,9 @@ constexpr int kAttnG = 16;               // head columns of the MFMA tile
 constexpr int kStep = 32;                // cache rows per wavefront step
 __device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mfma32(v8<bf16e> a, v8<bf16e> b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -44,36 +56,40 @@ __device__ __forceinline__ void attn_init(AttnState& s) {
 // B operand of S^T = K . Q^T: head lane%16, dims 32*s + 8*(lane/16) + {0..7} in the MFMA
 // of slice s (any assignment of dims to k-slots works if K uses the same one; this one lets
 // the four lanes of a K row read 64 contiguous bytes per load)
-__device__ __forceinline__ void load_qop(const f16* __restrict__ qhead0, int G, h8 (&qop)[4]) {
+template <typename T>
+__device__ __forceinline__ void load_qop(const T* __restrict__ qhead0, int G, v8<T> (&qop)[4]) {
   const int lane = threadIdx.x & 63;
   const int h = lane & 15;
   const int gq = lane >> 4;
   if (h < G) {
-    const h8* p = reinterpret_cast<const h8*>(qhead0 + (size_t)h * kD + 8 * gq);
+    const v8<T>* p = reinterpret_cast<const v8<T>*>(qhead0 + (size_t)h * kD + 8 * gq);
 #pragma unroll
     for (int s = 0; s < 4; s++) qop[s] = p[4 * s];
   } else {
 #pragma unroll
-    for (int s = 0; s < 4; s++) qop[s] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int s = 0; s < 4; s++)
+#pragma unroll
+      for (int i = 0; i < 8; i++) qop[s][i] = (T)0.0f;
   }
 }
 
+template <typename T>
 struct StepLoads {
-  h8 k[2][4];  // [tile][s]: K row (tile*16 + lane%16), dims 32*s + 8*gq ..
-  h8 v[8];     // [u]: V row of k-slot u (u<4: tile0 row 4gq+u; else tile1 row 4gq+u-4)
+  v8<T> k[2][4];  // [tile][s]: K row (tile*16 + lane%16), dims 32*s + 8*gq ..
+  v8<T> v[8];     // [u]: V row of k-slot u (u<4: tile0 row 4gq+u; else tile1 row 4gq+u-4)
 };
 
 // rows[i] for i in 0..31 supplied through `row_of(i)` (already clamped to a valid row)
-template <class RowOf>
-__device__ __forceinline__ void step_load(const f16* __restrict__ Kb, const f16* __restrict__ Vb,
-                                          RowOf row_of, StepLoads& ld) {
+template <typename T, class RowOf>
+__device__ __forceinline__ void step_load(const T* __restrict__ Kb, const T* __restrict__ Vb,
+                                          RowOf row_of, StepLoads<T>& ld) {
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
   const int gq = lane >> 4;
 #pragma unroll
   for (int t = 0; t < 2; t++) {
     const int r = row_of(t * 16 + c);
-    const h8* p = reinterpret_cast<const h8*>(Kb + (size_t)r * kD + 8 * gq);
+    const v8<T>* p = reinterpret_cast<const v8<T>*>(Kb + (size_t)r * kD + 8 * gq);
 #pragma unroll
     for (int s = 0; s < 4; s++) ld.k[t][s] = p[4 * s];
   }
@@ -81,15 +97,15 @@ __device__ __forceinline__ void step_load(const f16* __restrict__ Kb, const f16*
   for (int u = 0; u < 8; u++) {
     const int i = (u < 4) ? (4 * gq + u) : (16 + 4 * gq + (u - 4));
     const int r = row_of(i);
-    ld.v[u] = *reinterpret_cast<const h8*>(Vb + (size_t)r * kD + 8 * c);
+    ld.v[u] = *reinterpret_cast<const v8<T>*>(Vb + (size_t)r * kD + 8 * c);
   }
 }
 
 // One step over 32 rows.  active(i, h) says whether row i takes part for head h
 // (rows past the end and unselected rows are masked to -inf).
-template <class Active>
-__device__ __forceinline__ void step_compute(const StepLoads& ld, const h8 (&qop)[4], float scale2,
-                                             Active active, AttnState& st) {
+template <typename T, class Active>
+__device__ __forceinline__ void step_compute(const StepLoads<T>& ld, const v8<T> (&qop)[4],
+                                             float scale2, Active active, AttnState& st) {
   const int lane = threadIdx.x & 63;
   const int h = lane & 15;
   const int gq = lane >> 4;
@@ -112,16 +128,17 @@ __device__ __forceinline__ void step_compute(const StepLoads& ld, const h8 (&qop
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
   const float mn = fmaxf(st.m, mx);
   const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st.m - mn);
-  // P = hi + lo in fp16 keeps the weights at about fp32 accuracy through the fp16 MFMA
-  h8 pa, pb;
+  // P = hi + lo in the operand type keeps the weights at about fp32 accuracy (fp16: 22
+  // bits, bf16: 16 bits) through the 16-bit MFMA
+  v8<T> pa, pb;
   float psum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const float pv = (sc[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[i] - mn);
     psum += pv;
-    const f16 hi = (f16)pv;
+    const T hi = (T)pv;
     pa[i] = hi;
-    pb[i] = (f16)(pv - (float)hi);
+    pb[i] = (T)(pv - (float)hi);
   }
   st.l = st.l * alpha + psum;
   st.m = mn;
@@ -136,7 +153,7 @@ __device__ __forceinline__ void step_compute(const StepLoads& ld, const h8 (&qop
   }
 #pragma unroll
   for (int nb = 0; nb < 8; nb++) {
-    h8 vb;
+    v8<T> vb;
 #pragma unroll
     for (int u = 0; u < 8; u++) vb[u] = ld.v[u][nb];
     st.o[nb] = mfma32(pa, vb, st.o[nb]);

@@ -198,6 +198,7 @@ struct StepFusedPlan {
 
 struct StepFusedArgs {
   int B, Hq, Lmax, window, sinks;
+  int kv_dtype;  // 1: fp16, 2: bf16
   const int32_t* seq_lens;
   const void* q;
   const float* q_idx;

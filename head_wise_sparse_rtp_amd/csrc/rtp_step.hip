@@ -172,7 +172,7 @@ struct StageAParams {
   const int32_t* seq_lens;
   int B, Hq, G, Lmax;
   const float* q_idx;
-  const f16* k_idx;
+  const void* k_idx;  // fp16 or bf16 (the kernel's element type)
   HeadMap ret;
   int Hret, nchunk, ngg, nunits;
   int counts;  // unit weight per token (fixed top-k); c_log2 is then 0
@@ -187,9 +187,9 @@ struct StageAParams {
 struct WinParams {
   const int32_t* seq_lens;
   int Hq, G;
-  const f16* q;
-  const f16* K_loc;
-  const f16* V_loc;
+  const void* q;  // the kernel's element type, as K_loc and V_loc
+  const void* K_loc;
+  const void* V_loc;
   HeadMap loc;
   int Hloc, window, sinks, nws, wrows;
   float scale2;
@@ -212,8 +212,9 @@ struct WinParams {
 // lane's tokens form one code word (byte t = token 4w + t of word w).
 // Loads of one histogram unit (k_idx rows and the raw q_idx of the lane's head), issued
 // without waiting.
+template <typename T>
 struct HistIn {
-  h8 ka[8];
+  v8<T> ka[8];
   float4 q[2];  // q_idx[8*(kq&1) .. +7] of the lane's head
 };
 
@@ -234,14 +235,14 @@ __device__ __forceinline__ HistUnit hist_unit(const StageAParams& P, int hb) {
   return u;
 }
 
-template <int NT>
-__device__ __forceinline__ void hist_fetch(const StageAParams& P, const HistUnit& u, HistIn& in) {
+template <int NT, typename T>
+__device__ __forceinline__ void hist_fetch(const StageAParams& P, const HistUnit& u, HistIn<T>& in) {
   constexpr int TC = NT * 4;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int base = u.chunk * TC;
   const int kq = lane >> 4;
-  const f16* kb = P.k_idx + ((size_t)u.b * P.Hret + u.kr) * (size_t)P.Lmax * kR;
+  const T* kb = static_cast<const T*>(P.k_idx) + ((size_t)u.b * P.Hret + u.kr) * (size_t)P.Lmax * kR;
   const int wbase = base + wv * 256;
   // issued before the sequence length is read: rows past Lmax re-read the last row, and
   // tokens past the sequence's end are masked in hist_block
@@ -249,7 +250,7 @@ __device__ __forceinline__ void hist_fetch(const StageAParams& P, const HistUnit
 #pragma unroll
   for (int gi = 0; gi < 8; gi++) {
     const int n = min(wbase + gi * 32 + (lane & 15) + 16 * (kq >> 1), nlast);
-    in.ka[gi] = *reinterpret_cast<const h8*>(kb + (size_t)n * kR + 8 * (kq & 1));
+    in.ka[gi] = *reinterpret_cast<const v8<T>*>(kb + (size_t)n * kR + 8 * (kq & 1));
   }
   const int hh = lane & 7;
   const float4* qp = reinterpret_cast<const float4*>(
@@ -259,8 +260,8 @@ __device__ __forceinline__ void hist_fetch(const StageAParams& P, const HistUnit
   in.q[1] = qp[1];
 }
 
-template <int NT>
-__device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistIn& in,
+template <int NT, typename T>
+__device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistIn<T>& in,
                            unsigned char* smem) {
   constexpr int TC = NT * 4;
   constexpr int NWV = NT / 64;
@@ -289,8 +290,14 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
   const int kq = lane >> 4;        // k-group of the A / B operands
   const int wbase = base + wv * 256;
   // ---- q operands of head hh (zero for heads past nrows); lanes l and l^16 hold the
-  // two halves of the head's q_idx
-  h8 qhi = h8{0, 0, 0, 0, 0, 0, 0, 0}, qlo = qhi;
+  // two halves of the head's q_idx.  The parts of each entry sum to it exactly: two fp16
+  // parts (22 bits) or three bf16 parts (24 bits)
+  constexpr int NQP = __is_same(T, bf16e) ? 3 : 2;
+  v8<T> qp[NQP];
+#pragma unroll
+  for (int k = 0; k < NQP; k++)
+#pragma unroll
+    for (int i = 0; i < 8; i++) qp[k][i] = (T)0.0f;
   const float q[8] = {in.q[0].x, in.q[0].y, in.q[0].z, in.q[0].w,
                       in.q[1].x, in.q[1].y, in.q[1].z, in.q[1].w};
   float qm = 0.0f;
@@ -303,10 +310,13 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
   if (hh < nrows && (kq >> 1) == th) {
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      const float v = ldexpf(q[i], 14 - e);
-      const f16 hi = (f16)v;
-      qhi[i] = hi;
-      qlo[i] = (f16)(v - (float)hi);
+      float v = ldexpf(q[i], 14 - e);
+#pragma unroll
+      for (int k = 0; k < NQP; k++) {
+        const T part = (T)v;
+        qp[k][i] = part;
+        v -= (float)part;
+      }
     }
   }
   for (int i = tid; i < CP * GG * (kNB + kPad); i += NT) hist[i] = 0u;
@@ -317,8 +327,8 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
 #pragma unroll
   for (int gi = 0; gi < 8; gi++) {
     f4 d = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    d = mfma32(in.ka[gi], qhi, d);
-    d = mfma32(in.ka[gi], qlo, d);
+#pragma unroll
+    for (int k = 0; k < NQP; k++) d = mfma32(in.ka[gi], qp[k], d);
 #pragma unroll
     for (int t = 0; t < 4; t++) {
       float v = d[t] * ysc;
@@ -422,23 +432,23 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
 
 // One histogram unit per block: two blocks per CU hide the latency of the histogram
 // pass better than a block that prefetches a second unit.
-template <int NT>
+template <int NT, typename T>
 __global__ __launch_bounds__(NT, NT >= 512 ? 2 : 4) void k_stage_a(StageAParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   const HistUnit U = hist_unit<NT>(P, blockIdx.x);
-  HistIn in;
-  hist_fetch<NT>(P, U, in);
-  hist_block<NT>(P, U, in, smem);
+  HistIn<T> in;
+  hist_fetch<NT, T>(P, U, in);
+  hist_block<NT, T>(P, U, in, smem);
 }
 
 // Masked attention over the entries e = 0..n-1 of a row list: row_of(e) is the cache
 // row, mask_of(e) the heads that take part (bit h).  The list is cut into 32-row steps;
 // this block takes steps part, part + nparts, ... and its wavefront wv of NWV every NWV-th
 // of those, two steps' loads in flight before either is used.
-template <int NWV, class RowOf, class MaskOf>
-__device__ __forceinline__ void attend_list(const f16* __restrict__ Kb, const f16* __restrict__ Vb,
+template <int NWV, typename T, class RowOf, class MaskOf>
+__device__ __forceinline__ void attend_list(const T* __restrict__ Kb, const T* __restrict__ Vb,
                                             int n, RowOf row_of, MaskOf mask_of,
-                                            const h8 (&qop)[4], float scale2, AttnState& st,
+                                            const v8<T> (&qop)[4], float scale2, AttnState& st,
                                             int part = 0, int nparts = 1) {
   const int wv = threadIdx.x >> 6;
   const int nsteps = (n + kStep - 1) / kStep;
@@ -446,7 +456,7 @@ __device__ __forceinline__ void attend_list(const f16* __restrict__ Kb, const f1
   for (int s0 = part + nparts * wv; s0 < nsteps; s0 += 2 * stride) {
     const int s1 = s0 + stride;
     const int e0 = s0 * kStep, e1 = s1 * kStep;
-    StepLoads ld0, ld1;
+    StepLoads<T> ld0, ld1;
     step_load(Kb, Vb, [&](int i) { return row_of(e0 + i < n ? e0 + i : 0); }, ld0);
     if (s1 < nsteps) step_load(Kb, Vb, [&](int i) { return row_of(e1 + i < n ? e1 + i : 0); }, ld1);
     step_compute(ld0, qop, scale2,
@@ -463,6 +473,7 @@ __device__ __forceinline__ void attend_list(const f16* __restrict__ Kb, const f1
 // window block (local KV head): entries [wsplit*wrows, +wrows) of the window set of
 // sinks followed by the last `window` positions -> one partial per query head
 // ---------------------------------------------------------------------------
+template <typename T>
 __device__ void window_block(const WinParams& P, int wb, float* lds) {
   const int wsplit = wb % P.nws;
   const int kl = (wb / P.nws) % P.Hloc;
@@ -474,10 +485,10 @@ __device__ void window_block(const WinParams& P, int wb, float* lds) {
   const int ns = min(P.sinks, L);
   const int wstart = max(P.sinks, L - P.window);
   const int nwin = ns + max(0, L - wstart);
-  const f16* Kb = P.K_loc + ((size_t)b * P.Hloc + kl) * (size_t)ring * kD;
-  const f16* Vb = P.V_loc + ((size_t)b * P.Hloc + kl) * (size_t)ring * kD;
-  h8 qop[4];
-  load_qop(P.q + ((size_t)b * P.Hq + (size_t)P.loc.kv[kl] * G) * kD, G, qop);
+  const T* Kb = static_cast<const T*>(P.K_loc) + ((size_t)b * P.Hloc + kl) * (size_t)ring * kD;
+  const T* Vb = static_cast<const T*>(P.V_loc) + ((size_t)b * P.Hloc + kl) * (size_t)ring * kD;
+  v8<T> qop[4];
+  load_qop(static_cast<const T*>(P.q) + ((size_t)b * P.Hq + (size_t)P.loc.kv[kl] * G) * kD, G, qop);
   AttnState st;
   attn_init(st);
   const int elo = wsplit * P.wrows;
@@ -607,9 +618,9 @@ struct StageBParams {
   // (rw_nws per KV head, rw_rows rows each), whose partials follow the selection partials
   int rw_sinks, rw_window, rw_nws, rw_rows;
   int np_row;  // partials per retrieval KV head: nblk * nparts + rw_nws
-  const f16* q;
-  const f16* K_ret;
-  const f16* V_ret;
+  const void* q;  // the kernel's element type, as K_ret and V_ret
+  const void* K_ret;
+  const void* V_ret;
   HeadMap ret;
   float scale2;
   const int32_t* partA;
@@ -633,7 +644,7 @@ struct StageBParams {
 // A token is selected for head g iff its chunk-relative code j_c <= tau_g = b* - (A - A_c)
 // (all tokens when b* = 255).  Four codes are tested at once: with the bytes of a word
 // spread over two 16-bit lanes, (256 + tau) - j_c has bit 8 set iff j_c <= tau.
-template <int NWD, int GMAX>
+template <int NWD, int GMAX, typename T>
 __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) {
   constexpr int NT = kBThreads;
   constexpr int TB = NT * 4 * NWD;
@@ -660,12 +671,12 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
   const int cpb = TB / tc;     // chunks per block
   const int chunk0 = blk * cpb;
   const int tok0 = blk * TB;
-  const f16* Kb = P.K_ret + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kD;
-  const f16* Vb = P.V_ret + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kD;
+  const T* Kb = static_cast<const T*>(P.K_ret) + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kD;
+  const T* Vb = static_cast<const T*>(P.V_ret) + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kD;
 
   // ---- phase 0: every input of the selection is in flight at once
-  h8 qop[4];
-  load_qop(P.q + ((size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G) * kD, G, qop);
+  v8<T> qop[4];
+  load_qop(static_cast<const T*>(P.q) + ((size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G) * kD, G, qop);
   int Ac = kEmptyCell, Ag = kEmptyCell;
   if (tid < cpb * kAttnG) {
     const int cc = tid / kAttnG, g = tid % kAttnG;
@@ -768,11 +779,11 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
     uint32_t me = 0u, mo = 0u;
 #pragma unroll
     for (int g = 0; g < GMAX; g++) {
-      const uint32_t T = Tv[g];
-      if (T == 0u) continue;
+      const uint32_t Tc = Tv[g];
+      if (Tc == 0u) continue;
       const uint32_t x = cw[i][g];
-      const uint32_t de = T - (x & 0x00FF00FFu);
-      const uint32_t dd = T - ((x >> 8) & 0x00FF00FFu);
+      const uint32_t de = Tc - (x & 0x00FF00FFu);
+      const uint32_t dd = Tc - ((x >> 8) & 0x00FF00FFu);
       const uint32_t bit = 0x00010001u << g;
       if (g <= 8) {
         me |= (de >> (8 - g)) & bit;
@@ -861,6 +872,7 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
 // Retrieval window block: the sink and window rows of a retrieval KV head (positions of
 // the full cache, no ring), attended by all G query heads; its partial follows the
 // head's selection partials, with the row count as its count.
+template <typename T>
 __device__ void ret_window_block(const StageBParams& P, int wb, float* lds) {
   const int wsplit = wb % P.rw_nws;
   const int kr = (wb / P.rw_nws) % P.Hret;
@@ -870,10 +882,10 @@ __device__ void ret_window_block(const StageBParams& P, int wb, float* lds) {
   const int ns = min(P.rw_sinks, L);
   const int wstart = max(P.rw_sinks, L - P.rw_window);
   const int nwin = ns + max(0, L - wstart);
-  const f16* Kb = P.K_ret + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kD;
-  const f16* Vb = P.V_ret + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kD;
-  h8 qop[4];
-  load_qop(P.q + ((size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G) * kD, G, qop);
+  const T* Kb = static_cast<const T*>(P.K_ret) + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kD;
+  const T* Vb = static_cast<const T*>(P.V_ret) + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kD;
+  v8<T> qop[4];
+  load_qop(static_cast<const T*>(P.q) + ((size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G) * kD, G, qop);
   AttnState st;
   attn_init(st);
   const int elo = wsplit * P.rw_rows;
@@ -892,16 +904,16 @@ __device__ void ret_window_block(const StageBParams& P, int wb, float* lds) {
   if ((int)threadIdx.x < G) P.p1cnt[prow + threadIdx.x] = n;
 }
 
-template <int NWD, int GMAX>
+template <int NWD, int GMAX, typename T>
 __global__ __launch_bounds__(kBThreads, 2) void k_stage_b(StageBParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int nrw = P.rw_window > 0 ? P.B * P.Hret * P.rw_nws : 0;
   if ((int)blockIdx.x < P.nret_blocks)
-    select_attend_block<NWD, GMAX>(P, smem);
+    select_attend_block<NWD, GMAX, T>(P, smem);
   else if ((int)blockIdx.x < P.nret_blocks + nrw)
-    ret_window_block(P, blockIdx.x - P.nret_blocks, reinterpret_cast<float*>(smem));
+    ret_window_block<T>(P, blockIdx.x - P.nret_blocks, reinterpret_cast<float*>(smem));
   else
-    window_block(P.win, blockIdx.x - P.nret_blocks - nrw, reinterpret_cast<float*>(smem));
+    window_block<T>(P.win, blockIdx.x - P.nret_blocks - nrw, reinterpret_cast<float*>(smem));
 }
 
 // ---------------------------------------------------------------------------
@@ -1081,7 +1093,7 @@ int window_rows(int B, int Hloc, int ring) {
 
 bool step_fused_supported(int kv_dtype, int G, int Hloc, int window, int sinks, int B, int Hret,
                           int Lmax, bool ret_window) {
-  if (kv_dtype != 1 || G > kAttnG) return false;
+  if ((kv_dtype != 1 && kv_dtype != 2) || G > kAttnG) return false;
   if (Hloc > 0) {
     const int ring = window + sinks;
     const int wr = window_rows(B, Hloc, ring);
@@ -1200,7 +1212,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     P.G = G;
     P.Lmax = a.Lmax;
     P.q_idx = a.q_idx;
-    P.k_idx = static_cast<const f16*>(a.k_idx);
+    P.k_idx = a.k_idx;
     P.ret = a.ret;
     P.Hret = sp.Hret;
     P.nchunk = sp.nchunk;
@@ -1219,7 +1231,13 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     const size_t ldsA = sizeof(uint32_t) * cpA * GG * (kNB + kPad) + sizeof(float) * GG * 8 +
                         sizeof(uint32_t) * (sp.nt / 64) * GG * 64;
     const int nA = P.nunits;
-#define RTP_STAGE_A(NTV) k_stage_a<NTV><<<nA, NTV, ldsA, st>>>(P)
+#define RTP_STAGE_A(NTV)                                \
+  do {                                                  \
+    if (a.kv_dtype == 2)                                \
+      k_stage_a<NTV, bf16e><<<nA, NTV, ldsA, st>>>(P); \
+    else                                                \
+      k_stage_a<NTV, f16><<<nA, NTV, ldsA, st>>>(P);   \
+  } while (0)
     if (sp.nt == 256)
       RTP_STAGE_A(256);
     else
@@ -1273,9 +1291,9 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     Q.topk = a.topk;
     Q.rw_sinks = a.ret_window ? a.sinks : 0;
     Q.rw_window = a.ret_window ? a.window : 0;  // the plan holds rwnws > 0 blocks then
-    Q.q = static_cast<const f16*>(a.q);
-    Q.K_ret = static_cast<const f16*>(a.K_ret);
-    Q.V_ret = static_cast<const f16*>(a.V_ret);
+    Q.q = a.q;
+    Q.K_ret = a.K_ret;
+    Q.V_ret = a.V_ret;
     Q.ret = a.ret;
     Q.partA = P.partA;
     Q.codes = P.codes;
@@ -1299,9 +1317,9 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     W.seq_lens = a.seq_lens;
     W.Hq = a.Hq;
     W.G = G;
-    W.q = static_cast<const f16*>(a.q);
-    W.K_loc = static_cast<const f16*>(a.K_loc);
-    W.V_loc = static_cast<const f16*>(a.V_loc);
+    W.q = a.q;
+    W.K_loc = a.K_loc;
+    W.V_loc = a.V_loc;
     W.loc = a.loc;
     W.Hloc = sp.Hloc;
     W.window = a.window;
@@ -1317,7 +1335,13 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
   const size_t ldsB = std::max<size_t>(kBWaves * (32 + 2048) * sizeof(float),
                                        sizeof(uint32_t) * (size_t)(sp.Hret > 0 ? sp.tb : 0));
   const int nB = Q.nret_blocks + nrw_blocks + nwin_blocks;
-#define RTP_STAGE_B(NWDV, GMV) k_stage_b<NWDV, GMV><<<nB, kBThreads, ldsB, st>>>(Q)
+#define RTP_STAGE_B(NWDV, GMV)                                      \
+  do {                                                              \
+    if (a.kv_dtype == 2)                                            \
+      k_stage_b<NWDV, GMV, bf16e><<<nB, kBThreads, ldsB, st>>>(Q); \
+    else                                                            \
+      k_stage_b<NWDV, GMV, f16><<<nB, kBThreads, ldsB, st>>>(Q);   \
+  } while (0)
   if (G <= 8) {
     if (sp.nwd == 2)
       RTP_STAGE_B(2, 8);

@@ -453,8 +453,16 @@ def test_decode_step_deterministic(rtp):
         assert torch.equal(x, y)
 
 
+def test_decode_step_bf16_single_purpose(rtp):
+    """bfloat16 caches with 20 query heads per KV head: the single-purpose kernels."""
+    say("bf16 G=20")
+    wl = workloads.make_workload("t", 3, [5000, 1, 2300], 60, 3, [[1, 0, 1]], seed=93, p=0.9,
+                                 dtype="bf16", window=384, sinks=4, device=dev())
+    check_decode(rtp, wl, label="bf16-G20")
+
+
 def test_decode_step_bf16_64k(rtp):
-    """bfloat16 caches at the 64K layout (single-purpose kernels)."""
+    """bfloat16 caches at the 64K layout (the fused path on bf16 MFMAs)."""
     say("bf16 64K")
     wl = workloads.make_workload("c1-bf16", 1, [65536], 32, 4, [[1, 0, 0, 0]], seed=1,
                                  dtype="bf16", device=dev())
