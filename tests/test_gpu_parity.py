@@ -532,3 +532,20 @@ def test_prefill_long_prompt_sampled(rtp):
                                positions=pos)
     for (b, h, t), o in ref.items():
         assert max_err(out[b, h, t], o) <= 2e-3, (h, t)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (32, 2), (12, 4)])
+def test_prefill_heads_per_kv(rtp, Hq, Hkv):
+    """Query heads per KV head other than the eight wavefronts of a block: idle
+    wavefronts (G < 8), a second pass (G = 16), and G = 3."""
+    lens = [130, 47]
+    say("prefill heads", Hq, Hkv, lens)
+    mask = [1] + [0] * (Hkv - 1)
+    pr = workloads.make_prompt(lens, Hq, Hkv, mask, seed=94, device=dev())
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev())
+    scale = 1.0 / math.sqrt(128)
+    out = rtp.rtp_prefill(sl, pr.kv_is_retrieval, pr.q, pr.K, pr.V, 32, 2, scale).out
+    out = out.cpu().numpy()
+    ref = oracle.prefill_layer(pr.q, pr.K, pr.V, pr.kv_is_retrieval, lens, scale, 32, 2)
+    for (b, h, t), o in ref.items():
+        assert max_err(out[b, h, t], o) <= 2e-3, (b, h, t)
