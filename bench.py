@@ -220,7 +220,7 @@ def bench_prefill(args):
     dev = torch.device("cuda:0")
     L, Hq, Hkv, d, window, sinks = args.prefill, 32, 4, 128, 8192, 4
     mask = [1, 0, 0, 0]
-    pr = workloads.make_prompt([L], Hq, Hkv, mask, seed=7, device=dev)
+    pr = workloads.make_prompt([L], Hq, Hkv, mask, seed=7, device=dev, dtype=args.dtype)
     sl = torch.tensor([L], dtype=torch.int32, device=dev)
     pf = rtp.Prefill(sl, mask, pr.q, pr.K, pr.V, window, sinks, 1.0 / math.sqrt(d), pr.k_pre,
                      pr.Wk, with_state=True)
@@ -245,13 +245,14 @@ def bench_prefill(args):
         "metric": "prefill attention TFLOP/s (algorithmic: 4*d flops per attended query-key pair)",
         "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_prefill": round(ms, 4), "higher_is_better": True,
-        "dtype": "f16 q/K/V, fp32 accumulation", "data": "synthetic (counter-based N(0,1))",
+        "dtype": "%s q/K/V, fp32 accumulation" % args.dtype,
+        "data": "synthetic (counter-based N(0,1))",
         "config": {"workload": "prefill: B=1, L=%d, Hq=%d, Hkv=%d (retrieval [0]), d=%d, "
                                "window=%d+%d sinks; with the decode state (k_idx, caches, rings)"
                                % (L, Hq, Hkv, d, window, sinks)},
         "attended_pairs": pairs, "dense_causal_pairs": dense,
         "dense_over_sparse_work": round(dense / pairs, 3),
-        "roofline": {"kernel": "k_prefill_attn (MFMA 16x16x32 f16)", "bound": "mfma",
+        "roofline": {"kernel": "k_prefill_attn (MFMA 16x16x32 %s)" % args.dtype, "bound": "mfma",
                      "achieved": round(tfs, 2), "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tfs / PEAK_MFMA_F16_TFLOPS, 4), "traffic": None},
     }

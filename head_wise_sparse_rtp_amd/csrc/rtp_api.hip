@@ -346,7 +346,8 @@ rtp_status rtp_prefill(const rtp_prefill_desc* d, void* stream) {
     return RTP_EINVAL;
   const int G = d->Hq / d->Hkv;
   if (G > kMaxG || d->Hkv > kMaxHkv || d->Lmax > (1 << 24)) return RTP_EUNSUPPORTED;
-  if (d->r != kR || d->d != kD || d->kv_dtype != RTP_F16) return RTP_EUNSUPPORTED;
+  if (d->r != kR || d->d != kD || (d->kv_dtype != RTP_F16 && d->kv_dtype != RTP_BF16))
+    return RTP_EUNSUPPORTED;
   if (!d->kv_is_retrieval || !std::isfinite(d->scale_attn)) return RTP_EINVAL;
   PrefillArgs a{};
   a.B = d->B;
@@ -375,19 +376,19 @@ rtp_status rtp_prefill(const rtp_prefill_desc* d, void* stream) {
     return RTP_EINVAL;
   if (d->k_idx && (!ptr_ok(d->k_pre) || !ptr_ok(d->Wk_idx))) return RTP_EINVAL;
   a.seq_lens = d->seq_lens;
-  a.q = static_cast<const f16*>(d->q);
-  a.K = static_cast<const f16*>(d->K);
-  a.V = static_cast<const f16*>(d->V);
+  a.q = d->q;
+  a.K = d->K;
+  a.V = d->V;
   a.scale2 = d->scale_attn * 1.4426950408889634f;
   a.out = d->out;
   a.k_pre = d->k_pre;
   a.Wk = d->Wk_idx;
-  a.k_idx = a.Hret > 0 ? static_cast<f16*>(d->k_idx) : nullptr;
-  a.K_ret = a.Hret > 0 ? static_cast<f16*>(d->K_ret) : nullptr;
-  a.V_ret = a.Hret > 0 ? static_cast<f16*>(d->V_ret) : nullptr;
-  a.K_loc = a.Hloc > 0 ? static_cast<f16*>(d->K_loc) : nullptr;
-  a.V_loc = a.Hloc > 0 ? static_cast<f16*>(d->V_loc) : nullptr;
-  return hip_status(launch_prefill(a, (hipStream_t)stream));
+  a.k_idx = a.Hret > 0 ? d->k_idx : nullptr;
+  a.K_ret = a.Hret > 0 ? d->K_ret : nullptr;
+  a.V_ret = a.Hret > 0 ? d->V_ret : nullptr;
+  a.K_loc = a.Hloc > 0 ? d->K_loc : nullptr;
+  a.V_loc = a.Hloc > 0 ? d->V_loc : nullptr;
+  return hip_status(launch_prefill(a, d->kv_dtype, (hipStream_t)stream));
 }
 
 size_t rtp_decode_step_workspace_size(const rtp_layer_desc* desc) {

@@ -145,22 +145,22 @@ hipError_t launch_append_project(const AppendArgs& a, int kv_dtype, hipStream_t 
 struct PrefillArgs {
   int B, Hq, Hkv, G, Hret, Hloc, Lmax, window, sinks, ntile;
   const int32_t* seq_lens;  // prompt lengths
-  const f16* q;             // [B, Hq, Lmax, 128]
-  const f16* K;             // [B, Hkv, Lmax, 128]
-  const f16* V;
+  const void* q;            // [B, Hq, Lmax, 128] fp16 or bf16 (the K/V type)
+  const void* K;            // [B, Hkv, Lmax, 128]
+  const void* V;
   float scale2;             // scale_attn * log2(e)
   float* out;               // [B, Hq, Lmax, 128]
   const float* k_pre;       // [B, Hkv, Lmax, 128] (with k_idx)
   const float* Wk;          // [Hret, 128, 16]
-  f16* k_idx;               // [B, Hret, Lmax, 16] or null
-  f16* K_ret;               // [B, Hret, Lmax, 128] or null (with V_ret)
-  f16* V_ret;
-  f16* K_loc;               // [B, Hloc, sinks + window, 128] or null (with V_loc)
-  f16* V_loc;
+  void* k_idx;              // [B, Hret, Lmax, 16] or null (the K/V type)
+  void* K_ret;              // [B, Hret, Lmax, 128] or null (with V_ret)
+  void* V_ret;
+  void* K_loc;              // [B, Hloc, sinks + window, 128] or null (with V_loc)
+  void* V_loc;
   int32_t is_ret[kMaxHkv];
   int32_t rank[kMaxHkv];
 };
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // workspace planning

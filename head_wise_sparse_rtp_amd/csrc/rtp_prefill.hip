@@ -10,13 +10,16 @@
 // Attention: block (sequence, KV head, tile of 16 query positions), eight wavefronts;
 // wavefront w takes query head kv*G + w (then w + 8, ... in further passes) and runs the
 // decode step's MFMA tile with the tile's 16 positions as its columns: S^T = K . Q^T over
-// 32 keys per step, an online softmax per position, O += P . V (P as one fp16 operand),
-// and a per-(key, position)
-// mask for causality and the window.  The block stages each step's 32 K and V rows in LDS
-// once for all its wavefronts (two buffers, rows padded to 272 bytes; the next step's
+// 32 keys per step, an online softmax per position, O += P . V, and a per-(key, position)
+// mask for causality and the window.  The block stages each step's 32 K and V rows in
+// LDS once for all its wavefronts (two buffers, rows padded to 272 bytes; the next step's
 // global loads are in flight during this step's MFMAs).  The tile's keys are its sinks
 // followed by one contiguous run ending at its last position.  Longer tiles (later
 // positions) are launched first.
+//
+// Both kernels take the element type (fp16 or bf16) as a template parameter.  fp16
+// prompts enter P as one fp16 operand; bf16 prompts as a bf16 hi + lo pair (one bf16
+// operand would cost up to 2^-9 relative per weight).
 #include "rtp_attn_tile.h"
 
 namespace rtp {
@@ -32,31 +35,44 @@ __device__ __forceinline__ int clamp_len_p(const int32_t* seq_lens, int b, int L
   return L < 0 ? 0 : (L > Lmax ? Lmax : L);
 }
 
-constexpr int kKS = kD + 8;  // LDS row stride of a staged K/V tile (halfs): 272 bytes
+constexpr int kKS = kD + 8;  // LDS row stride of a staged K/V tile (elements): 272 bytes
+
+// a value written to a cache of element type T (round to nearest even), as its bits
+template <typename T>
+__device__ __forceinline__ uint16_t cache_bits(float x);
+template <>
+__device__ __forceinline__ uint16_t cache_bits<f16>(float x) {
+  return __builtin_bit_cast(uint16_t, (f16)x);
+}
+template <>
+__device__ __forceinline__ uint16_t cache_bits<bf16e>(float x) {
+  return f_to_bf16(x);
+}
 
 // One 32-row step from the staged tile, in the layout of the decode step's tile: the K
 // operands first (S^T = K . Q^T), the V operands only after the S MFMAs, so that the two
 // are never live together; P enters O += P . V as one fp16 operand (relative error 2^-11
-// per weight, against the decode step's hi + lo pair).
-template <class Active>
-__device__ __forceinline__ void step_lds(const f16* Kl, const f16* Vl, const h8 (&qop)[4],
+// per weight, against the decode step's hi + lo pair), or as a bf16 hi + lo pair.
+template <typename T, class Active>
+__device__ __forceinline__ void step_lds(const T* Kl, const T* Vl, const v8<T> (&qop)[4],
                                          float scale2, Active active, AttnState& st) {
+  constexpr bool kPair = __is_same(T, bf16e);
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
   const int gq = lane >> 4;
   f4 s0 = f4{0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
 #pragma unroll
   for (int s = 0; s < 4; s++) {
-    const h8 k0 = *reinterpret_cast<const h8*>(Kl + c * kKS + 8 * gq + 32 * s);
-    const h8 k1 = *reinterpret_cast<const h8*>(Kl + (16 + c) * kKS + 8 * gq + 32 * s);
+    const v8<T> k0 = *reinterpret_cast<const v8<T>*>(Kl + c * kKS + 8 * gq + 32 * s);
+    const v8<T> k1 = *reinterpret_cast<const v8<T>*>(Kl + (16 + c) * kKS + 8 * gq + 32 * s);
     s0 = mfma32(k0, qop[s], s0);
     s1 = mfma32(k1, qop[s], s1);
   }
-  h8 vv[8];
+  v8<T> vv[8];
 #pragma unroll
   for (int u = 0; u < 8; u++) {
     const int i = (u < 4) ? (4 * gq + u) : (16 + 4 * gq + (u - 4));
-    vv[u] = *reinterpret_cast<const h8*>(Vl + i * kKS + 8 * c);
+    vv[u] = *reinterpret_cast<const v8<T>*>(Vl + i * kKS + 8 * c);
   }
   float sc[8];
 #pragma unroll
@@ -71,13 +87,14 @@ __device__ __forceinline__ void step_lds(const f16* Kl, const f16* Vl, const h8 
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
   const float mn = fmaxf(st.m, mx);
   const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st.m - mn);
-  h8 pa;
+  v8<T> pa, pb;
   float psum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const float pv = (sc[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[i] - mn);
     psum += pv;
-    pa[i] = (f16)pv;
+    pa[i] = (T)pv;
+    if constexpr (kPair) pb[i] = (T)(pv - (float)pa[i]);
   }
   st.l = st.l * alpha + psum;
   st.m = mn;
@@ -93,16 +110,18 @@ __device__ __forceinline__ void step_lds(const f16* Kl, const f16* Vl, const h8 
   }
 #pragma unroll
   for (int nb = 0; nb < 8; nb++) {
-    h8 vb;
+    v8<T> vb;
 #pragma unroll
     for (int u = 0; u < 8; u++) vb[u] = vv[u][nb];
     st.o[nb] = mfma32(pa, vb, st.o[nb]);
+    if constexpr (kPair) st.o[nb] = mfma32(pb, vb, st.o[nb]);
   }
 }
 
+template <typename T>
 __global__ __launch_bounds__(kPW * 64, 4) void k_prefill_attn(PrefillArgs A) {
   // two buffers of a 32-row K tile and V tile
-  __shared__ __align__(16) f16 kvs[2][2][kStep * kKS];
+  __shared__ __align__(16) T kvs[2][2][kStep * kKS];
   const int qt = A.ntile - 1 - (int)(blockIdx.x % A.ntile);
   const int kv = (blockIdx.x / A.ntile) % A.Hkv;
   const int b = blockIdx.x / (A.ntile * A.Hkv);
@@ -118,8 +137,8 @@ __global__ __launch_bounds__(kPW * 64, 4) void k_prefill_attn(PrefillArgs A) {
   const int kstart = ret ? 0 : max(ns, t0 + 1 - window);
   const int nent = ns + max(0, tend - kstart);
   const int nsteps = (nent + kStep - 1) / kStep;
-  const f16* Kb = A.K + ((size_t)b * A.Hkv + kv) * (size_t)A.Lmax * kD;
-  const f16* Vb = A.V + ((size_t)b * A.Hkv + kv) * (size_t)A.Lmax * kD;
+  const T* Kb = static_cast<const T*>(A.K) + ((size_t)b * A.Hkv + kv) * (size_t)A.Lmax * kD;
+  const T* Vb = static_cast<const T*>(A.V) + ((size_t)b * A.Hkv + kv) * (size_t)A.Lmax * kD;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -143,8 +162,9 @@ __global__ __launch_bounds__(kPW * 64, 4) void k_prefill_attn(PrefillArgs A) {
     const int g = g0 + wv;
     const bool has = g < A.G;
     const int h = kv * A.G + (has ? g : 0);
-    h8 qop[4];
-    load_qop(A.q + ((size_t)(b * A.Hq + h) * A.Lmax + t0) * kD, has ? ncol : 0, qop);
+    v8<T> qop[4];
+    load_qop<T>(static_cast<const T*>(A.q) + ((size_t)(b * A.Hq + h) * A.Lmax + t0) * kD,
+                has ? ncol : 0, qop);
     AttnState st;
     attn_init(st);
     u4 kx, vx;
@@ -199,7 +219,9 @@ __global__ __launch_bounds__(kPW * 64, 4) void k_prefill_attn(PrefillArgs A) {
 // Decode state of the prompt: block (sequence, KV head, kPR prompt rows), 256 threads.
 // Retrieval heads: k_idx rows = fp32 fma chains over the 128 pre-RoPE inputs in order
 // (weights and inputs staged in LDS), rounded to the cache dtype; K/V rows copied.  Local
-// heads: rows of the final window set copied to their ring slots.
+// heads: rows of the final window set copied to their ring slots.  Rows move as 16-byte
+// pieces of 2-byte elements, whatever their type.
+template <typename T>
 __global__ __launch_bounds__(256) void k_prefill_cache(PrefillArgs A) {
   __shared__ __align__(16) float ws[kD * kR];
   __shared__ __align__(16) float xs[kPR][kD + 4];
@@ -213,14 +235,14 @@ __global__ __launch_bounds__(256) void k_prefill_cache(PrefillArgs A) {
   const int nr = min(kPR, L - n0);
   const int tid = threadIdx.x;
   const int kr = A.rank[kv];
-  const f16* Kb = A.K + ((size_t)b * A.Hkv + kv) * (size_t)A.Lmax * kD;
-  const f16* Vb = A.V + ((size_t)b * A.Hkv + kv) * (size_t)A.Lmax * kD;
+  const uint16_t* Kb = static_cast<const uint16_t*>(A.K) + ((size_t)b * A.Hkv + kv) * (size_t)A.Lmax * kD;
+  const uint16_t* Vb = static_cast<const uint16_t*>(A.V) + ((size_t)b * A.Hkv + kv) * (size_t)A.Lmax * kD;
   if (!A.is_ret[kv]) {
     if (!A.K_loc) return;
     const int ring = A.sinks + A.window;
     const int wstart = max(A.sinks, L - A.window);
-    f16* Kr = A.K_loc + ((size_t)b * A.Hloc + kr) * (size_t)ring * kD;
-    f16* Vr = A.V_loc + ((size_t)b * A.Hloc + kr) * (size_t)ring * kD;
+    uint16_t* Kr = static_cast<uint16_t*>(A.K_loc) + ((size_t)b * A.Hloc + kr) * (size_t)ring * kD;
+    uint16_t* Vr = static_cast<uint16_t*>(A.V_loc) + ((size_t)b * A.Hloc + kr) * (size_t)ring * kD;
     // 16 threads per row, 16 bytes each
     for (int i = tid; i < nr * 16; i += 256) {
       const int n = n0 + i / 16, p = i % 16;
@@ -232,8 +254,8 @@ __global__ __launch_bounds__(256) void k_prefill_cache(PrefillArgs A) {
     return;
   }
   if (A.K_ret) {
-    f16* Kd = A.K_ret + ((size_t)b * A.Hret + kr) * (size_t)A.Lmax * kD;
-    f16* Vd = A.V_ret + ((size_t)b * A.Hret + kr) * (size_t)A.Lmax * kD;
+    uint16_t* Kd = static_cast<uint16_t*>(A.K_ret) + ((size_t)b * A.Hret + kr) * (size_t)A.Lmax * kD;
+    uint16_t* Vd = static_cast<uint16_t*>(A.V_ret) + ((size_t)b * A.Hret + kr) * (size_t)A.Lmax * kD;
     for (int i = tid; i < nr * 16; i += 256) {
       const size_t n = n0 + i / 16;
       const int p = i % 16;
@@ -251,26 +273,33 @@ __global__ __launch_bounds__(256) void k_prefill_cache(PrefillArgs A) {
     reinterpret_cast<float4*>(&xs[rr][0])[p] = reinterpret_cast<const float4*>(kp + (size_t)rr * kD)[p];
   }
   __syncthreads();
-  f16* kd = A.k_idx + (((size_t)b * A.Hret + kr) * A.Lmax + n0) * kR;
+  uint16_t* kd = static_cast<uint16_t*>(A.k_idx) + (((size_t)b * A.Hret + kr) * A.Lmax + n0) * kR;
   for (int o = tid; o < nr * kR; o += 256) {
     const int rr = o / kR, i = o % kR;
     float a = 0.0f;
 #pragma unroll 16
     for (int cc = 0; cc < kD; cc++) a = __builtin_fmaf(xs[rr][cc], ws[cc * kR + i], a);
-    kd[(size_t)rr * kR + i] = (f16)a;
+    kd[(size_t)rr * kR + i] = cache_bits<T>(a);
   }
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
+hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, hipStream_t st) {
   const int nchunk = (a.Lmax + kPR - 1) / kPR;
+  const bool bf = kv_dtype == 2;
   if (a.k_idx || a.K_ret || a.K_loc) {
-    k_prefill_cache<<<a.B * a.Hkv * nchunk, 256, 0, st>>>(a);
+    if (bf)
+      k_prefill_cache<bf16e><<<a.B * a.Hkv * nchunk, 256, 0, st>>>(a);
+    else
+      k_prefill_cache<f16><<<a.B * a.Hkv * nchunk, 256, 0, st>>>(a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  k_prefill_attn<<<a.B * a.Hkv * a.ntile, kPW * 64, 0, st>>>(a);
+  if (bf)
+    k_prefill_attn<bf16e><<<a.B * a.Hkv * a.ntile, kPW * 64, 0, st>>>(a);
+  else
+    k_prefill_attn<f16><<<a.B * a.Hkv * a.ntile, kPW * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -249,15 +249,18 @@ rtp_status rtp_append_project(const rtp_append_desc* desc, void* stream);
  *     R = { n <= t } (retrieval KV head) or { n < min(sinks, t+1) } united with
  *         { max(sinks, t+1-window) <= n <= t } (local KV head: the decode window of a
  *         sequence of length t + 1).
- * fp16 inputs, fp32 accumulation; rows t >= L of out are left as they are.
+ * fp16 or bf16 inputs (q, K, V of one type), fp32 accumulation; rows t >= L of out are
+ * left as they are.
  * It also writes the decode state the prompt leaves, for each group whose pointers are
  * given (NULL skips the group):
  *   - k_idx[b,kr,n] = the fp32 fma chain of rtp_append_project over k_pre[b,kv,n] and
- *     Wk_idx[kr], rounded to fp16, for n < L (retrieval KV head kv, the kr-th flagged);
+ *     Wk_idx[kr], rounded to the K/V type (nearest even), for n < L (retrieval KV head kv,
+ *     the kr-th flagged);
  *   - K_ret/V_ret[b,kr,n] = K/V[b,kv,n] for n < L;
  *   - K_loc/V_loc[b,kl,slot(n)] = K/V[b,kv,n] for the positions n of the final window set
  *     (rtp_window_decode's ring; other slots are left as they are).
- * Only fp16 (RTP_F16) is supported.  No workspace; the call never allocates.
+ * kv_dtype is RTP_F16 or RTP_BF16 (else RTP_EUNSUPPORTED); every cache written has that
+ * type.  No workspace; the call never allocates.
  */
 typedef struct {
   int32_t B, Hq, Hkv, d, r, Lmax, window, sinks, kv_dtype;

@@ -366,7 +366,8 @@ def prefill_layer(q, K, V, kv_is_retrieval, seq_lens, scale: float, window: int,
 def prefill_state(K, V, k_pre, Wk, kv_is_retrieval, seq_lens, window: int, sinks: int,
                   Lmax: int):
     """The decode state a prompt leaves: for retrieval KV head kv (the kr-th flagged),
-    k_idx[b, kr, n] = fl(project(k_pre[b, kv, n], Wk[kr])) in K's dtype and the K/V rows
+    k_idx[b, kr, n] = project(k_pre[b, kv, n], Wk[kr]) rounded to K's dtype (nearest even;
+    bfloat16 tensors give fp32 arrays of bfloat16 values) and the K/V rows
     copied for every n < L; for local KV heads the ring [sinks + window] holding the
     positions of window_positions(L) at their ring slots (other slots zero)."""
     Kn, Vn, kp, W = np_of(K), np_of(V), np_of(k_pre), np_of(Wk)
@@ -384,7 +385,7 @@ def prefill_state(K, V, k_pre, Wk, kv_is_retrieval, seq_lens, window: int, sinks
         L = int(seq_lens[b])
         for kr, kv in enumerate(ret):
             for n in range(L):
-                k_idx[b, kr, n] = project(kp[b, kv, n], W[kr]).astype(Kn.dtype)
+                k_idx[b, kr, n] = _to_cache(project(kp[b, kv, n], W[kr]), K)
             K_ret[b, kr, :L] = Kn[b, kv, :L]
             V_ret[b, kr, :L] = Vn[b, kv, :L]
         pos = window_positions(L, window, sinks)

@@ -158,7 +158,13 @@ def test_prefill_validation(lib):
                       None)
     f = lambda: lib.rtp_prefill(ctypes.byref(d), None)
     d.kv_dtype = 0
-    assert f() == -2                     # fp16 only
+    assert f() == -2                     # fp16 or bf16 only
+    d.kv_dtype = 5
+    assert f() == -2
+    d.kv_dtype = 2
+    d.K_ret = FAKE                       # K_ret without V_ret (bf16)
+    assert f() == -1
+    d.K_ret = None
     d.kv_dtype = 1
     d.K_ret = FAKE                       # K_ret without V_ret
     assert f() == -1

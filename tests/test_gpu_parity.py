@@ -534,6 +534,32 @@ def test_prefill_long_prompt_sampled(rtp):
         assert max_err(out[b, h, t], o) <= 2e-3, (h, t)
 
 
+@pytest.mark.parametrize("lens,window,sinks", [([300, 37, 1], 64, 4), ([200], 4096, 4)])
+def test_prefill_bf16_matches_oracle(rtp, lens, window, sinks):
+    """bf16 prompt: outputs within the 2e-3 bar, and the decode state (k_idx rounded to
+    bf16, K/V rows, rings) bit-exact."""
+    say("prefill bf16", lens, window, sinks)
+    pr = workloads.make_prompt(lens, 8, 2, [1, 0], seed=95, device=dev(), dtype="bf16")
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev())
+    scale = 1.0 / math.sqrt(128)
+    pf = rtp.rtp_prefill(sl, pr.kv_is_retrieval, pr.q, pr.K, pr.V, window, sinks, scale,
+                         pr.k_pre, pr.Wk, with_state=True)
+    out = pf.out.cpu().numpy()
+    ref = oracle.prefill_layer(pr.q, pr.K, pr.V, pr.kv_is_retrieval, lens, scale, window, sinks)
+    worst = 0.0
+    for (b, h, t), o in ref.items():
+        e = max_err(out[b, h, t], o)
+        worst = max(worst, e)
+        assert e <= 2e-3, (b, h, t, e)
+    say("worst |dO|", worst)
+    want = oracle.prefill_state(pr.K, pr.V, pr.k_pre, pr.Wk, pr.kv_is_retrieval, lens, window,
+                                sinks, max(lens))
+    got = [pf.k_idx, pf.K_ret, pf.V_ret, pf.K_loc, pf.V_loc]
+    for name, g, w in zip(["k_idx", "K_ret", "V_ret", "K_loc", "V_loc"], got, want):
+        assert g.dtype == torch.bfloat16, name
+        assert np.array_equal(_bits(oracle.np_of(g)), _bits(w)), name
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(4, 2), (32, 2), (12, 4)])
 def test_prefill_heads_per_kv(rtp, Hq, Hkv):
     """Query heads per KV head other than the eight wavefronts of a block: idle

@@ -668,6 +668,23 @@ def test_prefill_state_places_the_prompt():
     assert [s for s in range(8) if K_loc[1, 0, s].any()] == [0, 1, 4]
 
 
+def test_prefill_state_bf16_rounds_the_projection():
+    # bf16 caches: each k_idx value is a bfloat16 number (low 16 bits of its fp32 zero)
+    # within half a bfloat16 ulp (2^-8 relative) of the fp32 projection; K/V rows copy as is
+    import workloads
+    pr = workloads.make_prompt([9], 2, 2, [1, 0], seed=5, dtype="bf16")
+    k_idx, K_ret, _, K_loc, _ = oracle.prefill_state(pr.K, pr.V, pr.k_pre, pr.Wk,
+                                                     pr.kv_is_retrieval, [9], 4, 1, 9)
+    assert k_idx.dtype == np.float32
+    assert not (k_idx.view(np.uint32) & 0xFFFF).any()
+    exact = np.stack([oracle.project(oracle.np_of(pr.k_pre)[0, 0, n], oracle.np_of(pr.Wk)[0])
+                      for n in range(9)]).astype(np.float64)
+    err = np.abs(k_idx[0, 0].astype(np.float64) - exact)
+    assert (err <= np.abs(exact) * 2.0 ** -8).all() and err.max() > 0
+    assert np.array_equal(K_ret[0, 0], oracle.np_of(pr.K)[0, 0])
+    assert np.array_equal(K_loc[0, 0, 0], oracle.np_of(pr.K)[0, 1, 0])
+
+
 def test_round_bf16_ties_and_library_conversion():
     # 1 + 2^-8 lies halfway between bf16 1 and 1 + 2^-7: ties to even give 1; 1 + 3 * 2^-8
     # lies halfway between 1 + 2^-7 and 1 + 2^-6: ties to even give 1 + 2^-6

@@ -487,13 +487,20 @@ class Prompt:
 
 
 def make_prompt(seq_lens, Hq: int, Hkv: int, mask, seed: int = 0, d: int = 128, r: int = 16,
-                device="cpu", Lmax: Optional[int] = None, with_kpre: bool = True) -> Prompt:
+                device="cpu", Lmax: Optional[int] = None, with_kpre: bool = True,
+                dtype: str = "f16") -> Prompt:
+    """q, K, V are N(0, 1) draws of the counter generator in fp16; dtype "bf16" converts
+    those fp16 values to bfloat16."""
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     B = len(seq_lens)
     Lmax = int(Lmax if Lmax is not None else seq_lens.max())
     q = counter_normal_f16((B, Hq, Lmax, d), seed, 11, device)
     K = counter_normal_f16((B, Hkv, Lmax, d), seed, 12, device)
     V = counter_normal_f16((B, Hkv, Lmax, d), seed, 13, device)
+    if dtype == "bf16":
+        q, K, V = q.to(torch.bfloat16), K.to(torch.bfloat16), V.to(torch.bfloat16)
+    elif dtype != "f16":
+        raise ValueError("prompt dtype must be f16 or bf16")
     nret = int(np.asarray(mask).sum())
     rng = np.random.default_rng(20_000 + seed)
     if with_kpre:
