@@ -344,6 +344,11 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
   ym = fmaxf(ym, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(ym), 0x401F)));
   ym = fmaxf(ym, __shfl_xor(ym, 32, 64));
   if (lane < GG) smax[lane * NWV + wv] = ym;
+  __syncthreads();
+  float m = smax[hh * NWV];
+#pragma unroll
+  for (int k = 1; k < NWV; k++) m = fmaxf(m, smax[hh * NWV + k]);
+  const float Acf = floorf(m);
 
   // ---- pass 2: per-bin sums of x * 2^22 (truncated to integers: at most 2^-22 / e^-w,
   // below 3e-7, relative to the token's mass; 512 tokens per copy cannot overflow 32
@@ -352,34 +357,9 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
   //   bin j = A_c - m,  x = 2^((y - m - 1) c),  c = w log2(e).
   // y - m is exact (it is fract(y) unless the token is in the tail) and a token past the
   // end (y = kMaskY) lands in bin 255 with zero mass.  With c = 0 every token adds 2^22.
-  // x needs only m, so each wavefront computes it before the block's top cell A_c is
-  // known, against its own top cell A_w <= A_c: m_w = max(g, A_w - 255) equals m for
-  // every token outside the chunk's tail (g >= A_c - 255 >= A_w - 255).  A token of the
-  // chunk's tail keeps x = 2^((y - m_w - 1) c) with m_w <= A_c - 255, so after bin 255's
-  // factor 2^(-255 c) it adds less than 2^(-255 c) = e^(-255 w) of the unit mass
-  // e^((A_c + 1) w), as its exact mass does: either way the tail bin holds less than
-  // L e^(-255 w) of it.  After the block's barrier the bin is min(A_c - m_w, 255).
   const float c = P.c_log2;
+  const float Kt = Acf - 255.0f;
   const float c22 = 22.0f - c;  // x * 2^22 = 2^((y - m - 1) c + 22)
-  // a wavefront whose tokens are all past the end has ym = kMaskY: keep its anchor finite
-  const float Ktw = fmaxf(floorf(ym), -1.0e30f) - 255.0f;
-  uint32_t xq[8][4];
-  float mcw[8][4];
-#pragma unroll
-  for (int gi = 0; gi < 8; gi++) {
-#pragma unroll
-    for (int t = 0; t < 4; t++) {
-      const float yv = y[gi][t];
-      const float mc = fmaxf(floorf(yv), Ktw);
-      xq[gi][t] = (uint32_t)__builtin_amdgcn_exp2f(__builtin_fmaf(yv - mc, c, c22));
-      mcw[gi][t] = mc;
-    }
-  }
-  __syncthreads();
-  float m = smax[hh * NWV];
-#pragma unroll
-  for (int k = 1; k < NWV; k++) m = fmaxf(m, smax[hh * NWV + k]);
-  const float Acf = floorf(m);
   uint32_t* hrow = hist + (((lane >> 3) & (CP - 1)) * GG + hh) * (kNB + kPad);
   // code words pass through LDS ([wave][head][64 words]) so that the global stores
   // cover whole 256-byte runs per head
@@ -390,8 +370,11 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
       uint32_t cw = 0u;
 #pragma unroll
       for (int t = 0; t < 4; t++) {
-        const uint32_t j = (uint32_t)fminf(Acf - mcw[gi][t], 255.0f);
-        atomicAdd(&hrow[j], xq[gi][t]);
+        const float yv = y[gi][t];
+        const float mc = fmaxf(floorf(yv), Kt);
+        const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(yv - mc, c, c22));
+        const uint32_t j = (uint32_t)(Acf - mc);
+        atomicAdd(&hrow[j], (uint32_t)ex);
         cw |= j << (8 * t);
       }
       cl[gi * 8] = cw;
