@@ -357,7 +357,6 @@ rtp_status rtp_prefill(const rtp_prefill_desc* d, void* stream) {
   a.Lmax = d->Lmax;
   a.window = d->window;
   a.sinks = d->sinks;
-  a.ntile = (d->Lmax + 15) / 16;
   for (int h = 0; h < d->Hkv; h++) {
     a.is_ret[h] = d->kv_is_retrieval[h] ? 1 : 0;
     a.rank[h] = a.is_ret[h] ? a.Hret++ : a.Hloc++;

@@ -143,7 +143,8 @@ hipError_t launch_append_project(const AppendArgs& a, int kv_dtype, hipStream_t 
 
 // Prefill of a prompt (fp16 prompt K/V and queries) and the decode state it leaves.
 struct PrefillArgs {
-  int B, Hq, Hkv, G, Hret, Hloc, Lmax, window, sinks, ntile;
+  int B, Hq, Hkv, G, Hret, Hloc, Lmax, window, sinks;
+  int ntile;  // query tiles per sequence (set by launch_prefill)
   const int32_t* seq_lens;  // prompt lengths
   const void* q;            // [B, Hq, Lmax, 128] fp16 or bf16 (the K/V type)
   const void* K;            // [B, Hkv, Lmax, 128]

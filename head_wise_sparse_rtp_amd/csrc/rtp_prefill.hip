@@ -7,11 +7,12 @@
 // test configuration: window 8192, 4 sinks) and section 三, 核心公式 (the indexer
 // projection to r = 16 dims before RoPE).
 //
-// Attention: block (sequence, KV head, tile of 16 query positions), eight wavefronts;
+// Attention: block (sequence, KV head, tile of 32 query positions), eight wavefronts;
 // wavefront w takes query head kv*G + w (then w + 8, ... in further passes) and runs the
-// decode step's MFMA tile with the tile's 16 positions as its columns: S^T = K . Q^T over
-// 32 keys per step, an online softmax per position, O += P . V, and a per-(key, position)
-// mask for causality and the window.  The block stages each step's 32 K and V rows in
+// decode step's MFMA tile twice, with positions t0..t0+15 and t0+16..t0+31 as the columns
+// of its two sets: S^T = K . Q^T over 32 keys per step, an online softmax per position,
+// O += P . V, and a per-(key, position) mask for causality and the window.  Each K and V
+// operand read from LDS serves both sets, which halves the LDS bytes per flop.  The block stages each step's 32 K and V rows in
 // LDS once for all its wavefronts (two buffers, rows padded to 272 bytes; the next step's
 // global loads are in flight during this step's MFMAs).  The tile's keys are its sinks
 // followed by one contiguous run ending at its last position.  Longer tiles (later
@@ -26,7 +27,7 @@ namespace rtp {
 
 namespace {
 
-constexpr int kPQ = 16;  // query positions per tile (the MFMA tile's columns)
+constexpr int kPQ = 32;  // query positions per tile: two sets of the MFMA tile's 16 columns
 constexpr int kPW = 8;   // wavefronts per attention block (query heads of one KV head)
 constexpr int kPR = 64;  // prompt rows per cache block
 
@@ -36,6 +37,7 @@ __device__ __forceinline__ int clamp_len_p(const int32_t* seq_lens, int b, int L
 }
 
 constexpr int kKS = kD + 8;  // LDS row stride of a staged K/V tile (elements): 272 bytes
+constexpr int kSR = 64;      // K/V rows staged per block barrier (two 32-row steps)
 
 // a value written to a cache of element type T (round to nearest even), as its bits
 template <typename T>
@@ -49,49 +51,46 @@ __device__ __forceinline__ uint16_t cache_bits<bf16e>(float x) {
   return f_to_bf16(x);
 }
 
-// One 32-row step from the staged tile, in the layout of the decode step's tile: the K
-// operands first (S^T = K . Q^T), the V operands only after the S MFMAs, so that the two
-// are never live together; P enters O += P . V as one fp16 operand (relative error 2^-11
-// per weight, against the decode step's hi + lo pair), or as a bf16 hi + lo pair.
+// max over the four lanes of one MFMA column (lanes l, l^16, l^32, l^48), on the VALU:
+// each swap leaves a lane its own value and its partner's, in some order
+__device__ __forceinline__ float col_max(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
+// Online-softmax update of one set of 16 query columns from its two 16 x 16 tiles of
+// S^T (keys 0-15 and 16-31 of the step): the set's running max and sum, the rescale of its
+// output rows when some column's maximum moved, and P in the operand type (fp16: one
+// part, relative error 2^-11 per weight; bf16: a hi + lo pair).  The maximum is taken on
+// the raw products (the scale is positive) and each weight is exp2(fma(s, scale2, -m));
+// a column with no active key so far takes m = 0 there, so its masked products (-inf)
+// give exactly 0.
 template <typename T, class Active>
-__device__ __forceinline__ void step_lds(const T* Kl, const T* Vl, const v8<T> (&qop)[4],
-                                         float scale2, Active active, AttnState& st) {
+__device__ __forceinline__ void softmax_set(const f4& s0, const f4& s1, float scale2, Active active,
+                                            AttnState& st, v8<T>& pa, v8<T>& pb) {
   constexpr bool kPair = __is_same(T, bf16e);
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
   const int gq = lane >> 4;
-  f4 s0 = f4{0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
-#pragma unroll
-  for (int s = 0; s < 4; s++) {
-    const v8<T> k0 = *reinterpret_cast<const v8<T>*>(Kl + c * kKS + 8 * gq + 32 * s);
-    const v8<T> k1 = *reinterpret_cast<const v8<T>*>(Kl + (16 + c) * kKS + 8 * gq + 32 * s);
-    s0 = mfma32(k0, qop[s], s0);
-    s1 = mfma32(k1, qop[s], s1);
-  }
-  v8<T> vv[8];
-#pragma unroll
-  for (int u = 0; u < 8; u++) {
-    const int i = (u < 4) ? (4 * gq + u) : (16 + 4 * gq + (u - 4));
-    vv[u] = *reinterpret_cast<const v8<T>*>(Vl + i * kKS + 8 * c);
-  }
-  float sc[8];
+  float r[8];
 #pragma unroll
   for (int t = 0; t < 4; t++) {
-    sc[t] = active(4 * gq + t, c) ? s0[t] * scale2 : -INFINITY;
-    sc[4 + t] = active(16 + 4 * gq + t, c) ? s1[t] * scale2 : -INFINITY;
+    r[t] = active(4 * gq + t, c) ? s0[t] : -INFINITY;
+    r[4 + t] = active(16 + 4 * gq + t, c) ? s1[t] : -INFINITY;
   }
-  float mx = sc[0];
+  float mx = r[0];
 #pragma unroll
-  for (int i = 1; i < 8; i++) mx = fmaxf(mx, sc[i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float mn = fmaxf(st.m, mx);
+  for (int i = 1; i < 8; i++) mx = fmaxf(mx, r[i]);
+  mx = col_max(mx);
+  const float mn = fmaxf(st.m, mx * scale2);
   const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st.m - mn);
-  v8<T> pa, pb;
+  const float mref = (mn == -INFINITY) ? 0.0f : mn;
   float psum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    const float pv = (sc[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[i] - mn);
+    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(r[i], scale2, -mref));
     psum += pv;
     pa[i] = (T)pv;
     if constexpr (kPair) pb[i] = (T)(pv - (float)pa[i]);
@@ -108,20 +107,81 @@ __device__ __forceinline__ void step_lds(const T* Kl, const T* Vl, const v8<T> (
 #pragma unroll
       for (int t = 0; t < 4; t++) st.o[nb][t] *= at[t];
   }
+}
+
+// One 32-row step from the staged tile for two sets of 16 query columns (positions
+// t0..t0+15 and t0+16..t0+31 of one head), in the layout of the decode step's tile: each
+// K operand read from LDS feeds the S MFMAs of both sets, and each V operand both sets'
+// O += P . V; the V operands are read only after the S MFMAs, so that K and V registers are
+// never live together.
+template <typename T, class ActA, class ActB>
+__device__ __forceinline__ void step_lds2(const T* Kl, const T* Vl, const v8<T> (&qa)[4],
+                                          const v8<T> (&qb)[4], float scale2, ActA act_a,
+                                          ActB act_b, AttnState& sa, AttnState& sb) {
+  constexpr bool kPair = __is_same(T, bf16e);
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int gq = lane >> 4;
+  f4 s0a = f4{0.0f, 0.0f, 0.0f, 0.0f}, s1a = s0a, s0b = s0a, s1b = s0a;
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    const v8<T> k0 = *reinterpret_cast<const v8<T>*>(Kl + c * kKS + 8 * gq + 32 * s);
+    const v8<T> k1 = *reinterpret_cast<const v8<T>*>(Kl + (16 + c) * kKS + 8 * gq + 32 * s);
+    s0a = mfma32(k0, qa[s], s0a);
+    s1a = mfma32(k1, qa[s], s1a);
+    s0b = mfma32(k0, qb[s], s0b);
+    s1b = mfma32(k1, qb[s], s1b);
+  }
+  v8<T> vv[8];
+#pragma unroll
+  for (int u = 0; u < 8; u++) {
+    const int i = (u < 4) ? (4 * gq + u) : (16 + 4 * gq + (u - 4));
+    vv[u] = *reinterpret_cast<const v8<T>*>(Vl + i * kKS + 8 * c);
+  }
+  v8<T> paa, pba, pab, pbb;
+  softmax_set<T>(s0a, s1a, scale2, act_a, sa, paa, pba);
+  softmax_set<T>(s0b, s1b, scale2, act_b, sb, pab, pbb);
 #pragma unroll
   for (int nb = 0; nb < 8; nb++) {
     v8<T> vb;
 #pragma unroll
     for (int u = 0; u < 8; u++) vb[u] = vv[u][nb];
-    st.o[nb] = mfma32(pa, vb, st.o[nb]);
-    if constexpr (kPair) st.o[nb] = mfma32(pb, vb, st.o[nb]);
+    sa.o[nb] = mfma32(paa, vb, sa.o[nb]);
+    sb.o[nb] = mfma32(pab, vb, sb.o[nb]);
+    if constexpr (kPair) {
+      sa.o[nb] = mfma32(pba, vb, sa.o[nb]);
+      sb.o[nb] = mfma32(pbb, vb, sb.o[nb]);
+    }
+  }
+}
+
+// write the normalised rows of one column set (positions p0 + col, col < ncol)
+__device__ __forceinline__ void store_set(const AttnState& st, float* out_head, int p0, int ncol) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int gq = lane >> 4;
+  // lane (gq, c) holds positions 4gq+t, dims 8c + nb; every position attends to itself,
+  // so its sum is positive
+  float l = st.l;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    const int col = 4 * gq + t;
+    const float lc = __shfl(l, col, 64);
+    if (col < ncol) {
+      const float r = 1.0f / lc;
+      float4* dst = reinterpret_cast<float4*>(out_head + (size_t)(p0 + col) * kD + 8 * c);
+      dst[0] = make_float4(st.o[0][t] * r, st.o[1][t] * r, st.o[2][t] * r, st.o[3][t] * r);
+      dst[1] = make_float4(st.o[4][t] * r, st.o[5][t] * r, st.o[6][t] * r, st.o[7][t] * r);
+    }
   }
 }
 
 template <typename T>
-__global__ __launch_bounds__(kPW * 64, 4) void k_prefill_attn(PrefillArgs A) {
-  // two buffers of a 32-row K tile and V tile
-  __shared__ __align__(16) T kvs[2][2][kStep * kKS];
+__global__ __launch_bounds__(kPW * 64, 2) void k_prefill_attn(PrefillArgs A) {
+  // two buffers of a kSR-row K tile and V tile (kSR / 32 steps per block barrier)
+  __shared__ __align__(16) T kvs[2][2][kSR * kKS];
   const int qt = A.ntile - 1 - (int)(blockIdx.x % A.ntile);
   const int kv = (blockIdx.x / A.ntile) % A.Hkv;
   const int b = blockIdx.x / (A.ntile * A.Hkv);
@@ -129,6 +189,8 @@ __global__ __launch_bounds__(kPW * 64, 4) void k_prefill_attn(PrefillArgs A) {
   const int t0 = qt * kPQ;
   if (t0 >= L) return;
   const int ncol = min(kPQ, L - t0);
+  const int ncol_a = min(kPQ / 2, ncol);
+  const int ncol_b = ncol - ncol_a;
   const int tend = t0 + ncol;
   const bool ret = A.is_ret[kv] != 0;
   const int sinks = A.sinks, window = A.window;
@@ -136,82 +198,78 @@ __global__ __launch_bounds__(kPW * 64, 4) void k_prefill_attn(PrefillArgs A) {
   const int ns = ret ? 0 : min(sinks, tend);
   const int kstart = ret ? 0 : max(ns, t0 + 1 - window);
   const int nent = ns + max(0, tend - kstart);
-  const int nsteps = (nent + kStep - 1) / kStep;
+  const int nstages = (nent + kSR - 1) / kSR;
   const T* Kb = static_cast<const T*>(A.K) + ((size_t)b * A.Hkv + kv) * (size_t)A.Lmax * kD;
   const T* Vb = static_cast<const T*>(A.V) + ((size_t)b * A.Hkv + kv) * (size_t)A.Lmax * kD;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int c = lane & 15;
-  const int gq = lane >> 4;
   auto key_of = [&](int e) { return e < ns ? e : kstart + (e - ns); };
-  // staging: thread tid moves 16 bytes of K and of V: row tid/16, piece tid%16
+  // staging: thread tid moves 16 bytes of K and of V in each of the rows tid/16 + 32 r,
+  // piece tid%16
+  constexpr int kRPT = kSR / 32;  // rows per thread
   const int srow = tid >> 4, spiece = tid & 15;
-  auto fetch = [&](int step, u4& kx, u4& vx) {
-    const int e = step * kStep + srow;
-    const size_t r = (size_t)key_of(e < nent ? e : 0);
-    kx = reinterpret_cast<const u4*>(Kb + r * kD)[spiece];
-    vx = reinterpret_cast<const u4*>(Vb + r * kD)[spiece];
+  auto fetch = [&](int stage, u4 (&kx)[kRPT], u4 (&vx)[kRPT]) {
+#pragma unroll
+    for (int r = 0; r < kRPT; r++) {
+      const int e = stage * kSR + srow + 32 * r;
+      const size_t row = (size_t)key_of(e < nent ? e : 0);
+      kx[r] = reinterpret_cast<const u4*>(Kb + row * kD)[spiece];
+      vx[r] = reinterpret_cast<const u4*>(Vb + row * kD)[spiece];
+    }
   };
-  auto store = [&](int buf, const u4& kx, const u4& vx) {
-    reinterpret_cast<u4*>(&kvs[buf][0][srow * kKS])[spiece] = kx;
-    reinterpret_cast<u4*>(&kvs[buf][1][srow * kKS])[spiece] = vx;
+  auto store = [&](int buf, const u4 (&kx)[kRPT], const u4 (&vx)[kRPT]) {
+#pragma unroll
+    for (int r = 0; r < kRPT; r++) {
+      reinterpret_cast<u4*>(&kvs[buf][0][(srow + 32 * r) * kKS])[spiece] = kx[r];
+      reinterpret_cast<u4*>(&kvs[buf][1][(srow + 32 * r) * kKS])[spiece] = vx[r];
+    }
   };
   // every wavefront takes one query head per pass; all take part in the staging
   for (int g0 = 0; g0 < A.G; g0 += kPW) {
     const int g = g0 + wv;
     const bool has = g < A.G;
     const int h = kv * A.G + (has ? g : 0);
-    v8<T> qop[4];
-    load_qop<T>(static_cast<const T*>(A.q) + ((size_t)(b * A.Hq + h) * A.Lmax + t0) * kD,
-                has ? ncol : 0, qop);
-    AttnState st;
-    attn_init(st);
-    u4 kx, vx;
+    const T* qh = static_cast<const T*>(A.q) + (size_t)(b * A.Hq + h) * A.Lmax * kD;
+    v8<T> qa[4], qb[4];
+    load_qop<T>(qh + (size_t)t0 * kD, has ? ncol_a : 0, qa);
+    load_qop<T>(qh + (size_t)(t0 + kPQ / 2) * kD, has ? ncol_b : 0, qb);
+    AttnState sa, sb;
+    attn_init(sa);
+    attn_init(sb);
+    u4 kx[kRPT], vx[kRPT];
     fetch(0, kx, vx);
     store(0, kx, vx);
     __syncthreads();
-    for (int s = 0; s < nsteps; s++) {
+    for (int s = 0; s < nstages; s++) {
       const int buf = s & 1;
-      if (s + 1 < nsteps) fetch(s + 1, kx, vx);  // in flight during this step's MFMAs
-      if (has) {
-        const int e0 = s * kStep;
+      if (s + 1 < nstages) fetch(s + 1, kx, vx);  // in flight during this stage's MFMAs
+#pragma unroll
+      for (int sub = 0; sub < kRPT; sub++) {
+        const int e0 = s * kSR + sub * kStep;
+        if (!has || e0 >= nent) continue;
         // a full step: every key exists, lies at or before the tile's first position and
         // (local heads) is a sink or inside every column's window; keys grow with e
         const int ehi = e0 + kStep - 1;
         bool full = ehi < nent && ncol == kPQ && key_of(ehi) <= t0;
         if (!ret && ehi >= ns) full = full && key_of(max(e0, ns)) >= tend - window;
-        step_lds(kvs[buf][0], kvs[buf][1], qop, A.scale2,
-                 [&](int i, int col) {
-                   if (full) return true;
-                   const int e = e0 + i;
-                   if (e >= nent || col >= ncol) return false;
-                   const int n = key_of(e), t = t0 + col;
-                   return n <= t && (ret || n < sinks || n > t - window);
-                 },
-                 st);
+        auto act = [&](int i, int col, int p0, int nc) {
+          if (full) return true;
+          const int e = e0 + i;
+          if (e >= nent || col >= nc) return false;
+          const int n = key_of(e), t = p0 + col;
+          return n <= t && (ret || n < sinks || n > t - window);
+        };
+        step_lds2<T>(kvs[buf][0] + sub * kStep * kKS, kvs[buf][1] + sub * kStep * kKS, qa, qb,
+                     A.scale2, [&](int i, int col) { return act(i, col, t0, ncol_a); },
+                     [&](int i, int col) { return act(i, col, t0 + kPQ / 2, ncol_b); }, sa, sb);
       }
-      if (s + 1 < nsteps) store(buf ^ 1, kx, vx);
+      if (s + 1 < nstages) store(buf ^ 1, kx, vx);
       __syncthreads();
     }
     if (has) {
-      // lane (gq, c) holds positions 4gq+t, dims 8c + nb; every position attends to
-      // itself, so its sum is positive
-      float l = st.l;
-      l += __shfl_xor(l, 16, 64);
-      l += __shfl_xor(l, 32, 64);
-#pragma unroll
-      for (int t = 0; t < 4; t++) {
-        const int col = 4 * gq + t;
-        const float lc = __shfl(l, col, 64);
-        if (col < ncol) {
-          const float r = 1.0f / lc;
-          float4* dst = reinterpret_cast<float4*>(
-              A.out + ((size_t)(b * A.Hq + h) * A.Lmax + t0 + col) * kD + 8 * c);
-          dst[0] = make_float4(st.o[0][t] * r, st.o[1][t] * r, st.o[2][t] * r, st.o[3][t] * r);
-          dst[1] = make_float4(st.o[4][t] * r, st.o[5][t] * r, st.o[6][t] * r, st.o[7][t] * r);
-        }
-      }
+      float* oh = A.out + (size_t)(b * A.Hq + h) * A.Lmax * kD;
+      store_set(sa, oh, t0, ncol_a);
+      store_set(sb, oh, t0 + kPQ / 2, ncol_b);
     }
   }
 }
@@ -285,7 +343,9 @@ __global__ __launch_bounds__(256) void k_prefill_cache(PrefillArgs A) {
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, hipStream_t st) {
+hipError_t launch_prefill(const PrefillArgs& args, int kv_dtype, hipStream_t st) {
+  PrefillArgs a = args;
+  a.ntile = (a.Lmax + kPQ - 1) / kPQ;
   const int nchunk = (a.Lmax + kPR - 1) / kPR;
   const bool bf = kv_dtype == 2;
   if (a.k_idx || a.K_ret || a.K_loc) {
