@@ -68,8 +68,8 @@ __device__ __forceinline__ float col_max(float v) {
 // a column with no active key so far takes m = 0 there, so its masked products (-inf)
 // give exactly 0.
 template <typename T, class Active>
-__device__ __forceinline__ void softmax_set(const f4& s0, const f4& s1, float scale2, Active active,
-                                            AttnState& st, v8<T>& pa, v8<T>& pb) {
+__device__ __forceinline__ void softmax_set(const f4& s0, const f4& s1, float scale2, bool full,
+                                            Active active, AttnState& st, v8<T>& pa, v8<T>& pb) {
   constexpr bool kPair = __is_same(T, bf16e);
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
@@ -77,8 +77,15 @@ __device__ __forceinline__ void softmax_set(const f4& s0, const f4& s1, float sc
   float r[8];
 #pragma unroll
   for (int t = 0; t < 4; t++) {
-    r[t] = active(4 * gq + t, c) ? s0[t] : -INFINITY;
-    r[4 + t] = active(16 + 4 * gq + t, c) ? s1[t] : -INFINITY;
+    r[t] = s0[t];
+    r[4 + t] = s1[t];
+  }
+  if (!full) {  // (uniform) steps that need the causal / window mask
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      if (!active(4 * gq + t, c)) r[t] = -INFINITY;
+      if (!active(16 + 4 * gq + t, c)) r[4 + t] = -INFINITY;
+    }
   }
   float mx = r[0];
 #pragma unroll
@@ -116,8 +123,8 @@ __device__ __forceinline__ void softmax_set(const f4& s0, const f4& s1, float sc
 // never live together.
 template <typename T, class ActA, class ActB>
 __device__ __forceinline__ void step_lds2(const T* Kl, const T* Vl, const v8<T> (&qa)[4],
-                                          const v8<T> (&qb)[4], float scale2, ActA act_a,
-                                          ActB act_b, AttnState& sa, AttnState& sb) {
+                                          const v8<T> (&qb)[4], float scale2, bool full,
+                                          ActA act_a, ActB act_b, AttnState& sa, AttnState& sb) {
   constexpr bool kPair = __is_same(T, bf16e);
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
@@ -139,8 +146,8 @@ __device__ __forceinline__ void step_lds2(const T* Kl, const T* Vl, const v8<T> 
     vv[u] = *reinterpret_cast<const v8<T>*>(Vl + i * kKS + 8 * c);
   }
   v8<T> paa, pba, pab, pbb;
-  softmax_set<T>(s0a, s1a, scale2, act_a, sa, paa, pba);
-  softmax_set<T>(s0b, s1b, scale2, act_b, sb, pab, pbb);
+  softmax_set<T>(s0a, s1a, scale2, full, act_a, sa, paa, pba);
+  softmax_set<T>(s0b, s1b, scale2, full, act_b, sb, pab, pbb);
 #pragma unroll
   for (int nb = 0; nb < 8; nb++) {
     v8<T> vb;
@@ -253,14 +260,13 @@ __global__ __launch_bounds__(kPW * 64, 2) void k_prefill_attn(PrefillArgs A) {
         bool full = ehi < nent && ncol == kPQ && key_of(ehi) <= t0;
         if (!ret && ehi >= ns) full = full && key_of(max(e0, ns)) >= tend - window;
         auto act = [&](int i, int col, int p0, int nc) {
-          if (full) return true;
           const int e = e0 + i;
           if (e >= nent || col >= nc) return false;
           const int n = key_of(e), t = p0 + col;
           return n <= t && (ret || n < sinks || n > t - window);
         };
         step_lds2<T>(kvs[buf][0] + sub * kStep * kKS, kvs[buf][1] + sub * kStep * kKS, qa, qb,
-                     A.scale2, [&](int i, int col) { return act(i, col, t0, ncol_a); },
+                     A.scale2, full, [&](int i, int col) { return act(i, col, t0, ncol_a); },
                      [&](int i, int col) { return act(i, col, t0 + kPQ / 2, ncol_b); }, sa, sb);
       }
       if (s + 1 < nstages) store(buf ^ 1, kx, vx);
