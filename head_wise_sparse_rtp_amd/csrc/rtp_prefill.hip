@@ -37,7 +37,12 @@ __device__ __forceinline__ int clamp_len_p(const int32_t* seq_lens, int b, int L
 }
 
 constexpr int kKS = kD + 8;  // LDS row stride of a staged K/V tile (elements): 272 bytes
-constexpr int kSR = 64;      // K/V rows staged per block barrier (two 32-row steps)
+// K/V rows staged per block barrier: 32-row steps per barrier x 32 (fp16: 4, bf16: 2, whose
+// weight pairs leave no registers for more staging)
+template <typename T>
+constexpr int stage_rows() {
+  return __is_same(T, bf16e) ? 64 : 128;
+}
 
 // a value written to a cache of element type T (round to nearest even), as its bits
 template <typename T>
@@ -187,6 +192,7 @@ __device__ __forceinline__ void store_set(const AttnState& st, float* out_head, 
 
 template <typename T>
 __global__ __launch_bounds__(kPW * 64, 2) void k_prefill_attn(PrefillArgs A) {
+  constexpr int kSR = stage_rows<T>();
   // two buffers of a kSR-row K tile and V tile (kSR / 32 steps per block barrier)
   __shared__ __align__(16) T kvs[2][2][kSR * kKS];
   const int qt = A.ntile - 1 - (int)(blockIdx.x % A.ntile);
