@@ -12,11 +12,11 @@
 // decode step's MFMA tile twice, with positions t0..t0+15 and t0+16..t0+31 as the columns
 // of its two sets: S^T = K . Q^T over 32 keys per step, an online softmax per position,
 // O += P . V, and a per-(key, position) mask for causality and the window.  Each K and V
-// operand read from LDS serves both sets, which halves the LDS bytes per flop.  The block stages each step's 32 K and V rows in
-// LDS once for all its wavefronts (two buffers, rows padded to 272 bytes; the next step's
-// global loads are in flight during this step's MFMAs).  The tile's keys are its sinks
-// followed by one contiguous run ending at its last position.  Longer tiles (later
-// positions) are launched first.
+// operand read from LDS serves both sets, which halves the LDS bytes per flop.  The block
+// stages 128 keys (bf16: 64) of K and V in LDS per barrier, once for all its wavefronts
+// (two buffers, rows padded to 272 bytes; the next stage's global loads are in flight
+// during this stage's MFMAs).  The tile's keys are its sinks followed by one contiguous run
+// ending at its last position.  Longer tiles (later positions) are launched first.
 //
 // Both kernels take the element type (fp16 or bf16) as a template parameter.  fp16
 // prompts enter P as one fp16 operand; bf16 prompts as a bf16 hi + lo pair (one bf16
