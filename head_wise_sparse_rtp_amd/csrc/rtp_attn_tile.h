@@ -37,6 +37,15 @@ __device__ __forceinline__ f4 mfma32(v8<bf16e> a, v8<bf16e> b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// max over the four lanes of one MFMA column (lanes l, l^16, l^32, l^48), on the VALU:
+// each permlane swap leaves a lane its own value and its partner's, in some order
+__device__ __forceinline__ float col_max(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
 // ---------------------------------------------------------------------------
 // MFMA attention engine
 // ---------------------------------------------------------------------------
@@ -115,26 +124,29 @@ __device__ __forceinline__ void step_compute(const StepLoads<T>& ld, const v8<T>
     s0 = mfma32(ld.k[0][s], qop[s], s0);
     s1 = mfma32(ld.k[1][s], qop[s], s1);
   }
-  float sc[8];
+  // the maximum is taken on the raw products (the scale is positive) and each weight is
+  // exp2(fma(s, scale2, -m)); a head with no active row so far takes m = 0 there, so its
+  // masked products (-inf) give exactly 0
+  float r[8];
 #pragma unroll
   for (int t = 0; t < 4; t++) {
-    sc[t] = active(4 * gq + t, h) ? s0[t] * scale2 : -INFINITY;
-    sc[4 + t] = active(16 + 4 * gq + t, h) ? s1[t] * scale2 : -INFINITY;
+    r[t] = active(4 * gq + t, h) ? s0[t] : -INFINITY;
+    r[4 + t] = active(16 + 4 * gq + t, h) ? s1[t] : -INFINITY;
   }
-  float mx = sc[0];
+  float mx = r[0];
 #pragma unroll
-  for (int i = 1; i < 8; i++) mx = fmaxf(mx, sc[i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float mn = fmaxf(st.m, mx);
+  for (int i = 1; i < 8; i++) mx = fmaxf(mx, r[i]);
+  mx = col_max(mx);
+  const float mn = fmaxf(st.m, mx * scale2);
   const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st.m - mn);
+  const float mref = (mn == -INFINITY) ? 0.0f : mn;
   // P = hi + lo in the operand type keeps the weights at about fp32 accuracy (fp16: 22
   // bits, bf16: 16 bits) through the 16-bit MFMA
   v8<T> pa, pb;
   float psum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    const float pv = (sc[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[i] - mn);
+    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(r[i], scale2, -mref));
     psum += pv;
     const T hi = (T)pv;
     pa[i] = hi;
@@ -142,14 +154,17 @@ __device__ __forceinline__ void step_compute(const StepLoads<T>& ld, const v8<T>
   }
   st.l = st.l * alpha + psum;
   st.m = mn;
-  // rescale the output rows (heads 4gq+t) by their heads' alpha
-  float at[4];
+  // rescale the output rows (heads 4gq+t) by their heads' alpha, when some head's maximum
+  // moved
+  if (__ballot(alpha != 1.0f) != 0ull) {
+    float at[4];
 #pragma unroll
-  for (int t = 0; t < 4; t++) at[t] = __shfl(alpha, 4 * gq + t, 64);
+    for (int t = 0; t < 4; t++) at[t] = __shfl(alpha, 4 * gq + t, 64);
 #pragma unroll
-  for (int nb = 0; nb < 8; nb++) {
+    for (int nb = 0; nb < 8; nb++) {
 #pragma unroll
-    for (int t = 0; t < 4; t++) st.o[nb][t] *= at[t];
+      for (int t = 0; t < 4; t++) st.o[nb][t] *= at[t];
+    }
   }
 #pragma unroll
   for (int nb = 0; nb < 8; nb++) {

@@ -56,15 +56,6 @@ __device__ __forceinline__ uint16_t cache_bits<bf16e>(float x) {
   return f_to_bf16(x);
 }
 
-// max over the four lanes of one MFMA column (lanes l, l^16, l^32, l^48), on the VALU:
-// each swap leaves a lane its own value and its partner's, in some order
-__device__ __forceinline__ float col_max(float v) {
-  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
-}
-
 // Online-softmax update of one set of 16 query columns from its two 16 x 16 tiles of
 // S^T (keys 0-15 and 16-31 of the step): the set's running max and sum, the rescale of its
 // output rows when some column's maximum moved, and P in the operand type (fp16: one
