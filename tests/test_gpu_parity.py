@@ -534,6 +534,48 @@ def test_prefill_long_prompt_sampled(rtp):
         assert max_err(out[b, h, t], o) <= 2e-3, (h, t)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_64k_sampled(rtp, dtype):
+    """The prefill the bench times (one 64K-token prompt, 32 query heads on 4 KV heads,
+    KV head 0 dense, window 8192 + 4 sinks), every head at positions around the tile,
+    stage and window edges, against the oracle."""
+    L = 65536
+    say("prefill 64K sampled", dtype)
+    pr = workloads.make_prompt([L], 32, 4, [1, 0, 0, 0], seed=7, device=dev(), with_kpre=False,
+                               dtype=dtype)
+    sl = torch.tensor([L], dtype=torch.int32, device=dev())
+    scale = 1.0 / math.sqrt(128)
+    out = rtp.rtp_prefill(sl, pr.kv_is_retrieval, pr.q, pr.K, pr.V, 8192, 4, scale).out
+    pos = [0, 3, 4, 31, 32, 127, 128, 8191, 8195, 8196, 8197, 8227, 32768, 40000, 65503,
+           65504, 65535]
+    got = out[0][:, pos].cpu().numpy()
+    ref = oracle.prefill_layer(pr.q, pr.K, pr.V, pr.kv_is_retrieval, [L], scale, 8192, 4,
+                               positions=pos)
+    worst = 0.0
+    for (b, h, t), o in ref.items():
+        e = max_err(got[h, pos.index(t)], o)
+        worst = max(worst, e)
+        assert e <= 2e-3, (h, t, e)
+    say("worst |dO|", worst)
+
+
+def test_prefill_bf16_long_prompt_sampled(rtp):
+    """A 9000-token bf16 prompt (its kernel stages 64 keys per barrier, fp16 128)."""
+    L = 9000
+    say("prefill bf16 9000 sampled")
+    pr = workloads.make_prompt([L], 8, 2, [1, 0], seed=96, device=dev(), with_kpre=False,
+                               dtype="bf16")
+    sl = torch.tensor([L], dtype=torch.int32, device=dev())
+    scale = 1.0 / math.sqrt(128)
+    out = rtp.rtp_prefill(sl, pr.kv_is_retrieval, pr.q, pr.K, pr.V, 8192, 4, scale).out
+    out = out.cpu().numpy()
+    pos = [0, 1, 31, 32, 63, 64, 65, 4099, 8191, 8192, 8196, 8197, 8999]
+    ref = oracle.prefill_layer(pr.q, pr.K, pr.V, pr.kv_is_retrieval, [L], scale, 8192, 4,
+                               positions=pos)
+    for (b, h, t), o in ref.items():
+        assert max_err(out[b, h, t], o) <= 2e-3, (h, t)
+
+
 @pytest.mark.parametrize("lens,window,sinks", [([300, 37, 1], 64, 4), ([200], 4096, 4)])
 def test_prefill_bf16_matches_oracle(rtp, lens, window, sinks):
     """bf16 prompt: outputs within the 2e-3 bar, and the decode state (k_idx rounded to
