@@ -112,6 +112,26 @@ __device__ __forceinline__ void softmax_set(const f4& s0, const f4& s1, float sc
   }
 }
 
+// B operand of O += P . V for output columns 16 nb .. 16 nb + 15 (head-dims), read with
+// the transposing LDS load: inside each group of 16 lanes (one k-group kg), output lane i
+// receives element i%4 of the 4 halfs that lane 4k + i/4 of the group addressed, for
+// k = 0..3.  Lane j of the group therefore addresses row 4 kg + j/4 (+16 for the second
+// read), dims 16 nb + 4 (j%4) .. +3; lane i then holds dim 16 nb + i of rows 4 kg + k and
+// 16 + 4 kg + k, which are exactly the key rows of its P operand's k-slots.
+typedef short s4v __attribute__((ext_vector_type(4)));
+typedef short s8v __attribute__((ext_vector_type(8)));
+template <typename T>
+__device__ __forceinline__ v8<T> v_operand_tr(const T* Vl, int nb) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15;
+  const int row = 4 * (lane >> 4) + (j >> 2);
+  const int col = 16 * nb + 4 * (j & 3);
+  typedef __attribute__((address_space(3))) s4v* lds_s4;
+  const s4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(Vl + row * kKS + col));
+  const s4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(Vl + (row + 16) * kKS + col));
+  return __builtin_bit_cast(v8<T>, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // One 32-row step from the staged tile for two sets of 16 query columns (positions
 // t0..t0+15 and t0+16..t0+31 of one head), in the layout of the decode step's tile: each
 // K operand read from LDS feeds the S MFMAs of both sets, and each V operand both sets'
@@ -135,20 +155,13 @@ __device__ __forceinline__ void step_lds2(const T* Kl, const T* Vl, const v8<T> 
     s0b = mfma32(k0, qb[s], s0b);
     s1b = mfma32(k1, qb[s], s1b);
   }
-  v8<T> vv[8];
-#pragma unroll
-  for (int u = 0; u < 8; u++) {
-    const int i = (u < 4) ? (4 * gq + u) : (16 + 4 * gq + (u - 4));
-    vv[u] = *reinterpret_cast<const v8<T>*>(Vl + i * kKS + 8 * c);
-  }
   v8<T> paa, pba, pab, pbb;
   softmax_set<T>(s0a, s1a, scale2, full, act_a, sa, paa, pba);
   softmax_set<T>(s0b, s1b, scale2, full, act_b, sb, pab, pbb);
+  // output columns of MFMA nb are head-dims 16 nb .. 16 nb + 15
 #pragma unroll
   for (int nb = 0; nb < 8; nb++) {
-    v8<T> vb;
-#pragma unroll
-    for (int u = 0; u < 8; u++) vb[u] = vv[u][nb];
+    const v8<T> vb = v_operand_tr<T>(Vl, nb);
     sa.o[nb] = mfma32(paa, vb, sa.o[nb]);
     sb.o[nb] = mfma32(pab, vb, sb.o[nb]);
     if constexpr (kPair) {
@@ -163,8 +176,8 @@ __device__ __forceinline__ void store_set(const AttnState& st, float* out_head, 
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
   const int gq = lane >> 4;
-  // lane (gq, c) holds positions 4gq+t, dims 8c + nb; every position attends to itself,
-  // so its sum is positive
+  // lane (gq, c) holds positions 4gq+t, dims 16 nb + c; every position attends to
+  // itself, so its sum is positive
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
@@ -174,9 +187,9 @@ __device__ __forceinline__ void store_set(const AttnState& st, float* out_head, 
     const float lc = __shfl(l, col, 64);
     if (col < ncol) {
       const float r = 1.0f / lc;
-      float4* dst = reinterpret_cast<float4*>(out_head + (size_t)(p0 + col) * kD + 8 * c);
-      dst[0] = make_float4(st.o[0][t] * r, st.o[1][t] * r, st.o[2][t] * r, st.o[3][t] * r);
-      dst[1] = make_float4(st.o[4][t] * r, st.o[5][t] * r, st.o[6][t] * r, st.o[7][t] * r);
+      float* dst = out_head + (size_t)(p0 + col) * kD + c;
+#pragma unroll
+      for (int nb = 0; nb < 8; nb++) dst[16 * nb] = st.o[nb][t] * r;
     }
   }
 }
