@@ -36,7 +36,7 @@ __device__ __forceinline__ int clamp_len_p(const int32_t* seq_lens, int b, int L
   return L < 0 ? 0 : (L > Lmax ? Lmax : L);
 }
 
-constexpr int kKS = kD + 8;  // LDS row stride of a staged K/V tile (elements): 272 bytes
+constexpr int kKS = kD + 16;  // LDS row stride of a staged K/V tile (elements): 288 bytes
 // K/V rows staged per block barrier: 32-row steps per barrier x 32 (fp16: 4, bf16: 2, whose
 // weight pairs leave no registers for more staging)
 template <typename T>
