@@ -52,7 +52,8 @@ __device__ __forceinline__ float col_max(float v) {
 struct AttnState {
   float m;     // running max (base-2 logits) of head lane%16
   float l;     // this lane's share of sum 2^(s - m) for head lane%16
-  f4 o[8];     // o[nb][t]: head 4*(lane/16)+t, dim 8*(lane%16)+nb
+  f4 o[8];     // o[nb][t]: head 4*(lane/16)+t, dim 8*(lane%16)+nb (the prefill's tile
+               // maps dim 16*nb + lane%16 instead)
 };
 
 __device__ __forceinline__ void attn_init(AttnState& s) {
