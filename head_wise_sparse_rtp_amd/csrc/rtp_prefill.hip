@@ -119,7 +119,6 @@ __device__ __forceinline__ void softmax_set(const f4& s0, const f4& s1, float sc
 // read), dims 16 nb + 4 (j%4) .. +3; lane i then holds dim 16 nb + i of rows 4 kg + k and
 // 16 + 4 kg + k, which are exactly the key rows of its P operand's k-slots.
 typedef short s4v __attribute__((ext_vector_type(4)));
-typedef short s8v __attribute__((ext_vector_type(8)));
 template <typename T>
 __device__ __forceinline__ v8<T> v_operand_tr(const T* Vl, int nb) {
   const int lane = threadIdx.x & 63;
@@ -138,7 +137,7 @@ __device__ __forceinline__ v8<T> v_operand_tr(const T* Vl, int nb) {
 // O += P . V; the V operands are read only after the S MFMAs, so that K and V registers are
 // never live together.
 template <typename T, class ActA, class ActB>
-__device__ __forceinline__ void step_lds2(const T* Kl, const T* Vl, const v8<T> (&qa)[4],
+__device__ __forceinline__ void step_lds(const T* Kl, const T* Vl, const v8<T> (&qa)[4],
                                           const v8<T> (&qb)[4], float scale2, bool full,
                                           ActA act_a, ActB act_b, AttnState& sa, AttnState& sb) {
   constexpr bool kPair = __is_same(T, bf16e);
@@ -275,7 +274,7 @@ __global__ __launch_bounds__(kPW * 64, 2) void k_prefill_attn(PrefillArgs A) {
           const int n = key_of(e), t = p0 + col;
           return n <= t && (ret || n < sinks || n > t - window);
         };
-        step_lds2<T>(kvs[buf][0] + sub * kStep * kKS, kvs[buf][1] + sub * kStep * kKS, qa, qb,
+        step_lds<T>(kvs[buf][0] + sub * kStep * kKS, kvs[buf][1] + sub * kStep * kKS, qa, qb,
                      A.scale2, full, [&](int i, int col) { return act(i, col, t0, ncol_a); },
                      [&](int i, int col) { return act(i, col, t0 + kPQ / 2, ncol_b); }, sa, sb);
       }
