@@ -482,7 +482,8 @@ def main():
     ms_step = elapsed_ms(h, e0, e1) / K
 
     # ---- per-kernel durations, timed live with HIP events on the launch stream ----
-    # events: [0] before stage A, [1] after stage A (indexer score + chunk histograms),
+    # events: [0] and [1] the start and the end of stage A (indexer score + chunk
+    # histograms; the library binds them to that kernel's launch when both are given),
     # [2] after stage T (suffix tables), [3] after the last kernel (stage B: selection,
     # sparse and window attention; stage M: merges).  Each profiled step is queued behind
     # a short busy kernel, so that all of its commands wait in the queue when the GPU

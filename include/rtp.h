@@ -180,10 +180,11 @@ typedef struct {
   float* lse;                     /* [B, Hq] fp32 out or NULL */
   int32_t* thresh_out;            /* [B, Hq, 2] {A, b*} for retrieval query heads, or NULL */
   int32_t* count_out;             /* [B, Hq] |S| for retrieval query heads, or NULL */
-  /* Optional profiling: hipEvent_t handles (or NULL) recorded on `stream`: [0] before
-   * the first kernel, [1] after the indexer-score/histogram kernel, [2] after the
-   * suffix-table (threshold) kernel, [3] after the last kernel.  [4..7] are reserved
-   * and must be NULL. */
+  /* Optional profiling: hipEvent_t handles (or NULL) on `stream`.  With retrieval heads and
+   * both [0] and [1] given, [0] and [1] track the start and the end of the indexer-score/
+   * histogram kernel itself (bound to its launch); otherwise [0] is recorded before the
+   * first kernel and [1] after that kernel.  [2] is recorded after the suffix-table
+   * (threshold) kernel, [3] after the last kernel.  [4..7] are reserved and must be NULL. */
   void* prof_ev[8];
   int32_t topk;                   /* 0: top-p with p; > 0: fixed top-k (rtp_topk_select's rule)
                                    * for every retrieval query head; < 0: RTP_EINVAL */
