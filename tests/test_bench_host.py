@@ -1,0 +1,68 @@
+"""Host-side logic of bench.py (no GPU): the prefill's work count, the counter summary
+behind `roofline.traffic`, and the single-GPU guard."""
+from __future__ import annotations
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("L,window,sinks", [(1, 4, 2), (7, 4, 2), (40, 8, 4), (40, 8, 0),
+                                            (13, 64, 4), (100, 1, 1)])
+def test_prefill_pairs_counts_the_attended_keys(L, window, sinks):
+    # the flop count of the prefill roofline (4 * d per pair) against the key sets the
+    # oracle attends, position by position
+    for retrieval in (True, False):
+        brute = sum(len(oracle.prefill_rows(t, retrieval, window, sinks)) for t in range(L))
+        assert bench.prefill_pairs(L, retrieval, window, sinks) == brute
+
+
+def _pmc_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, value in rows:
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_summarize_pmc_scales_by_the_copy(tmp_path):
+    # FETCH_SIZE reads half of the copy's 1 MiB (scale 2), WRITE_SIZE all of it (scale 1);
+    # the stage-A mean is taken over its dispatches, the largest copy is the calibration
+    name = "void rtp::(anonymous namespace)::k_stage_a<512, _Float16>(rtp::StageAParams)"
+    copy = "void at::native::vectorized_elementwise_kernel<neg_kernel>(int)"
+    f, w, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "t.json"
+    _pmc_csv(f, "FETCH_SIZE", [(name, 100.0), (name, 300.0), (copy, 512.0), (copy, 2.0)])
+    _pmc_csv(w, "WRITE_SIZE", [(name, 50.0), (name, 50.0), (copy, 1024.0)])
+    bench.summarize_pmc(str(f), str(w), "c4", 2 ** 20, str(out))
+    res = json.loads(out.read_text())
+    assert res["FETCH_SIZE"]["scale"] == 2.0 and res["WRITE_SIZE"]["scale"] == 1.0
+    assert res["FETCH_SIZE"]["bytes_per_launch"] == 200 * 1024 * 2
+    assert res["WRITE_SIZE"]["bytes_per_launch"] == 50 * 1024
+    assert res["bytes_per_launch"] == 200 * 1024 * 2 + 50 * 1024
+    assert res["source_sha256"] == bench.source_sha256()
+
+
+def test_summarize_pmc_needs_both_kernels(tmp_path):
+    f, w, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "t.json"
+    _pmc_csv(f, "FETCH_SIZE", [("k_stage_a", 1.0)])  # no copy kernel
+    _pmc_csv(w, "WRITE_SIZE", [("k_stage_a", 1.0)])
+    with pytest.raises(SystemExit):
+        bench.summarize_pmc(str(f), str(w), "c4", 2 ** 20, str(out))
+    assert not out.exists()
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "one GPU" in r.stderr
+    assert not r.stdout.strip()
