@@ -402,7 +402,25 @@ def test_decode_step_retrieval_window_small_ragged(rtp, dtype, p):
     check_decode(rtp, wl, label="retwin-%s-p%g" % (dtype, p))
 
 
-@pytest.mark.parametrize("name", ["c1", "c4"])
+def test_append_then_decode_c4(rtp):
+    """The bench's `--with-append` step at 1M context: the cache update with the inputs
+    that reproduce the workload's state, then the layer step; the oracle runs its own."""
+    say("append + decode c4")
+    wl = workloads.make_config("c4", device=dev())
+    lay = wl.layers[0]
+    si = workloads.make_embedding_step_inputs(wl, device=dev())
+    want = oracle.append_project(lay, wl.seq_lens, si.q_pre, si.k_pre, si.k_new, si.v_new, si.Wq,
+                                 si.Wk, wl.window, wl.sinks)
+    olay = _oracle_layer(lay, want)
+    sl = torch.tensor(wl.seq_lens, dtype=torch.int32, device=dev())
+    rtp.rtp_append_project(lay, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window, wl.sinks, si.q_pre,
+                           si.k_pre, si.Wq, si.Wk, si.k_new, si.v_new)
+    assert np.array_equal(_bits(oracle.np_of(lay.k_idx)), _bits(want[1]))
+    assert np.array_equal(_bits(oracle.np_of(lay.q_idx)), _bits(want[0]))
+    check_decode(rtp, wl, label="append-c4", oracle_layers=[olay])
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c4"])
 def test_decode_step_retrieval_window_config(rtp, name):
     say("config", name, "retrieval + window")
     wl = workloads.make_config(name, device=dev())
@@ -467,6 +485,14 @@ def test_decode_step_bf16_64k(rtp):
     wl = workloads.make_workload("c1-bf16", 1, [65536], 32, 4, [[1, 0, 0, 0]], seed=1,
                                  dtype="bf16", device=dev())
     check_decode(rtp, wl, label="c1-bf16")
+
+
+@pytest.mark.parametrize("name", ["c2", "c4"])
+def test_decode_step_config_bf16(rtp, name):
+    """The bench's `--dtype bf16` configurations at full size."""
+    say("config", name, "bf16")
+    wl = workloads.make_config(name, device=dev(), dtype="bf16")
+    check_decode(rtp, wl, label="%s-bf16" % name)
 
 
 @pytest.mark.parametrize("name", ["c0", "c1", "c2", "c4"])
