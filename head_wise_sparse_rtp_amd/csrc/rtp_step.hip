@@ -176,7 +176,7 @@ struct StageAParams {
   const float* q_idx;
   const void* k_idx;  // fp16 or bf16 (the kernel's element type)
   HeadMap ret;
-  int Hret, nchunk, ngg, nunits;
+  int Hret, nchunk, ngg;
   int counts;  // unit weight per token (fixed top-k); c_log2 is then 0
   float yscale, c_log2;
   double w;
@@ -225,13 +225,15 @@ struct HistUnit {
   size_t rowb;
 };
 
+// grid (chunk, head group, sequence x retrieval KV head): the unit needs no division
+// but b = z / Hret, in scalar registers
 template <int NT>
-__device__ __forceinline__ HistUnit hist_unit(const StageAParams& P, int hb) {
+__device__ __forceinline__ HistUnit hist_unit(const StageAParams& P) {
   HistUnit u;
-  u.chunk = hb % P.nchunk;
-  u.grp = (hb / P.nchunk) % P.ngg;
-  u.kr = (hb / (P.nchunk * P.ngg)) % P.Hret;
-  u.b = hb / (P.nchunk * P.ngg * P.Hret);
+  u.chunk = blockIdx.x;
+  u.grp = blockIdx.y;
+  u.kr = blockIdx.z % P.Hret;
+  u.b = blockIdx.z / P.Hret;
   u.nrows = min(8, P.G - u.grp * 8);
   u.rowb = (size_t)u.b * P.Hret * P.G + (size_t)u.kr * P.G + u.grp * 8;
   return u;
@@ -306,7 +308,10 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
   float qm = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; i++) qm = fmaxf(qm, fabsf(q[i]));
-  qm = fmaxf(qm, __shfl_xor(qm, 16, 64));
+  {  // lanes l and l^16 hold the two halves of the head's q_idx
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(qm), __float_as_uint(qm), false, false);
+    qm = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  }
   int e = 0;
   (void)frexpf(qm, &e);  // qm < 2^e
   const float ysc = hh < nrows ? ldexpf(P.yscale, e - 14) : 0.0f;
@@ -333,18 +338,23 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
 #pragma unroll
     for (int k = 0; k < NQP; k++) d = mfma32(in.ka[gi], qp[k], d);
 #pragma unroll
-    for (int t = 0; t < 4; t++) {
-      float v = d[t] * ysc;
-      if (!full && wbase + gi * 32 + 16 * th + 4 * kq + t >= L) v = kMaskY;
-      y[gi][t] = v;
-      ym = fmaxf(ym, v);
-    }
+    for (int t = 0; t < 4; t++) y[gi][t] = d[t] * ysc;
   }
-  // lanes of one head differ in bits 3..5: rotate by 8 inside the row, swap the rows of
-  // each half, then the halves
+  if (!full) {  // (uniform) the chunk runs past the sequence's end
+#pragma unroll
+    for (int gi = 0; gi < 8; gi++)
+#pragma unroll
+      for (int t = 0; t < 4; t++)
+        if (wbase + gi * 32 + 16 * th + 4 * kq + t >= L) y[gi][t] = kMaskY;
+  }
+#pragma unroll
+  for (int gi = 0; gi < 8; gi++)
+#pragma unroll
+    for (int t = 0; t < 4; t++) ym = fmaxf(ym, y[gi][t]);
+  // lanes of one head differ in bits 3..5: rotate by 8 inside the row (bit 3), then the
+  // permlane swaps (bits 4 and 5)
   ym = fmaxf(ym, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ym), 0x128, 0xf, 0xf, false)));
-  ym = fmaxf(ym, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(ym), 0x401F)));
-  ym = fmaxf(ym, __shfl_xor(ym, 32, 64));
+  ym = col_max(ym);
   if (lane < GG) smax[lane * NWV + wv] = ym;
   __syncthreads();
   float m = smax[hh * NWV];
@@ -438,7 +448,7 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
 template <int NT, typename T>
 __global__ __launch_bounds__(NT, NT >= 512 ? 2 : 4) void k_stage_a(StageAParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const HistUnit U = hist_unit<NT>(P, blockIdx.x);
+  const HistUnit U = hist_unit<NT>(P);
   HistIn<T> in;
   hist_fetch<NT, T>(P, U, in);
   hist_block<NT, T>(P, U, in, smem);
@@ -1231,23 +1241,22 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     P.partA = at<int32_t>(ws, sp.partA);
     P.codes = at<uint32_t>(ws, sp.codes);
     P.sufq = at<unsigned long long>(ws, sp.sufq);
-    P.nunits = B * sp.Hret * P.ngg * sp.nchunk;
     // histogram copies, the top cells of the wavefronts, the code words of the wavefronts
     const int cpA = sp.nt >= 512 ? copies_of<512>() : copies_of<256>();
     const size_t ldsA = sizeof(uint32_t) * cpA * GG * (kNB + kPad) + sizeof(float) * GG * 8 +
                         sizeof(uint32_t) * (sp.nt / 64) * GG * 64;
-    const int nA = P.nunits;
+    const dim3 gA(sp.nchunk, P.ngg, B * sp.Hret);
 #define RTP_STAGE_A(NTV)                                                                    \
   do {                                                                                      \
     if (bind_a) {                                                                           \
       const void* fn = a.kv_dtype == 2 ? reinterpret_cast<const void*>(&k_stage_a<NTV, bf16e>) \
                                        : reinterpret_cast<const void*>(&k_stage_a<NTV, f16>);   \
       void* args[] = {&P};                                                                  \
-      e = hipExtLaunchKernel(fn, dim3(nA), dim3(NTV), args, ldsA, st, ev[0], ev[1], 0);     \
+      e = hipExtLaunchKernel(fn, gA, dim3(NTV), args, ldsA, st, ev[0], ev[1], 0);            \
     } else if (a.kv_dtype == 2) {                                                           \
-      k_stage_a<NTV, bf16e><<<nA, NTV, ldsA, st>>>(P);                                     \
+      k_stage_a<NTV, bf16e><<<gA, NTV, ldsA, st>>>(P);                                     \
     } else {                                                                                \
-      k_stage_a<NTV, f16><<<nA, NTV, ldsA, st>>>(P);                                       \
+      k_stage_a<NTV, f16><<<gA, NTV, ldsA, st>>>(P);                                       \
     }                                                                                       \
   } while (0)
     if (sp.nt == 256)
