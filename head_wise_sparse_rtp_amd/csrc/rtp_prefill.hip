@@ -56,16 +56,33 @@ __device__ __forceinline__ uint16_t cache_bits<bf16e>(float x) {
   return f_to_bf16(x);
 }
 
+// Running state of one set of 16 query columns: max (base 2) of column lane%16, the row
+// sums and the output rows in the MFMA output layout (lane (c, gq): positions 4gq+t).  The
+// row sums come from one more MFMA per step, P times a ones operand, so they add exactly
+// the rounded weights the output rows add, and need neither VALU adds nor shuffles.
+struct PfState {
+  float m;
+  f4 lsum;   // lsum[t]: sum of the weights of position 4*(lane/16)+t
+  f4 o[8];   // o[nb][t]: position 4*(lane/16)+t, head-dim 16 nb + lane%16
+};
+
+__device__ __forceinline__ void pf_init(PfState& s) {
+  s.m = -INFINITY;
+  s.lsum = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int nb = 0; nb < 8; nb++) s.o[nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
 // Online-softmax update of one set of 16 query columns from its two 16 x 16 tiles of
-// S^T (keys 0-15 and 16-31 of the step): the set's running max and sum, the rescale of its
-// output rows when some column's maximum moved, and P in the operand type (fp16: one
+// S^T (keys 0-15 and 16-31 of the step): the set's running max, the rescale of its output
+// rows and sums when some column's maximum moved, and P in the operand type (fp16: one
 // part, relative error 2^-11 per weight; bf16: a hi + lo pair).  The maximum is taken on
 // the raw products (the scale is positive) and each weight is exp2(fma(s, scale2, -m));
 // a column with no active key so far takes m = 0 there, so its masked products (-inf)
 // give exactly 0.
 template <typename T, class Active>
 __device__ __forceinline__ void softmax_set(const f4& s0, const f4& s1, float scale2, bool full,
-                                            Active active, AttnState& st, v8<T>& pa, v8<T>& pb) {
+                                            Active active, PfState& st, v8<T>& pa, v8<T>& pb) {
   constexpr bool kPair = __is_same(T, bf16e);
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
@@ -90,21 +107,20 @@ __device__ __forceinline__ void softmax_set(const f4& s0, const f4& s1, float sc
   const float mn = fmaxf(st.m, mx * scale2);
   const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st.m - mn);
   const float mref = (mn == -INFINITY) ? 0.0f : mn;
-  float psum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(r[i], scale2, -mref));
-    psum += pv;
     pa[i] = (T)pv;
     if constexpr (kPair) pb[i] = (T)(pv - (float)pa[i]);
   }
-  st.l = st.l * alpha + psum;
   st.m = mn;
-  // the output rows need rescaling only when some column's maximum moved
+  // the output rows and sums need rescaling only when some column's maximum moved
   if (__ballot(alpha != 1.0f) != 0ull) {
     float at[4];
 #pragma unroll
     for (int t = 0; t < 4; t++) at[t] = __shfl(alpha, 4 * gq + t, 64);
+#pragma unroll
+    for (int t = 0; t < 4; t++) st.lsum[t] *= at[t];
 #pragma unroll
     for (int nb = 0; nb < 8; nb++)
 #pragma unroll
@@ -139,7 +155,7 @@ __device__ __forceinline__ v8<T> v_operand_tr(const T* Vl, int nb) {
 template <typename T, class ActA, class ActB>
 __device__ __forceinline__ void step_lds(const T* Kl, const T* Vl, const v8<T> (&qa)[4],
                                           const v8<T> (&qb)[4], float scale2, bool full,
-                                          ActA act_a, ActB act_b, AttnState& sa, AttnState& sb) {
+                                          ActA act_a, ActB act_b, PfState& sa, PfState& sb) {
   constexpr bool kPair = __is_same(T, bf16e);
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
@@ -168,24 +184,30 @@ __device__ __forceinline__ void step_lds(const T* Kl, const T* Vl, const v8<T> (
       sb.o[nb] = mfma32(pbb, vb, sb.o[nb]);
     }
   }
+  // the row sums: P times ones
+  v8<T> ones;
+#pragma unroll
+  for (int i = 0; i < 8; i++) ones[i] = (T)1.0f;
+  sa.lsum = mfma32(paa, ones, sa.lsum);
+  sb.lsum = mfma32(pab, ones, sb.lsum);
+  if constexpr (kPair) {
+    sa.lsum = mfma32(pba, ones, sa.lsum);
+    sb.lsum = mfma32(pbb, ones, sb.lsum);
+  }
 }
 
 // write the normalised rows of one column set (positions p0 + col, col < ncol)
-__device__ __forceinline__ void store_set(const AttnState& st, float* out_head, int p0, int ncol) {
+__device__ __forceinline__ void store_set(const PfState& st, float* out_head, int p0, int ncol) {
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
   const int gq = lane >> 4;
-  // lane (gq, c) holds positions 4gq+t, dims 16 nb + c; every position attends to
-  // itself, so its sum is positive
-  float l = st.l;
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  // lane (gq, c) holds positions 4gq+t, dims 16 nb + c, and their sums; every position
+  // attends to itself, so its sum is positive
 #pragma unroll
   for (int t = 0; t < 4; t++) {
     const int col = 4 * gq + t;
-    const float lc = __shfl(l, col, 64);
     if (col < ncol) {
-      const float r = 1.0f / lc;
+      const float r = 1.0f / st.lsum[t];
       float* dst = out_head + (size_t)(p0 + col) * kD + c;
 #pragma unroll
       for (int nb = 0; nb < 8; nb++) dst[16 * nb] = st.o[nb][t] * r;
@@ -249,9 +271,9 @@ __global__ __launch_bounds__(kPW * 64, 2) void k_prefill_attn(PrefillArgs A) {
     v8<T> qa[4], qb[4];
     load_qop<T>(qh + (size_t)t0 * kD, has ? ncol_a : 0, qa);
     load_qop<T>(qh + (size_t)(t0 + kPQ / 2) * kD, has ? ncol_b : 0, qb);
-    AttnState sa, sb;
-    attn_init(sa);
-    attn_init(sb);
+    PfState sa, sb;
+    pf_init(sa);
+    pf_init(sb);
     u4 kx[kRPT], vx[kRPT];
     fetch(0, kx, vx);
     store(0, kx, vx);
