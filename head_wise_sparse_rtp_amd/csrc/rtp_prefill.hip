@@ -75,7 +75,7 @@ __device__ __forceinline__ void pf_init(PfState& s) {
 
 // Online-softmax update of one set of 16 query columns from its two 16 x 16 tiles of
 // S^T (keys 0-15 and 16-31 of the step): the set's running max, the rescale of its output
-// rows and sums when some column's maximum moved, and P in the operand type (fp16: one
+// rows and sums when it moves, and P in the operand type (fp16: one
 // part, relative error 2^-11 per weight; bf16: a hi + lo pair).  The maximum is taken on
 // the raw products (the scale is positive) and each weight is exp2(fma(s, scale2, -m));
 // a column with no active key so far takes m = 0 there, so its masked products (-inf)
@@ -103,19 +103,14 @@ __device__ __forceinline__ void softmax_set(const f4& s0, const f4& s1, float sc
   float mx = r[0];
 #pragma unroll
   for (int i = 1; i < 8; i++) mx = fmaxf(mx, r[i]);
-  mx = col_max(mx);
-  const float mn = fmaxf(st.m, mx * scale2);
-  const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st.m - mn);
-  const float mref = (mn == -INFINITY) ? 0.0f : mn;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(r[i], scale2, -mref));
-    pa[i] = (T)pv;
-    if constexpr (kPair) pb[i] = (T)(pv - (float)pa[i]);
-  }
-  st.m = mn;
-  // the output rows and sums need rescaling only when some column's maximum moved
-  if (__ballot(alpha != 1.0f) != 0ull) {
+  mx = col_max(mx) * scale2;  // this step's maximum, base 2
+  // the running maximum moves (and the rows and sums are rescaled) only when some column's
+  // step maximum exceeds it by more than 8, so every weight stays below 2^8 (far inside
+  // the fp16/bf16 operand and fp32 accumulator ranges); a first active key always moves it
+  if (__ballot(mx > st.m + 8.0f) != 0ull) {
+    const float mn = fmaxf(st.m, mx);
+    const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st.m - mn);
+    st.m = mn;
     float at[4];
 #pragma unroll
     for (int t = 0; t < 4; t++) at[t] = __shfl(alpha, 4 * gq + t, 64);
@@ -125,6 +120,13 @@ __device__ __forceinline__ void softmax_set(const f4& s0, const f4& s1, float sc
     for (int nb = 0; nb < 8; nb++)
 #pragma unroll
       for (int t = 0; t < 4; t++) st.o[nb][t] *= at[t];
+  }
+  const float mref = (st.m == -INFINITY) ? 0.0f : st.m;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(r[i], scale2, -mref));
+    pa[i] = (T)pv;
+    if constexpr (kPair) pb[i] = (T)(pv - (float)pa[i]);
   }
 }
 
