@@ -348,6 +348,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4")
+    ap.add_argument("--context", type=int, default=0, metavar="L",
+                    help="sequence length of the c3/c4 workload (default: its own)")
     ap.add_argument("--p", type=float, default=None)
     ap.add_argument("--topk", type=int, default=0,
                     help="fixed top-k through the histogram instead of top-p")
@@ -396,6 +398,10 @@ def main():
     kw = {} if args.p is None else {"p": args.p}
     if args.dtype != "f16":
         kw["dtype"] = args.dtype
+    if args.context:
+        if args.workload not in ("c3", "c4"):
+            sys.exit("--context applies to the c3 and c4 workloads")
+        kw["L"] = args.context
     wl = workloads.make_config(args.workload, device=dev, **kw)
     if len(wl.layers) > 1:
         bench_layers(args, wl)
@@ -553,7 +559,11 @@ def main():
         "roofline": {"kernel": "k_stage_a (indexer score on MFMA + 256-bin chunk histograms)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None if args.topk else measured_traffic(args.workload),
+                     # the counters were taken on the fp16 top-p step at the workload's own
+                     # length
+                     "traffic": (measured_traffic(args.workload)
+                                 if not (args.topk or args.context or args.dtype != "f16")
+                                 else None),
                      "avg_us": round(a_us, 3), "algorithmic_bytes_per_launch": a_bytes},
         "phases_us": {k: round(v, 3) for k, v in ph.items()},
     }

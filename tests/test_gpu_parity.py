@@ -515,6 +515,16 @@ def test_decode_step_c3_48_layers(rtp):
     check_decode(rtp, wl, local_sample=8, label="c3")
 
 
+def test_decode_step_max_context(rtp):
+    """The longest sequence the fused step takes, Lmax = 2^24 tokens (the 1M layer's heads
+    and classes): 8192 histogram chunks, stage-T blocks of 32 chunks, 4096 selection blocks
+    and 4096 partials per retrieval head in the merge (its limit), and suffix-table sums
+    near the top of the fixed-point range."""
+    say("config c4 at 2^24 tokens")
+    wl = workloads.make_c4(device=dev(), L=1 << 24)
+    check_decode(rtp, wl, label="c4-16M")
+
+
 # ---------------------------------------------------------------------------
 # rtp_prefill: causal attention of a prompt and the decode state it leaves
 # ---------------------------------------------------------------------------
