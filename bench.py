@@ -350,6 +350,9 @@ def main():
     ap.add_argument("--workload", default="c4")
     ap.add_argument("--context", type=int, default=0, metavar="L",
                     help="sequence length of the c3/c4 workload (default: its own)")
+    ap.add_argument("--dense", action="store_true",
+                    help="dense decode attention on the same GPU: C4's shape with every KV head "
+                         "local and a window covering the whole context")
     ap.add_argument("--p", type=float, default=None)
     ap.add_argument("--topk", type=int, default=0,
                     help="fixed top-k through the histogram instead of top-p")
@@ -402,7 +405,17 @@ def main():
         if args.workload not in ("c3", "c4"):
             sys.exit("--context applies to the c3 and c4 workloads")
         kw["L"] = args.context
-    wl = workloads.make_config(args.workload, device=dev, **kw)
+    if args.dense:
+        # a window of L positions (plus the sinks) holds every token: exact dense attention
+        # for all 32 query heads, through the same fused step
+        if args.workload != "c4" or args.topk or args.ret_window or args.with_append:
+            sys.exit("--dense is the c4 shape alone")
+        L = args.context or 1048576
+        args.workload = "dense"
+        wl = workloads.make_workload("dense", 1, [L], 32, 4, [[0, 0, 0, 0]], seed=4, window=L,
+                                     device=dev, dtype=args.dtype)
+    else:
+        wl = workloads.make_config(args.workload, device=dev, **kw)
     if len(wl.layers) > 1:
         bench_layers(args, wl)
         return
@@ -506,10 +519,10 @@ def main():
         torch.cuda._sleep(200000)  # a spinning kernel (tens of us, touches no memory)
         st()
         torch.cuda.synchronize()
-        ph[names[0]] += elapsed_ms(h, evs[0], evs[1])
         if has_ret:
+            ph[names[0]] += elapsed_ms(h, evs[0], evs[1])
             ph[names[1]] += elapsed_ms(h, evs[1], evs[2])
-            ph[names[2]] += elapsed_ms(h, evs[2], evs[3])
+        ph[names[2]] += elapsed_ms(h, evs[2], evs[3])
         for j in range(4):
             st.desc.prof_ev[j] = None
     ph = {k: v / K * 1000.0 for k, v in ph.items()}  # microseconds
@@ -524,8 +537,12 @@ def main():
             torch.cuda.synchronize()
             tot += elapsed_ms(h, evs[0], evs[1])
         ph["append_project"] = tot / K * 1000.0
-    a_us = ph["stageA_score_hist"]
-    a_bytes = detail["kidx"]
+    if has_ret:
+        a_us = ph["stageA_score_hist"]
+        a_bytes = detail["kidx"]
+    else:  # window attention only: stage B's window blocks (and the merge) are the step
+        a_us = ph["stageBM_select_attend_merge"]
+        a_bytes = detail["window_kv"]
     achieved = a_bytes / (a_us * 1e-6) / 1e9 if a_us > 0 else 0.0
 
     value = bytes_step / (ms_step * 1e-3) / 1e9
@@ -556,7 +573,9 @@ def main():
         "bytes_detail": {k: v for k, v in detail.items() if k not in ("sel_tokens", "sel_mass")},
         "sel_tokens_per_head": detail["sel_tokens"],
         "sel_mass_per_head": detail["sel_mass"],
-        "roofline": {"kernel": "k_stage_a (indexer score on MFMA + 256-bin chunk histograms)",
+        "roofline": {"kernel": ("k_stage_a (indexer score on MFMA + 256-bin chunk histograms)"
+                                if has_ret else
+                                "k_stage_b window blocks (MFMA attention) + k_stage_m merge"),
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      # the counters were taken on the fp16 top-p step at the workload's own

@@ -515,6 +515,16 @@ def test_decode_step_c3_48_layers(rtp):
     check_decode(rtp, wl, local_sample=8, label="c3")
 
 
+def test_decode_step_dense_window_1m(rtp):
+    """The bench's dense reference (`--dense`): every KV head local, with a window that
+    holds all 1M tokens, which is exact dense decode attention for the 32 query heads."""
+    say("dense decode at 1M (window = L)")
+    L = 1 << 20
+    wl = workloads.make_workload("dense", 1, [L], 32, 4, [[0, 0, 0, 0]], seed=4, window=L,
+                                 device=dev())
+    check_decode(rtp, wl, label="dense-1M")
+
+
 def test_decode_step_max_context(rtp):
     """The longest sequence the fused step takes, Lmax = 2^24 tokens (the 1M layer's heads
     and classes): 8192 histogram chunks, stage-T blocks of 32 chunks, 4096 selection blocks
