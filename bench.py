@@ -219,7 +219,8 @@ def bench_prefill(args):
     import workloads
     dev = torch.device("cuda:0")
     L, Hq, Hkv, d, window, sinks = args.prefill, 32, 4, 128, 8192, 4
-    mask = [1, 0, 0, 0]
+    # --dense: every KV head dense causal, the dense prefill of the same prompt
+    mask = [1, 1, 1, 1] if args.dense else [1, 0, 0, 0]
     pr = workloads.make_prompt([L], Hq, Hkv, mask, seed=7, device=dev, dtype=args.dtype)
     sl = torch.tensor([L], dtype=torch.int32, device=dev)
     pf = rtp.Prefill(sl, mask, pr.q, pr.K, pr.V, window, sinks, 1.0 / math.sqrt(d), pr.k_pre,
@@ -247,9 +248,10 @@ def bench_prefill(args):
         "warmup": args.warmup, "ms_per_prefill": round(ms, 4), "higher_is_better": True,
         "dtype": "%s q/K/V, fp32 accumulation" % args.dtype,
         "data": "synthetic (counter-based N(0,1))",
-        "config": {"workload": "prefill: B=1, L=%d, Hq=%d, Hkv=%d (retrieval [0]), d=%d, "
+        "config": {"workload": "prefill: B=1, L=%d, Hq=%d, Hkv=%d (retrieval %s), d=%d, "
                                "window=%d+%d sinks; with the decode state (k_idx, caches, rings)"
-                               % (L, Hq, Hkv, d, window, sinks)},
+                               % (L, Hq, Hkv, [i for i, m in enumerate(mask) if m], d, window,
+                                  sinks)},
         "attended_pairs": pairs, "dense_causal_pairs": dense,
         "dense_over_sparse_work": round(dense / pairs, 3),
         "roofline": {"kernel": "k_prefill_attn (MFMA 16x16x32 %s)" % args.dtype, "bound": "mfma",
@@ -351,8 +353,9 @@ def main():
     ap.add_argument("--context", type=int, default=0, metavar="L",
                     help="sequence length of the c3/c4 workload (default: its own)")
     ap.add_argument("--dense", action="store_true",
-                    help="dense decode attention on the same GPU: C4's shape with every KV head "
-                         "local and a window covering the whole context")
+                    help="the dense counterpart on the same GPU: decode, C4's shape with every KV "
+                         "head local and a window covering the whole context; with --prefill, "
+                         "every KV head dense causal")
     ap.add_argument("--p", type=float, default=None)
     ap.add_argument("--topk", type=int, default=0,
                     help="fixed top-k through the histogram instead of top-p")
@@ -405,7 +408,7 @@ def main():
         if args.workload not in ("c3", "c4"):
             sys.exit("--context applies to the c3 and c4 workloads")
         kw["L"] = args.context
-    if args.dense:
+    if args.dense and not args.prefill:
         # a window of L positions (plus the sinks) holds every token: exact dense attention
         # for all 32 query heads, through the same fused step
         if args.workload != "c4" or args.topk or args.ret_window or args.with_append:

@@ -605,6 +605,33 @@ def test_prefill_64k_sampled(rtp, dtype):
     say("worst |dO|", worst)
 
 
+def test_prefill_1m_sampled(rtp):
+    """A 1M-token prompt (the context of the decode step), KV head 0 dense, window 8192 + 4
+    sinks: every head at positions near the start, the window edge, the middle and the end,
+    against the oracle's attention over the same key sets."""
+    L = 1 << 20
+    say("prefill 1M sampled")
+    pr = workloads.make_prompt([L], 32, 4, [1, 0, 0, 0], seed=7, device=dev(), with_kpre=False)
+    sl = torch.tensor([L], dtype=torch.int32, device=dev())
+    scale = 1.0 / math.sqrt(128)
+    out = rtp.rtp_prefill(sl, pr.kv_is_retrieval, pr.q, pr.K, pr.V, 8192, 4, scale).out
+    pos = [0, 31, 32, 8195, 8196, 524287, 1048543, 1048575]
+    got = out[0][:, pos].cpu().numpy()
+    del out
+    qs = pr.q[0][:, pos].cpu().numpy()
+    Kn, Vn = oracle.np_of(pr.K[0]), oracle.np_of(pr.V[0])
+    worst = 0.0
+    for h in range(32):
+        kv = h // 8
+        for i, t in enumerate(pos):
+            rows = oracle.prefill_rows(t, kv == 0, 8192, 4)
+            o, _ = oracle.attention(qs[h, i], Kn[kv], Vn[kv], rows, scale)
+            e = max_err(got[h, i], o)
+            worst = max(worst, e)
+            assert e <= 2e-3, (h, t, e)
+    say("worst |dO|", worst)
+
+
 def test_prefill_bf16_long_prompt_sampled(rtp):
     """A 9000-token bf16 prompt (its kernel stages 64 keys per barrier, fp16 128)."""
     L = 9000
