@@ -1095,11 +1095,24 @@ int chunk_tokens(int B, int Hret, int Lmax) {
   const int64_t units = (int64_t)B * (Hret > 0 ? Hret : 1);
   return units * ((Lmax + 2047) / 2048) >= 256 ? 2048 : 1024;
 }
-int window_rows(int B, int Hloc, int ring) {
-  // rows per window block: one step per wavefront unless that makes more than 256
-  // window blocks; then up to 16 steps per wavefront
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  return n;
+}
+// window blocks the stage-B grid can hold beside the selection blocks (4096 tokens each)
+// at two blocks per CU, and at least 256
+int64_t window_budget(int B, int Hret, int Lmax, int ncu) {
+  const int64_t nsel = (int64_t)B * Hret * ((Lmax + 4095) / 4096);
+  return std::max<int64_t>(256, 2 * (int64_t)ncu - nsel);
+}
+int window_rows(int B, int Hloc, int ring, int64_t budget) {
+  // rows per window block: one step per wavefront unless that makes more window blocks
+  // than the budget; then up to 16 steps per wavefront
   int wr = kBWaves * kStep;
-  while (wr < 16 * kBWaves * kStep && (int64_t)B * Hloc * ((ring + wr - 1) / wr) > 256) wr *= 2;
+  while (wr < 16 * kBWaves * kStep && (int64_t)B * Hloc * ((ring + wr - 1) / wr) > budget) wr *= 2;
   return wr;
 }
 }  // namespace
@@ -1109,12 +1122,12 @@ bool step_fused_supported(int kv_dtype, int G, int Hloc, int window, int sinks, 
   if ((kv_dtype != 1 && kv_dtype != 2) || G > kAttnG) return false;
   if (Hloc > 0) {
     const int ring = window + sinks;
-    const int wr = window_rows(B, Hloc, ring);
+    const int wr = window_rows(B, Hloc, ring, window_budget(B, Hret, Lmax, device_cus()));
     if ((ring + wr - 1) / wr > kMaxParts) return false;
   }
   if (Hret > 0 && ret_window) {
     const int ring = window + sinks;
-    const int wr = window_rows(B, Hret, ring);
+    const int wr = window_rows(B, Hret, ring, 256);
     if ((ring + wr - 1) / wr + (Lmax + 2047) / 2048 > kMaxParts) return false;
   }
   if (Hret > 0 && (Lmax + 4095) / 4096 > kMaxParts) return false;  // stage-M LDS
@@ -1130,21 +1143,15 @@ StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int
   sp.Hloc = Hloc;
   sp.tc = chunk_tokens(B, Hret, Lmax);
   sp.nt = sp.tc / 4;
-  {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    sp.ncu = n;
-  }
+  sp.ncu = device_cus();
   int nwin_blocks = 0;
   if (Hloc > 0) {
-    sp.wrows = window_rows(B, Hloc, window + sinks);
+    sp.wrows = window_rows(B, Hloc, window + sinks, window_budget(B, Hret, Lmax, sp.ncu));
     sp.nws = (window + sinks + sp.wrows - 1) / sp.wrows;
     nwin_blocks = B * Hloc * sp.nws;
   }
   if (Hret > 0 && ret_window) {  // window blocks of the retrieval heads, sized the same way
-    sp.rwrows = window_rows(B, Hret, window + sinks);
+    sp.rwrows = window_rows(B, Hret, window + sinks, 256);
     sp.rwnws = (window + sinks + sp.rwrows - 1) / sp.rwrows;
     nwin_blocks += B * Hret * sp.rwnws;
   }
