@@ -66,3 +66,16 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0 and "one GPU" in r.stderr
     assert not r.stdout.strip()
+
+
+@pytest.mark.parametrize("argv,msg", [
+    (["--context", "4096", "--workload", "c1"], "--context applies to the c3 and c4 workloads"),
+    (["--dense", "--topk", "64"], "--dense is the c4 shape alone"),
+    (["--dense", "--workload", "c2"], "--dense is the c4 shape alone"),
+])
+def test_bench_rejects_options_it_cannot_honour(argv, msg):
+    # checked before any device work: the run ends with the message and no result line
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + argv,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0 and msg in r.stderr
+    assert not r.stdout.strip()
