@@ -696,3 +696,44 @@ def test_round_bf16_ties_and_library_conversion():
                         np.array([0.0, 3e-39, -1e-40, 2.0 ** -126, 1e38])]).astype(np.float32)
     want = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
     assert np.array_equal(oracle.round_bf16(x), want)
+
+
+# ---------------------------------------------------------------------------
+# the set rule at a given (A, b*): the form the GPU parity checker falls back to when
+# the GPU's top cell or threshold bin differs from the oracle's by a tie
+# ---------------------------------------------------------------------------
+GOLD_SWB = os.path.join(os.path.dirname(__file__), "golden", "select_with_bstar.json")
+
+
+def _swb_cases():
+    with open(GOLD_SWB) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("ex", _swb_cases(), ids=lambda e: e["name"])
+def test_select_with_bstar_worked_examples(ex):
+    z = np.array(ex["z"], dtype=np.float32)
+    if "cells" in ex:
+        assert oracle.cells(z).tolist() == ex["cells"]
+    got = oracle.select_with_bstar(z, ex["A"], ex["bstar"])
+    assert got.tolist() == ex["S"]
+    assert got.dtype == np.int32
+
+
+@pytest.mark.parametrize("name,z", LOGITS, ids=[n for n, _ in LOGITS])
+def test_select_with_bstar_reproduces_the_rule(name, z):
+    """At the oracle's own (A, b*), the set must be the C rule's set, for top-p at every p
+    of the sweep and for top-k at several budgets; one bin more or less must give the
+    nested sets that the bins' definition implies."""
+    for p in PS + [1.0]:
+        s = oracle.topp_select(z, p)
+        got = oracle.select_with_bstar(z, s.A, s.bstar)
+        assert np.array_equal(got, s.idx), (name, p)
+        # b* + 1 adds exactly the tokens of bin b* + 1 (the tail bin holds everything further)
+        if s.bstar < 255:
+            up = oracle.select_with_bstar(z, s.A, s.bstar + 1)
+            j = np.minimum(s.A - oracle.cells(z), 255)
+            assert set(up.tolist()) == set(s.idx.tolist()) | set(np.nonzero(j == s.bstar + 1)[0].tolist())
+    for k in (1, 7, 100, 3000):
+        s = oracle.topk_select(z, k)
+        assert np.array_equal(oracle.select_with_bstar(z, s.A, s.bstar), s.idx), (name, k)
