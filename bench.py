@@ -27,6 +27,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+REPEATS = 5  # timed repeats of K steps; the median is the reported time
 
 
 def hip():
@@ -59,43 +60,40 @@ def elapsed_ms(h, a, b):
 
 
 def algorithmic_bytes(rtp, wl, layer, torch, topk=0, ret_window=False):
-    """Realised bytes of one step: the union of the selected sets per retrieval KV head
-    comes from the GPU selection (the same rule the step runs: top-p, or the fixed top-k
-    when topk > 0).  Also returns, per retrieval query head, the share of the indexer
-    softmax mass that its selected set holds (outside any timed region)."""
+    """Realised bytes of one step.  The union of the selected sets per retrieval KV head
+    comes from the sets the step itself attended to (exported by rtp_decode_step, the rule
+    the timed step runs: top-p, or the fixed top-k when topk > 0; with ret_window the sink
+    and window rows are part of them).  Also returns, per retrieval query head, the share of
+    the indexer softmax mass that its selected set holds (outside any timed region)."""
     dev = layer.q.device
     sl = torch.as_tensor(wl.seq_lens, dtype=torch.int32, device=dev)
     e_idx = 4 if wl.dtype == "f32" else 2
     e_kv = e_idx
-    total = 0
     detail = {"kidx": 0, "sparse_kv": 0, "window_kv": 0, "union_tokens": 0, "sel_tokens": [],
               "sel_mass": []}
     G = wl.G
     ret = layer.ret_heads
     if ret:
+        _, _, _, _, sidx, scnt = rtp.rtp_decode_step(
+            layer, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window, wl.sinks, wl.p, wl.bin_width,
+            wl.scale_idx, wl.scale_attn, topk=topk, ret_window=ret_window, want_sets=wl.Lmax)
         qi = torch.stack([layer.q_idx[:, h * G:(h + 1) * G] for h in ret], 1).reshape(
             wl.B, len(ret) * G, wl.r).contiguous()
-        z = rtp.rtp_index_score(qi, layer.k_idx, sl, wl.scale_idx)
-        if topk > 0:
-            sel, cnt, _, _ = rtp.rtp_topk_select(z, sl, topk, wl.bin_width, want_hist=False)
-        else:
-            sel, cnt, _, _ = rtp.rtp_topp_select(z, sl, wl.p, wl.bin_width, want_hist=False)
-        zc, sel, cnt = z.double().cpu(), sel.cpu(), cnt.cpu()
+        z = rtp.rtp_index_score(qi, layer.k_idx, sl, wl.scale_idx).double().cpu()
+        sidx, scnt = sidx.cpu(), scnt.cpu()
         for b in range(wl.B):
             L = int(wl.seq_lens[b])
-            for k in range(len(ret)):
+            for k, kv in enumerate(ret):
                 u = set()
                 for g in range(G):
-                    n = int(cnt[b, k * G + g])
+                    h = kv * G + g
+                    n = int(scnt[b, h])
                     detail["sel_tokens"].append(n)
-                    idx = sel[b, k * G + g, :n].long()
-                    zz = zc[b, k * G + g, :L]
+                    idx = sidx[b, h, :n].long()
+                    zz = z[b, k * G + g, :L]
                     e = torch.exp(zz - zz.max())
                     detail["sel_mass"].append(round(float(e[idx].sum() / e.sum()), 4))
                     u.update(idx.tolist())
-                if ret_window:  # the retrieval head also reads its sinks and window rows
-                    u.update(range(min(wl.sinks, L)))
-                    u.update(range(max(wl.sinks, L - wl.window), L))
                 detail["kidx"] += L * wl.r * e_idx
                 detail["sparse_kv"] += len(u) * 2 * wl.d * e_kv
                 detail["union_tokens"] += len(u)
@@ -106,8 +104,52 @@ def algorithmic_bytes(rtp, wl, layer, torch, topk=0, ret_window=False):
     return total, detail
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_stage_a_c4.json")
+HBM_READ_LIB = os.path.join(ROOT, "head_wise_sparse_rtp_amd", "libhbmread.so")
+
+
+def hbm_read_ceiling(torch, gib=4, reps=8):
+    """Streaming-read ceiling of this GPU's HBM: the hand-written read kernel of
+    libhbmread.so (16-byte loads, 4 or 8 in flight per thread, plain or nontemporal) over a
+    `gib` GiB buffer, the best of a few grid sizes; GB/s."""
+    lib = ctypes.CDLL(HBM_READ_LIB)
+    lib.hbm_read.restype = ctypes.c_int
+    lib.hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                             ctypes.c_int, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    grids = (1024, 2048, 4096, 8192)
+    sink = torch.empty(max(grids) * 256, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(st.cuda_stream)
+    best = (0.0, None)
+    for blocks in grids:
+        for var in range(4):
+            def run():
+                rc = lib.hbm_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                  ctypes.c_void_p(sink.data_ptr()), blocks, var, sp)
+                assert rc == 0, rc
+            run()
+            run()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(reps):
+                run()
+            e1.record(st)
+            e1.synchronize()
+            gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            if gbs > best[0]:
+                best = (gbs, {"blocks": blocks, "loads_in_flight": 4 if var % 2 == 0 else 8,
+                              "nontemporal": var >= 2})
+    del buf, sink
+    torch.cuda.synchronize()
+    return {"value": round(best[0], 1), "unit": "GB/s", "bytes": nbytes,
+            "kernel": "hbm_read (libhbmread.so)", "best_shape": best[1]}
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_step_c4.json")
 KERNEL_SOURCE = os.path.join(ROOT, "head_wise_sparse_rtp_amd", "csrc", "rtp_step.hip")
+TRAFFIC_KERNELS = ("k_stage_a", "k_stage_b")
 
 
 def source_sha256() -> str:
@@ -116,8 +158,8 @@ def source_sha256() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of k_stage_a from the committed counter summary, or None when
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when
     there is none for this workload or the kernel source changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
@@ -126,13 +168,15 @@ def measured_traffic(workload: str):
         return None
     if t.get("workload") != workload or t.get("source_sha256") != source_sha256():
         return None
-    return t.get("bytes_per_launch")
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
 
 
 def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, out):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of k_stage_a and of the calibration copy
-    kernel (a unary elementwise kernel over copy_bytes bytes) from two rocprofv3 --pmc
-    runs; each counter is scaled by copy_bytes / (its reading for the copy)."""
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the step's kernels and of the
+    calibration copy kernel (a unary elementwise kernel over copy_bytes bytes) from two
+    rocprofv3 --pmc runs; each counter is scaled by copy_bytes / (its reading for the
+    copy)."""
     import csv
     import re
 
@@ -146,19 +190,26 @@ def summarize_pmc(fetch_csv, write_csv, workload, copy_bytes, out):
                 agg.setdefault(n, []).append(float(r["Counter_Value"]))
         return agg
 
-    res = {"workload": workload, "source_sha256": source_sha256(), "copy_bytes": copy_bytes}
+    res = {"workload": workload, "source_sha256": source_sha256(), "copy_bytes": copy_bytes,
+           "kernels": {}}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         agg = per_kernel(path, counter)
-        stage = [v for n, vs in agg.items() if "k_stage_a" in n for v in vs]
         copy = [v for n, vs in agg.items() if "neg_kernel" in n for v in vs]
-        if not stage or not copy:
-            raise SystemExit("no %s readings for k_stage_a or the copy kernel in %s" % (counter, path))
+        if not copy:
+            raise SystemExit("no %s readings for the copy kernel in %s" % (counter, path))
         copy_kib = max(copy)  # the large calibration copies (the bench also negates tiny tensors)
         factor = copy_bytes / (copy_kib * 1024.0)
-        kib = sum(stage) / len(stage)
-        res[counter] = {"kib_per_launch": round(kib, 1), "copy_kib": round(copy_kib, 1),
-                        "scale": round(factor, 4), "bytes_per_launch": round(kib * 1024.0 * factor)}
-    res["bytes_per_launch"] = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
+        res.setdefault("scale", {})[counter] = {"copy_kib": round(copy_kib, 1),
+                                                "factor": round(factor, 4)}
+        for kern in TRAFFIC_KERNELS:
+            vals = [v for n, vs in agg.items() if kern in n for v in vs]
+            if not vals:
+                raise SystemExit("no %s readings for %s in %s" % (counter, kern, path))
+            kib = sum(vals) / len(vals)
+            res["kernels"].setdefault(kern, {})[counter] = {
+                "kib_per_launch": round(kib, 1), "bytes_per_launch": round(kib * 1024.0 * factor)}
+    for kern, d in res["kernels"].items():
+        d["bytes_per_launch"] = d["FETCH_SIZE"]["bytes_per_launch"] + d["WRITE_SIZE"]["bytes_per_launch"]
     with open(out, "w") as f:
         json.dump(res, f, indent=1)
         f.write("\n")
@@ -179,20 +230,41 @@ def calibrate_copy(mib: int, reps: int):
 
 
 def cpu_baseline(wl, bytes_per_step, budget_s):
+    """The oracle as it is, timed on this host: its per-head C loops run for every
+    (sequence, query head) of the step, the heads spread over a thread pool (the C calls
+    release the interpreter lock), as many threads as the host gives this process, at most
+    16 (one GPU's share of the box)."""
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     cpu_wl = wl.to("cpu")
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        oracle.decode_step(cpu_wl)
-        n += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = (time.perf_counter() - t0) / n
-    return {"value": round(bytes_per_step / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "s_per_step": round(dt, 4),
-            "sample": "%d full decode step(s) of the same workload (all 32 query heads), "
-                      "single-threaded C oracle, inputs copied to host memory" % n}
+    host = len(os.sched_getaffinity(0))
+    tasks = [(li, b, h) for li in range(len(cpu_wl.layers)) for b in range(cpu_wl.B)
+             for h in range(cpu_wl.Hq)]
+    nthr = max(1, min(16, host, len(tasks)))
+
+    def one(t):
+        li, b, h = t
+        lay = cpu_wl.layers[li]
+        return oracle.decode_layer(lay, cpu_wl.seq_lens, cpu_wl.Hq, cpu_wl.Hkv, cpu_wl.p,
+                                   cpu_wl.bin_width, cpu_wl.scale_idx, cpu_wl.scale_attn,
+                                   cpu_wl.window, cpu_wl.sinks, heads=[h], batches=[b],
+                                   topk=getattr(cpu_wl, "topk", 0),
+                                   ret_window=getattr(cpu_wl, "ret_window", False))
+
+    with ThreadPoolExecutor(nthr) as pool:
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            list(pool.map(one, tasks))
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = (time.perf_counter() - t0) / n
+    return {"value": round(bytes_per_step / dt / 1e9, 4), "unit": "GB/s", "cores": nthr,
+            "host_cores": host, "kind": "oracle", "s_per_step": round(dt, 4),
+            "sample": "%d full decode step(s) of the same workload (all %d query heads), the C "
+                      "oracle per (sequence, query head) on %d threads, inputs copied to host "
+                      "memory" % (n, cpu_wl.Hq, nthr)}
 
 
 PEAK_MFMA_F16_TFLOPS = 2500.0
@@ -307,15 +379,11 @@ def bench_layers(args, wl):
     for st, layer in zip(steps, wl.layers):
         if not layer.ret_heads:
             continue
-        for j in range(4):
-            st.desc.prof_ev[j] = evs[j].value
         torch.cuda._sleep(200000)
-        st()
+        st.profiled([e.value for e in evs])
         torch.cuda.synchronize()
         a_tot += elapsed_ms(h, evs[0], evs[1])
         a_n += 1
-        for j in range(4):
-            st.desc.prof_ev[j] = None
     a_us = a_tot / max(a_n, 1) * 1000.0
     nret = sum(len(l.ret_heads) for l in wl.layers)
     a_bytes = kidx_bytes / max(a_n, 1)
@@ -360,7 +428,8 @@ def main():
     ap.add_argument("--topk", type=int, default=0,
                     help="fixed top-k through the histogram instead of top-p")
     ap.add_argument("--dtype", default="f16", choices=["f16", "bf16"],
-                    help="cache dtype of the single-layer configs (bf16: single-purpose kernels)")
+                    help="cache dtype of the single-layer configs (fp16 or bf16; both run the fused "
+                         "kernels)")
     ap.add_argument("--ret-window", action="store_true",
                     help="retrieval heads also attend to the sinks and the window")
     ap.add_argument("--with-append", action="store_true",
@@ -370,6 +439,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--skip-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling measurement")
     ap.add_argument("--phases", action="store_true", help="print a per-phase breakdown")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (counter calibration)")
@@ -486,48 +557,49 @@ def main():
             g_full.replay()
         torch.cuda.synchronize()
 
-    # ---- timed region: exactly K steps ----
+    # ---- timed region: exactly K steps, repeated REPEATS times; the median is reported ----
     e0, e1 = make_events(h, 2)
-    torch.cuda.synchronize()
-    h.hipEventRecord(e0, ctypes.c_void_p(stream.cuda_stream))
-    if g_full is not None:
-        for _ in range(K // R):
-            g_full.replay()
-        if g_rest is not None:
-            g_rest.replay()
-    else:
-        for i in range(K):
-            step(i % R)
-    h.hipEventRecord(e1, ctypes.c_void_p(stream.cuda_stream))
-    h.hipEventSynchronize(e1)
-    torch.cuda.synchronize()
-    ms_step = elapsed_ms(h, e0, e1) / K
+    rep_ms = []
+    for _ in range(REPEATS):
+        torch.cuda.synchronize()
+        h.hipEventRecord(e0, ctypes.c_void_p(stream.cuda_stream))
+        if g_full is not None:
+            for _ in range(K // R):
+                g_full.replay()
+            if g_rest is not None:
+                g_rest.replay()
+        else:
+            for i in range(K):
+                step(i % R)
+        h.hipEventRecord(e1, ctypes.c_void_p(stream.cuda_stream))
+        h.hipEventSynchronize(e1)
+        torch.cuda.synchronize()
+        rep_ms.append(elapsed_ms(h, e0, e1) / K)
+    ms_step = sorted(rep_ms)[len(rep_ms) // 2]
 
     # ---- per-kernel durations, timed live with HIP events on the launch stream ----
-    # events: [0] and [1] the start and the end of stage A (indexer score + chunk
-    # histograms; the library binds them to that kernel's launch when both are given),
-    # [2] after stage T (suffix tables), [3] after the last kernel (stage B: selection,
-    # sparse and window attention; stage M: merges).  Each profiled step is queued behind
-    # a short busy kernel, so that all of its commands wait in the queue when the GPU
-    # reaches them and the events time the kernels, not the host-side enqueue.
-    names = ("stageA_score_hist", "stageT_suffix_tables", "stageBM_select_attend_merge")
-    ph = {k: 0.0 for k in names}
+    # events [0]/[1] are bound to stage A's execution (indexer score + chunk histograms)
+    # and [2]/[3] to stage B's (selection + sparse and window attention); two more,
+    # recorded on the stream around the call, time the whole eager step.  Each profiled
+    # step is queued behind a short busy kernel, so that all of its commands wait in the
+    # queue when the GPU reaches them and the events time the kernels, not the host-side
+    # enqueue.
+    ph = {"stageA_score_hist": 0.0, "stageB_select_attend": 0.0, "eager_step": 0.0}
     has_ret = bool(layer.ret_heads)
     evs = make_events(h, 4, HIP_EVENT_TIMING_NO_FENCE)
+    ew = make_events(h, 2, HIP_EVENT_TIMING_NO_FENCE)
     torch.cuda.synchronize()
     for k in range(K):
         st = steps[k % R]
-        for j in range(4):
-            st.desc.prof_ev[j] = evs[j].value
         torch.cuda._sleep(200000)  # a spinning kernel (tens of us, touches no memory)
-        st()
+        h.hipEventRecord(ew[0], ctypes.c_void_p(stream.cuda_stream))
+        st.profiled([e.value for e in evs])
+        h.hipEventRecord(ew[1], ctypes.c_void_p(stream.cuda_stream))
         torch.cuda.synchronize()
         if has_ret:
-            ph[names[0]] += elapsed_ms(h, evs[0], evs[1])
-            ph[names[1]] += elapsed_ms(h, evs[1], evs[2])
-        ph[names[2]] += elapsed_ms(h, evs[2], evs[3])
-        for j in range(4):
-            st.desc.prof_ev[j] = None
+            ph["stageA_score_hist"] += elapsed_ms(h, evs[0], evs[1])
+        ph["stageB_select_attend"] += elapsed_ms(h, evs[2], evs[3])
+        ph["eager_step"] += elapsed_ms(h, ew[0], ew[1])
     ph = {k: v / K * 1000.0 for k, v in ph.items()}  # microseconds
     if apps:
         # the cache update alone, timed the same way
@@ -540,14 +612,30 @@ def main():
             torch.cuda.synchronize()
             tot += elapsed_ms(h, evs[0], evs[1])
         ph["append_project"] = tot / K * 1000.0
-    if has_ret:
-        a_us = ph["stageA_score_hist"]
-        a_bytes = detail["kidx"]
-    else:  # window attention only: stage B's window blocks (and the merge) are the step
-        a_us = ph["stageBM_select_attend_merge"]
-        a_bytes = detail["window_kv"]
-    achieved = a_bytes / (a_us * 1e-6) / 1e9 if a_us > 0 else 0.0
 
+    def roofline(kernel, desc, us, nbytes):
+        gbs = nbytes / (us * 1e-6) / 1e9 if us > 0 else 0.0
+        wl_key = args.workload if not (args.topk or args.context or args.dtype != "f16"
+                                       or args.ret_window or apps) else None
+        return {"kernel": "%s (%s)" % (kernel, desc), "bound": "hbm", "achieved": round(gbs, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                # the counters were taken on the fp16 top-p step of the workload at its own
+                # length
+                "traffic": measured_traffic(wl_key, kernel) if wl_key else None,
+                "avg_us": round(us, 3), "algorithmic_bytes_per_launch": nbytes}
+
+    kern = {}
+    if has_ret:
+        kern["k_stage_a"] = roofline("k_stage_a", "indexer score on MFMA + 256-bin chunk "
+                                     "histograms; algorithmic bytes: the indexer keys",
+                                     ph["stageA_score_hist"], detail["kidx"])
+    kern["k_stage_b"] = roofline("k_stage_b", "selection + sparse attention + window attention; "
+                                 "algorithmic bytes: the selected and the window K/V rows",
+                                 ph["stageB_select_attend"],
+                                 detail["sparse_kv"] + detail["window_kv"])
+    dominant = max(kern, key=lambda k: kern[k]["avg_us"])
+
+    ceiling = hbm_read_ceiling(torch) if not args.skip_ceiling else None
     value = bytes_step / (ms_step * 1e-3) / 1e9
     res = {
         "metric": "decode attention us/step and achieved HBM GB/s (% of peak) at 1M context",
@@ -558,6 +646,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "us_per_step": round(ms_step * 1000.0, 2),
+        "repeats": REPEATS,
+        "repeat_us_per_step": [round(x * 1000.0, 3) for x in rep_ms],
         "pct_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
@@ -576,19 +666,13 @@ def main():
         "bytes_detail": {k: v for k, v in detail.items() if k not in ("sel_tokens", "sel_mass")},
         "sel_tokens_per_head": detail["sel_tokens"],
         "sel_mass_per_head": detail["sel_mass"],
-        "roofline": {"kernel": ("k_stage_a (indexer score on MFMA + 256-bin chunk histograms)"
-                                if has_ret else
-                                "k_stage_b window blocks (MFMA attention) + k_stage_m merge"),
-                     "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     # the counters were taken on the fp16 top-p step at the workload's own
-                     # length
-                     "traffic": (measured_traffic(args.workload)
-                                 if not (args.topk or args.context or args.dtype != "f16")
-                                 else None),
-                     "avg_us": round(a_us, 3), "algorithmic_bytes_per_launch": a_bytes},
+        "roofline": kern[dominant],
+        "kernels": kern,
         "phases_us": {k: round(v, 3) for k, v in ph.items()},
     }
+    if ceiling is not None:
+        res["hbm_read_ceiling"] = ceiling
+        res["pct_of_read_ceiling"] = round(100.0 * value / ceiling["value"], 2)
     if not args.skip_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, bytes_step, args.cpu_seconds)
     print(json.dumps(res), flush=True)

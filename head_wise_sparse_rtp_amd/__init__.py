@@ -37,7 +37,8 @@ EXPORTED = [
     "rtp_topk_select_workspace_size", "rtp_topk_select",
     "rtp_sparse_decode_workspace_size", "rtp_sparse_decode",
     "rtp_window_decode_workspace_size", "rtp_window_decode",
-    "rtp_decode_step_workspace_size", "rtp_decode_step", "rtp_append_project", "rtp_prefill",
+    "rtp_decode_step_workspace_size", "rtp_decode_step", "rtp_decode_step_profiled",
+    "rtp_append_project", "rtp_prefill",
 ]
 
 _lib = None
@@ -58,8 +59,8 @@ class LayerDesc(ctypes.Structure):
         ("k_idx", P), ("K_loc", P), ("V_loc", P), ("seq_lens", P),
         ("p", F64), ("bin_width", F32), ("scale_idx", F32), ("scale_attn", F32),
         ("out", P), ("lse", P), ("thresh_out", P), ("count_out", P),
-        ("prof_ev", P * 8),
         ("topk", I32), ("ret_window", I32),
+        ("sel_idx", P), ("sel_count", P), ("sel_cap", I32),
     ]
 
 
@@ -127,6 +128,8 @@ def lib():
         L.rtp_decode_step_workspace_size.argtypes = [ctypes.POINTER(LayerDesc)]
         L.rtp_decode_step.restype = I32
         L.rtp_decode_step.argtypes = [ctypes.POINTER(LayerDesc), P, SZ, P]
+        L.rtp_decode_step_profiled.restype = I32
+        L.rtp_decode_step_profiled.argtypes = [ctypes.POINTER(LayerDesc), P, SZ, P, P * 4]
         L.rtp_append_project.restype = I32
         L.rtp_append_project.argtypes = [ctypes.POINTER(AppendDesc), P]
         L.rtp_prefill.restype = I32
@@ -275,13 +278,15 @@ def rtp_window_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_len
 # ---------------------------------------------------------------------------
 class DecodeStep:
     """Holds the descriptor, host mask and workspace of one layer so that repeated
-    calls (a decode loop, a captured graph) only enqueue kernels."""
+    calls (a decode loop, a captured graph) only enqueue kernels.  want_sets > 0 also
+    exports the token set each retrieval query head attended to (sel_idx [B, Hq,
+    want_sets] ascending, -1 past the set; sel_count [B, Hq])."""
 
     def __init__(self, layer, seq_lens: torch.Tensor, B: int, Hq: int, Hkv: int, Lmax: int,
                  window: int, sinks: int, p: float, bin_width: float, scale_idx: float,
                  scale_attn: float, out: Optional[torch.Tensor] = None, want_lse: bool = True,
                  want_debug: bool = False, ws: Optional[torch.Tensor] = None, topk: int = 0,
-                 ret_window: bool = False):
+                 ret_window: bool = False, want_sets: int = 0):
         dev = layer.q.device
         self.keep = [layer.q, layer.q_idx, layer.K_ret, layer.V_ret, layer.k_idx, layer.K_loc,
                      layer.V_loc, seq_lens]
@@ -293,6 +298,10 @@ class DecodeStep:
         self.thresh = (torch.zeros((B, Hq, 2), dtype=torch.int32, device=dev)
                        if want_debug else None)
         self.count = torch.zeros((B, Hq), dtype=torch.int32, device=dev) if want_debug else None
+        self.sel_idx = self.sel_count = None
+        if want_sets:
+            self.sel_idx = torch.full((B, Hq, int(want_sets)), -1, dtype=torch.int32, device=dev)
+            self.sel_count = torch.full((B, Hq), -1, dtype=torch.int32, device=dev)
         nret = int(sum(int(x) for x in layer.kv_is_retrieval))
         nloc = Hkv - nret
 
@@ -309,6 +318,9 @@ class DecodeStep:
             _ptr(self.thresh), _ptr(self.count))
         self.desc.topk = int(topk)
         self.desc.ret_window = 1 if ret_window else 0
+        self.desc.sel_idx = _ptr(self.sel_idx)
+        self.desc.sel_count = _ptr(self.sel_count)
+        self.desc.sel_cap = int(want_sets)
         nb = lib().rtp_decode_step_workspace_size(ctypes.byref(self.desc))
         if nb == 0:
             raise RtpError(RTP_EINVAL)
@@ -320,14 +332,27 @@ class DecodeStep:
                                      _stream(stream)))
         return self.out
 
+    def profiled(self, events, stream=None):
+        """One call with kernel timing events (hipEvent_t handles as ints or None, four of
+        them; see rtp_decode_step_profiled)."""
+        ev = (P * 4)(*[e for e in events])
+        _check(lib().rtp_decode_step_profiled(ctypes.byref(self.desc), _ptr(self.ws),
+                                              self.ws.numel(), _stream(stream), ev))
+        return self.out
+
 
 def rtp_decode_step(layer, seq_lens, B, Hq, Hkv, Lmax, window, sinks, p, bin_width, scale_idx,
-                    scale_attn, want_debug=False, stream=None, topk=0, ret_window=False):
-    """One layer's decode step; returns (out, lse, thresh, count).  topk > 0 selects the
-    retrieval heads' tokens with the fixed top-k rule instead of top-p."""
+                    scale_attn, want_debug=False, stream=None, topk=0, ret_window=False,
+                    want_sets=0):
+    """One layer's decode step; returns (out, lse, thresh, count), followed by (sel_idx,
+    sel_count) when want_sets > 0.  topk > 0 selects the retrieval heads' tokens with the
+    fixed top-k rule instead of top-p."""
     st = DecodeStep(layer, seq_lens, B, Hq, Hkv, Lmax, window, sinks, p, bin_width, scale_idx,
-                    scale_attn, want_debug=want_debug, topk=topk, ret_window=ret_window)
+                    scale_attn, want_debug=want_debug, topk=topk, ret_window=ret_window,
+                    want_sets=want_sets)
     st(stream)
+    if want_sets:
+        return st.out, st.lse, st.thresh, st.count, st.sel_idx, st.sel_count
     return st.out, st.lse, st.thresh, st.count
 
 
@@ -416,13 +441,14 @@ def rtp_prefill(seq_lens, mask, q, K, V, window, sinks, scale_attn, k_pre=None, 
     return pf
 
 
-def decode_workload(wl, want_debug: bool = False, stream=None):
+def decode_workload(wl, want_debug: bool = False, stream=None, want_sets: int = 0):
     """Run every layer of a `workloads.Workload` already on the GPU; returns per-layer
-    (out, lse, thresh, count)."""
+    (out, lse, thresh, count), plus (sel_idx, sel_count) when want_sets > 0."""
     sl = torch.as_tensor(wl.seq_lens, dtype=torch.int32).to(wl.layers[0].q.device)
     res = []
     for layer in wl.layers:
         res.append(rtp_decode_step(layer, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window, wl.sinks,
                                    wl.p, wl.bin_width, wl.scale_idx, wl.scale_attn, want_debug,
-                                   stream, getattr(wl, "topk", 0), getattr(wl, "ret_window", False)))
+                                   stream, getattr(wl, "topk", 0), getattr(wl, "ret_window", False),
+                                   want_sets))
     return res

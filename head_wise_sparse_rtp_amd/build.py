@@ -14,6 +14,9 @@ LIB = os.path.join(HERE, "librtp.so")
 SOURCES = ["rtp_api.hip", "rtp_score.hip", "rtp_select.hip", "rtp_attn.hip", "rtp_step.hip",
            "rtp_append.hip", "rtp_prefill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# the benchmark's streaming-read ceiling (not part of librtp)
+HBM_READ_SRC = "hbm_read.hip"
+HBM_READ_LIB = os.path.join(HERE, "libhbmread.so")
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -25,9 +28,8 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _compile(srcs, out, verbose):
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC] + FLAGS + ["-I", os.path.join(HERE, "..", "include"), "-o", tmp] + srcs
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -36,10 +38,17 @@ def build(verbose: bool = False) -> str:
             if "packed-fp32-ops' is not a recognized feature" not in l]
     if r.returncode != 0:
         sys.stderr.write("\n".join(errs) + "\n")
-        raise RuntimeError("hipcc failed building librtp.so")
+        raise RuntimeError("hipcc failed building %s" % os.path.basename(out))
     if verbose and errs:
         sys.stderr.write("\n".join(errs) + "\n")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Build librtp.so and the benchmark's libhbmread.so; returns librtp.so's path."""
+    _compile([os.path.join(CSRC, s) for s in SOURCES], LIB, verbose)
+    _compile([os.path.join(CSRC, HBM_READ_SRC)], HBM_READ_LIB, verbose)
     return LIB
 
 

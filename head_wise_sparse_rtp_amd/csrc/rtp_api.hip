@@ -22,6 +22,10 @@ bool pow2_width(float w) {
   return m == 0.5f && e >= -9 && e <= 1;  // 2^-10 .. 1
 }
 
+// the attention scale is a softmax temperature: positive and finite (the MFMA tile takes
+// each row maximum on the raw products, which needs a positive scale)
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.0f; }
+
 rtp_status hip_status(hipError_t e) { return e == hipSuccess ? RTP_OK : RTP_EHIP; }
 
 HeadMap identity_map(int n) {
@@ -120,7 +124,7 @@ rtp_status plan_step(const rtp_layer_desc* d, StepPlan& sp) {
     sp.fused = true;
     WsPlanner wp;
     sp.fp = plan_step_fused(wp, d->B, d->Hq, sp.G, d->Lmax, sp.Hret, sp.Hloc, d->window,
-                            d->sinks, d->ret_window != 0);
+                            d->sinks, d->ret_window != 0, d->sel_idx != nullptr);
     sp.bytes = sp.fp.bytes;
     return RTP_OK;
   }
@@ -252,7 +256,7 @@ rtp_status rtp_sparse_decode(const void* q, const void* K, const void* V, int32_
       !ptr_ok(ws))
     return RTP_EINVAL;
   if (cap > 0 && !ptr_ok(sel_idx)) return RTP_EINVAL;
-  if (!opt_ptr_ok(lse) || !std::isfinite(scale_attn)) return RTP_EINVAL;
+  if (!opt_ptr_ok(lse) || !scale_ok(scale_attn)) return RTP_EINVAL;
   const int maxs = sparse_maxs(cap);
   const PartPlan pp = plan_parts(0, (size_t)B * Hr * G, maxs);
   if (ws_bytes < pp.bytes) return RTP_EWORKSPACE;
@@ -281,7 +285,7 @@ rtp_status rtp_window_decode(const void* q, const void* K, const void* V, int32_
   if (d != kD || !dtype_ok(kv_dtype)) return RTP_EUNSUPPORTED;
   if (!ptr_ok(q) || !ptr_ok(K) || !ptr_ok(V) || !ptr_ok(seq_lens) || !ptr_ok(out) || !ptr_ok(ws))
     return RTP_EINVAL;
-  if (!opt_ptr_ok(lse) || !std::isfinite(scale_attn)) return RTP_EINVAL;
+  if (!opt_ptr_ok(lse) || !scale_ok(scale_attn)) return RTP_EINVAL;
   const int maxs = window_maxs(window, sinks);
   const PartPlan pp = plan_parts(0, (size_t)B * Hl * G, maxs);
   if (ws_bytes < pp.bytes) return RTP_EWORKSPACE;
@@ -348,7 +352,7 @@ rtp_status rtp_prefill(const rtp_prefill_desc* d, void* stream) {
   if (G > kMaxG || d->Hkv > kMaxHkv || d->Lmax > (1 << 24)) return RTP_EUNSUPPORTED;
   if (d->r != kR || d->d != kD || (d->kv_dtype != RTP_F16 && d->kv_dtype != RTP_BF16))
     return RTP_EUNSUPPORTED;
-  if (!d->kv_is_retrieval || !std::isfinite(d->scale_attn)) return RTP_EINVAL;
+  if (!d->kv_is_retrieval || !scale_ok(d->scale_attn)) return RTP_EINVAL;
   PrefillArgs a{};
   a.B = d->B;
   a.Hq = d->Hq;
@@ -396,14 +400,19 @@ size_t rtp_decode_step_workspace_size(const rtp_layer_desc* desc) {
   return sp.bytes;
 }
 
-rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+rtp_status decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, void* stream,
+                       void* const* events) {
   StepPlan sp;
   rtp_status s = plan_step(d, sp);
   if (s != RTP_OK) return s;
   if (!ptr_ok(d->q) || !ptr_ok(d->seq_lens) || !ptr_ok(d->out) || !ptr_ok(ws)) return RTP_EINVAL;
   if (!opt_ptr_ok(d->lse) || !opt_ptr_ok(d->thresh_out) || !opt_ptr_ok(d->count_out))
     return RTP_EINVAL;
-  if (!std::isfinite(d->scale_attn) || !std::isfinite(d->scale_idx)) return RTP_EINVAL;
+  if (!scale_ok(d->scale_attn) || !std::isfinite(d->scale_idx)) return RTP_EINVAL;
   if (sp.Hret > 0) {
     if (!ptr_ok(d->q_idx) || !ptr_ok(d->K_ret) || !ptr_ok(d->V_ret) || !ptr_ok(d->k_idx))
       return RTP_EINVAL;
@@ -413,6 +422,9 @@ rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, v
     if (d->topk == 0 && (!(d->p > 0.0) || std::isnan(d->p))) return RTP_EINVAL;
   }
   if (sp.Hloc > 0 && (!ptr_ok(d->K_loc) || !ptr_ok(d->V_loc))) return RTP_EINVAL;
+  if ((d->sel_idx == nullptr) != (d->sel_count == nullptr)) return RTP_EINVAL;
+  if (d->sel_idx && (!ptr_ok(d->sel_idx) || !ptr_ok(d->sel_count) || d->sel_cap < 1))
+    return RTP_EINVAL;
   if (ws_bytes < sp.bytes) return RTP_EWORKSPACE;
 
   hipStream_t st = (hipStream_t)stream;
@@ -448,14 +460,17 @@ rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, v
     a.hist_out = nullptr;
     a.thresh_out = d->thresh_out;
     a.count_out = d->count_out;
-    hipEvent_t ev[4];
-    for (int i = 0; i < 4; i++) ev[i] = (hipEvent_t)d->prof_ev[i];
-    return hip_status(launch_step_fused(sp.fp, w, a, st, ev));
+    a.sel_idx = d->sel_idx;
+    a.sel_count = d->sel_count;
+    a.sel_cap = d->sel_cap;
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    if (events)
+      for (int i = 0; i < 4; i++) ev[i] = (hipEvent_t)events[i];
+    return hip_status(launch_step_fused(sp.fp, w, a, st, events ? ev : nullptr));
   }
   auto mark = [&](int i) {
-    if (e == hipSuccess && d->prof_ev[i]) e = hipEventRecord((hipEvent_t)d->prof_ev[i], st);
+    if (e == hipSuccess && events && events[i]) e = hipEventRecord((hipEvent_t)events[i], st);
   };
-  mark(0);
   if (sp.Hloc > 0) {
     const AttnPartials pa = bind_parts(w, sp.win);
     if (e == hipSuccess)
@@ -471,6 +486,7 @@ rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, v
     const SelectBufs sb = bind_select(w, sp.sel.offs);
     int32_t* sel_idx = reinterpret_cast<int32_t*>(w + sp.sel_idx);
     int32_t* sel_cnt = reinterpret_cast<int32_t*>(w + sp.sel_cnt);
+    mark(0);
     if (e == hipSuccess)
       e = launch_hist_from_kidx(d->q_idx, d->k_idx, d->kv_dtype, d->seq_lens, sp.ret, d->B,
                                 d->Hq, sp.Hret, G, d->Lmax, d->scale_idx, d->bin_width,
@@ -479,22 +495,40 @@ rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, v
     if (e == hipSuccess)
       e = launch_threshold(d->seq_lens, d->B, H, d->Lmax, d->p, d->topk, d->bin_width, sp.sel.cg,
                            sb, nullptr, d->thresh_out, &sp.ret, G, d->Hq, st);
-    mark(2);
     if (e == hipSuccess)
       e = launch_select(d->seq_lens, d->B, H, d->Lmax, sp.sel.cg, sb, sel_idx, sel_cnt, d->Lmax,
                         d->count_out, &sp.ret, G, d->Hq, st, d->ret_window ? d->sinks : 0,
                         d->ret_window ? d->window : 0);
     const AttnPartials pa = bind_parts(w, sp.sparse);
+    mark(2);
     if (e == hipSuccess)
       e = launch_sparse_partial(d->q, d->K_ret, d->V_ret, d->kv_dtype, sel_idx, sel_cnt, d->Lmax,
                                 sp.ret, d->B, d->Hq, sp.Hret, G, d->Lmax, d->scale_attn, pa,
                                 sp.smaxs, st);
+    mark(3);
     if (e == hipSuccess)
       e = launch_merge(pa, sp.smaxs, sel_cnt, d->Lmax, sp.ret, d->B, d->Hq, sp.Hret, G, d->out,
                        d->lse, st);
+    if (e == hipSuccess && d->sel_idx)
+      e = launch_export_sets(sel_idx, sel_cnt, d->Lmax, sp.ret, d->B, d->Hq, sp.Hret, G,
+                             d->sel_idx, d->sel_count, d->sel_cap, st);
   }
-  mark(3);
   return hip_status(e);
 }
+
+}  // namespace
+
+extern "C" {
+
+rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, void* stream) {
+  return decode_step(d, ws, ws_bytes, stream, nullptr);
+}
+
+rtp_status rtp_decode_step_profiled(const rtp_layer_desc* d, void* ws, size_t ws_bytes,
+                                    void* stream, void* const events[4]) {
+  return decode_step(d, ws, ws_bytes, stream, events);
+}
+
+
 
 }  // extern "C"

@@ -114,6 +114,12 @@ hipError_t launch_window_partial(const void* q, const void* K, const void* V, in
                                  int Hl, int G, int window, int sinks, float scale_attn,
                                  const AttnPartials& pa, int maxs, hipStream_t st);
 
+// Copy the selected sets of retrieval rows (row kr*G+g, cap_in entries each) into the
+// per-query-head arrays out_idx [B, Hq, cap_out] / out_count [B, Hq].
+hipError_t launch_export_sets(const int32_t* sel_idx, const int32_t* sel_count, int cap_in,
+                              const HeadMap& map, int B, int Hq, int Hr, int G, int32_t* out_idx,
+                              int32_t* out_count, int cap_out, hipStream_t st);
+
 // Merge split partials into out [B, Hq, d] / lse [B, Hq].  For sparse rows the number of
 // used splits comes from sel_count (ceil(min(count, cap) / kSplit)); otherwise all `maxs`.
 hipError_t launch_merge(const AttnPartials& pa, int maxs, const int32_t* sel_count, int cap,
@@ -194,6 +200,8 @@ struct StepFusedPlan {
   size_t suf, partA, codes, bstar, Aglob, sufq;
   size_t p1m, p1l, p1acc, p1cnt;
   size_t wpm, wpl, wpacc;
+  size_t xlist, xn;  // set export: union lists per slice and their lengths (0: no export)
+  bool exp;
   size_t bytes;
 };
 
@@ -214,14 +222,17 @@ struct StepFusedArgs {
   float* hist_out;
   int32_t* thresh_out;
   int32_t* count_out;
+  int32_t* sel_idx;  // [B, Hq, sel_cap] or null: the exported sets
+  int32_t* sel_count;
+  int sel_cap;
 };
 
 bool step_fused_supported(int kv_dtype, int G, int Hloc, int window, int sinks, int B, int Hret,
                           int Lmax, bool ret_window);
 StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int Hret, int Hloc,
-                              int window, int sinks, bool ret_window);
-// ev (may be null): events recorded before stage A, after stage A, after stage T and
-// after the last kernel
+                              int window, int sinks, bool ret_window, bool export_sets);
+// ev (may be null): events bound to the execution of stage A ([0] start, [1] end) and of
+// stage B ([2] start, [3] end), each pair only when both of its events are given
 hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedArgs& a,
                              hipStream_t st, hipEvent_t* ev);
 

@@ -46,7 +46,8 @@ __device__ double shift_merge(const int32_t* sA, const MT* __restrict__ m, int n
     const int Ai = sA[i];
     if (Ai == kEmptyCell) continue;
     const long long s = (long long)Ag - (long long)Ai;
-    if (w > 0.0 && s > 4096) continue;  // exp(-s w) underflows for every supported w
+    // exp(-s w) is exactly zero in fp64 beyond this: skipping such a partial changes nothing
+    if (w > 0.0 && (double)s * w > 746.0) continue;
     const double f = exp(-(double)s * w);
     const MT* mi = m + (size_t)i * kNB;
     if (j < kNB - 1 && j - s >= 0) acc += (double)mi[j - s] * f;
@@ -270,7 +271,32 @@ __global__ __launch_bounds__(kThreads) void k_select_write(
   }
 }
 
+// Row (b, h) of the retrieval rows (h = kr*G + g): its set, already ascending, into the
+// caller's per-query-head arrays.
+__global__ __launch_bounds__(kThreads) void k_export_sets(
+    const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_count, int cap_in,
+    HeadMap map, int H, int G, int Hq, int32_t* __restrict__ out_idx,
+    int32_t* __restrict__ out_count, int cap_out) {
+  const size_t row = blockIdx.x;
+  const int b = (int)(row / H);
+  const int h = (int)(row % H);
+  const size_t orow = (size_t)b * Hq + (size_t)map.kv[h / G] * G + (h % G);
+  const int n = sel_count[row];
+  const int m = min(min(n, cap_in), cap_out);
+  for (int i = threadIdx.x; i < m; i += kThreads)
+    out_idx[orow * cap_out + i] = sel_idx[row * cap_in + i];
+  if (threadIdx.x == 0) out_count[orow] = n;
+}
+
 }  // namespace
+
+hipError_t launch_export_sets(const int32_t* sel_idx, const int32_t* sel_count, int cap_in,
+                              const HeadMap& map, int B, int Hq, int Hr, int G, int32_t* out_idx,
+                              int32_t* out_count, int cap_out, hipStream_t st) {
+  k_export_sets<<<B * Hr * G, kThreads, 0, st>>>(sel_idx, sel_count, cap_in, map, Hr * G, G, Hq,
+                                                 out_idx, out_count, cap_out);
+  return hipGetLastError();
+}
 
 hipError_t launch_threshold(const int32_t* seq_lens, int B, int H, int Lmax, double p, int topk,
                             float bin_width, const ChunkGeom& cg, const SelectBufs& sb,

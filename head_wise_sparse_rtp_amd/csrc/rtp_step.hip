@@ -1,4 +1,4 @@
-// Decode step for fp16 caches in four launches per layer.
+// Decode step for fp16 and bf16 caches in four launches per layer.
 //
 //   K1 stage A  indexer score and per-chunk 256-bin histograms of every retrieval query
 //               head (chunk-relative bin codes, suffix sums of the bin masses, top cell).
@@ -31,6 +31,7 @@
 #include "rtp_attn_tile.h"
 
 #include <algorithm>
+#include <cmath>
 
 namespace rtp {
 
@@ -545,7 +546,7 @@ struct StageTParams {
   const float* suf;
   const int32_t* partA;
   int nchunk, cpb, nseg;
-  int maxshift;  // chunks more than this many cells below the top add nothing (masses)
+  int maxshift;  // chunks more than this many cells below the top add exactly nothing
   float c_log2;
   unsigned long long* sufq;
   int32_t* Aglob;
@@ -646,6 +647,9 @@ struct StageBParams {
   float* p1acc;
   int32_t* p1cnt;
   int want_count;
+  // export of the attended sets: each slice's union list (part 0) and its length
+  uint32_t* xlist;
+  int32_t* xn;
   int nret_blocks;  // blocks past this index run window attention
   WinParams win;
 };
@@ -864,6 +868,12 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
     }
   }
   __syncthreads();
+  if (P.xlist && part == 0) {  // the list the attention below consumes, for the set export
+    const size_t xs = (size_t)(b * P.Hret + kr) * P.nblk + blk;
+    uint32_t* dst = P.xlist + xs * TB;
+    for (int e = tid; e < U; e += NT) dst[e] = lst[e];
+    if (tid == 0) P.xn[xs] = U;
+  }
 
   // ---- phase 2: masked MFMA attention over the listed rows
   AttnState st;
@@ -1083,6 +1093,99 @@ __global__ __launch_bounds__(kThreads) void k_stage_m(StageMParams P) {
               mlds);
 }
 
+// ---------------------------------------------------------------------------
+// stage X (only when the sets are exported): block (slice, head g, sequence x retrieval
+// KV head) turns the slice's union list into head g's tokens in ascending order, at the
+// offset given by the head's counts in the earlier slices.
+// ---------------------------------------------------------------------------
+struct StageXParams {
+  const int32_t* seq_lens;
+  int Hq, G, Hret, Lmax, nblk, nparts, np_row, tb;
+  HeadMap ret;
+  const uint32_t* xlist;
+  const int32_t* xn;
+  const int32_t* p1cnt;
+  int rw_sinks, rw_window;  // rw_window > 0: the sink and window positions join every set
+  int32_t* sel_idx;
+  int32_t* sel_count;
+  int cap;
+};
+
+__global__ __launch_bounds__(kThreads) void k_stage_x(StageXParams P) {
+  constexpr int kMaxTB = 16 * kThreads;  // 16 token bits per thread
+  __shared__ uint32_t bm[kMaxTB / 32];
+  __shared__ int red[kThreads / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int slice = blockIdx.x;
+  const int g = blockIdx.y;
+  const int u = blockIdx.z;  // b * Hret + kr
+  const int b = u / P.Hret;
+  const int kr = u % P.Hret;
+  const int L = clamp_len(P.seq_lens, b, P.Lmax);
+  const int TB = P.tb;
+  const int tok0 = slice * TB;
+  const bool rw = P.rw_window > 0;
+  const int ns = min(P.rw_sinks, L);
+  const int wstart = max(P.rw_sinks, L - P.rw_window);
+  // window positions below x: |([0, ns) u [wstart, L)) n [0, x)|
+  auto win_below = [&](int x) { return rw ? min(x, ns) + max(0, min(x, L) - wstart) : 0; };
+  // ---- the head's tokens in the earlier slices
+  int off = 0;
+  for (int sl = tid; sl < slice; sl += kThreads)
+    off += P.p1cnt[((size_t)u * P.np_row + (size_t)sl * P.nparts) * P.G + g];
+  for (int o = 32; o > 0; o >>= 1) off += __shfl_xor(off, o, 64);
+  for (int i = tid; i < kMaxTB / 32; i += kThreads) bm[i] = 0u;
+  if (lane == 0) red[wv] = off;
+  __syncthreads();
+  off = red[0] + red[1] + red[2] + red[3] + win_below(tok0);
+  // ---- bitmap of the slice's tokens that carry head g
+  const size_t xs = (size_t)u * P.nblk + slice;
+  const int U = P.xn[xs];
+  const uint32_t* lst = P.xlist + xs * TB;
+  for (int e = tid; e < U; e += kThreads) {
+    const uint32_t v = lst[e];
+    if ((v >> (16 + g)) & 1u) atomicOr(&bm[(v & 0xFFFFu) >> 5], 1u << (v & 31u));
+  }
+  __syncthreads();
+  uint32_t bits = 0u;
+  const int t0 = 16 * tid;
+  if (t0 < TB) {
+    bits = (bm[tid >> 1] >> (16 * (tid & 1))) & 0xFFFFu;
+    if (rw)
+      for (int k = 0; k < 16; k++) {
+        const int n = tok0 + t0 + k;
+        if (n < L && (n < ns || n >= wstart)) bits |= 1u << k;
+      }
+  }
+  // ---- exclusive scan of the per-thread counts, then the ascending write
+  const int c = __popc(bits);
+  int incl = c;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  __syncthreads();
+  if (lane == 63) red[wv] = incl;
+  __syncthreads();
+  int pos = incl - c;
+  int total = 0;
+  for (int k = 0; k < kThreads / 64; k++) {
+    if (k < wv) pos += red[k];
+    total += red[k];
+  }
+  const size_t orow = (size_t)b * P.Hq + (size_t)P.ret.kv[kr] * P.G + g;
+  int idx = off + pos;
+  while (bits) {
+    const int k = __ffs(bits) - 1;
+    bits &= bits - 1u;
+    if (idx < P.cap) P.sel_idx[orow * P.cap + idx] = tok0 + t0 + k;
+    idx++;
+  }
+  if (slice == P.nblk - 1 && tid == 0) P.sel_count[orow] = off + total;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1135,9 +1238,10 @@ bool step_fused_supported(int kv_dtype, int G, int Hloc, int window, int sinks, 
 }
 
 StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int Hret, int Hloc,
-                              int window, int sinks, bool ret_window) {
+                              int window, int sinks, bool ret_window, bool export_sets) {
   (void)Hq;
   StepFusedPlan sp{};
+  sp.exp = export_sets && Hret > 0;
   sp.G = G;
   sp.Hret = Hret;
   sp.Hloc = Hloc;
@@ -1192,6 +1296,10 @@ StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int
     sp.p1l = wp.take<float>(n1);
     sp.p1acc = wp.take<float>(n1 * kD);
     sp.p1cnt = wp.take<int32_t>(n1);
+    if (sp.exp) {
+      sp.xlist = wp.take<uint32_t>((size_t)B * Hret * sp.nblk * sp.tb);
+      sp.xn = wp.take<int32_t>((size_t)B * Hret * sp.nblk);
+    }
   }
   if (Hloc > 0) {
     const size_t nw = (size_t)B * Hloc * sp.nws * G;
@@ -1209,22 +1317,32 @@ static T* at(char* ws, size_t off) {
   return reinterpret_cast<T*>(ws + off);
 }
 
+// Launch of a one-argument kernel; with both events given they are bound to the kernel's
+// own start and end (a profiler's view of its execution, not of its dispatch).
+template <typename PT>
+static hipError_t launch1(void (*fn)(PT), dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                          PT& arg, hipEvent_t e0, hipEvent_t e1) {
+  if (e0 && e1) {
+    void* args[] = {&arg};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(fn), grid, block, args, lds, st, e0,
+                              e1, 0);
+  }
+  fn<<<grid, block, lds, st>>>(arg);
+  return hipGetLastError();
+}
+
 hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedArgs& a,
                              hipStream_t st, hipEvent_t* ev) {
   const int G = sp.G;
   const int B = a.B;
   const int H = sp.Hret * G;
-  auto rec = [&](int i) {
-    if (ev && ev[i]) (void)hipEventRecord(ev[i], st);
-  };
+  // profiling: events 0/1 bound to stage A's execution, 2/3 to stage B's
+  hipEvent_t ea0 = ev ? ev[0] : nullptr, ea1 = ev ? ev[1] : nullptr;
+  hipEvent_t eb0 = ev ? ev[2] : nullptr, eb1 = ev ? ev[3] : nullptr;
   const float scale2 = a.scale_attn * 1.4426950408889634f;
   // top-k weighs every token one: a zero exponent turns the bin masses into counts
   const float c_log2 = a.topk > 0 ? 0.0f : (float)((double)a.bin_width * 1.4426950408889634);
   hipError_t e = hipSuccess;
-  // profiling: events 0 and 1 are bound to the score kernel's own start and end (they then
-  // time that kernel alone, not its dispatch); otherwise recorded around it
-  const bool bind_a = ev && ev[0] && ev[1] && sp.Hret > 0;
-  if (!bind_a) rec(0);
   // ---- K1: indexer score + chunk histograms
   StageAParams P{};
   if (sp.Hret > 0) {
@@ -1253,28 +1371,14 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     const size_t ldsA = sizeof(uint32_t) * cpA * GG * (kNB + kPad) + sizeof(float) * GG * 8 +
                         sizeof(uint32_t) * (sp.nt / 64) * GG * 64;
     const dim3 gA(sp.nchunk, P.ngg, B * sp.Hret);
-#define RTP_STAGE_A(NTV)                                                                    \
-  do {                                                                                      \
-    if (bind_a) {                                                                           \
-      const void* fn = a.kv_dtype == 2 ? reinterpret_cast<const void*>(&k_stage_a<NTV, bf16e>) \
-                                       : reinterpret_cast<const void*>(&k_stage_a<NTV, f16>);   \
-      void* args[] = {&P};                                                                  \
-      e = hipExtLaunchKernel(fn, gA, dim3(NTV), args, ldsA, st, ev[0], ev[1], 0);            \
-    } else if (a.kv_dtype == 2) {                                                           \
-      k_stage_a<NTV, bf16e><<<gA, NTV, ldsA, st>>>(P);                                     \
-    } else {                                                                                \
-      k_stage_a<NTV, f16><<<gA, NTV, ldsA, st>>>(P);                                       \
-    }                                                                                       \
-  } while (0)
     if (sp.nt == 256)
-      RTP_STAGE_A(256);
+      e = a.kv_dtype == 2 ? launch1(&k_stage_a<256, bf16e>, gA, dim3(256), ldsA, st, P, ea0, ea1)
+                          : launch1(&k_stage_a<256, f16>, gA, dim3(256), ldsA, st, P, ea0, ea1);
     else
-      RTP_STAGE_A(512);
-#undef RTP_STAGE_A
-    if (e == hipSuccess) e = hipGetLastError();
+      e = a.kv_dtype == 2 ? launch1(&k_stage_a<512, bf16e>, gA, dim3(512), ldsA, st, P, ea0, ea1)
+                          : launch1(&k_stage_a<512, f16>, gA, dim3(512), ldsA, st, P, ea0, ea1);
     if (e != hipSuccess) return e;
   }
-  if (!bind_a) rec(1);
   // ---- K2: suffix tables
   StageTParams T{};
   if (sp.Hret > 0) {
@@ -1282,7 +1386,11 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     T.partA = P.partA;
     T.nchunk = sp.nchunk;
     T.cpb = sp.tcpb;
-    T.maxshift = a.topk > 0 ? INT_MAX : 4096;
+    // a chunk s cells below the top scales by exp2f(-s c): below 2^-150 that is exactly zero
+    // in fp32, so chunks further down than that are skipped without changing the table
+    // (counts under top-k never decay)
+    T.maxshift = a.topk > 0 ? INT_MAX
+                            : (int)std::min<double>(INT_MAX - 1, std::ceil(150.0 / (double)c_log2) + 1.0);
     T.nseg = sp.tseg;
     T.c_log2 = c_log2;
     T.sufq = P.sufq;
@@ -1299,7 +1407,6 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  rec(2);
   // ---- K3: selection + sparse attention (retrieval) and window attention (local)
   StageBParams Q{};
   Q.seq_lens = a.seq_lens;
@@ -1332,7 +1439,9 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     Q.p1l = at<float>(ws, sp.p1l);
     Q.p1acc = at<float>(ws, sp.p1acc);
     Q.p1cnt = at<int32_t>(ws, sp.p1cnt);
-    Q.want_count = a.count_out != nullptr;
+    Q.want_count = a.count_out != nullptr || sp.exp;
+    Q.xlist = sp.exp ? at<uint32_t>(ws, sp.xlist) : nullptr;
+    Q.xn = sp.exp ? at<int32_t>(ws, sp.xn) : nullptr;
     Q.nret_blocks = B * sp.Hret * sp.nblk * sp.nparts;
     Q.rw_nws = sp.rwnws;
     Q.rw_rows = sp.rwrows;
@@ -1363,27 +1472,18 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
   const size_t ldsB = std::max<size_t>(kBWaves * (32 + 2048) * sizeof(float),
                                        sizeof(uint32_t) * (size_t)(sp.Hret > 0 ? sp.tb : 0));
   const int nB = Q.nret_blocks + nrw_blocks + nwin_blocks;
-#define RTP_STAGE_B(NWDV, GMV)                                      \
-  do {                                                              \
-    if (a.kv_dtype == 2)                                            \
-      k_stage_b<NWDV, GMV, bf16e><<<nB, kBThreads, ldsB, st>>>(Q); \
-    else                                                            \
-      k_stage_b<NWDV, GMV, f16><<<nB, kBThreads, ldsB, st>>>(Q);   \
-  } while (0)
-  if (G <= 8) {
-    if (sp.nwd == 2)
-      RTP_STAGE_B(2, 8);
+  {
+    void (*fb)(StageBParams) = nullptr;
+    const bool bf = a.kv_dtype == 2;
+    if (G <= 8)
+      fb = sp.nwd == 2 ? (bf ? &k_stage_b<2, 8, bf16e> : &k_stage_b<2, 8, f16>)
+                       : (bf ? &k_stage_b<4, 8, bf16e> : &k_stage_b<4, 8, f16>);
     else
-      RTP_STAGE_B(4, 8);
-  } else {
-    if (sp.nwd == 2)
-      RTP_STAGE_B(2, 16);
-    else
-      RTP_STAGE_B(4, 16);
+      fb = sp.nwd == 2 ? (bf ? &k_stage_b<2, 16, bf16e> : &k_stage_b<2, 16, f16>)
+                       : (bf ? &k_stage_b<4, 16, bf16e> : &k_stage_b<4, 16, f16>);
+    e = launch1(fb, dim3(nB), dim3(kBThreads), ldsB, st, Q, eb0, eb1);
+    if (e != hipSuccess) return e;
   }
-#undef RTP_STAGE_B
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   // ---- K4: merges
   StageMParams M{};
   M.G = G;
@@ -1418,7 +1518,29 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
   const size_t ldsM = sizeof(float) * (3 * (size_t)nmax + 8 + kThreads / 8 * kMSlice);
   k_stage_m<<<(M.nret + nwm) * kMSlices, kThreads, ldsM, st>>>(M);
   e = hipGetLastError();
-  rec(3);
+  if (e == hipSuccess && sp.exp) {
+    StageXParams X{};
+    X.seq_lens = a.seq_lens;
+    X.Hq = a.Hq;
+    X.G = G;
+    X.Hret = sp.Hret;
+    X.Lmax = a.Lmax;
+    X.nblk = sp.nblk;
+    X.nparts = sp.nparts;
+    X.np_row = Q.np_row;
+    X.tb = sp.tb;
+    X.ret = a.ret;
+    X.xlist = Q.xlist;
+    X.xn = Q.xn;
+    X.p1cnt = Q.p1cnt;
+    X.rw_sinks = Q.rw_sinks;
+    X.rw_window = Q.rw_window;
+    X.sel_idx = a.sel_idx;
+    X.sel_count = a.sel_count;
+    X.cap = a.sel_cap;
+    k_stage_x<<<dim3(sp.nblk, G, B * sp.Hret), kThreads, 0, st>>>(X);
+    e = hipGetLastError();
+  }
   return e;
 }
 

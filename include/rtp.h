@@ -31,6 +31,9 @@
  *     output are fp32; accumulation is fp32.  Every stored value converts to fp32
  *     exactly; values written in a cache dtype (rtp_append_project, rtp_prefill) are
  *     rounded to nearest, ties to even.
+ *   - Attention scales (scale_attn, the softmax temperature 1/sqrt(d)) must be positive
+ *     and finite; RTP_EINVAL otherwise.
+ *   - Logits must satisfy |z / bin_width| < 2^30, so that their cells fit in int32.
  *   - A sequence with length 0 yields out = 0, lse = -inf, sel_count = 0.
  *   - Results are deterministic: repeated calls on the same inputs are bitwise equal.
  */
@@ -44,7 +47,7 @@
 extern "C" {
 #endif
 
-#define RTP_ABI_VERSION 2
+#define RTP_ABI_VERSION 3
 
 typedef int32_t rtp_status;
 enum {
@@ -180,28 +183,41 @@ typedef struct {
   float* lse;                     /* [B, Hq] fp32 out or NULL */
   int32_t* thresh_out;            /* [B, Hq, 2] {A, b*} for retrieval query heads, or NULL */
   int32_t* count_out;             /* [B, Hq] |S| for retrieval query heads, or NULL */
-  /* Optional profiling: hipEvent_t handles (or NULL) on `stream`.  With retrieval heads and
-   * both [0] and [1] given, [0] and [1] track the start and the end of the indexer-score/
-   * histogram kernel itself (bound to its launch); otherwise [0] is recorded before the
-   * first kernel and [1] after that kernel.  [2] is recorded after the suffix-table
-   * (threshold) kernel, [3] after the last kernel.  [4..7] are reserved and must be NULL. */
-  void* prof_ev[8];
   int32_t topk;                   /* 0: top-p with p; > 0: fixed top-k (rtp_topk_select's rule)
                                    * for every retrieval query head; < 0: RTP_EINVAL */
   int32_t ret_window;             /* 0: retrieval heads attend to their selected set only;
                                    * 1: to that set united with { n < sinks } and
                                    * { n >= L - window } (the local heads' window, in the
                                    * full cache); count_out then counts the union */
+  /* Optional export of the token sets the step attended to, per retrieval query head (the
+   * lists the attention kernels consumed, not a recomputation): sel_idx[b,h,:] holds the
+   * first min(n, sel_cap) indices of the set in ascending order and sel_count[b,h] = n.  The
+   * set is S_h (top-p or top-k), united with the sink and window positions when
+   * ret_window = 1.  Rows of local query heads are left as they are.  NULL (both) skips the
+   * export; the workspace query accounts for it, so query the size with the pointers set. */
+  int32_t* sel_idx;               /* [B, Hq, sel_cap] int32 out, or NULL */
+  int32_t* sel_count;             /* [B, Hq] int32 out, or NULL (NULL exactly when sel_idx is) */
+  int32_t sel_cap;                /* >= 1 when sel_idx is given */
 } rtp_layer_desc;
 
-/* fp16 caches with G <= 16 run four kernels per call: indexer score + chunk histograms;
- * per-head suffix tables of the bin masses (token counts under top-k); selection +
- * sparse attention together with the window attention of local heads; merge of the
- * split partials.  Other shapes (bf16 or fp32 caches, G > 16) run the single-purpose
- * kernels in sequence.  The workspace needs no initialisation; calls that may overlap
- * must not share one. */
+/* fp16 and bf16 caches with G <= 16 run four kernels per call: indexer score + chunk
+ * histograms; per-head suffix tables of the bin masses (token counts under top-k);
+ * selection + sparse attention together with the window attention of local heads; merge of
+ * the split partials (plus a fifth that writes the exported sets, when asked for).  Other
+ * shapes (fp32 caches, G > 16) run the single-purpose kernels in sequence.  The workspace
+ * needs no initialisation; calls that may overlap must not share one. */
 size_t rtp_decode_step_workspace_size(const rtp_layer_desc* desc);
 rtp_status rtp_decode_step(const rtp_layer_desc* desc, void* ws, size_t ws_bytes, void* stream);
+
+/* rtp_decode_step with kernel timing for a profiler: events[0..3] are hipEvent_t handles
+ * (each may be NULL) created on the calling process's device.  On the four-kernel path,
+ * events[0] and [1] (when both are given) are bound to the start and the end of the
+ * indexer-score / histogram kernel's own execution, and events[2] and [3] to those of the
+ * selection + attention kernel (not to their dispatch).  The single-purpose path records
+ * [0] and [1] on `stream` around its histogram kernel and [2] and [3] around its sparse
+ * attention kernel.  Everything else is rtp_decode_step's. */
+rtp_status rtp_decode_step_profiled(const rtp_layer_desc* desc, void* ws, size_t ws_bytes,
+                                    void* stream, void* const events[4]);
 
 /*
  * Cache update of one decode step, before rtp_decode_step (section 三, 核心公式: the

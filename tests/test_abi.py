@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.rtp_abi_version() == 2
+    assert lib.rtp_abi_version() == 3
     for code in [0, -1, -2, -3, -4]:
         assert lib.rtp_status_string(code).startswith(b"RTP_")
     assert lib.rtp_status_string(7) == b"unknown rtp_status"
@@ -177,6 +177,10 @@ def test_prefill_validation(lib):
     d.window = 8192
     d.out = MIS
     assert f() == -1
+    d.out = FAKE
+    for bad in (0.0, -0.088, float("nan")):
+        d.scale_attn = bad
+        assert f() == -1, bad
     assert lib.rtp_prefill(None, None) == -1
 
 
@@ -227,6 +231,12 @@ def test_sparse_and_window_validation(lib):
     assert g(*a) == -3
     a = list(okw); a[1] = MIS
     assert g(*a) == -1
+    # the attention scale is a softmax temperature: positive and finite
+    for bad in (0.0, -0.088, float("nan"), float("inf")):
+        a = list(ok); a[12] = bad
+        assert f(*a) == -1, bad
+        a = list(okw); a[11] = bad
+        assert g(*a) == -1, bad
 
 
 def test_decode_step_validation(lib):
@@ -258,3 +268,35 @@ def test_decode_step_validation(lib):
     d.p = 0.9
     d.k_idx = None
     assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nb, None) == -1
+    d.k_idx = FAKE
+    # a negative or zero attention scale would turn the MFMA tile's row maxima into minima
+    for bad in (0.0, -0.088, float("nan")):
+        d.scale_attn = bad
+        assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nb, None) == -1, bad
+    d.scale_attn = 0.088
+
+
+def test_decode_step_set_export_and_profiled_validation(lib):
+    import head_wise_sparse_rtp_amd as m
+    mask = (ctypes.c_uint8 * 4)(1, 0, 0, 0)
+    d = m.LayerDesc(1, 32, 4, 128, 16, 65536, 8192, 4, 1, ctypes.cast(mask, ctypes.c_void_p),
+                    FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.9, 0.125, 0.25, 0.088,
+                    FAKE, None, None, None)
+    nb = lib.rtp_decode_step_workspace_size(ctypes.byref(d))
+    d.sel_idx, d.sel_count, d.sel_cap = FAKE, FAKE, 4096
+    nbx = lib.rtp_decode_step_workspace_size(ctypes.byref(d))
+    assert nbx > nb                      # the exported lists need room of their own
+    assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nbx - 1, None) == -3
+    d.sel_count = None                   # one without the other
+    assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nbx, None) == -1
+    d.sel_count = MIS
+    assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nbx, None) == -1
+    d.sel_count = FAKE
+    d.sel_cap = 0
+    assert lib.rtp_decode_step(ctypes.byref(d), FAKE, nbx, None) == -1
+    # the profiled call validates exactly like the plain one (nothing is enqueued)
+    ev = (ctypes.c_void_p * 4)()
+    assert lib.rtp_decode_step_profiled(ctypes.byref(d), FAKE, nbx, None, ev) == -1
+    d.sel_cap = 4096
+    assert lib.rtp_decode_step_profiled(ctypes.byref(d), FAKE, nbx - 1, None, ev) == -3
+    assert lib.rtp_decode_step_profiled(None, FAKE, nbx, None, ev) == -1

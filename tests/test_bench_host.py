@@ -37,25 +37,34 @@ def _pmc_csv(path, counter, rows):
 
 def test_summarize_pmc_scales_by_the_copy(tmp_path):
     # FETCH_SIZE reads half of the copy's 1 MiB (scale 2), WRITE_SIZE all of it (scale 1);
-    # the stage-A mean is taken over its dispatches, the largest copy is the calibration
-    name = "void rtp::(anonymous namespace)::k_stage_a<512, _Float16>(rtp::StageAParams)"
+    # each kernel's mean is taken over its dispatches, the largest copy is the calibration
+    a = "void rtp::(anonymous namespace)::k_stage_a<512, _Float16>(rtp::StageAParams)"
+    b = "void rtp::(anonymous namespace)::k_stage_b<2, 8, _Float16>(rtp::StageBParams)"
     copy = "void at::native::vectorized_elementwise_kernel<neg_kernel>(int)"
     f, w, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "t.json"
-    _pmc_csv(f, "FETCH_SIZE", [(name, 100.0), (name, 300.0), (copy, 512.0), (copy, 2.0)])
-    _pmc_csv(w, "WRITE_SIZE", [(name, 50.0), (name, 50.0), (copy, 1024.0)])
+    _pmc_csv(f, "FETCH_SIZE", [(a, 100.0), (a, 300.0), (b, 40.0), (copy, 512.0), (copy, 2.0)])
+    _pmc_csv(w, "WRITE_SIZE", [(a, 50.0), (a, 50.0), (b, 4.0), (copy, 1024.0)])
     bench.summarize_pmc(str(f), str(w), "c4", 2 ** 20, str(out))
     res = json.loads(out.read_text())
-    assert res["FETCH_SIZE"]["scale"] == 2.0 and res["WRITE_SIZE"]["scale"] == 1.0
-    assert res["FETCH_SIZE"]["bytes_per_launch"] == 200 * 1024 * 2
-    assert res["WRITE_SIZE"]["bytes_per_launch"] == 50 * 1024
-    assert res["bytes_per_launch"] == 200 * 1024 * 2 + 50 * 1024
+    assert res["scale"]["FETCH_SIZE"]["factor"] == 2.0 and res["scale"]["WRITE_SIZE"]["factor"] == 1.0
+    ka, kb = res["kernels"]["k_stage_a"], res["kernels"]["k_stage_b"]
+    assert ka["FETCH_SIZE"]["bytes_per_launch"] == 200 * 1024 * 2
+    assert ka["WRITE_SIZE"]["bytes_per_launch"] == 50 * 1024
+    assert ka["bytes_per_launch"] == 200 * 1024 * 2 + 50 * 1024
+    assert kb["bytes_per_launch"] == 40 * 1024 * 2 + 4 * 1024
     assert res["source_sha256"] == bench.source_sha256()
 
 
-def test_summarize_pmc_needs_both_kernels(tmp_path):
+def test_summarize_pmc_needs_the_copy_and_every_kernel(tmp_path):
     f, w, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "t.json"
-    _pmc_csv(f, "FETCH_SIZE", [("k_stage_a", 1.0)])  # no copy kernel
-    _pmc_csv(w, "WRITE_SIZE", [("k_stage_a", 1.0)])
+    _pmc_csv(f, "FETCH_SIZE", [("k_stage_a", 1.0), ("k_stage_b", 1.0)])  # no copy kernel
+    _pmc_csv(w, "WRITE_SIZE", [("k_stage_a", 1.0), ("k_stage_b", 1.0)])
+    with pytest.raises(SystemExit):
+        bench.summarize_pmc(str(f), str(w), "c4", 2 ** 20, str(out))
+    assert not out.exists()
+    copy = "vectorized_elementwise_kernel<neg_kernel>"
+    _pmc_csv(f, "FETCH_SIZE", [("k_stage_a", 1.0), (copy, 8.0)])       # no stage-B reading
+    _pmc_csv(w, "WRITE_SIZE", [("k_stage_a", 1.0), (copy, 8.0)])
     with pytest.raises(SystemExit):
         bench.summarize_pmc(str(f), str(w), "c4", 2 ** 20, str(out))
     assert not out.exists()

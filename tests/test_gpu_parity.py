@@ -119,6 +119,53 @@ def test_topp_select_matches_oracle(rtp, p, lens):
     say("mass ties", st.mass_ties, "edge tokens", st.edge_tokens)
 
 
+@pytest.mark.parametrize("p", [0.5, 0.9, 0.999])
+def test_topp_select_smallest_bin_width(rtp, p):
+    """w = 2^-10, the smallest accepted width: 256 bins then span a quarter of a nat, so
+    chunks far below the top cell in cells still weigh in (one token at 0 and 8191 at -4.5
+    put almost all the mass in the tail bin: b* = 255)."""
+    w = 2.0 ** -10
+    say("topp_select w=2^-10", p)
+    rows = []
+    z = np.full(8192, -4.5, dtype=np.float32)
+    z[3000] = 0.0
+    rows.append(z)
+    rng = np.random.default_rng(17)
+    rows.append((0.3 * rng.standard_normal(8192)).astype(np.float32))
+    z = (rng.standard_normal(8192) - 3).astype(np.float32)
+    z[rng.choice(8192, 40, replace=False)] = 0.1 * rng.standard_normal(40).astype(np.float32)
+    rows.append(z)
+    zr = np.stack(rows)
+    H, Lmax = zr.shape
+    zt = torch.from_numpy(zr).view(H, 1, Lmax).to(dev())
+    sl = torch.tensor([Lmax] * H, dtype=torch.int32, device=dev())
+    sel_idx, cnt, hist, thr = rtp.rtp_topp_select(zt, sl, p, bin_width=w)
+    sel_idx, cnt, hist, thr = (t.cpu().numpy() for t in (sel_idx, cnt, hist, thr))
+    st = SelCheck()
+    for i in range(H):
+        so = oracle.topp_select(zr[i], p, bin_width=w)
+        where = "row %d p=%g w=2^-10" % (i, p)
+        ex = expected_set(zr[i], so, int(thr[i, 0, 0]), int(thr[i, 0, 1]), p, w, st, where)
+        n = int(cnt[i, 0])
+        compare_sets(sel_idx[i, 0, :n], ex, zr[i], w, st, where)
+        Z = so.hist.sum()
+        assert np.max(np.abs(hist[i, 0] - so.hist)) <= 2e-6 * Z, where
+    # the first row is the case a fixed cutoff of 4096 cells would get wrong
+    assert oracle.topp_select(zr[0], 0.9, bin_width=w).bstar == 255
+
+
+@pytest.mark.parametrize("p", [0.5, 0.9])
+def test_decode_step_smallest_bin_width(rtp, p):
+    """The fused step (f16) and the single-purpose kernels (f32) at w = 2^-10, with
+    sequences long enough that chunk top cells lie thousands of cells below the head's."""
+    say("decode_step w=2^-10", p)
+    for dtype in ("f16", "f32"):
+        wl = workloads.make_workload("t", 2, [20000, 5000], 32, 4, [[1, 0, 1, 0]], seed=67, p=p,
+                                     dtype=dtype, window=256, sinks=4, device=dev(),
+                                     bin_width=2.0 ** -10)
+        check_decode(rtp, wl, label="w2^-10-%s-p%g" % (dtype, p))
+
+
 @pytest.mark.parametrize("k", [1, 3, 100, 4096, 100000])
 @pytest.mark.parametrize("lens", [[9000, 1, 2, 4097, 2048, 12345, 3, 777], [70000, 70000]])
 def test_topk_select_bit_exact(rtp, k, lens):
@@ -241,15 +288,26 @@ def test_window_decode_matches_oracle(rtp, dtype, window, sinks, lens):
 # ---------------------------------------------------------------------------
 # rtp_decode_step
 # ---------------------------------------------------------------------------
-def check_decode(rtp, wl, local_sample=None, layers=None, label="", oracle_layers=None):
+# Beside the 2e-3 / 1e-5 bar of the outputs, the measured error of a correct step is far
+# smaller (about 1e-7 with fp16 K/V): one token wrongly kept or dropped in a set of a few
+# thousand moves an output by about 1e-4, so the tighter diagnostic bound below catches
+# it even where the exported sets could not.
+DIAG_TOL = {"f16": 1e-4, "bf16": 1e-4, "f32": 1e-5}
+
+
+def check_decode(rtp, wl, local_sample=None, layers=None, label="", oracle_layers=None,
+                 sets=True):
     """Run every layer on the GPU and compare with the oracle (all retrieval heads; all
     local heads or the first `local_sample` of each layer).  `oracle_layers`, when given,
-    are the oracle's own copies of the layers (after its own cache update)."""
-    res = rtp.decode_workload(wl, want_debug=True)
+    are the oracle's own copies of the layers (after its own cache update).  With `sets`
+    the step also exports the token set each retrieval query head attended to, and every
+    set is compared with the oracle's element by element (up to edge-band tokens)."""
+    res = rtp.decode_workload(wl, want_debug=True, want_sets=wl.Lmax if sets else 0)
     torch.cuda.synchronize()
     st = SelCheck()
     tol = out_tol(wl.dtype)
     worst = 0.0
+    nsets = 0
     for li, layer in enumerate(wl.layers):
         if layers is not None and li not in layers:
             continue
@@ -257,11 +315,15 @@ def check_decode(rtp, wl, local_sample=None, layers=None, label="", oracle_layer
             say(label, "layer", li)
         if oracle_layers is not None:
             layer = oracle_layers[li]
-        out, lse, thr, cnt = (t.cpu().numpy() for t in res[li])
+        out, lse, thr, cnt = (t.cpu().numpy() for t in res[li][:4])
+        ret_q = [kh * wl.G + g for kh in layer.ret_heads for g in range(wl.G)]
+        sidx = scnt = None
+        if sets and ret_q:
+            sidx = res[li][4][:, ret_q].cpu().numpy()   # retrieval rows only
+            scnt = res[li][5].cpu().numpy()
         heads = None
         if local_sample is not None:
             loc_q = [kh * wl.G + g for kh in layer.loc_heads for g in range(wl.G)][:local_sample]
-            ret_q = [kh * wl.G + g for kh in layer.ret_heads for g in range(wl.G)]
             heads = ret_q + loc_q
         orc = oracle.decode_layer(layer, wl.seq_lens, wl.Hq, wl.Hkv, wl.p, wl.bin_width,
                                   wl.scale_idx, wl.scale_attn, wl.window, wl.sinks, heads=heads,
@@ -277,6 +339,18 @@ def check_decode(rtp, wl, local_sample=None, layers=None, label="", oracle_layer
                     win = oracle.window_positions(int(wl.seq_lens[b]), wl.window, wl.sinks)
                     ex = np.union1d(ex, win).astype(np.int64)
                 compare_count(int(cnt[b, h]), ex, r.z, wl.bin_width, A, bs, st, where)
+                if sidx is not None:
+                    n = int(scnt[b, h])
+                    assert n == int(cnt[b, h]), "%s: exported %d tokens, counted %d" % (
+                        where, n, int(cnt[b, h]))
+                    got = sidx[b, ret_q.index(h), :n]
+                    assert np.all(np.diff(got) > 0), "%s: exported set not ascending" % where
+                    compare_sets(got, ex, r.z, wl.bin_width, st, where)
+                    nsets += 1
+                    if not np.array_equal(got, ex):
+                        # edge-band tokens differ (allowed): the arithmetic is compared on the
+                        # set the step attended to
+                        ex, same = got, False
                 if not same:
                     kr = layer.ret_heads.index(h // wl.G)
                     o_ref, _ = oracle.attention(oracle.np_of(layer.q)[b, h],
@@ -286,8 +360,10 @@ def check_decode(rtp, wl, local_sample=None, layers=None, label="", oracle_layer
             worst = max(worst, e)
             assert e <= tol, "%s: max |dO| = %g > %g" % (where, e, tol)
             assert abs(lse[b, h] - r.lse) <= 1e-3 * max(1.0, abs(r.lse)), where
-    say(label, "rows", st.rows, "mass ties", st.mass_ties, "edge tokens", st.edge_tokens,
-        "worst |dO|", worst)
+    say(label, "rows", st.rows, "sets compared", nsets, "mass ties", st.mass_ties,
+        "edge tokens", st.edge_tokens, "worst |dO|", worst)
+    assert worst <= DIAG_TOL[wl.dtype], "%s: worst |dO| = %g above the diagnostic bound %g" % (
+        label, worst, DIAG_TOL[wl.dtype])
     return res
 
 
