@@ -28,7 +28,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librtp.so")
 
-RTP_OK, RTP_EINVAL, RTP_EUNSUPPORTED, RTP_EWORKSPACE, RTP_EHIP = 0, -1, -2, -3, -4
+RTP_OK, RTP_EINVAL, RTP_EUNSUPPORTED, RTP_EWORKSPACE, RTP_EHIP, RTP_ESCRATCH = 0, -1, -2, -3, -4, -5
 RTP_F32, RTP_F16, RTP_BF16 = 0, 1, 2
 NBINS = 256
 EXPORTED = [
@@ -38,7 +38,7 @@ EXPORTED = [
     "rtp_sparse_decode_workspace_size", "rtp_sparse_decode",
     "rtp_window_decode_workspace_size", "rtp_window_decode",
     "rtp_decode_step_workspace_size", "rtp_decode_step", "rtp_decode_step_profiled",
-    "rtp_append_project", "rtp_prefill",
+    "rtp_decode_step_noalloc", "rtp_append_project", "rtp_prefill",
 ]
 
 _lib = None
@@ -130,6 +130,8 @@ def lib():
         L.rtp_decode_step.argtypes = [ctypes.POINTER(LayerDesc), P, SZ, P]
         L.rtp_decode_step_profiled.restype = I32
         L.rtp_decode_step_profiled.argtypes = [ctypes.POINTER(LayerDesc), P, SZ, P, P * 4]
+        L.rtp_decode_step_noalloc.restype = I32
+        L.rtp_decode_step_noalloc.argtypes = [ctypes.POINTER(LayerDesc), P]
         L.rtp_append_project.restype = I32
         L.rtp_append_project.argtypes = [ctypes.POINTER(AppendDesc), P]
         L.rtp_prefill.restype = I32
@@ -330,6 +332,12 @@ class DecodeStep:
     def __call__(self, stream=None):
         _check(lib().rtp_decode_step(ctypes.byref(self.desc), _ptr(self.ws), self.ws.numel(),
                                      _stream(stream)))
+        return self.out
+
+    def noalloc(self, stream=None):
+        """The same step on the library's fixed scratch (rtp_decode_step_noalloc): no
+        workspace is used and nothing is allocated."""
+        _check(lib().rtp_decode_step_noalloc(ctypes.byref(self.desc), _stream(stream)))
         return self.out
 
     def profiled(self, events, stream=None):

@@ -160,6 +160,7 @@ const char* rtp_status_string(rtp_status s) {
     case RTP_EUNSUPPORTED: return "RTP_EUNSUPPORTED: unsupported shape or dtype (r must be 16, d 128, G <= 64, Lmax <= 2^24)";
     case RTP_EWORKSPACE: return "RTP_EWORKSPACE: workspace smaller than the size query";
     case RTP_EHIP: return "RTP_EHIP: a HIP kernel launch failed";
+    case RTP_ESCRATCH: return "RTP_ESCRATCH: the step needs more scratch than the library's fixed buffer holds (use rtp_decode_step with a workspace)";
     default: return "unknown rtp_status";
   }
 }
@@ -402,10 +403,10 @@ size_t rtp_decode_step_workspace_size(const rtp_layer_desc* desc) {
 
 }  // extern "C"
 
-namespace {
+namespace rtp {
 
-rtp_status decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, void* stream,
-                       void* const* events) {
+rtp_status decode_step_impl(const rtp_layer_desc* d, void* ws, size_t ws_bytes, void* stream,
+                            void* const* events) {
   StepPlan sp;
   rtp_status s = plan_step(d, sp);
   if (s != RTP_OK) return s;
@@ -516,17 +517,17 @@ rtp_status decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, void*
   return hip_status(e);
 }
 
-}  // namespace
+}  // namespace rtp
 
 extern "C" {
 
 rtp_status rtp_decode_step(const rtp_layer_desc* d, void* ws, size_t ws_bytes, void* stream) {
-  return decode_step(d, ws, ws_bytes, stream, nullptr);
+  return decode_step_impl(d, ws, ws_bytes, stream, nullptr);
 }
 
 rtp_status rtp_decode_step_profiled(const rtp_layer_desc* d, void* ws, size_t ws_bytes,
                                     void* stream, void* const events[4]) {
-  return decode_step(d, ws, ws_bytes, stream, events);
+  return decode_step_impl(d, ws, ws_bytes, stream, events);
 }
 
 

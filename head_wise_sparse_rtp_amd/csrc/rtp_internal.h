@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "../../include/rtp.h"
+
 #include <climits>
 #include <cstddef>
 #include <cstdint>
@@ -235,6 +237,11 @@ StepFusedPlan plan_step_fused(WsPlanner& wp, int B, int Hq, int G, int Lmax, int
 // stage B ([2] start, [3] end), each pair only when both of its events are given
 hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedArgs& a,
                              hipStream_t st, hipEvent_t* ev);
+
+// rtp_decode_step on the workspace ws (validation, planning and launches); events may be
+// null (see rtp_decode_step_profiled)
+rtp_status decode_step_impl(const rtp_layer_desc* d, void* ws, size_t ws_bytes, void* stream,
+                            void* const* events);
 
 size_t plan_select(WsPlanner& wp, int B, int H, int Lmax, const ChunkGeom& cg, size_t offs[7]);
 SelectBufs bind_select(char* ws, const size_t offs[7]);

@@ -55,7 +55,8 @@ enum {
   RTP_EINVAL = -1,        /* null/misaligned pointer, bad size or parameter */
   RTP_EUNSUPPORTED = -2,  /* r != 16, d != 128, G or Lmax out of range, bad dtype */
   RTP_EWORKSPACE = -3,    /* ws_bytes below the size query */
-  RTP_EHIP = -4           /* a HIP launch failed */
+  RTP_EHIP = -4,          /* a HIP launch failed */
+  RTP_ESCRATCH = -5       /* rtp_decode_step_noalloc: the step needs more than its fixed scratch */
 };
 enum { RTP_F32 = 0, RTP_F16 = 1, RTP_BF16 = 2 };
 
@@ -218,6 +219,18 @@ rtp_status rtp_decode_step(const rtp_layer_desc* desc, void* ws, size_t ws_bytes
  * attention kernel.  Everything else is rtp_decode_step's. */
 rtp_status rtp_decode_step_profiled(const rtp_layer_desc* desc, void* ws, size_t ws_bytes,
                                     void* stream, void* const events[4]);
+
+/* rtp_decode_step for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels, on a
+ * fixed scratch array that the library holds on each device it runs on (64 MiB, kept until
+ * the process ends; resolved on the first call on a device) instead of a caller workspace.
+ * The call allocates nothing.  A step whose rtp_decode_step_workspace_size exceeds 64 MiB
+ * returns RTP_ESCRATCH and enqueues nothing (every step with B x (retrieval KV heads) x Lmax
+ * up to 2^21 tokens fits, exported sets included).  All calls on one device share its array,
+ * which keeps the last call's contents (the kernels need no particular contents): calls
+ * that may overlap on one device -- on different streams, or from different threads --
+ * race, and the caller must order them. */
+rtp_status rtp_decode_step_noalloc(const rtp_layer_desc* desc, void* stream);
 
 /*
  * Cache update of one decode step, before rtp_decode_step (section 三, 核心公式: the

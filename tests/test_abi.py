@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.rtp_abi_version() == 3
-    for code in [0, -1, -2, -3, -4]:
+    for code in [0, -1, -2, -3, -4, -5]:
         assert lib.rtp_status_string(code).startswith(b"RTP_")
     assert lib.rtp_status_string(7) == b"unknown rtp_status"
 
@@ -300,3 +300,20 @@ def test_decode_step_set_export_and_profiled_validation(lib):
     d.sel_cap = 4096
     assert lib.rtp_decode_step_profiled(ctypes.byref(d), FAKE, nbx - 1, None, ev) == -3
     assert lib.rtp_decode_step_profiled(None, FAKE, nbx, None, ev) == -1
+
+
+def test_decode_step_noalloc_checks_before_any_device_call(lib):
+    import head_wise_sparse_rtp_amd as m
+    mask = (ctypes.c_uint8 * 4)(1, 0, 0, 0)
+    d = m.LayerDesc(1, 32, 4, 128, 16, 1 << 24, 8192, 4, 1, ctypes.cast(mask, ctypes.c_void_p),
+                    FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.9, 0.125, 0.25, 0.088,
+                    FAKE, None, None, None)
+    # 2^24 tokens need about 209 MiB of workspace: beyond the fixed 64 MiB scratch
+    assert lib.rtp_decode_step_workspace_size(ctypes.byref(d)) > 64 << 20
+    assert lib.rtp_decode_step_noalloc(ctypes.byref(d), None) == -5
+    assert lib.rtp_status_string(-5).startswith(b"RTP_ESCRATCH")
+    # an invalid descriptor is reported as rtp_decode_step reports it
+    d.Lmax = 65536
+    d.Hq = 30
+    assert lib.rtp_decode_step_noalloc(ctypes.byref(d), None) == -1
+    assert lib.rtp_decode_step_noalloc(None, None) == -1
