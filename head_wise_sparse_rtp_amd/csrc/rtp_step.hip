@@ -42,16 +42,16 @@ constexpr int kBWaves = kBThreads / 64;  // wavefronts of a stage-B block
 constexpr int kMaxCPB = 4;               // histogram chunks per selection block (at most)
 constexpr int kMSlice = 32;              // output dims per stage-M block
 constexpr int kMSlices = kD / kMSlice;
-constexpr int kMaxParts = 4096;          // partials merged per head (stage-M LDS)
+constexpr int kMaxParts = 4096;          // partials merged per head (at most)
 
-// Sequence length of batch row b through the scalar cache.  A vector load here would be
-// waited for with the in-order vector-memory counter, i.e. together with every load
-// issued before its first use; the scalar load waits only for itself (and LDS).
+// Sequence length of batch row b through the scalar cache: a load through the constant
+// address space at a uniform index is a scalar load, waited for at its first use with the
+// scalar counter.  A vector load would be waited for with the in-order vector-memory
+// counter, i.e. together with every load issued before it.  (The lengths are not written
+// while a step runs.)
+typedef const __attribute__((address_space(4))) int32_t cint32_t;
 __device__ __forceinline__ int seq_len(const int32_t* seq_lens, int b) {
-  const int32_t* p = seq_lens + b;
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
-  return v;
+  return *((cint32_t*)seq_lens + __builtin_amdgcn_readfirstlane(b));
 }
 
 __device__ __forceinline__ int clamp_len(const int32_t* seq_lens, int b, int Lmax) {
@@ -172,33 +172,36 @@ constexpr int kPad = 1;
 constexpr float kMaskY = -3.0e38f;
 
 struct StageAParams {
-  const int32_t* seq_lens;
-  int B, Hq, G, Lmax;
-  const float* q_idx;
+  // line 0 (read before the first loads): the key and query addresses
   const void* k_idx;  // fp16 or bf16 (the kernel's element type)
-  HeadMap ret;
-  int Hret, nchunk, ngg;
+  const float* q_idx;
+  const int32_t* seq_lens;
+  float* suf;
+  int Lmax, Hret, G, Hq;
+  int nchunk;
   int counts;  // unit weight per token (fixed top-k); c_log2 is then 0
   float yscale, c_log2;
-  double w;
-  float* suf;
+  // line 1
   int32_t* partA;
   uint32_t* codes;
   unsigned long long* sufq;  // zeroed here (rows of the unit, by its chunk-0 block)
+  int B, ngg;
+  double w;
+  HeadMap ret;  // last: indexed by a computed head (a dependent read)
 };
 
 struct WinParams {
   const int32_t* seq_lens;
-  int Hq, G;
   const void* q;  // the kernel's element type, as K_loc and V_loc
   const void* K_loc;
   const void* V_loc;
-  HeadMap loc;
-  int Hloc, window, sinks, nws, wrows;
-  float scale2;
   float* wpm;
   float* wpl;
   float* wpacc;
+  int Hq, G;
+  int Hloc, window, sinks, nws, wrows;
+  float scale2;
+  HeadMap loc;  // last: indexed by a computed head (a dependent read)
 };
 
 // Histogram block: chunk `chunk` (TC = 4*NT tokens) of up to 8 query heads g0.. of
@@ -252,7 +255,8 @@ __device__ __forceinline__ void hist_fetch(const StageAParams& P, const HistUnit
   // issued before the sequence length is read: rows past Lmax re-read the last row, and
   // tokens past the sequence's end are masked in hist_block
   const int nlast = P.Lmax - 1;
-  // q_idx first: its operands are prepared while the keys are in flight
+  // q_idx first: vector loads complete in order, so q_idx, issued ahead of the keys, is
+  // ready when they arrive and its operands are prepared while they are in flight
   const int hh = lane & 7;
   const float4* qp = reinterpret_cast<const float4*>(
       P.q_idx + ((size_t)u.b * P.Hq + (size_t)P.ret.kv[u.kr] * P.G + u.grp * 8 + min(hh, u.nrows - 1)) * kR +
@@ -487,13 +491,21 @@ __device__ __forceinline__ void attend_list(const T* __restrict__ Kb, const T* _
 // window block (local KV head): entries [wsplit*wrows, +wrows) of the window set of
 // sinks followed by the last `window` positions -> one partial per query head
 // ---------------------------------------------------------------------------
+// Window blocks share the launch with the selection blocks, whose first loads (suffix
+// tables, code words) gate their whole chain.  With selection blocks present, a window
+// block first waits about 2 us, so that its bulk K/V traffic lands while the selection
+// blocks work on the VALU instead of ahead of their first loads (it still ends well before
+// them).
 template <typename T>
-__device__ void window_block(const WinParams& P, int wb, float* lds) {
+__device__ void window_block(const WinParams& P, int wb, float* lds, bool delay) {
+  if (delay) __builtin_amdgcn_s_sleep(72);  // 72 x 64 cycles: about 1.9 us at 2.4 GHz
   const int wsplit = wb % P.nws;
   const int kl = (wb / P.nws) % P.Hloc;
   const int b = wb / (P.nws * P.Hloc);
   const int G = P.G;
   const int ring = P.sinks + P.window;
+  v8<T> qop[4];  // in flight while the sequence length is read
+  load_qop(static_cast<const T*>(P.q) + ((size_t)b * P.Hq + (size_t)P.loc.kv[kl] * G) * kD, G, qop);
   int L = seq_len(P.seq_lens, b);
   L = L < 0 ? 0 : L;
   const int ns = min(P.sinks, L);
@@ -501,8 +513,6 @@ __device__ void window_block(const WinParams& P, int wb, float* lds) {
   const int nwin = ns + max(0, L - wstart);
   const T* Kb = static_cast<const T*>(P.K_loc) + ((size_t)b * P.Hloc + kl) * (size_t)ring * kD;
   const T* Vb = static_cast<const T*>(P.V_loc) + ((size_t)b * P.Hloc + kl) * (size_t)ring * kD;
-  v8<T> qop[4];
-  load_qop(static_cast<const T*>(P.q) + ((size_t)b * P.Hq + (size_t)P.loc.kv[kl] * G) * kD, G, qop);
   AttnState st;
   attn_init(st);
   const int elo = wsplit * P.wrows;
@@ -622,36 +632,44 @@ __global__ __launch_bounds__(kThreads) void k_stage_t(StageTParams P) {
 // ---------------------------------------------------------------------------
 // stage B
 // ---------------------------------------------------------------------------
+// Kernel arguments are read through the scalar cache, one 64-byte line per miss: the
+// fields a block needs before its first loads come first, in the first two lines, and the
+// head map (indexed by a computed head, hence a dependent read) comes last.
 struct StageBParams {
-  const int32_t* seq_lens;
-  int B, Hq, G, Lmax, Hret, nchunk, tc, nblk, nparts;
+  // line 0: block kind, slice geometry and the selection inputs
+  const unsigned long long* sufq;
+  const uint32_t* codes;
+  const int32_t* partA;
+  const int32_t* Aglob;
+  int nret_blocks;  // blocks below this index run the selection
+  int nrw_end;      // blocks below this index (and from nret_blocks on) run the retrieval window
+  int nparts, nblk, Hret, G, tc, nchunk;
+  // line 1
   double p;
   int topk;  // > 0: b* from token counts (fixed top-k) instead of masses
+  int want_count;
+  int Lmax, B, Hq;
   // rw_window > 0: every head also attends to n < rw_sinks and n >= L - rw_window; those
   // rows are left out of the selection lists and taken by the retrieval window blocks
   // (rw_nws per KV head, rw_rows rows each), whose partials follow the selection partials
-  int rw_sinks, rw_window, rw_nws, rw_rows;
-  int np_row;  // partials per retrieval KV head: nblk * nparts + rw_nws
+  int rw_window;
+  const int32_t* seq_lens;
   const void* q;  // the kernel's element type, as K_ret and V_ret
   const void* K_ret;
   const void* V_ret;
-  HeadMap ret;
+  int rw_sinks, rw_nws, rw_rows;
+  int np_row;  // partials per retrieval KV head: nblk * nparts + rw_nws
   float scale2;
-  const int32_t* partA;
-  const uint32_t* codes;
-  const unsigned long long* sufq;
-  const int32_t* Aglob;
   int32_t* bstar;
   float* p1m;
   float* p1l;
   float* p1acc;
   int32_t* p1cnt;
-  int want_count;
   // export of the attended sets: each slice's union list (part 0) and its length
   uint32_t* xlist;
   int32_t* xn;
-  int nret_blocks;  // blocks past this index run window attention
   WinParams win;
+  HeadMap ret;
 };
 
 // Selection block over the TB = 1024*NWD tokens [blk*TB, (blk+1)*TB) of retrieval KV
@@ -682,7 +700,6 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
   const int b = blockIdx.x / (P.nparts * P.nblk * P.Hret);
   const int G = P.G;
   const size_t row0 = (size_t)b * P.Hret * G + (size_t)kr * G;
-  const int L = clamp_len(P.seq_lens, b, P.Lmax);
   const int tc = P.tc;
   const int WPC = tc >> 2;     // code words per chunk
   const int cpb = TB / tc;     // chunks per block
@@ -691,9 +708,8 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
   const T* Kb = static_cast<const T*>(P.K_ret) + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kD;
   const T* Vb = static_cast<const T*>(P.V_ret) + ((size_t)b * P.Hret + kr) * (size_t)P.Lmax * kD;
 
-  // ---- phase 0: every input of the selection is in flight at once
-  v8<T> qop[4];
-  load_qop(static_cast<const T*>(P.q) + ((size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G) * kD, G, qop);
+  // ---- phase 0: every input of the selection is in flight at once (the q operand last:
+  // its address needs the head map, a dependent argument read)
   int Ac = kEmptyCell, Ag = kEmptyCell;
   if (tid < cpb * kAttnG) {
     const int cc = tid / kAttnG, g = tid % kAttnG;
@@ -741,7 +757,12 @@ __device__ void select_attend_block(const StageBParams& P, unsigned char* smem) 
       }
     }
   }
+  v8<T> qop[4];  // used by the attention only
+  load_qop(static_cast<const T*>(P.q) + ((size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G) * kD, G, qop);
   if (tid < kAttnG) s_cnt[tid] = 0;
+  // the sequence length only now: its scalar load waits for itself, so the loads above
+  // are already in flight while it does
+  const int L = clamp_len(P.seq_lens, b, P.Lmax);
   // b*: least J < 255 with Z - SUF_{J+1} >= p Z (top-k: >= k tokens), else 255
 #pragma unroll
   for (int u = 0; u < HPW; u++) {
@@ -930,13 +951,13 @@ __device__ void ret_window_block(const StageBParams& P, int wb, float* lds) {
 template <int NWD, int GMAX, typename T>
 __global__ __launch_bounds__(kBThreads, 2) void k_stage_b(StageBParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int nrw = P.rw_window > 0 ? P.B * P.Hret * P.rw_nws : 0;
   if ((int)blockIdx.x < P.nret_blocks)
     select_attend_block<NWD, GMAX, T>(P, smem);
-  else if ((int)blockIdx.x < P.nret_blocks + nrw)
+  else if ((int)blockIdx.x < P.nrw_end)
     ret_window_block<T>(P, blockIdx.x - P.nret_blocks, reinterpret_cast<float*>(smem));
   else
-    window_block<T>(P.win, blockIdx.x - P.nret_blocks - nrw, reinterpret_cast<float*>(smem));
+    window_block<T>(P.win, blockIdx.x - P.nrw_end, reinterpret_cast<float*>(smem),
+                    P.nret_blocks > 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -944,37 +965,89 @@ __global__ __launch_bounds__(kBThreads, 2) void k_stage_b(StageBParams P) {
 // (m, l at [k*G + g], acc at [(k*G + g)*128 + d]) in a fixed order.
 // ---------------------------------------------------------------------------
 struct StageMParams {
+  // line 0: what a block needs to issue its loads
   const float* p1m;
   const float* p1l;
   const float* p1acc;
   const int32_t* p1cnt;
-  const int32_t* Aglob;
-  const int32_t* bstar;
-  int nblk, Hret, G, Hq, nret;
-  HeadMap ret;
+  int nblk, Hret, G, nret, nws, Hloc;
+  // line 1
   const float* wpm;
   const float* wpl;
   const float* wpacc;
-  int nws, Hloc;
-  HeadMap loc;
   float* out;
   float* lse;
   int32_t* count_out;
   int32_t* thresh_out;
+  const int32_t* Aglob;
+  const int32_t* bstar;
+  int Hq;
+  HeadMap ret;  // last: indexed by a computed head (a dependent read)
+  HeadMap loc;
 };
 
-// thread (sub = t/8, dq = t%8): float4 dq of the slice for partials sub, sub+32, ...
+// Merge state of a set of partials: running maximum M (base-2 logits), L = sum of
+// l_k 2^(m_k - M), a = sum of acc_k 2^(m_k - M) over four output dims, C = sum of counts.
+struct MState {
+  float M, L;
+  float4 a;
+  int C;
+};
+
+__device__ __forceinline__ void mstate_fold(MState& s, float m, float l, float4 x) {
+  if (m == -INFINITY) return;  // an empty partial
+  if (m > s.M) {
+    const float f = s.M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s.M - m);
+    s.L *= f;
+    s.a.x *= f;
+    s.a.y *= f;
+    s.a.z *= f;
+    s.a.w *= f;
+    s.M = m;
+  }
+  const float f = __builtin_amdgcn_exp2f(m - s.M);
+  s.L += l * f;
+  s.a.x += x.x * f;
+  s.a.y += x.y * f;
+  s.a.z += x.z * f;
+  s.a.w += x.w * f;
+}
+
+__device__ __forceinline__ MState mstate_merge(const MState& p, const MState& q) {
+  MState r;
+  r.M = fmaxf(p.M, q.M);
+  r.C = p.C + q.C;
+  const float fp = p.M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(p.M - r.M);
+  const float fq = q.M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(q.M - r.M);
+  r.L = p.L * fp + q.L * fq;
+  r.a = make_float4(p.a.x * fp + q.a.x * fq, p.a.y * fp + q.a.y * fq, p.a.z * fp + q.a.z * fq,
+                    p.a.w * fp + q.a.w * fq);
+  return r;
+}
+
+__device__ __forceinline__ MState mstate_shfl_xor(const MState& s, int o) {
+  MState r;
+  r.M = __shfl_xor(s.M, o, 64);
+  r.L = __shfl_xor(s.L, o, 64);
+  r.a = make_float4(__shfl_xor(s.a.x, o, 64), __shfl_xor(s.a.y, o, 64), __shfl_xor(s.a.z, o, 64),
+                    __shfl_xor(s.a.w, o, 64));
+  r.C = __shfl_xor(s.C, o, 64);
+  return r;
+}
+
+// Thread (sub = t/8, dq = t%8) folds partials sub, sub + 32, ... of float4 dq of the slice
+// (each round's loads -- value rows, maxima, sums and counts -- issued together, so n <= 256
+// partials take one memory round trip), then the 32 streams of each dq merge on wave
+// shuffles and across the wavefronts through LDS (lds >= 4 * 8 * 8 floats).
+// The output row (head-map read) is computed by orow_of() once the loads are issued.
+template <class OrowOf>
 __device__ __forceinline__ void merge_slice(const float* __restrict__ pm, const float* __restrict__ pl,
                             const float* __restrict__ pacc, const int32_t* __restrict__ pcnt,
                             int n, int G, int g, int slice, float* __restrict__ out,
-                            float* __restrict__ lse, int32_t* __restrict__ count_out, size_t orow,
-                            float* lds) {
+                            float* __restrict__ lse, int32_t* __restrict__ count_out,
+                            OrowOf orow_of, float* lds) {
   constexpr int NSUB = kThreads / (kMSlice / 4);  // 32
-  float* racc = lds;                                     // [NSUB][32] (16-byte aligned)
-  float* red = racc + NSUB * kMSlice;                    // [8]
-  float* wk = red + 8;                                   // [n] m, then weights
-  float* wl = wk + n;                                    // [n] l
-  int* wc = reinterpret_cast<int*>(wl + n);              // [n] counts
+  constexpr int UPT = 8;                          // partials per thread and round
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -982,71 +1055,68 @@ __device__ __forceinline__ void merge_slice(const float* __restrict__ pm, const 
   const int dq = tid & 7;
   const size_t kst = (size_t)G * (kD / 4);  // float4 stride between partials
   const float4* accb = reinterpret_cast<const float4*>(pacc + (size_t)g * kD + slice * kMSlice) + dq;
-  float4 x[8];
+  MState s;
+  s.M = -INFINITY;
+  s.L = 0.0f;
+  s.a = make_float4(0.f, 0.f, 0.f, 0.f);
+  s.C = 0;
+  for (int k0 = 0; k0 < n; k0 += NSUB * UPT) {
+    float4 x[UPT];
+    float mk[UPT], lk[UPT];
+    int ck[UPT];
 #pragma unroll
-  for (int u = 0; u < 8; u++) x[u] = accb[(size_t)min(sub + NSUB * u, n - 1) * kst];
-  float mloc = -INFINITY;
-  for (int k = tid; k < n; k += kThreads) {
-    const float m = pm[(size_t)k * G + g];
-    wk[k] = m;
-    wl[k] = pl[(size_t)k * G + g];
-    if (pcnt) wc[k] = pcnt[(size_t)k * G + g];
-    mloc = fmaxf(mloc, m);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, 64));
-  if (lane == 0) red[wv] = mloc;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float lloc = 0.0f;
-  int cloc = 0;
-  for (int k = tid; k < n; k += kThreads) {
-    const float m = wk[k];
-    const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-    wk[k] = f;
-    lloc += wl[k] * f;
-    if (pcnt) cloc += wc[k];
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    lloc += __shfl_xor(lloc, o, 64);
-    cloc += __shfl_xor(cloc, o, 64);
-  }
-  __syncthreads();
-  if (lane == 0) {
-    red[wv] = lloc;
-    reinterpret_cast<int*>(red)[4 + wv] = cloc;
-  }
-  __syncthreads();
-  const float Lsum = (red[0] + red[1]) + (red[2] + red[3]);
-  const int* ired = reinterpret_cast<const int*>(red) + 4;
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k0 = 0; k0 < n; k0 += NSUB * 8) {
-    if (k0 > 0) {
-#pragma unroll
-      for (int u = 0; u < 8; u++) x[u] = accb[(size_t)min(k0 + sub + NSUB * u, n - 1) * kst];
+    for (int u = 0; u < UPT; u++) {
+      const size_t k = (size_t)min(k0 + sub + NSUB * u, n - 1);
+      x[u] = accb[k * kst];
+      mk[u] = pm[k * G + g];
+      lk[u] = pl[k * G + g];
+      ck[u] = pcnt ? pcnt[k * G + g] : 0;
     }
 #pragma unroll
-    for (int u = 0; u < 8; u++) {
-      const int k = k0 + sub + NSUB * u;
-      const float f = k < n ? wk[k] : 0.0f;
-      a.x += x[u].x * f;
-      a.y += x[u].y * f;
-      a.z += x[u].z * f;
-      a.w += x[u].w * f;
+    for (int u = 0; u < UPT; u++) {
+      if (k0 + sub + NSUB * u < n) {
+        mstate_fold(s, mk[u], lk[u], x[u]);
+        s.C += ck[u];
+      }
     }
   }
-  reinterpret_cast<float4*>(racc + sub * kMSlice)[dq] = a;
+  const size_t orow = orow_of();
+  // lanes l, l^8, l^16, l^32 hold the same dims
+  s = mstate_merge(s, mstate_shfl_xor(s, 8));
+  s = mstate_merge(s, mstate_shfl_xor(s, 16));
+  s = mstate_merge(s, mstate_shfl_xor(s, 32));
+  float* red = lds;  // [wave][dq][M, L, a.x, a.y, a.z, a.w, C, -]
+  if (lane < 8) {
+    float* r = red + (wv * 8 + lane) * 8;
+    r[0] = s.M;
+    r[1] = s.L;
+    r[2] = s.a.x;
+    r[3] = s.a.y;
+    r[4] = s.a.z;
+    r[5] = s.a.w;
+    r[6] = __int_as_float(s.C);
+  }
   __syncthreads();
-  if (tid < kMSlice) {
-    float v = 0.0f;
+  if (tid < kMSlice) {  // output dim 4*dq + comp of the slice
+    const int oq = tid >> 2, comp = tid & 3;
+    float M = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < NSUB; s++) v += racc[s * kMSlice + tid];
+    for (int w = 0; w < kThreads / 64; w++) M = fmaxf(M, red[(w * 8 + oq) * 8]);
+    float Lsum = 0.0f, v = 0.0f;
+    int C = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; w++) {
+      const float* r = red + (w * 8 + oq) * 8;
+      const float f = r[0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(r[0] - M);
+      Lsum += r[1] * f;
+      v += r[2 + comp] * f;
+      C += __float_as_int(r[6]);
+    }
     out[orow * kD + slice * kMSlice + tid] = Lsum > 0.0f ? v / Lsum : 0.0f;
-  }
-  if (slice == 0 && tid == 0) {
-    if (lse) lse[orow] = Lsum > 0.0f ? (M + __log2f(Lsum)) * 0.69314718055994531f : -INFINITY;
-    if (count_out) count_out[orow] = (ired[0] + ired[1]) + (ired[2] + ired[3]);
+    if (slice == 0 && tid == 0) {
+      if (lse) lse[orow] = Lsum > 0.0f ? (M + __log2f(Lsum)) * 0.69314718055994531f : -INFINITY;
+      if (count_out) count_out[orow] = C;
+    }
   }
 }
 
@@ -1058,39 +1128,40 @@ __global__ __launch_bounds__(kThreads) void k_stage_m(StageMParams P) {
   const bool win = hb >= P.nret;
   const float *pm, *pl, *pacc;
   const int32_t* pcnt = nullptr;
-  int n, g;
-  size_t orow;
+  int n, g, b, kh;
   if (win) {
     const int wm = hb - P.nret;
     g = wm % G;
-    const int kl = (wm / G) % P.Hloc;
-    const int b = wm / (G * P.Hloc);
-    const size_t p0 = (size_t)(b * P.Hloc + kl) * P.nws * G;
+    kh = (wm / G) % P.Hloc;
+    b = wm / (G * P.Hloc);
+    const size_t p0 = (size_t)(b * P.Hloc + kh) * P.nws * G;
     pm = P.wpm + p0;
     pl = P.wpl + p0;
     pacc = P.wpacc + p0 * kD;
     n = P.nws;
-    orow = (size_t)b * P.Hq + (size_t)P.loc.kv[kl] * G + g;
   } else {
     g = hb % G;
-    const int kr = (hb / G) % P.Hret;
-    const int b = hb / (G * P.Hret);
-    const size_t p0 = (size_t)(b * P.Hret + kr) * P.nblk * G;
+    kh = (hb / G) % P.Hret;
+    b = hb / (G * P.Hret);
+    const size_t p0 = (size_t)(b * P.Hret + kh) * P.nblk * G;
     pm = P.p1m + p0;
     pl = P.p1l + p0;
     pacc = P.p1acc + p0 * kD;
     if (P.count_out) pcnt = P.p1cnt + p0;
     n = P.nblk;
-    orow = (size_t)b * P.Hq + (size_t)P.ret.kv[kr] * G + g;
-    if (slice == 0 && P.thresh_out && threadIdx.x == 0) {
-      const size_t row = (size_t)b * P.Hret * G + (size_t)kr * G + g;
-      const int A = P.Aglob[row];
-      P.thresh_out[orow * 2 + 0] = A == kEmptyCell ? 0 : A;
-      P.thresh_out[orow * 2 + 1] = A == kEmptyCell ? 0 : P.bstar[row];
-    }
   }
-  merge_slice(pm, pl, pacc, pcnt, n, G, g, slice, P.out, P.lse, win ? nullptr : P.count_out, orow,
-              mlds);
+  auto orow_of = [&]() {
+    return (size_t)b * P.Hq + (size_t)(win ? P.loc.kv[kh] : P.ret.kv[kh]) * G + g;
+  };
+  merge_slice(pm, pl, pacc, pcnt, n, G, g, slice, P.out, P.lse, win ? nullptr : P.count_out,
+              orow_of, mlds);
+  if (!win && slice == 0 && P.thresh_out && threadIdx.x == 0) {
+    const size_t row = (size_t)b * P.Hret * G + (size_t)kh * G + g;
+    const size_t orow = orow_of();
+    const int A = P.Aglob[row];
+    P.thresh_out[orow * 2 + 0] = A == kEmptyCell ? 0 : A;
+    P.thresh_out[orow * 2 + 1] = A == kEmptyCell ? 0 : P.bstar[row];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1448,6 +1519,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     Q.np_row = sp.nblk * sp.nparts + sp.rwnws;
   }
   const int nrw_blocks = Q.rw_window > 0 ? B * sp.Hret * sp.rwnws : 0;
+  Q.nrw_end = Q.nret_blocks + nrw_blocks;
   int nwin_blocks = 0;
   if (sp.Hloc > 0) {
     WinParams& W = Q.win;
@@ -1513,9 +1585,7 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     M.Hloc = sp.Hloc;
     M.loc = a.loc;
   }
-  const int nmax =
-      std::max(sp.Hret > 0 ? sp.nblk * sp.nparts + sp.rwnws : 0, sp.Hloc > 0 ? sp.nws : 0);
-  const size_t ldsM = sizeof(float) * (3 * (size_t)nmax + 8 + kThreads / 8 * kMSlice);
+  const size_t ldsM = sizeof(float) * (kThreads / 64) * 8 * 8;
   k_stage_m<<<(M.nret + nwm) * kMSlices, kThreads, ldsM, st>>>(M);
   e = hipGetLastError();
   if (e == hipSuccess && sp.exp) {
