@@ -434,7 +434,10 @@ def main():
                     help="retrieval heads also attend to the sinks and the window")
     ap.add_argument("--with-append", action="store_true",
                     help="each step also runs the cache update of the new token "
-                         "(indexer projections + K/V append) before the attention")
+                         "(indexer projections + K/V append), fused into the step")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="with --with-append: the update as its own kernel (rtp_append_project) "
+                         "before the step, instead of fused into it")
     ap.add_argument("--rotations", type=int, default=0)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -517,13 +520,15 @@ def main():
     apps = []
     ws = None
     out = None
+    fused_app = si is not None and not args.separate_append
     for lay in layers:
         st = rtp.DecodeStep(lay, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window, wl.sinks, wl.p,
                             wl.bin_width, wl.scale_idx, wl.scale_attn, out=out, want_lse=False,
-                            ws=ws, topk=args.topk, ret_window=args.ret_window)
+                            ws=ws, topk=args.topk, ret_window=args.ret_window,
+                            append=si if fused_app else None)
         ws, out = st.ws, st.out
         steps.append(st)
-        if si is not None:
+        if si is not None and not fused_app:
             apps.append(rtp.AppendProject(lay, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window,
                                           wl.sinks, si.q_pre, si.k_pre, si.Wq, si.Wk, si.k_new,
                                           si.v_new))
@@ -616,7 +621,7 @@ def main():
     def roofline(kernel, desc, us, nbytes):
         gbs = nbytes / (us * 1e-6) / 1e9 if us > 0 else 0.0
         wl_key = args.workload if not (args.topk or args.context or args.dtype != "f16"
-                                       or args.ret_window or apps) else None
+                                       or args.ret_window or si is not None) else None
         return {"kernel": "%s (%s)" % (kernel, desc), "bound": "hbm", "achieved": round(gbs, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                 # the counters were taken on the fp16 top-p step of the workload at its own
@@ -661,7 +666,9 @@ def main():
                                    "top-k k=%d" % args.topk if args.topk else "p=%g" % wl.p),
                    "global_batch": wl.B, "seq_len": int(wl.seq_lens.max()),
                    "parallelism": "single GPU", "graph": g_full is not None, "rotations": R,
-                   "with_append": bool(apps), "retrieval_window": bool(args.ret_window)},
+                   "with_append": ("fused" if si is not None and not args.separate_append
+                                   else "separate kernel" if si is not None else False),
+                   "retrieval_window": bool(args.ret_window)},
         "bytes_per_step": bytes_step,
         "bytes_detail": {k: v for k, v in detail.items() if k not in ("sel_tokens", "sel_mass")},
         "sel_tokens_per_head": detail["sel_tokens"],

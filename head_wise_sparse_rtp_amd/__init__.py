@@ -26,7 +26,8 @@ from typing import Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "librtp.so")
+# RTP_LIBRARY names another build of the same sources to load (the host-sanitizer build)
+LIB_PATH = os.environ.get("RTP_LIBRARY") or os.path.join(_HERE, "librtp.so")
 
 RTP_OK, RTP_EINVAL, RTP_EUNSUPPORTED, RTP_EWORKSPACE, RTP_EHIP, RTP_ESCRATCH = 0, -1, -2, -3, -4, -5
 RTP_F32, RTP_F16, RTP_BF16 = 0, 1, 2
@@ -61,7 +62,14 @@ class LayerDesc(ctypes.Structure):
         ("out", P), ("lse", P), ("thresh_out", P), ("count_out", P),
         ("topk", I32), ("ret_window", I32),
         ("sel_idx", P), ("sel_count", P), ("sel_cap", I32),
+        ("append", P),
     ]
+
+
+class StepAppend(ctypes.Structure):
+    """Mirror of rtp_step_append (the cache update fused into the decode step)."""
+    _fields_ = [("q_pre", P), ("k_pre", P), ("Wq_idx", P), ("Wk_idx", P), ("k_new", P),
+                ("v_new", P)]
 
 
 class AppendDesc(ctypes.Structure):
@@ -288,7 +296,7 @@ class DecodeStep:
                  window: int, sinks: int, p: float, bin_width: float, scale_idx: float,
                  scale_attn: float, out: Optional[torch.Tensor] = None, want_lse: bool = True,
                  want_debug: bool = False, ws: Optional[torch.Tensor] = None, topk: int = 0,
-                 ret_window: bool = False, want_sets: int = 0):
+                 ret_window: bool = False, want_sets: int = 0, append=None):
         dev = layer.q.device
         self.keep = [layer.q, layer.q_idx, layer.K_ret, layer.V_ret, layer.k_idx, layer.K_loc,
                      layer.V_loc, seq_lens]
@@ -323,6 +331,16 @@ class DecodeStep:
         self.desc.sel_idx = _ptr(self.sel_idx)
         self.desc.sel_count = _ptr(self.sel_count)
         self.desc.sel_cap = int(want_sets)
+        self.app = None
+        if append is not None:
+            # the new token's cache update, fused into the step: `append` holds q_pre,
+            # k_pre, Wq, Wk, k_new, v_new (see rtp_step_append); the layer's caches are
+            # updated in place by every call
+            self.keep += [append.q_pre, append.k_pre, append.Wq, append.Wk, append.k_new,
+                          append.v_new]
+            self.app = StepAppend(_ptr(append.q_pre), _ptr(append.k_pre), _ptr(append.Wq),
+                                  _ptr(append.Wk), _ptr(append.k_new), _ptr(append.v_new))
+            self.desc.append = ctypes.cast(ctypes.pointer(self.app), ctypes.c_void_p)
         nb = lib().rtp_decode_step_workspace_size(ctypes.byref(self.desc))
         if nb == 0:
             raise RtpError(RTP_EINVAL)
@@ -351,13 +369,13 @@ class DecodeStep:
 
 def rtp_decode_step(layer, seq_lens, B, Hq, Hkv, Lmax, window, sinks, p, bin_width, scale_idx,
                     scale_attn, want_debug=False, stream=None, topk=0, ret_window=False,
-                    want_sets=0):
+                    want_sets=0, append=None):
     """One layer's decode step; returns (out, lse, thresh, count), followed by (sel_idx,
     sel_count) when want_sets > 0.  topk > 0 selects the retrieval heads' tokens with the
     fixed top-k rule instead of top-p."""
     st = DecodeStep(layer, seq_lens, B, Hq, Hkv, Lmax, window, sinks, p, bin_width, scale_idx,
                     scale_attn, want_debug=want_debug, topk=topk, ret_window=ret_window,
-                    want_sets=want_sets)
+                    want_sets=want_sets, append=append)
     st(stream)
     if want_sets:
         return st.out, st.lse, st.thresh, st.count, st.sel_idx, st.sel_count
@@ -449,14 +467,16 @@ def rtp_prefill(seq_lens, mask, q, K, V, window, sinks, scale_attn, k_pre=None, 
     return pf
 
 
-def decode_workload(wl, want_debug: bool = False, stream=None, want_sets: int = 0):
+def decode_workload(wl, want_debug: bool = False, stream=None, want_sets: int = 0,
+                    appends=None):
     """Run every layer of a `workloads.Workload` already on the GPU; returns per-layer
-    (out, lse, thresh, count), plus (sel_idx, sel_count) when want_sets > 0."""
+    (out, lse, thresh, count), plus (sel_idx, sel_count) when want_sets > 0.  appends, when
+    given, holds per layer the inputs of the cache update fused into its step (or None)."""
     sl = torch.as_tensor(wl.seq_lens, dtype=torch.int32).to(wl.layers[0].q.device)
     res = []
-    for layer in wl.layers:
+    for li, layer in enumerate(wl.layers):
         res.append(rtp_decode_step(layer, sl, wl.B, wl.Hq, wl.Hkv, wl.Lmax, wl.window, wl.sinks,
                                    wl.p, wl.bin_width, wl.scale_idx, wl.scale_attn, want_debug,
                                    stream, getattr(wl, "topk", 0), getattr(wl, "ret_window", False),
-                                   want_sets))
+                                   want_sets, appends[li] if appends is not None else None))
     return res

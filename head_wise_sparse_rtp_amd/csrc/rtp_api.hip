@@ -149,6 +149,36 @@ rtp_status plan_step(const rtp_layer_desc* d, StepPlan& sp) {
   return RTP_OK;
 }
 
+// The standalone cache update's arguments for a layer descriptor with an append group.
+AppendArgs append_args_of(const rtp_layer_desc* d, const rtp_step_append* ap) {
+  AppendArgs a{};
+  a.B = d->B;
+  a.Hq = d->Hq;
+  a.Hkv = d->Hkv;
+  a.G = d->Hq / d->Hkv;
+  a.Lmax = d->Lmax;
+  a.window = d->window;
+  a.sinks = d->sinks;
+  for (int h = 0; h < d->Hkv; h++) {
+    a.is_ret[h] = d->kv_is_retrieval[h] ? 1 : 0;
+    a.rank[h] = a.is_ret[h] ? a.Hret++ : a.Hloc++;
+  }
+  a.seq_lens = d->seq_lens;
+  a.q_pre = ap->q_pre;
+  a.k_pre = ap->k_pre;
+  a.Wq = ap->Wq_idx;
+  a.Wk = ap->Wk_idx;
+  a.k_new = ap->k_new;
+  a.v_new = ap->v_new;
+  a.q_idx = const_cast<float*>(d->q_idx);
+  a.k_idx = const_cast<void*>(d->k_idx);
+  a.K_ret = const_cast<void*>(d->K_ret);
+  a.V_ret = const_cast<void*>(d->V_ret);
+  a.K_loc = const_cast<void*>(d->K_loc);
+  a.V_loc = const_cast<void*>(d->V_loc);
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -424,6 +454,13 @@ rtp_status decode_step_impl(const rtp_layer_desc* d, void* ws, size_t ws_bytes, 
   }
   if (sp.Hloc > 0 && (!ptr_ok(d->K_loc) || !ptr_ok(d->V_loc))) return RTP_EINVAL;
   if ((d->sel_idx == nullptr) != (d->sel_count == nullptr)) return RTP_EINVAL;
+  const rtp_step_append* ap = d->append;
+  if (ap) {
+    if (!ptr_ok(ap->k_new) || !ptr_ok(ap->v_new)) return RTP_EINVAL;
+    if (sp.Hret > 0 && (!ptr_ok(ap->q_pre) || !ptr_ok(ap->k_pre) || !ptr_ok(ap->Wq_idx) ||
+                        !ptr_ok(ap->Wk_idx)))
+      return RTP_EINVAL;
+  }
   if (d->sel_idx && (!ptr_ok(d->sel_idx) || !ptr_ok(d->sel_count) || d->sel_cap < 1))
     return RTP_EINVAL;
   if (ws_bytes < sp.bytes) return RTP_EWORKSPACE;
@@ -464,6 +501,14 @@ rtp_status decode_step_impl(const rtp_layer_desc* d, void* ws, size_t ws_bytes, 
     a.sel_idx = d->sel_idx;
     a.sel_count = d->sel_count;
     a.sel_cap = d->sel_cap;
+    a.Hkv = d->Hkv;
+    // the cache update runs inside stage A; without retrieval heads there is no stage A,
+    // and the standalone update kernel runs first
+    a.app = sp.Hret > 0 ? ap : nullptr;
+    if (ap && sp.Hret == 0) {
+      const hipError_t ea = launch_append_project(append_args_of(d, ap), d->kv_dtype, st);
+      if (ea != hipSuccess) return RTP_EHIP;
+    }
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     if (events)
       for (int i = 0; i < 4; i++) ev[i] = (hipEvent_t)events[i];
@@ -472,6 +517,7 @@ rtp_status decode_step_impl(const rtp_layer_desc* d, void* ws, size_t ws_bytes, 
   auto mark = [&](int i) {
     if (e == hipSuccess && events && events[i]) e = hipEventRecord((hipEvent_t)events[i], st);
   };
+  if (ap) e = launch_append_project(append_args_of(d, ap), d->kv_dtype, st);
   if (sp.Hloc > 0) {
     const AttnPartials pa = bind_parts(w, sp.win);
     if (e == hipSuccess)

@@ -227,6 +227,9 @@ struct StepFusedArgs {
   int32_t* sel_idx;  // [B, Hq, sel_cap] or null: the exported sets
   int32_t* sel_count;
   int sel_cap;
+  // cache update fused into stage A (app == null: none); the caches above are then written
+  const rtp_step_append* app;
+  int Hkv;
 };
 
 bool step_fused_supported(int kv_dtype, int G, int Hloc, int window, int sinks, int B, int Hret,

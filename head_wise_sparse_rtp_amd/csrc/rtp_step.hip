@@ -166,6 +166,28 @@ constexpr int copies_of() {
   return NT >= 512 ? 4 : 2;
 }
 constexpr int kPad = 1;
+// A projection chain's LDS region (floats): half of a 128 x 16 matrix (64 rows), stored
+// transposed (output i's 64 coefficients at i kRowT, the 4 floats of padding spread the
+// outputs over the banks), then the 128-float input row.  The fused cache update stages one
+// region per query head of the group (region g for head g) and a ninth for the new key, in
+// the histogram's space before the histogram uses it.
+constexpr int kRowT = kD / 2 + 4;
+constexpr int kRgn = kR * kRowT + kD;
+// stage-A LDS: histogram copies, the wavefronts' head maxima, the code-word staging; with
+// the fused cache update the eight chain regions share that space, and the group's
+// projected q_idx and the new token's key follow it (they live across the histogram's
+// first use of its space)
+__host__ __device__ constexpr int stage_a_base_lds(int nt) {
+  return (int)sizeof(uint32_t) * (nt >= 512 ? 4 : 2) * 8 * (kNB + kPad) + (int)sizeof(float) * 8 * (nt / 64) +
+         (int)sizeof(uint32_t) * (nt / 64) * 8 * 64;
+}
+__host__ __device__ constexpr int stage_a_qsh(int nt) {
+  return stage_a_base_lds(nt) > (int)sizeof(float) * 9 * kRgn ? stage_a_base_lds(nt)
+                                                             : (int)sizeof(float) * 9 * kRgn;
+}
+__host__ __device__ constexpr int stage_a_lds(int nt, bool app) {
+  return app ? stage_a_qsh(nt) + (int)sizeof(float) * 9 * kR : stage_a_base_lds(nt);
+}
 // y of a token past the sequence's end: finite and far below every cell, so that its
 // mass is exactly zero and it lands in the tail bin (with unit weights it is taken back
 // out of that bin after the pass)
@@ -187,7 +209,22 @@ struct StageAParams {
   unsigned long long* sufq;  // zeroed here (rows of the unit, by its chunk-0 block)
   int B, ngg;
   double w;
+  // cache update fused into the step (kernels instantiated with APP only)
+  const float* q_pre;  // [B, Hq, 128]
+  const float* k_pre;  // [B, Hkv, 128]
+  const float* Wq;     // [Hq, 128, 16]
+  const float* Wk;     // [Hret, 128, 16]
+  const void* k_new;   // [B, Hkv, 128] (the kernel's element type)
+  const void* v_new;
+  float* q_idx_w;      // the q_idx cache: the chunk-0 blocks write the projections
+  void* k_idx_w;       // row L-1 written by the block that holds the token
+  void* K_ret_w;
+  void* V_ret_w;
+  void* K_loc_w;
+  void* V_loc_w;
+  int Hkv, Hloc, window, sinks;
   HeadMap ret;  // last: indexed by a computed head (a dependent read)
+  HeadMap loc;
 };
 
 struct WinParams {
@@ -221,7 +258,11 @@ struct WinParams {
 template <typename T>
 struct HistIn {
   v8<T> ka[8];
-  float4 q[2];  // q_idx[8*(kq&1) .. +7] of the lane's head
+  float4 q[2];   // q_idx[8*(kq&1) .. +7] of the lane's head
+  // with the fused update: the projection matrix (float4 lane + 64 j of its 128 x 16 floats)
+  // and input row (floats 2 lane, 2 lane + 1) of the wave's query heads wv and wv + NWV
+  float4 w[2][8];
+  float2 x[2];
 };
 
 struct HistUnit {
@@ -243,7 +284,7 @@ __device__ __forceinline__ HistUnit hist_unit(const StageAParams& P) {
   return u;
 }
 
-template <int NT, typename T>
+template <int NT, typename T, bool APP>
 __device__ __forceinline__ void hist_fetch(const StageAParams& P, const HistUnit& u, HistIn<T>& in) {
   constexpr int TC = NT * 4;
   const int lane = threadIdx.x & 63;
@@ -256,13 +297,30 @@ __device__ __forceinline__ void hist_fetch(const StageAParams& P, const HistUnit
   // tokens past the sequence's end are masked in hist_block
   const int nlast = P.Lmax - 1;
   // q_idx first: vector loads complete in order, so q_idx, issued ahead of the keys, is
-  // ready when they arrive and its operands are prepared while they are in flight
+  // ready when they arrive and its operands are prepared while they are in flight.  With
+  // the fused cache update the block projects q_idx itself: the wave's projection matrix
+  // and input row take q_idx's place.
   const int hh = lane & 7;
-  const float4* qp = reinterpret_cast<const float4*>(
-      P.q_idx + ((size_t)u.b * P.Hq + (size_t)P.ret.kv[u.kr] * P.G + u.grp * 8 + min(hh, u.nrows - 1)) * kR +
-      8 * (kq & 1));
-  in.q[0] = qp[0];
-  in.q[1] = qp[1];
+  if constexpr (APP) {
+    constexpr int NWV = NT / 64;
+#pragma unroll
+    for (int s = 0; s < 8 / NWV; s++) {
+      const int g = wv + NWV * s;  // the wave's query heads of the group
+      if (g < u.nrows) {
+        const size_t qh = (size_t)P.ret.kv[u.kr] * P.G + u.grp * 8 + g;
+        const float4* W = reinterpret_cast<const float4*>(P.Wq + qh * kD * kR);
+#pragma unroll
+        for (int j = 0; j < 8; j++) in.w[s][j] = W[lane + 64 * j];
+        in.x[s] = reinterpret_cast<const float2*>(P.q_pre + ((size_t)u.b * P.Hq + qh) * kD)[lane];
+      }
+    }
+  } else {
+    const float4* qp = reinterpret_cast<const float4*>(
+        P.q_idx + ((size_t)u.b * P.Hq + (size_t)P.ret.kv[u.kr] * P.G + u.grp * 8 + min(hh, u.nrows - 1)) * kR +
+        8 * (kq & 1));
+    in.q[0] = qp[0];
+    in.q[1] = qp[1];
+  }
 #pragma unroll
   for (int gi = 0; gi < 8; gi++) {
     const int n = min(wbase + gi * 32 + (lane & 15) + 16 * (kq >> 1), nlast);
@@ -270,8 +328,67 @@ __device__ __forceinline__ void hist_fetch(const StageAParams& P, const HistUnit
   }
 }
 
-template <int NT, typename T>
-__device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistIn<T>& in,
+// Orders one wave's LDS accesses across its lanes: what a lane wrote before the call is
+// seen by every lane of the wave after it.  Lanes of a wave issue LDS operations in order,
+// so this only has to stop the compiler from moving accesses across it (without it, the
+// lanes that skip a divergent read may write the next piece before the others read).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The indexer projection of a pre-RoPE vector, as the cache update defines it: one fp32
+// chain per output i, a <- fma(x[c], W[c][i], a) for c = 0..127 in order.  A chain region
+// holds half of the 128 x 16 matrix (64 rows) and the input row; every lane of the wave
+// writes its share of a half before any lane reads it, so each chain makes two passes.
+
+// Half h (rows 64 h .. 64 h + 63) of a matrix held as float4 lane + 64 j of the lanes'
+// registers is the registers j = 4 h .. 4 h + 3: register j holds row (lane >> 2) + 16 j of
+// the half, columns 4 (lane & 3) .. + 3, written here to the transposed rows.
+__device__ __forceinline__ void chain_put(float* rgn, float4 w0, float4 w1, float4 w2, float4 w3) {
+  const int lane = threadIdx.x & 63;
+  float* t = rgn + 4 * (lane & 3) * kRowT + (lane >> 2);
+  const float4 w[4] = {w0, w1, w2, w3};
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    t[16 * j] = w[j].x;
+    t[kRowT + 16 * j] = w[j].y;
+    t[2 * kRowT + 16 * j] = w[j].z;
+    t[3 * kRowT + 16 * j] = w[j].w;
+  }
+}
+__device__ __forceinline__ void chain_put_x(float* rgn, float2 x) {
+  reinterpret_cast<float2*>(rgn + kR * kRowT)[threadIdx.x & 63] = x;
+}
+// rows 64 h .. 64 h + 63 of output i's chain, four coefficients and four inputs per read
+__device__ __forceinline__ float chain_half(const float* rgn, int h, int i, float a) {
+  const float4* wt = reinterpret_cast<const float4*>(rgn + i * kRowT);
+  const float4* xs = reinterpret_cast<const float4*>(rgn + kR * kRowT + 64 * h);
+#pragma unroll
+  for (int c4 = 0; c4 < 16; c4++) {
+    const float4 w = wt[c4], x = xs[c4];
+    a = __builtin_fmaf(x.x, w.x, a);
+    a = __builtin_fmaf(x.y, w.y, a);
+    a = __builtin_fmaf(x.z, w.z, a);
+    a = __builtin_fmaf(x.w, w.w, a);
+  }
+  return a;
+}
+
+template <typename T>
+__device__ __forceinline__ T to_elem(float x);
+template <>
+__device__ __forceinline__ f16 to_elem<f16>(float x) {
+  return (f16)x;
+}
+template <>
+__device__ __forceinline__ bf16e to_elem<bf16e>(float x) {
+  return __builtin_bit_cast(bf16e, (uint16_t)f_to_bf16(x));
+}
+
+template <int NT, typename T, bool APP>
+__device__ void hist_block(const StageAParams& P, const HistUnit& U, HistIn<T>& in,
                            unsigned char* smem) {
   constexpr int TC = NT * 4;
   constexpr int NWV = NT / 64;
@@ -308,8 +425,106 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
   for (int k = 0; k < NQP; k++)
 #pragma unroll
     for (int i = 0; i < 8; i++) qp[k][i] = (T)0.0f;
-  const float q[8] = {in.q[0].x, in.q[0].y, in.q[0].z, in.q[0].w,
-                      in.q[1].x, in.q[1].y, in.q[1].z, in.q[1].w};
+  float q[8] = {in.q[0].x, in.q[0].y, in.q[0].z, in.q[0].w,
+                in.q[1].x, in.q[1].y, in.q[1].z, in.q[1].w};
+  using u4t = uint32_t __attribute__((ext_vector_type(4)));
+  const int n = L - 1;  // the new token
+  // (uniform per wave) the fused update's key of the new token is this wave's
+  const bool tokw = APP && n >= base && n < base + TC && (n - base) / 256 == wv;
+  u4t kvr[4];  // its K/V rows, stored at the block's end: retrieval K, V, local K, V
+  if constexpr (APP) {
+    // the fused cache update: q_idx of the group's heads, then the indexer key of token n
+    // in the wave whose tokens hold it, which also loads the new K/V rows.  Every wave
+    // stages its heads' matrices (heads wv and wv + NWV), half by half; the chains then run
+    // four to a wave (head c in lanes 16 (c & 3) .. + 15 of wave c / 4), so that the few
+    // fma chains do not share the SIMDs with one another.
+    constexpr int QPW = 8 / NWV;
+    float* qsh = reinterpret_cast<float*>(smem + stage_a_qsh(NT));  // [8 heads][16], then the key
+    float* rg = reinterpret_cast<float*>(smem);  // region of head c: rg + c kRgn
+    const size_t kvq = (size_t)P.ret.kv[U.kr] * P.G + U.grp * 8;
+    const int i16 = lane & 15;
+    const int cl = 4 * wv + (lane >> 4);  // the head whose chain the lane runs
+    const bool act = cl < nrows;           // (waves 0 and 1 only)
+    const float* mr = rg + (act ? cl : 0) * kRgn;
+#pragma unroll
+    for (int s = 0; s < QPW; s++) {
+      const int g = wv + NWV * s;
+      if (g < nrows) {
+        chain_put(rg + g * kRgn, in.w[s][0], in.w[s][1], in.w[s][2], in.w[s][3]);
+        chain_put_x(rg + g * kRgn, in.x[s]);
+      }
+    }
+    __syncthreads();
+    float a = 0.0f;
+    if (act) a = chain_half(mr, 0, i16, a);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < QPW; s++) {
+      const int g = wv + NWV * s;
+      if (g < nrows) chain_put(rg + g * kRgn, in.w[s][4], in.w[s][5], in.w[s][6], in.w[s][7]);
+    }
+    __syncthreads();
+    if (act) {
+      a = chain_half(mr, 1, i16, a);
+      qsh[cl * kR + i16] = a;
+      if (chunk == 0) P.q_idx_w[((size_t)U.b * P.Hq + kvq + cl) * kR + i16] = a;
+    }
+    if (tokw) {
+      const int kv = P.ret.kv[U.kr];
+      float4 w[8];
+      const float4* W = reinterpret_cast<const float4*>(P.Wk + (size_t)U.kr * kD * kR);
+#pragma unroll
+      for (int j = 0; j < 8; j++) w[j] = W[lane + 64 * j];
+      const float2 x = reinterpret_cast<const float2*>(P.k_pre + ((size_t)U.b * P.Hkv + kv) * kD)[lane];
+      float* kr = rg + 8 * kRgn;  // the ninth region
+      chain_put(kr, w[0], w[1], w[2], w[3]);
+      chain_put_x(kr, x);
+      wave_lds_sync();
+      float ak = 0.0f;
+      if (lane < kR) ak = chain_half(kr, 0, lane, ak);
+      wave_lds_sync();
+      chain_put(kr, w[4], w[5], w[6], w[7]);
+      wave_lds_sync();
+      float* ksh = qsh + 8 * kR;
+      const size_t krow = ((size_t)U.b * P.Hret + U.kr) * (size_t)P.Lmax + n;
+      if (lane < kR) {
+        ak = chain_half(kr, 1, lane, ak);
+        ksh[lane] = ak;
+        if (U.grp == 0) static_cast<T*>(P.k_idx_w)[krow * kR + lane] = to_elem<T>(ak);
+      }
+      wave_lds_sync();
+      // the token's key row in the score tile: lanes (r & 15) + 16 (2 (r >> 4) + half)
+      const int r = (n - base) & 255;
+      const int gin = r >> 5, rr = r & 31;
+      if ((lane & 15) == (rr & 15) && ((lane >> 4) >> 1) == (rr >> 4)) {
+        const int half = (lane >> 4) & 1;
+#pragma unroll
+        for (int gi = 0; gi < 8; gi++)
+          if (gi == gin)
+#pragma unroll
+            for (int i = 0; i < 8; i++) in.ka[gi][i] = to_elem<T>(ksh[8 * half + i]);
+      }
+      if (U.grp == 0) {
+        // the new K/V rows: retrieval cache row n (lanes 0..15), and with the first
+        // retrieval head the ring slot of local head lane / 16 (the rest at the block's end)
+        const u4t* kn = reinterpret_cast<const u4t*>(static_cast<const T*>(P.k_new) + ((size_t)U.b * P.Hkv + kv) * kD);
+        const u4t* vn = reinterpret_cast<const u4t*>(static_cast<const T*>(P.v_new) + ((size_t)U.b * P.Hkv + kv) * kD);
+        if (lane < 16) {
+          kvr[0] = kn[lane];
+          kvr[1] = vn[lane];
+        }
+        const int kl = lane >> 4;
+        if (U.kr == 0 && kl < P.Hloc) {
+          const int kvl = P.loc.kv[kl];
+          kvr[2] = reinterpret_cast<const u4t*>(static_cast<const T*>(P.k_new) + ((size_t)U.b * P.Hkv + kvl) * kD)[lane & 15];
+          kvr[3] = reinterpret_cast<const u4t*>(static_cast<const T*>(P.v_new) + ((size_t)U.b * P.Hkv + kvl) * kD)[lane & 15];
+        }
+      }
+    }
+    __syncthreads();  // every head's q_idx in LDS; the regions are free again
+#pragma unroll
+    for (int i = 0; i < 8; i++) q[i] = qsh[min(hh, nrows - 1) * kR + 8 * (kq & 1) + i];
+  }
   float qm = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; i++) qm = fmaxf(qm, fabsf(q[i]));
@@ -446,17 +661,42 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, const HistI
       P.partA[(rowb + gg) * P.nchunk + chunk] = (int)floorf(mm);
     }
   }
+  if constexpr (APP) {
+    if (tokw && U.grp == 0) {
+      // the new K/V rows, loaded before the histogram: retrieval cache row n, and with the
+      // first retrieval head the ring slot of every local head
+      const size_t krow = ((size_t)U.b * P.Hret + U.kr) * (size_t)P.Lmax + n;
+      if (lane < 16) {
+        reinterpret_cast<u4t*>(static_cast<T*>(P.K_ret_w) + krow * kD)[lane] = kvr[0];
+        reinterpret_cast<u4t*>(static_cast<T*>(P.V_ret_w) + krow * kD)[lane] = kvr[1];
+      }
+      if (U.kr == 0) {
+        const int slot = n < P.sinks ? n : P.sinks + n % P.window;
+        for (int kl = lane >> 4; kl < P.Hloc; kl += 4) {
+          const size_t lrow = ((size_t)U.b * P.Hloc + kl) * (size_t)(P.sinks + P.window) + slot;
+          u4t kv4 = kvr[2], vv4 = kvr[3];
+          if (kl >= 4) {
+            const int kvl = P.loc.kv[kl];
+            kv4 = reinterpret_cast<const u4t*>(static_cast<const T*>(P.k_new) + ((size_t)U.b * P.Hkv + kvl) * kD)[lane & 15];
+            vv4 = reinterpret_cast<const u4t*>(static_cast<const T*>(P.v_new) + ((size_t)U.b * P.Hkv + kvl) * kD)[lane & 15];
+          }
+          reinterpret_cast<u4t*>(static_cast<T*>(P.K_loc_w) + lrow * kD)[lane & 15] = kv4;
+          reinterpret_cast<u4t*>(static_cast<T*>(P.V_loc_w) + lrow * kD)[lane & 15] = vv4;
+        }
+      }
+    }
+  }
 }
 
 // One histogram unit per block: two blocks per CU hide the latency of the histogram
 // pass better than a block that prefetches a second unit.
-template <int NT, typename T>
+template <int NT, typename T, bool APP>
 __global__ __launch_bounds__(NT, NT >= 512 ? 2 : 4) void k_stage_a(StageAParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   const HistUnit U = hist_unit<NT>(P);
   HistIn<T> in;
-  hist_fetch<NT, T>(P, U, in);
-  hist_block<NT, T>(P, U, in, smem);
+  hist_fetch<NT, T, APP>(P, U, in);
+  hist_block<NT, T, APP>(P, U, in, smem);
 }
 
 // Masked attention over the entries e = 0..n-1 of a row list: row_of(e) is the cache
@@ -1437,17 +1677,37 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
     P.partA = at<int32_t>(ws, sp.partA);
     P.codes = at<uint32_t>(ws, sp.codes);
     P.sufq = at<unsigned long long>(ws, sp.sufq);
-    // histogram copies, the top cells of the wavefronts, the code words of the wavefronts
-    const int cpA = sp.nt >= 512 ? copies_of<512>() : copies_of<256>();
-    const size_t ldsA = sizeof(uint32_t) * cpA * GG * (kNB + kPad) + sizeof(float) * GG * 8 +
-                        sizeof(uint32_t) * (sp.nt / 64) * GG * 64;
+    const bool app = a.app != nullptr;
+    if (app) {
+      P.q_pre = a.app->q_pre;
+      P.k_pre = a.app->k_pre;
+      P.Wq = a.app->Wq_idx;
+      P.Wk = a.app->Wk_idx;
+      P.k_new = a.app->k_new;
+      P.v_new = a.app->v_new;
+      P.q_idx_w = const_cast<float*>(a.q_idx);
+      P.k_idx_w = const_cast<void*>(a.k_idx);
+      P.K_ret_w = const_cast<void*>(a.K_ret);
+      P.V_ret_w = const_cast<void*>(a.V_ret);
+      P.K_loc_w = const_cast<void*>(a.K_loc);
+      P.V_loc_w = const_cast<void*>(a.V_loc);
+      P.Hkv = a.Hkv;
+      P.Hloc = sp.Hloc;
+      P.window = a.window;
+      P.sinks = a.sinks;
+      P.loc = a.loc;
+    }
+    const size_t ldsA = (size_t)stage_a_lds(sp.nt, app);
     const dim3 gA(sp.nchunk, P.ngg, B * sp.Hret);
+    const bool bf = a.kv_dtype == 2;
+    void (*fa)(StageAParams) = nullptr;
     if (sp.nt == 256)
-      e = a.kv_dtype == 2 ? launch1(&k_stage_a<256, bf16e>, gA, dim3(256), ldsA, st, P, ea0, ea1)
-                          : launch1(&k_stage_a<256, f16>, gA, dim3(256), ldsA, st, P, ea0, ea1);
+      fa = app ? (bf ? &k_stage_a<256, bf16e, true> : &k_stage_a<256, f16, true>)
+               : (bf ? &k_stage_a<256, bf16e, false> : &k_stage_a<256, f16, false>);
     else
-      e = a.kv_dtype == 2 ? launch1(&k_stage_a<512, bf16e>, gA, dim3(512), ldsA, st, P, ea0, ea1)
-                          : launch1(&k_stage_a<512, f16>, gA, dim3(512), ldsA, st, P, ea0, ea1);
+      fa = app ? (bf ? &k_stage_a<512, bf16e, true> : &k_stage_a<512, f16, true>)
+               : (bf ? &k_stage_a<512, bf16e, false> : &k_stage_a<512, f16, false>);
+    e = launch1(fa, gA, dim3(sp.nt), ldsA, st, P, ea0, ea1);
     if (e != hipSuccess) return e;
   }
   // ---- K2: suffix tables

@@ -199,7 +199,23 @@ typedef struct {
   int32_t* sel_idx;               /* [B, Hq, sel_cap] int32 out, or NULL */
   int32_t* sel_count;             /* [B, Hq] int32 out, or NULL (NULL exactly when sel_idx is) */
   int32_t sel_cap;                /* >= 1 when sel_idx is given */
+  /* Optional cache update fused into the step (NULL: none).  The step first does exactly
+   * what rtp_append_project does with these inputs -- the new token's indexer projections
+   * into q_idx and k_idx[L-1], its K/V rows into K_ret/V_ret[L-1] or the local ring -- and
+   * then attends over the updated caches; seq_lens holds the lengths after the append.
+   * q_idx, k_idx, K_ret, V_ret, K_loc and V_loc are then written as well as read. */
+  const struct rtp_step_append* append;
 } rtp_layer_desc;
+
+/* Inputs of the cache update fused into rtp_decode_step (rtp_append_project's inputs). */
+typedef struct rtp_step_append {
+  const float* q_pre;             /* [B, Hq, d] fp32 pre-RoPE queries (retrieval rows read) */
+  const float* k_pre;             /* [B, Hkv, d] fp32 pre-RoPE keys of the new token */
+  const float* Wq_idx;            /* [Hq, d, r] fp32 */
+  const float* Wk_idx;            /* [Hret, d, r] fp32, retrieval KV heads in ascending order */
+  const void* k_new;              /* [B, Hkv, d] (kv_dtype) key of the new token (post-RoPE) */
+  const void* v_new;              /* [B, Hkv, d] (kv_dtype) */
+} rtp_step_append;
 
 /* fp16 and bf16 caches with G <= 16 run four kernels per call: indexer score + chunk
  * histograms; per-head suffix tables of the bin masses (token counts under top-k);

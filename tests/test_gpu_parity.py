@@ -296,13 +296,14 @@ DIAG_TOL = {"f16": 1e-4, "bf16": 1e-4, "f32": 1e-5}
 
 
 def check_decode(rtp, wl, local_sample=None, layers=None, label="", oracle_layers=None,
-                 sets=True):
+                 sets=True, appends=None):
     """Run every layer on the GPU and compare with the oracle (all retrieval heads; all
     local heads or the first `local_sample` of each layer).  `oracle_layers`, when given,
     are the oracle's own copies of the layers (after its own cache update).  With `sets`
     the step also exports the token set each retrieval query head attended to, and every
     set is compared with the oracle's element by element (up to edge-band tokens)."""
-    res = rtp.decode_workload(wl, want_debug=True, want_sets=wl.Lmax if sets else 0)
+    res = rtp.decode_workload(wl, want_debug=True, want_sets=wl.Lmax if sets else 0,
+                              appends=appends)
     torch.cuda.synchronize()
     st = SelCheck()
     tol = out_tol(wl.dtype)
@@ -464,6 +465,80 @@ def test_append_then_decode_c1(rtp):
                            si.k_pre, si.Wq, si.Wk, si.k_new, si.v_new)
     assert np.array_equal(_bits(oracle.np_of(lay.k_idx)), _bits(want[1]))
     check_decode(rtp, wl, label="append-c1", oracle_layers=[olay])
+
+
+def _check_caches(lay, want, label):
+    got = [oracle.np_of(t) for t in (lay.q_idx, lay.k_idx, lay.K_ret, lay.V_ret, lay.K_loc,
+                                     lay.V_loc)]
+    for name, g, w in zip(["q_idx", "k_idx", "K_ret", "V_ret", "K_loc", "V_loc"], got, want):
+        assert np.array_equal(_bits(g), _bits(w)), "%s: %s" % (label, name)
+
+
+@pytest.mark.parametrize("dtype,mask,ret_window", [
+    ("f16", [1, 0, 1, 0], False), ("bf16", [1, 0, 1, 0], False), ("f16", [1, 0, 1, 0], True),
+    ("f32", [1, 0, 1, 0], False), ("f16", [0, 0, 0, 0], False), ("f16", [1, 1, 1, 1], False)])
+def test_decode_step_fused_append_small_ragged(rtp, dtype, mask, ret_window):
+    """The cache update fused into the step: stage A projects the group's q_idx and the new
+    token's indexer key and copies the new K/V rows (the standalone update kernel runs first
+    on the single-purpose path, fp32, and for layers without retrieval heads).  Every cache
+    must equal the oracle's update bit for bit, and the outputs its decode over the updated
+    caches; lengths put the new token on sinks, ring wraps, chunk and wave edges."""
+    lens = [1, 5000, 70, 3, 4099, 2049]
+    label = "fused-append-%s-%s%s" % (dtype, "".join(map(str, mask)), "-rw" if ret_window else "")
+    say(label, lens)
+    wl = workloads.make_workload("t", len(lens), lens, 32, 4, [mask], seed=83, dtype=dtype,
+                                 window=64, sinks=4, device=dev(), Lmax=5000)
+    wl.ret_window = ret_window
+    lay = wl.layers[0]
+    si = workloads.make_step_inputs(wl, seed=3, device=dev())
+    want = oracle.append_project(lay, lens, si.q_pre, si.k_pre, si.k_new, si.v_new, si.Wq, si.Wk,
+                                 wl.window, wl.sinks)
+    olay = _oracle_layer(lay, want)
+    check_decode(rtp, wl, label=label, oracle_layers=[olay], appends=[si])
+    _check_caches(lay, want, label)
+
+
+def test_decode_step_fused_append_empty_sequence(rtp):
+    """A sequence of length 0 takes no update and yields zeros; the others are updated."""
+    lens = [0, 3000, 1]
+    say("fused append with an empty sequence", lens)
+    wl = workloads.make_workload("t", 3, lens, 32, 4, [[1, 0, 1, 0]], seed=84, dtype="f16",
+                                 window=64, sinks=4, device=dev(), Lmax=3000)
+    lay = wl.layers[0]
+    si = workloads.make_step_inputs(wl, seed=4, device=dev())
+    want = oracle.append_project(lay, lens, si.q_pre, si.k_pre, si.k_new, si.v_new, si.Wq, si.Wk,
+                                 wl.window, wl.sinks)
+    out, lse, _, _ = rtp.decode_workload(wl, want_debug=True, appends=[si])[0]
+    torch.cuda.synchronize()
+    _check_caches(lay, want, "empty")
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(out[0] == 0) and np.all(lse[0] == -np.inf)
+    olay = _oracle_layer(lay, want)
+    orc = oracle.decode_layer(olay, lens, wl.Hq, wl.Hkv, wl.p, wl.bin_width, wl.scale_idx,
+                              wl.scale_attn, wl.window, wl.sinks, batches=[1, 2])
+    for (b, h), r in orc.items():
+        assert max_err(out[b, h], r.out) <= 2e-3, (b, h)
+
+
+@pytest.mark.parametrize("name", ["c1", "c4"])
+def test_decode_step_fused_append_config(rtp, name):
+    """The bench's `--with-append` step: the update fused into the step at 64K and 1M
+    context (inputs that reproduce the workload's own last row and q_idx, so the selection
+    stays the planted one); the oracle runs its own update and its own decode."""
+    say("fused append + decode", name)
+    wl = workloads.make_config(name, device=dev())
+    lay = wl.layers[0]
+    si = workloads.make_embedding_step_inputs(wl, device=dev())
+    want = oracle.append_project(lay, wl.seq_lens, si.q_pre, si.k_pre, si.k_new, si.v_new, si.Wq,
+                                 si.Wk, wl.window, wl.sinks)
+    olay = _oracle_layer(lay, want)
+    check_decode(rtp, wl, label="fused-append-" + name, oracle_layers=[olay], appends=[si])
+    assert np.array_equal(_bits(oracle.np_of(lay.k_idx)), _bits(want[1]))
+    assert np.array_equal(_bits(oracle.np_of(lay.q_idx)), _bits(want[0]))
+    n = int(wl.seq_lens[0]) - 1
+    assert np.array_equal(_bits(oracle.np_of(lay.K_ret[:, :, n])), _bits(want[2][:, :, n]))
+    assert np.array_equal(_bits(oracle.np_of(lay.K_loc)), _bits(want[4]))
+    assert np.array_equal(_bits(oracle.np_of(lay.V_loc)), _bits(want[5]))
 
 
 @pytest.mark.parametrize("dtype", ["f16", "f32"])
