@@ -45,6 +45,31 @@ def _compile(srcs, out, verbose):
     return out
 
 
+# the host code (argument checks, size queries, status strings) under AddressSanitizer and
+# UndefinedBehaviorSanitizer, for CPU tests that launch no kernel; the device code is built
+# plainly (every flag below that names a sanitizer applies to the host pass alone)
+SANITIZE_FLAGS = [
+    "--offload-arch=gfx950", "-O1", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Xarch_host", "-g",
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+]
+
+
+def build_host_sanitized(out: str) -> str:
+    """Build the host side of librtp.so with ASan and UBSan into `out` (CPU tests only)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ([HIPCC] + SANITIZE_FLAGS + ["-I", os.path.join(HERE, "..", "include"), "-o", tmp] +
+           [os.path.join(CSRC, s) for s in SOURCES])
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stderr)
+        raise RuntimeError("hipcc failed building the sanitized host library")
+    os.replace(tmp, out)
+    return out
+
+
 def build(verbose: bool = False) -> str:
     """Build librtp.so and the benchmark's libhbmread.so; returns librtp.so's path."""
     _compile([os.path.join(CSRC, s) for s in SOURCES], LIB, verbose)

@@ -34,6 +34,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "rtp_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# a build of the same source to load instead (the sanitizer test's instrumented copy)
+_LIB_OVERRIDE = os.environ.get("RTP_ORACLE_LIBRARY")
 NBINS = 256
 
 _lib = None
@@ -49,11 +51,24 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+def build_sanitized(out: str) -> str:
+    """The same source under AddressSanitizer and UndefinedBehaviorSanitizer (for a child
+    process that preloads libasan and names `out` in RTP_ORACLE_LIBRARY)."""
+    subprocess.check_call(["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-ffp-contract=off",
+                           "-fno-fast-math", "-fPIC", "-shared", "-std=c99",
+                           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                           "-o", out, _SRC, "-lm"])
+    return out
+
+
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            build()
+            L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         L.rtpo_half_to_double.restype = ctypes.c_double
         L.rtpo_half_to_double.argtypes = [ctypes.c_uint16]
