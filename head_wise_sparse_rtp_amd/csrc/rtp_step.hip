@@ -314,6 +314,9 @@ __device__ __forceinline__ void hist_fetch(const StageAParams& P, const HistUnit
         in.x[s] = reinterpret_cast<const float2*>(P.q_pre + ((size_t)u.b * P.Hq + qh) * kD)[lane];
       }
     }
+    // every wavefront's matrix loads enter the CU's memory pipeline ahead of the block's
+    // key loads (an execution barrier only: no load is waited for)
+    __builtin_amdgcn_s_barrier();
   } else {
     const float4* qp = reinterpret_cast<const float4*>(
         P.q_idx + ((size_t)u.b * P.Hq + (size_t)P.ret.kv[u.kr] * P.G + u.grp * 8 + min(hh, u.nrows - 1)) * kR +
