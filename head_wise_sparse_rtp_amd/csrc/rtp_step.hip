@@ -1199,8 +1199,10 @@ __global__ __launch_bounds__(kBThreads, 2) void k_stage_b(StageBParams P) {
   else if ((int)blockIdx.x < P.nrw_end)
     ret_window_block<T>(P, blockIdx.x - P.nret_blocks, reinterpret_cast<float*>(smem));
   else
+    // local window blocks wait behind the selection blocks' first loads, unless the
+    // retrieval heads' own window blocks already sit between them (measured slower then)
     window_block<T>(P.win, blockIdx.x - P.nrw_end, reinterpret_cast<float*>(smem),
-                    P.nret_blocks > 0);
+                    P.nret_blocks > 0 && P.nrw_end == P.nret_blocks);
 }
 
 // ---------------------------------------------------------------------------
