@@ -59,6 +59,27 @@ __device__ __forceinline__ int clamp_len(const int32_t* seq_lens, int b, int Lma
   return L < 0 ? 0 : (L > Lmax ? Lmax : L);
 }
 
+// Brings every 64-byte line of a kernel's argument block into the scalar cache at once: one
+// scalar load per line, all in flight together, waited for here.  The fields read later then
+// hit the cache instead of paying a round trip for each line they first touch (a block's
+// early fields span several lines, and some are indexed by values read from the first).
+template <class Params>
+__device__ __forceinline__ void fetch_args(const Params& P) {
+  constexpr int kLines = (int)((sizeof(Params) + 63) / 64);
+  const int32_t* w = reinterpret_cast<const int32_t*>(&P);
+  int32_t acc = 0;
+#pragma unroll
+  for (int i = 0; i < kLines; i++) acc ^= w[16 * i];
+  asm volatile("" ::"s"(acc));
+}
+// The same for the given lines only (a kernel whose first loads need few of them).
+template <int... LINES, class Params>
+__device__ __forceinline__ void fetch_arg_lines(const Params& P) {
+  const int32_t* w = reinterpret_cast<const int32_t*>(&P);
+  const int32_t acc = (w[16 * LINES] ^ ...);
+  asm volatile("" ::"s"(acc));
+}
+
 // ---------------------------------------------------------------------------
 // wavefront scans and reductions on DPP lane moves (no LDS round trip)
 // ---------------------------------------------------------------------------
@@ -696,6 +717,9 @@ __device__ void hist_block(const StageAParams& P, const HistUnit& U, HistIn<T>& 
 template <int NT, typename T, bool APP>
 __global__ __launch_bounds__(NT, NT >= 512 ? 2 : 4) void k_stage_a(StageAParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
+  // the first argument line and the line of the retrieval heads' KV map, which the q_idx
+  // address reads
+  fetch_arg_lines<0, (int)(offsetof(StageAParams, ret) / 64)>(P);
   const HistUnit U = hist_unit<NT>(P);
   HistIn<T> in;
   hist_fetch<NT, T, APP>(P, U, in);
@@ -809,6 +833,7 @@ struct StageTParams {
 // load is unconditional (indices clamped into the row) so that none waits on another.
 template <int PPT>
 __global__ __launch_bounds__(kThreads) void k_stage_t(StageTParams P) {
+  fetch_args(P);
   __shared__ __align__(16) float sb[4 * PPT * kNB];  // the block's chunk suffix rows
   constexpr int NCA = 4 * PPT < 8 ? 8 : 4 * PPT;
   __shared__ __align__(16) int sAc[NCA];  // top cells of the block's chunks (kEmptyCell past nc)
@@ -1194,6 +1219,7 @@ __device__ void ret_window_block(const StageBParams& P, int wb, float* lds) {
 template <int NWD, int GMAX, typename T>
 __global__ __launch_bounds__(kBThreads, 2) void k_stage_b(StageBParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
+  fetch_args(P);
   if ((int)blockIdx.x < P.nret_blocks)
     select_attend_block<NWD, GMAX, T>(P, smem);
   else if ((int)blockIdx.x < P.nrw_end)
@@ -1367,6 +1393,7 @@ __device__ __forceinline__ void merge_slice(const float* __restrict__ pm, const 
 
 __global__ __launch_bounds__(kThreads) void k_stage_m(StageMParams P) {
   extern __shared__ __align__(16) float mlds[];
+  fetch_args(P);
   const int G = P.G;
   const int slice = blockIdx.x % kMSlices;
   const int hb = blockIdx.x / kMSlices;
