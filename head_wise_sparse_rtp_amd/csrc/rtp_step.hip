@@ -718,8 +718,11 @@ template <int NT, typename T, bool APP>
 __global__ __launch_bounds__(NT, NT >= 512 ? 2 : 4) void k_stage_a(StageAParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   // the first argument line and the line of the retrieval heads' KV map, which the q_idx
-  // address reads
-  fetch_arg_lines<0, (int)(offsetof(StageAParams, ret) / 64)>(P);
+  // address reads (and with the fused cache update, the line of its input addresses)
+  if constexpr (APP)  // the cache update's inputs too
+    fetch_arg_lines<0, (int)(offsetof(StageAParams, q_pre) / 64), (int)(offsetof(StageAParams, ret) / 64)>(P);
+  else
+    fetch_arg_lines<0, (int)(offsetof(StageAParams, ret) / 64)>(P);
   const HistUnit U = hist_unit<NT>(P);
   HistIn<T> in;
   hist_fetch<NT, T, APP>(P, U, in);
@@ -1226,9 +1229,11 @@ __global__ __launch_bounds__(kBThreads, 2) void k_stage_b(StageBParams P) {
     ret_window_block<T>(P, blockIdx.x - P.nret_blocks, reinterpret_cast<float*>(smem));
   else
     // local window blocks wait behind the selection blocks' first loads, unless the
-    // retrieval heads' own window blocks already sit between them (measured slower then)
+    // retrieval heads' own window blocks already sit between them, or the window blocks
+    // are heavy enough (over 256 rows each) that their K/V traffic is the launch's bulk
+    // (both measured slower with the wait)
     window_block<T>(P.win, blockIdx.x - P.nrw_end, reinterpret_cast<float*>(smem),
-                    P.nret_blocks > 0 && P.nrw_end == P.nret_blocks);
+                    P.nret_blocks > 0 && P.nrw_end == P.nret_blocks && P.win.wrows <= 256);
 }
 
 // ---------------------------------------------------------------------------
