@@ -520,11 +520,11 @@ def test_decode_step_fused_append_empty_sequence(rtp):
         assert max_err(out[b, h], r.out) <= 2e-3, (b, h)
 
 
-@pytest.mark.parametrize("name", ["c1", "c4"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c4"])
 def test_decode_step_fused_append_config(rtp, name):
-    """The bench's `--with-append` step: the update fused into the step at 64K and 1M
-    context (inputs that reproduce the workload's own last row and q_idx, so the selection
-    stays the planted one); the oracle runs its own update and its own decode."""
+    """The bench's `--with-append` step: the update fused into the step at 64K, 8 x 128K
+    and 1M context (inputs that reproduce the workload's own last row and q_idx, so the
+    selection stays the planted one); the oracle runs its own update and its own decode."""
     say("fused append + decode", name)
     wl = workloads.make_config(name, device=dev())
     lay = wl.layers[0]
@@ -535,8 +535,11 @@ def test_decode_step_fused_append_config(rtp, name):
     check_decode(rtp, wl, label="fused-append-" + name, oracle_layers=[olay], appends=[si])
     assert np.array_equal(_bits(oracle.np_of(lay.k_idx)), _bits(want[1]))
     assert np.array_equal(_bits(oracle.np_of(lay.q_idx)), _bits(want[0]))
-    n = int(wl.seq_lens[0]) - 1
-    assert np.array_equal(_bits(oracle.np_of(lay.K_ret[:, :, n])), _bits(want[2][:, :, n]))
+    for b in range(wl.B):  # the new token's retrieval K/V rows of every sequence
+        n = int(wl.seq_lens[b]) - 1
+        if n >= 0:
+            assert np.array_equal(_bits(oracle.np_of(lay.K_ret[b, :, n])), _bits(want[2][b, :, n]))
+            assert np.array_equal(_bits(oracle.np_of(lay.V_ret[b, :, n])), _bits(want[3][b, :, n]))
     assert np.array_equal(_bits(oracle.np_of(lay.K_loc)), _bits(want[4]))
     assert np.array_equal(_bits(oracle.np_of(lay.V_loc)), _bits(want[5]))
 
