@@ -498,6 +498,26 @@ def test_decode_step_fused_append_small_ragged(rtp, dtype, mask, ret_window):
     _check_caches(lay, want, label)
 
 
+@pytest.mark.parametrize("Hq,Hkv,mask", [(32, 2, [1, 0]), (12, 4, [1, 0, 0, 1]), (10, 2, [1, 1]),
+                                          (4, 4, [1, 0, 1, 1])])
+def test_decode_step_fused_append_heads_per_kv(rtp, Hq, Hkv, mask):
+    """The fused update with 16, 3, 5 and 1 query heads per KV head: two head groups per
+    retrieval KV head (16), and groups whose chains leave lanes idle (3, 5, 1).  Every
+    cache bit-exact, then the step's parity."""
+    lens = [4099, 1, 2049, 300]
+    label = "fused-append-G%d-%s" % (Hq // Hkv, "".join(map(str, mask)))
+    say(label, lens)
+    wl = workloads.make_workload("t", len(lens), lens, Hq, Hkv, [mask], seed=91, window=64,
+                                 sinks=4, device=dev(), Lmax=4099)
+    lay = wl.layers[0]
+    si = workloads.make_step_inputs(wl, seed=5, device=dev())
+    want = oracle.append_project(lay, lens, si.q_pre, si.k_pre, si.k_new, si.v_new, si.Wq, si.Wk,
+                                 wl.window, wl.sinks)
+    olay = _oracle_layer(lay, want)
+    check_decode(rtp, wl, label=label, oracle_layers=[olay], appends=[si])
+    _check_caches(lay, want, label)
+
+
 def test_decode_step_fused_append_empty_sequence(rtp):
     """A sequence of length 0 takes no update and yields zeros; the others are updated."""
     lens = [0, 3000, 1]
