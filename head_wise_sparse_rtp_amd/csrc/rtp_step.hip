@@ -1222,7 +1222,13 @@ __device__ void ret_window_block(const StageBParams& P, int wb, float* lds) {
 template <int NWD, int GMAX, typename T>
 __global__ __launch_bounds__(kBThreads, 2) void k_stage_b(StageBParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
-  fetch_args(P);
+  // the lines of the fields every block type reads, the window parameters with the first
+  // local heads' map entries, and the first retrieval heads' map entries (not the maps'
+  // tails: waiting for them too measured slower)
+  constexpr int kLocLine = (int)((offsetof(StageBParams, win) + offsetof(WinParams, loc)) / 64);
+  constexpr int kRetLine = (int)(offsetof(StageBParams, ret) / 64);
+  static_assert(kLocLine == 4 && kRetLine == 8, "argument layout");
+  fetch_arg_lines<0, 1, 2, 3, kLocLine, kRetLine>(P);
   if ((int)blockIdx.x < P.nret_blocks)
     select_attend_block<NWD, GMAX, T>(P, smem);
   else if ((int)blockIdx.x < P.nrw_end)
