@@ -1404,7 +1404,12 @@ __device__ __forceinline__ void merge_slice(const float* __restrict__ pm, const 
 
 __global__ __launch_bounds__(kThreads) void k_stage_m(StageMParams P) {
   extern __shared__ __align__(16) float mlds[];
-  fetch_args(P);
+  // the fields' lines (the last one also holds the retrieval heads' map entries) and the
+  // first local heads' map entries (not the maps' tails)
+  constexpr int kRetLine = (int)((offsetof(StageMParams, ret) + offsetof(HeadMap, kv)) / 64);
+  constexpr int kLocLine = (int)((offsetof(StageMParams, loc) + offsetof(HeadMap, kv)) / 64);
+  static_assert(kRetLine == 2 && kLocLine == 6, "argument layout");
+  fetch_arg_lines<0, 1, kRetLine, kLocLine>(P);
   const int G = P.G;
   const int slice = blockIdx.x % kMSlices;
   const int hb = blockIdx.x / kMSlices;
