@@ -220,9 +220,12 @@ typedef struct rtp_step_append {
 /* fp16 and bf16 caches with G <= 16 run four kernels per call: indexer score + chunk
  * histograms; per-head suffix tables of the bin masses (token counts under top-k);
  * selection + sparse attention together with the window attention of local heads; merge of
- * the split partials (plus a fifth that writes the exported sets, when asked for).  Other
- * shapes (fp32 caches, G > 16) run the single-purpose kernels in sequence.  The workspace
- * needs no initialisation; calls that may overlap must not share one. */
+ * the split partials (plus a fifth that writes the exported sets, when asked for).  With
+ * desc->append, the first kernel also does the cache update (layers without retrieval
+ * heads run rtp_append_project's kernel first).  Other shapes (fp32 caches, G > 16) run
+ * the single-purpose kernels in sequence, after rtp_append_project's kernel when desc->append
+ * is given.  The workspace needs no initialisation; calls that may overlap must not share
+ * one. */
 size_t rtp_decode_step_workspace_size(const rtp_layer_desc* desc);
 rtp_status rtp_decode_step(const rtp_layer_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
