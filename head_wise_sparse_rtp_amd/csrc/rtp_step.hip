@@ -348,7 +348,10 @@ __device__ __forceinline__ void hist_fetch(const StageAParams& P, const HistUnit
 #pragma unroll
   for (int gi = 0; gi < 8; gi++) {
     const int n = min(wbase + gi * 32 + (lane & 15) + 16 * (kq >> 1), nlast);
-    in.ka[gi] = *reinterpret_cast<const v8<T>*>(kb + (size_t)n * kR + 8 * (kq & 1));
+    // streamed once: nontemporal, so that the stream does not displace the lines the
+    // rest of the step reads back (measured 0.8-2 us per step faster; the gathered K/V
+    // rows, code words, suffix rows and partials measured no better or slower that way)
+    in.ka[gi] = __builtin_nontemporal_load(reinterpret_cast<const v8<T>*>(kb + (size_t)n * kR + 8 * (kq & 1)));
   }
 }
 
