@@ -89,8 +89,9 @@ struct StepLoads {
   v8<T> v[8];     // [u]: V row of k-slot u (u<4: tile0 row 4gq+u; else tile1 row 4gq+u-4)
 };
 
-// rows[i] for i in 0..31 supplied through `row_of(i)` (already clamped to a valid row)
-template <typename T, class RowOf>
+// rows[i] for i in 0..31 supplied through `row_of(i)` (already clamped to a valid row);
+// NTL: nontemporal loads (rows that nothing reads again soon)
+template <bool NTL = false, typename T, class RowOf>
 __device__ __forceinline__ void step_load(const T* __restrict__ Kb, const T* __restrict__ Vb,
                                           RowOf row_of, StepLoads<T>& ld) {
   const int lane = threadIdx.x & 63;
@@ -101,13 +102,14 @@ __device__ __forceinline__ void step_load(const T* __restrict__ Kb, const T* __r
     const int r = row_of(t * 16 + c);
     const v8<T>* p = reinterpret_cast<const v8<T>*>(Kb + (size_t)r * kD + 8 * gq);
 #pragma unroll
-    for (int s = 0; s < 4; s++) ld.k[t][s] = p[4 * s];
+    for (int s = 0; s < 4; s++) ld.k[t][s] = NTL ? __builtin_nontemporal_load(p + 4 * s) : p[4 * s];
   }
 #pragma unroll
   for (int u = 0; u < 8; u++) {
     const int i = (u < 4) ? (4 * gq + u) : (16 + 4 * gq + (u - 4));
     const int r = row_of(i);
-    ld.v[u] = *reinterpret_cast<const v8<T>*>(Vb + (size_t)r * kD + 8 * c);
+    const v8<T>* pv = reinterpret_cast<const v8<T>*>(Vb + (size_t)r * kD + 8 * c);
+    ld.v[u] = NTL ? __builtin_nontemporal_load(pv) : *pv;
   }
 }
 
