@@ -108,9 +108,10 @@ HBM_READ_LIB = os.path.join(ROOT, "head_wise_sparse_rtp_amd", "libhbmread.so")
 
 
 def hbm_read_ceiling(torch, gib=4, reps=8):
-    """Streaming-read ceiling of this GPU's HBM: the hand-written read kernel of
-    libhbmread.so (16-byte loads, 4 or 8 in flight per thread, plain or nontemporal) over a
-    `gib` GiB buffer, the best of a few grid sizes; GB/s."""
+    """Streaming-read ceiling of this GPU's HBM: the hand-written read kernels of
+    libhbmread.so (16-byte loads in grid-stride or per-block span order, 4 to 16 in flight
+    per thread, plain or nontemporal) over a `gib` GiB buffer, the best of a few grid sizes;
+    GB/s."""
     lib = ctypes.CDLL(HBM_READ_LIB)
     lib.hbm_read.restype = ctypes.c_int
     lib.hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
@@ -118,13 +119,13 @@ def hbm_read_ceiling(torch, gib=4, reps=8):
     dev = torch.device("cuda:0")
     nbytes = gib << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
-    grids = (1024, 2048, 4096, 8192)
+    grids = (256, 512, 1024, 2048, 4096, 8192, 16384)
     sink = torch.empty(max(grids) * 256, dtype=torch.int32, device=dev)
     st = torch.cuda.current_stream()
     sp = ctypes.c_void_p(st.cuda_stream)
     best = (0.0, None)
     for blocks in grids:
-        for var in range(4):
+        for var in range(8):
             def run():
                 rc = lib.hbm_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
                                   ctypes.c_void_p(sink.data_ptr()), blocks, var, sp)
@@ -139,8 +140,9 @@ def hbm_read_ceiling(torch, gib=4, reps=8):
             e1.synchronize()
             gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
             if gbs > best[0]:
-                best = (gbs, {"blocks": blocks, "loads_in_flight": 4 if var % 2 == 0 else 8,
-                              "nontemporal": var >= 2})
+                best = (gbs, {"blocks": blocks, "order": "span" if var >= 4 else "grid-stride",
+                              "loads_in_flight": (4, 8, 8, 16)[var // 4 * 2 + var % 2],
+                              "nontemporal": var % 4 >= 2})
     del buf, sink
     torch.cuda.synchronize()
     return {"value": round(best[0], 1), "unit": "GB/s", "bytes": nbytes,

@@ -735,8 +735,17 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 2 : 4) void k_stage_a(StageAParams 
 // Masked attention over the entries e = 0..n-1 of a row list: row_of(e) is the cache
 // row, mask_of(e) the heads that take part (bit h).  The list is cut into 32-row steps;
 // this block takes steps part, part + nparts, ... and its wavefront wv of NWV every NWV-th
-// of those, two steps' loads in flight before either is used.
-template <int NWV, typename T, bool NTL = false, class RowOf, class MaskOf>
+// of those, in that order, with two steps' loads in flight.
+//  - Default: steps in pairs, both loads issued before either step is computed.  The
+//    second load sits behind a branch, so the wait before the first step's products must
+//    also hold on the path that skipped it: the first step waits for both.
+//  - ROLL (long lists): two buffers roll.  As soon as a step is computed, its buffer is
+//    refilled with the step after next, and no load sits behind a branch of its own, so
+//    the wait before a step's first use counts exactly the other buffer's younger loads.
+//    A refill past the end reloads entry 0's row (cached) and is not used.  On lists of
+//    one or two steps per wavefront the extra refills cost more than the overlap gains.
+// NTL: nontemporal K/V loads.  The step order, and so the result, is the same either way.
+template <int NWV, typename T, bool NTL = false, bool ROLL = false, class RowOf, class MaskOf>
 __device__ __forceinline__ void attend_list(const T* __restrict__ Kb, const T* __restrict__ Vb,
                                             int n, RowOf row_of, MaskOf mask_of,
                                             const v8<T> (&qop)[4], float scale2, AttnState& st,
@@ -744,19 +753,40 @@ __device__ __forceinline__ void attend_list(const T* __restrict__ Kb, const T* _
   const int wv = threadIdx.x >> 6;
   const int nsteps = (n + kStep - 1) / kStep;
   const int stride = nparts * NWV;
-  for (int s0 = part + nparts * wv; s0 < nsteps; s0 += 2 * stride) {
-    const int s1 = s0 + stride;
-    const int e0 = s0 * kStep, e1 = s1 * kStep;
-    StepLoads<T> ld0, ld1;
-    step_load<NTL>(Kb, Vb, [&](int i) { return row_of(e0 + i < n ? e0 + i : 0); }, ld0);
-    if (s1 < nsteps) step_load<NTL>(Kb, Vb, [&](int i) { return row_of(e1 + i < n ? e1 + i : 0); }, ld1);
-    step_compute(ld0, qop, scale2,
+  auto load = [&](int s, StepLoads<T>& ld) {
+    const int e0 = s * kStep;
+    step_load<NTL>(Kb, Vb, [&](int i) { return row_of(e0 + i < n ? e0 + i : 0); }, ld);
+  };
+  auto compute = [&](int s, const StepLoads<T>& ld) {
+    const int e0 = s * kStep;
+    step_compute(ld, qop, scale2,
                  [&](int i, int h) { return e0 + i < n && ((mask_of(e0 + i < n ? e0 + i : 0) >> h) & 1u); },
                  st);
-    if (s1 < nsteps)
-      step_compute(ld1, qop, scale2,
-                   [&](int i, int h) { return e1 + i < n && ((mask_of(e1 + i < n ? e1 + i : 0) >> h) & 1u); },
-                   st);
+  };
+  int s = part + nparts * wv;
+  if constexpr (!ROLL) {
+    for (; s < nsteps; s += 2 * stride) {
+      StepLoads<T> ld0, ld1;
+      load(s, ld0);
+      if (s + stride < nsteps) load(s + stride, ld1);
+      compute(s, ld0);
+      if (s + stride < nsteps) compute(s + stride, ld1);
+    }
+  } else {
+    if (s >= nsteps) return;
+    StepLoads<T> ld0, ld1;
+    load(s, ld0);
+    load(s + stride, ld1);
+    for (;;) {
+      compute(s, ld0);
+      load(s + 2 * stride, ld0);
+      s += stride;
+      if (s >= nsteps) break;
+      compute(s, ld1);
+      load(s + 2 * stride, ld1);
+      s += stride;
+      if (s >= nsteps) break;
+    }
   }
 }
 
@@ -769,7 +799,7 @@ __device__ __forceinline__ void attend_list(const T* __restrict__ Kb, const T* _
 // block first waits about 2 us, so that its bulk K/V traffic lands while the selection
 // blocks work on the VALU instead of ahead of their first loads (it still ends well before
 // them).
-template <typename T>
+template <typename T, bool HEAVY>
 __device__ void window_block(const WinParams& P, int wb, float* lds, bool delay) {
   if (delay) __builtin_amdgcn_s_sleep(72);  // 72 x 64 cycles: about 1.9 us at 2.4 GHz
   const int wsplit = wb % P.nws;
@@ -802,10 +832,11 @@ __device__ void window_block(const WinParams& P, int wb, float* lds, bool delay)
     return sinks + v;
   };
   auto all_heads = [&](int) { return 0xFFFFu; };
-  // heavy window blocks (over 256 rows: their rows are the launch's bulk) read them
-  // nontemporally; light ones do not (measured: C2 61.0 -> 59.2 us, C4 29.5 -> 30.2 us)
-  if (P.wrows > 256)
-    attend_list<kBWaves, T, true>(Kb, Vb, n, slot_of, all_heads, qop, P.scale2, st);
+  // heavy window blocks (HEAVY: over 256 rows, so their rows are the launch's bulk and a
+  // wavefront has 8 or more steps) read them nontemporally through the rolling loop; light
+  // ones do neither (measured: nontemporal C2 61.0 -> 59.2 us but C4 29.5 -> 30.2 us)
+  if constexpr (HEAVY)
+    attend_list<kBWaves, T, true, true>(Kb, Vb, n, slot_of, all_heads, qop, P.scale2, st);
   else
     attend_list<kBWaves>(Kb, Vb, n, slot_of, all_heads, qop, P.scale2, st);
   const size_t prow = ((size_t)(b * P.Hloc + kl) * P.nws + wsplit) * G;
@@ -1226,7 +1257,11 @@ __device__ void ret_window_block(const StageBParams& P, int wb, float* lds) {
   if ((int)threadIdx.x < G) P.p1cnt[prow + threadIdx.x] = n;
 }
 
-template <int NWD, int GMAX, typename T>
+// HEAVY: the local window blocks have over 256 rows each (chosen on the host from
+// win.wrows).  It is a template argument so that the kernels with light window blocks
+// carry none of the heavy blocks' code: with it present but unused, the selection blocks
+// measured slower (C4 +0.7 us, 16M tokens +3.8 us).
+template <int NWD, int GMAX, typename T, bool HEAVY>
 __global__ __launch_bounds__(kBThreads, 2) void k_stage_b(StageBParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   // the lines of the fields every block type reads, the window parameters with the first
@@ -1245,8 +1280,17 @@ __global__ __launch_bounds__(kBThreads, 2) void k_stage_b(StageBParams P) {
     // retrieval heads' own window blocks already sit between them, or the window blocks
     // are heavy enough (over 256 rows each) that their K/V traffic is the launch's bulk
     // (both measured slower with the wait)
-    window_block<T>(P.win, blockIdx.x - P.nrw_end, reinterpret_cast<float*>(smem),
-                    P.nret_blocks > 0 && P.nrw_end == P.nret_blocks && P.win.wrows <= 256);
+    window_block<T, HEAVY>(P.win, blockIdx.x - P.nrw_end, reinterpret_cast<float*>(smem),
+                           !HEAVY && P.nret_blocks > 0 && P.nrw_end == P.nret_blocks);
+}
+
+template <bool HEAVY>
+void (*stage_b_kernel(int nwd, int G, bool bf))(StageBParams) {
+  if (G <= 8)
+    return nwd == 2 ? (bf ? &k_stage_b<2, 8, bf16e, HEAVY> : &k_stage_b<2, 8, f16, HEAVY>)
+                    : (bf ? &k_stage_b<4, 8, bf16e, HEAVY> : &k_stage_b<4, 8, f16, HEAVY>);
+  return nwd == 2 ? (bf ? &k_stage_b<2, 16, bf16e, HEAVY> : &k_stage_b<2, 16, f16, HEAVY>)
+                  : (bf ? &k_stage_b<4, 16, bf16e, HEAVY> : &k_stage_b<4, 16, f16, HEAVY>);
 }
 
 // ---------------------------------------------------------------------------
@@ -1860,14 +1904,10 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
                                        sizeof(uint32_t) * (size_t)(sp.Hret > 0 ? sp.tb : 0));
   const int nB = Q.nret_blocks + nrw_blocks + nwin_blocks;
   {
-    void (*fb)(StageBParams) = nullptr;
     const bool bf = a.kv_dtype == 2;
-    if (G <= 8)
-      fb = sp.nwd == 2 ? (bf ? &k_stage_b<2, 8, bf16e> : &k_stage_b<2, 8, f16>)
-                       : (bf ? &k_stage_b<4, 8, bf16e> : &k_stage_b<4, 8, f16>);
-    else
-      fb = sp.nwd == 2 ? (bf ? &k_stage_b<2, 16, bf16e> : &k_stage_b<2, 16, f16>)
-                       : (bf ? &k_stage_b<4, 16, bf16e> : &k_stage_b<4, 16, f16>);
+    void (*fb)(StageBParams) = nwin_blocks > 0 && sp.wrows > 256
+                                   ? stage_b_kernel<true>(sp.nwd, G, bf)
+                                   : stage_b_kernel<false>(sp.nwd, G, bf);
     e = launch1(fb, dim3(nB), dim3(kBThreads), ldsB, st, Q, eb0, eb1);
     if (e != hipSuccess) return e;
   }
