@@ -209,6 +209,10 @@ __host__ __device__ constexpr int stage_a_qsh(int nt) {
 __host__ __device__ constexpr int stage_a_lds(int nt, bool app) {
   return app ? stage_a_qsh(nt) + (int)sizeof(float) * 9 * kR : stage_a_base_lds(nt);
 }
+// an LDS request above a third of a CU's 160 KB: at most two stage-A blocks per CU
+constexpr size_t kStageALds2PerCu = 56 * 1024;
+static_assert(3 * kStageALds2PerCu > 160 * 1024 && 2 * kStageALds2PerCu <= 160 * 1024, "two blocks per CU");
+static_assert(stage_a_lds(512, true) <= (int)kStageALds2PerCu, "the floor only raises the request");
 // y of a token past the sequence's end: finite and far below every cell, so that its
 // mass is exactly zero and it lands in the tail bin (with unit weights it is taken back
 // out of that bin after the pass)
@@ -1796,8 +1800,14 @@ hipError_t launch_step_fused(const StepFusedPlan& sp, char* ws, const StepFusedA
       P.sinks = a.sinks;
       P.loc = a.loc;
     }
-    const size_t ldsA = (size_t)stage_a_lds(sp.nt, app);
     const dim3 gA(sp.nchunk, P.ngg, B * sp.Hret);
+    // 512-thread blocks take 48-49 KB of LDS, so three fit a CU's 160 KB.  On grids of 16 or
+    // more blocks per CU (8M tokens and up at one retrieval head) two per CU stream the keys
+    // faster: the LDS request is raised past a third of the CU's (8M 133.2 -> 129.0 us,
+    // 16M 258.8 -> 244.9 us per step; at 4M, 8 blocks per CU, three per CU stay 0.5 us ahead)
+    size_t ldsA = (size_t)stage_a_lds(sp.nt, app);
+    if (sp.nt == 512 && (int64_t)gA.x * gA.y * gA.z >= 16 * (int64_t)sp.ncu)
+      ldsA = std::max<size_t>(ldsA, kStageALds2PerCu);
     const bool bf = a.kv_dtype == 2;
     void (*fa)(StageAParams) = nullptr;
     if (sp.nt == 256)
