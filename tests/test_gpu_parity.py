@@ -635,6 +635,39 @@ def test_decode_step_empty_sequence(rtp):
     assert np.all(np.isfinite(out[1]))
 
 
+HEAVY_WINDOW_LENS = [9000, 1, 700, 5000, 8196, 8197, 20000, 8200]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_decode_step_heavy_window_ragged(rtp, dtype):
+    """Eight sequences with three local heads each: their 8196-row rings need more window
+    blocks than the launch holds beside the selection blocks at 256 rows, so every window
+    block takes 512 rows and the step runs the heavy-window kernel (nontemporal rows through
+    the rolling two-buffer loop).  The ragged lengths leave blocks with a full list, a
+    partial list (700 rows: one block of 512, one of 188), a single row, and none."""
+    say("decode_step heavy windows", dtype)
+    wl = workloads.make_workload("t", 8, HEAVY_WINDOW_LENS, 32, 4, [[1, 0, 0, 0]], seed=65,
+                                 p=0.9, dtype=dtype, window=8192, sinks=4, device=dev())
+    check_decode(rtp, wl, label="heavy-window-%s" % dtype)
+
+
+def test_decode_step_heavy_window_empty_sequence(rtp):
+    """The heavy-window kernel with an empty sequence in the batch: its heads come out zero
+    with lse = -inf, and the other sequences still match the oracle."""
+    say("decode_step heavy windows, empty sequence")
+    lens = [0] + HEAVY_WINDOW_LENS[1:]
+    wl = workloads.make_workload("t", 8, lens, 32, 4, [[1, 0, 0, 0]], seed=66, p=0.9,
+                                 dtype="f16", window=8192, sinks=4, device=dev())
+    out, lse, thr, cnt = (t.cpu().numpy() for t in rtp.decode_workload(wl, want_debug=True)[0][:4])
+    assert np.all(out[0] == 0) and np.all(lse[0] == -np.inf) and np.all(cnt[0] == 0)
+    orc = oracle.decode_layer(wl.layers[0], wl.seq_lens, wl.Hq, wl.Hkv, wl.p, wl.bin_width,
+                              wl.scale_idx, wl.scale_attn, wl.window, wl.sinks,
+                              heads=list(range(8, 32)), batches=range(1, 8))
+    for (b, h), r in orc.items():
+        e = max_err(out[b, h], r.out)
+        assert e <= out_tol("f16"), "b %d head %d: max |dO| = %g" % (b, h, e)
+
+
 def test_decode_step_deterministic(rtp):
     say("decode_step determinism")
     wl = workloads.make_workload("t", 2, [20000, 9000], 32, 4, [[1, 0, 0, 1]], seed=64, p=0.9,
