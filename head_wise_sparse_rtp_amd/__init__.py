@@ -290,7 +290,8 @@ class DecodeStep:
     """Holds the descriptor, host mask and workspace of one layer so that repeated
     calls (a decode loop, a captured graph) only enqueue kernels.  want_sets > 0 also
     exports the token set each retrieval query head attended to (sel_idx [B, Hq,
-    want_sets] ascending, -1 past the set; sel_count [B, Hq])."""
+    want_sets]: the first sel_count entries ascending, the rest left as they were, -1
+    after construction; sel_count [B, Hq])."""
 
     def __init__(self, layer, seq_lens: torch.Tensor, B: int, Hq: int, Hkv: int, Lmax: int,
                  window: int, sinks: int, p: float, bin_width: float, scale_idx: float,
