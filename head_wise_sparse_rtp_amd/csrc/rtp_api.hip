@@ -37,6 +37,12 @@ HeadMap identity_map(int n) {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Rows of query heads over the batch (B x heads) are a launch's y or z grid dimension, or a
+// factor of its one-dimensional block count; 65535 bounds the former and keeps the latter
+// far inside an int.
+constexpr int64_t kMaxRows = 65535;
+bool rows_ok(int64_t B, int64_t heads) { return B * heads <= kMaxRows; }
+
 // --- shared size checks -------------------------------------------------------
 rtp_status check_common(int32_t B, int32_t G, int32_t Lmax) {
   if (B < 1 || Lmax < 1) return RTP_EINVAL;
@@ -105,6 +111,7 @@ rtp_status plan_step(const rtp_layer_desc* d, StepPlan& sp) {
   sp.G = d->Hq / d->Hkv;
   rtp_status s = check_common(d->B, sp.G, d->Lmax);
   if (s != RTP_OK) return s;
+  if (!rows_ok(d->B, d->Hq)) return RTP_EUNSUPPORTED;
   if (d->r != kR || d->d != kD || !dtype_ok(d->kv_dtype)) return RTP_EUNSUPPORTED;
   if (!d->kv_is_retrieval) return RTP_EINVAL;
   sp.ret.n = sp.loc.n = 0;
@@ -187,7 +194,7 @@ const char* rtp_status_string(rtp_status s) {
   switch (s) {
     case RTP_OK: return "RTP_OK: success";
     case RTP_EINVAL: return "RTP_EINVAL: invalid argument (null or misaligned pointer, bad size or parameter)";
-    case RTP_EUNSUPPORTED: return "RTP_EUNSUPPORTED: unsupported shape or dtype (r must be 16, d 128, G <= 64, Lmax <= 2^24)";
+    case RTP_EUNSUPPORTED: return "RTP_EUNSUPPORTED: unsupported shape or dtype (r must be 16, d 128, G <= 64, Lmax <= 2^24, B x query heads <= 65535)";
     case RTP_EWORKSPACE: return "RTP_EWORKSPACE: workspace smaller than the size query";
     case RTP_EHIP: return "RTP_EHIP: a HIP kernel launch failed";
     case RTP_ESCRATCH: return "RTP_ESCRATCH: the step needs more scratch than the library's fixed buffer holds (use rtp_decode_step with a workspace)";
@@ -203,7 +210,7 @@ rtp_status rtp_index_score(const float* q_idx, const void* k_idx, int32_t k_dtyp
   rtp_status s = check_common(B, G, Lmax);
   if (s != RTP_OK) return s;
   if (Hr < 1) return RTP_EINVAL;
-  if (r != kR || !dtype_ok(k_dtype)) return RTP_EUNSUPPORTED;
+  if (r != kR || !dtype_ok(k_dtype) || !rows_ok(B, (int64_t)Hr * G)) return RTP_EUNSUPPORTED;
   if (!ptr_ok(q_idx) || !ptr_ok(k_idx) || !ptr_ok(seq_lens) || !ptr_ok(z)) return RTP_EINVAL;
   if (!std::isfinite(scale_idx)) return RTP_EINVAL;
   return hip_status(launch_index_score(q_idx, k_idx, k_dtype, seq_lens, B, Hr, G, Lmax,
@@ -211,7 +218,7 @@ rtp_status rtp_index_score(const float* q_idx, const void* k_idx, int32_t k_dtyp
 }
 
 size_t rtp_topp_select_workspace_size(int32_t B, int32_t H, int32_t Lmax) {
-  if (B < 1 || H < 1 || Lmax < 1 || Lmax > (1 << 24)) return 0;
+  if (B < 1 || H < 1 || Lmax < 1 || Lmax > (1 << 24) || !rows_ok(B, H)) return 0;
   return plan_topp(B, H, Lmax, (int64_t)B * H).bytes;
 }
 
@@ -220,7 +227,7 @@ rtp_status rtp_topp_select(const float* z, const int32_t* seq_lens, int32_t B, i
                            int32_t* sel_count, int32_t cap, float* hist, int32_t* thresh,
                            void* ws, size_t ws_bytes, void* stream) {
   if (B < 1 || H < 1 || Lmax < 1 || cap < 0) return RTP_EINVAL;
-  if (Lmax > (1 << 24)) return RTP_EUNSUPPORTED;
+  if (Lmax > (1 << 24) || !rows_ok(B, H)) return RTP_EUNSUPPORTED;
   if (!(p > 0.0) || std::isnan(p)) return RTP_EINVAL;
   if (!pow2_width(bin_width)) return RTP_EINVAL;
   if (!ptr_ok(z) || !ptr_ok(seq_lens) || !ptr_ok(sel_count) || !ptr_ok(ws)) return RTP_EINVAL;
@@ -249,7 +256,7 @@ rtp_status rtp_topk_select(const float* z, const int32_t* seq_lens, int32_t B, i
                            int32_t* sel_count, int32_t cap, float* hist, int32_t* thresh,
                            void* ws, size_t ws_bytes, void* stream) {
   if (B < 1 || H < 1 || Lmax < 1 || cap < 0 || k < 1) return RTP_EINVAL;
-  if (Lmax > (1 << 24)) return RTP_EUNSUPPORTED;
+  if (Lmax > (1 << 24) || !rows_ok(B, H)) return RTP_EUNSUPPORTED;
   if (!pow2_width(bin_width)) return RTP_EINVAL;
   if (!ptr_ok(z) || !ptr_ok(seq_lens) || !ptr_ok(sel_count) || !ptr_ok(ws)) return RTP_EINVAL;
   if (cap > 0 && !ptr_ok(sel_idx)) return RTP_EINVAL;
@@ -269,7 +276,7 @@ rtp_status rtp_topk_select(const float* z, const int32_t* seq_lens, int32_t B, i
 }
 
 size_t rtp_sparse_decode_workspace_size(int32_t B, int32_t Hr, int32_t G, int32_t cap) {
-  if (B < 1 || Hr < 1 || G < 1 || cap < 0) return 0;
+  if (B < 1 || Hr < 1 || G < 1 || cap < 0 || !rows_ok(B, (int64_t)Hr * G)) return 0;
   return plan_parts(0, (size_t)B * Hr * G, sparse_maxs(cap)).bytes;
 }
 
@@ -281,7 +288,7 @@ rtp_status rtp_sparse_decode(const void* q, const void* K, const void* V, int32_
   rtp_status s = check_common(B, G, Lmax);
   if (s != RTP_OK) return s;
   if (Hr < 1 || cap < 0) return RTP_EINVAL;
-  if (Hr > kMaxHkv) return RTP_EUNSUPPORTED;
+  if (Hr > kMaxHkv || !rows_ok(B, (int64_t)Hr * G)) return RTP_EUNSUPPORTED;
   if (d != kD || !dtype_ok(kv_dtype)) return RTP_EUNSUPPORTED;
   if (!ptr_ok(q) || !ptr_ok(K) || !ptr_ok(V) || !ptr_ok(sel_count) || !ptr_ok(out) ||
       !ptr_ok(ws))
@@ -302,7 +309,7 @@ rtp_status rtp_sparse_decode(const void* q, const void* K, const void* V, int32_
 
 size_t rtp_window_decode_workspace_size(int32_t B, int32_t Hl, int32_t G, int32_t window,
                                         int32_t sinks) {
-  if (B < 1 || Hl < 1 || G < 1 || window < 1 || sinks < 0) return 0;
+  if (B < 1 || Hl < 1 || G < 1 || window < 1 || sinks < 0 || !rows_ok(B, (int64_t)Hl * G)) return 0;
   return plan_parts(0, (size_t)B * Hl * G, window_maxs(window, sinks)).bytes;
 }
 
@@ -311,7 +318,8 @@ rtp_status rtp_window_decode(const void* q, const void* K, const void* V, int32_
                              int32_t d, int32_t window, int32_t sinks, float scale_attn,
                              float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (B < 1 || Hl < 1 || window < 1 || sinks < 0) return RTP_EINVAL;
-  if (G < 1 || G > kMaxG || Hl > kMaxHkv || (int64_t)window + sinks > (1 << 24))
+  if (G < 1 || G > kMaxG || Hl > kMaxHkv || (int64_t)window + sinks > (1 << 24) ||
+      !rows_ok(B, (int64_t)Hl * G))
     return RTP_EUNSUPPORTED;
   if (d != kD || !dtype_ok(kv_dtype)) return RTP_EUNSUPPORTED;
   if (!ptr_ok(q) || !ptr_ok(K) || !ptr_ok(V) || !ptr_ok(seq_lens) || !ptr_ok(out) || !ptr_ok(ws))
@@ -334,7 +342,8 @@ rtp_status rtp_append_project(const rtp_append_desc* d, void* stream) {
   if (d->B < 1 || d->Lmax < 1 || d->Hkv < 1 || d->Hq < 1 || d->Hq % d->Hkv != 0)
     return RTP_EINVAL;
   const int G = d->Hq / d->Hkv;
-  if (G > kMaxG || d->Hkv > kMaxHkv || d->Lmax > (1 << 24)) return RTP_EUNSUPPORTED;
+  if (G > kMaxG || d->Hkv > kMaxHkv || d->Lmax > (1 << 24) || !rows_ok(d->B, d->Hq))
+    return RTP_EUNSUPPORTED;
   if (d->r != kR || d->d != kD || !dtype_ok(d->kv_dtype)) return RTP_EUNSUPPORTED;
   if (!d->kv_is_retrieval) return RTP_EINVAL;
   AppendArgs a{};
@@ -381,6 +390,10 @@ rtp_status rtp_prefill(const rtp_prefill_desc* d, void* stream) {
     return RTP_EINVAL;
   const int G = d->Hq / d->Hkv;
   if (G > kMaxG || d->Hkv > kMaxHkv || d->Lmax > (1 << 24)) return RTP_EUNSUPPORTED;
+  // its launches are one-dimensional, B * Hkv * (blocks per sequence) blocks: at most 2^31 - 1
+  // with a block per 16 prompt rows
+  if (!rows_ok(d->B, d->Hq) || (int64_t)d->B * d->Hkv * ((d->Lmax + 15) / 16) > INT32_MAX)
+    return RTP_EUNSUPPORTED;
   if (d->r != kR || d->d != kD || (d->kv_dtype != RTP_F16 && d->kv_dtype != RTP_BF16))
     return RTP_EUNSUPPORTED;
   if (!d->kv_is_retrieval || !scale_ok(d->scale_attn)) return RTP_EINVAL;

@@ -53,7 +53,8 @@ typedef int32_t rtp_status;
 enum {
   RTP_OK = 0,
   RTP_EINVAL = -1,        /* null/misaligned pointer, bad size or parameter */
-  RTP_EUNSUPPORTED = -2,  /* r != 16, d != 128, G or Lmax out of range, bad dtype */
+  RTP_EUNSUPPORTED = -2,  /* r != 16, d != 128, G or Lmax out of range, B x query heads
+                             above 65535 (a launch's grid dimension), bad dtype */
   RTP_EWORKSPACE = -3,    /* ws_bytes below the size query */
   RTP_EHIP = -4,          /* a HIP launch failed */
   RTP_ESCRATCH = -5       /* rtp_decode_step_noalloc: the step needs more than its fixed scratch */

@@ -317,3 +317,49 @@ def test_decode_step_noalloc_checks_before_any_device_call(lib):
     d.Hq = 30
     assert lib.rtp_decode_step_noalloc(ctypes.byref(d), None) == -1
     assert lib.rtp_decode_step_noalloc(None, None) == -1
+
+
+def test_batch_rows_beyond_the_grid_limit_are_unsupported(lib):
+    """B x query heads above 65535 would exceed a launch's y/z grid dimension (or push a
+    one-dimensional block count towards the int range): every entry point says so on the
+    host, and the size queries return 0."""
+    import head_wise_sparse_rtp_amd as m
+    # index score: B x Hr x G rows
+    assert lib.rtp_index_score(FAKE, FAKE, 1, FAKE, 8193, 1, 8, 1024, 16, 0.25, FAKE, None) == -2
+    # selection: B x H rows
+    assert lib.rtp_topp_select_workspace_size(8191, 8, 4096) > 0   # 65528 rows
+    assert lib.rtp_topp_select_workspace_size(8193, 8, 4096) == 0
+    assert lib.rtp_topk_select_workspace_size(8193, 8, 4096) == 0
+    args = [FAKE, FAKE, 8193, 8, 4096, 0.9, 0.125, FAKE, FAKE, 4096, None, None, FAKE, 1 << 40, None]
+    assert lib.rtp_topp_select(*args) == -2
+    args[5] = 64
+    assert lib.rtp_topk_select(*args) == -2
+    # sparse and window decode: B x heads x G rows
+    assert lib.rtp_sparse_decode_workspace_size(8193, 1, 8, 4096) == 0
+    assert lib.rtp_sparse_decode(FAKE, FAKE, FAKE, 1, FAKE, FAKE, 4096, 8193, 1, 8, 4096, 128,
+                                 0.088, FAKE, None, FAKE, 1 << 40, None) == -2
+    assert lib.rtp_window_decode_workspace_size(2731, 3, 8, 8192, 4) == 0
+    assert lib.rtp_window_decode(FAKE, FAKE, FAKE, 1, FAKE, 2731, 3, 8, 128, 8192, 4, 0.088, FAKE,
+                                 None, FAKE, 1 << 40, None) == -2
+    # the decode step, the cache update and the prefill: B x Hq rows
+    mask = (ctypes.c_uint8 * 4)(1, 0, 0, 0)
+    d = m.LayerDesc(2047, 32, 4, 128, 16, 4096, 8192, 4, 1, ctypes.cast(mask, ctypes.c_void_p),
+                    FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.9, 0.125, 0.25, 0.088,
+                    FAKE, None, None, None)
+    assert lib.rtp_decode_step_workspace_size(ctypes.byref(d)) > 0   # 65504 rows
+    d.B = 2048                                                         # 65536 rows
+    assert lib.rtp_decode_step_workspace_size(ctypes.byref(d)) == 0
+    assert lib.rtp_decode_step(ctypes.byref(d), FAKE, 1 << 40, None) == -2
+    a = m.AppendDesc(2049, 32, 4, 128, 16, 4096, 8192, 4, 1, ctypes.cast(mask, ctypes.c_void_p),
+                     *([FAKE] * 13))
+    assert lib.rtp_append_project(ctypes.byref(a), None) == -2
+    pd = m.PrefillDesc(2049, 32, 4, 128, 16, 4096, 8192, 4, 1, ctypes.cast(mask, ctypes.c_void_p),
+                       FAKE, FAKE, FAKE, FAKE, 0.088, FAKE, None, None, None, None, None, None,
+                       None)
+    assert lib.rtp_prefill(ctypes.byref(pd), None) == -2
+    # a long prompt over many heads: the prefill's one-dimensional grid would pass 2^31 blocks
+    pd.B, pd.Hq, pd.Hkv, pd.Lmax = 64, 64, 64, 1 << 24
+    mask64 = (ctypes.c_uint8 * 64)(*([0] * 64))
+    pd.kv_is_retrieval = ctypes.cast(mask64, ctypes.c_void_p)
+    assert lib.rtp_prefill(ctypes.byref(pd), None) == -2
+
