@@ -30,6 +30,15 @@ PEAK_HBM_GBS = 8000.0
 REPEATS = 5  # timed repeats of K steps; the median is the reported time
 
 
+def context_label(L):
+    """A context length as the metric names it: 64K, 1M, 1.5M, 12345."""
+    for unit, name in ((1 << 20, "M"), (1 << 10, "K")):
+        if L >= unit and L % (unit // 2) == 0:
+            v = L / unit
+            return ("%d%s" % (v, name)) if v == int(v) else ("%.1f%s" % (v, name))
+    return str(L)
+
+
 def hip():
     h = ctypes.CDLL("libamdhip64.so")
     h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
@@ -645,7 +654,8 @@ def main():
     ceiling = hbm_read_ceiling(torch) if not args.skip_ceiling else None
     value = bytes_step / (ms_step * 1e-3) / 1e9
     res = {
-        "metric": "decode attention us/step and achieved HBM GB/s (% of peak) at 1M context",
+        "metric": "decode attention us/step and achieved HBM GB/s (% of peak) at %s context"
+                  % context_label(wl.Lmax),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,

@@ -88,3 +88,15 @@ def test_bench_rejects_options_it_cannot_honour(argv, msg):
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0 and msg in r.stderr
     assert not r.stdout.strip()
+
+
+def test_context_label():
+    import bench
+    assert bench.context_label(1 << 20) == "1M"
+    assert bench.context_label(65536) == "64K"
+    assert bench.context_label(131072) == "128K"
+    assert bench.context_label(1 << 24) == "16M"
+    assert bench.context_label(3 << 19) == "1.5M"
+    assert bench.context_label(4096) == "4K"
+    assert bench.context_label(5000) == "5000"
+
