@@ -39,6 +39,10 @@ def context_label(L):
     return str(L)
 
 
+def decode_metric(L):
+    return "decode attention us/step and achieved HBM GB/s (% of peak) at " + context_label(L) + " context"
+
+
 def hip():
     h = ctypes.CDLL("libamdhip64.so")
     h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
@@ -654,8 +658,7 @@ def main():
     ceiling = hbm_read_ceiling(torch) if not args.skip_ceiling else None
     value = bytes_step / (ms_step * 1e-3) / 1e9
     res = {
-        "metric": "decode attention us/step and achieved HBM GB/s (% of peak) at %s context"
-                  % context_label(wl.Lmax),
+        "metric": decode_metric(wl.Lmax),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,

@@ -100,3 +100,10 @@ def test_context_label():
     assert bench.context_label(4096) == "4K"
     assert bench.context_label(5000) == "5000"
 
+
+def test_decode_metric_label():
+    import bench
+    assert bench.decode_metric(1 << 20) == \
+        "decode attention us/step and achieved HBM GB/s (% of peak) at 1M context"
+    assert bench.decode_metric(65536).endswith("at 64K context")
+
